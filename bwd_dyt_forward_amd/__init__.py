@@ -1,0 +1,27 @@
+"""Fused Dynamic Tanh (DyT) layer for AMD Instinct MI355X (gfx950).
+
+y = gamma * tanh(alpha * x) + beta over an M x N row-major activation and its
+backward (dx, dgamma, dbeta, dalpha), computed by hand-written HIP kernels
+behind a C ABI (``include/dyt.h``, library ``libdyt.so`` in this package).
+The Python functions below carry the ABI's names and only marshal tensors.
+"""
+from ._lib import (  # noqa: F401
+    DYT_BF16,
+    DYT_F32,
+    DYT_OK,
+    LIB_FILE,
+    DytError,
+    dyt_abi_version,
+    dyt_backward,
+    dyt_backward_workspace_size,
+    dyt_forward,
+    dyt_get_plan,
+    dyt_status_string,
+    lib,
+)
+
+__all__ = [
+    "DYT_F32", "DYT_BF16", "DYT_OK", "DytError", "LIB_FILE", "lib",
+    "dyt_forward", "dyt_backward", "dyt_backward_workspace_size",
+    "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
+]

@@ -1,0 +1,186 @@
+"""Python binding of the DyT C ABI (include/dyt.h): argument marshalling only.
+
+Every computation runs in the HIP library ``libdyt.so``; this module only
+checks tensor shapes, allocates outputs and workspace with PyTorch, and
+passes device pointers and torch's current HIP stream across the ABI. There
+is no CPU fallback: importing this module fails if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch first: libdyt.so then binds to the HIP runtime torch already loaded
+# (same SONAME), so torch's streams and allocations are valid across the ABI.
+import torch
+
+from .build import LIB_PATH
+
+DYT_F32 = 0
+DYT_BF16 = 1
+DYT_OK = 0
+
+_TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16}
+_CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
+
+
+class DytError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} ({status})")
+        self.status = status
+
+
+class DytPlan(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_int32), ("vec", ctypes.c_int32), ("slots", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("rows_per_tile", ctypes.c_int64),
+        ("tile_elems", ctypes.c_int64), ("col_blocks", ctypes.c_int64), ("tiles", ctypes.c_int64),
+        ("fwd_grid", ctypes.c_int64), ("bwd_grid", ctypes.c_int64), ("ws_row", ctypes.c_int64),
+        ("fin_grid", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
+    ]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+SIGNATURES = {
+    "dyt_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_workspace_size": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
+    "dyt_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                            _i64, _i64, _int, _int, _vp]),
+    "dyt_status_string": (ctypes.c_char_p, [_int]),
+    "dyt_abi_version": (_int, []),
+    "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
+}
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"DyT HIP library not found at {path}; build it first "
+            "(python -m bwd_dyt_forward_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+LIB_FILE = LIB_PATH
+
+
+def _check(fn: str, status: int) -> None:
+    if status != DYT_OK:
+        raise DytError(fn, status, lib.dyt_status_string(status).decode())
+
+
+def _code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        return {"f32": DYT_F32, "bf16": DYT_BF16}[dtype]
+    try:
+        return _TORCH_TO_CODE[dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {dtype}") from None
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_act(name: str, t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D [M, N] tensor")
+
+
+def _check_params(N: int, alpha, *vecs) -> None:
+    if alpha.numel() != 1:
+        raise ValueError("alpha must hold one element")
+    for v in vecs:
+        if v.numel() != N or not v.is_contiguous():
+            raise ValueError("gamma/beta must be contiguous with N elements")
+    dts = {alpha.dtype, *(v.dtype for v in vecs)}
+    if len(dts) != 1:
+        raise ValueError("alpha, gamma and beta must share one dtype")
+
+
+def dyt_forward(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+                y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = gamma * tanh(alpha * x) + beta on the HIP stream (async)."""
+    _check_act("x", x)
+    M, N = x.shape
+    _check_params(N, alpha, gamma, beta)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.dyt_forward(_ptr(x), _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(y), M, N,
+                         _code(x.dtype), _code(alpha.dtype), _stream(stream))
+    _check("dyt_forward", st)
+    return y
+
+
+def dyt_backward_workspace_size(M: int, N: int, x_dtype, param_dtype) -> int:
+    return int(lib.dyt_backward_workspace_size(int(M), int(N), _code(x_dtype), _code(param_dtype)))
+
+
+def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
+                 dx: torch.Tensor | None = None, dalpha: torch.Tensor | None = None,
+                 dgamma: torch.Tensor | None = None, dbeta: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None):
+    """Returns (dx, dalpha, dgamma, dbeta); enqueued on the HIP stream (async)."""
+    _check_act("x", x)
+    _check_act("dy", dy)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    M, N = x.shape
+    _check_params(N, alpha, gamma)
+    pdt = alpha.dtype
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=pdt, device=dev)
+    if dgamma is None:
+        dgamma = torch.empty(N, dtype=pdt, device=dev)
+    if dbeta is None:
+        dbeta = torch.empty(N, dtype=pdt, device=dev)
+    need = dyt_backward_workspace_size(M, N, x.dtype, pdt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.dyt_backward(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx), _ptr(dalpha),
+                          _ptr(dgamma), _ptr(dbeta), _ptr(workspace), wbytes, M, N,
+                          _code(x.dtype), _code(pdt), _stream(stream))
+    _check("dyt_backward", st)
+    return dx, dalpha, dgamma, dbeta
+
+
+def dyt_status_string(status: int) -> str:
+    return lib.dyt_status_string(int(status)).decode()
+
+
+def dyt_abi_version() -> int:
+    return int(lib.dyt_abi_version())
+
+
+def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_aligned: bool = True) -> dict:
+    p = DytPlan()
+    st = lib.dyt_get_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
+                          1 if vector_aligned else 0, ctypes.byref(p))
+    _check("dyt_get_plan", st)
+    return {name: getattr(p, name) for name, _ in DytPlan._fields_}

@@ -1,0 +1,67 @@
+"""Build step: compile the HIP sources into the in-tree C-ABI library.
+
+``python -m bwd_dyt_forward_amd.build`` (or ``build()``) runs hipcc for gfx950
+and writes ``bwd_dyt_forward_amd/libdyt.so``. Cross-compiling needs no GPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_DIR, "include")
+LIB_NAME = "libdyt.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = [os.path.join(CSRC, "dyt_api.hip")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "dyt_kernels.hpp"), os.path.join(CSRC, "dyt_math.hpp"),
+                     os.path.join(INCLUDE, "dyt.h")]
+
+ARCH = "gfx950"
+
+# No fast-math and no denormal flushing: float32 subnormals must survive
+# (x subnormal with alpha = inf gives +-gamma + beta, not NaN). Packed fp32
+# VALU ops are disabled for the device pass.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the DyT library needs ROCm's hipcc to build")
+
+
+def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile the library; returns its path. Always recompiles."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra_flags or []),
+           "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, out)
+    return out
+
+
+def is_stale(path: str = LIB_PATH) -> bool:
+    if not os.path.exists(path):
+        return True
+    t = os.path.getmtime(path)
+    return any(os.path.getmtime(d) > t for d in DEPENDS)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

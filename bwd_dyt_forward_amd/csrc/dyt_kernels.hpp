@@ -1,0 +1,459 @@
+// dyt_kernels.hpp - HIP kernels of the fused DyT layer for CDNA4 (gfx950).
+//
+// Work decomposition (shared by the forward and the first backward pass)
+// ----------------------------------------------------------------------
+// The M x N row-major tensor is cut into tiles that a 256-thread workgroup
+// streams with one 16-byte access per thread and "slot" (K slots per
+// thread, V elements per slot, so a tile holds at most 256*V*K elements):
+//
+//  * packed tiles (several whole rows; used whenever two or more rows fit a
+//    4096-element tile): tile t is the contiguous run of R rows starting at
+//    row t*R, i.e. elements [t*R*N, (t+1)*R*N). R*N*sizeof(x) is a multiple
+//    of 16, so every tile starts 16-byte aligned and the element at tile
+//    offset o always sits in column o mod N. Each thread therefore owns the
+//    same columns in every tile: its gamma/beta values live in registers for
+//    the whole kernel and its backward accumulators are per (slot, lane).
+//  * row segments (wide rows): tile t is row t / nb, column block t % nb of
+//    width Wc. The grid size is a multiple of nb, so a workgroup always sees
+//    the same column block.
+//
+// The grid is one-dimensional and persistent: workgroup w processes tiles
+// w, w + G, w + 2G, ... (G = gridDim.x). Rows never map to a grid
+// dimension, so there is no 65,535 limit on M (the Liger-Kernel pull
+// request "fix(dyt): use a 1D grid and tile small-width rows", Summary,
+// "Launch limit" and "Small widths" bullets, describes both problems for
+// its Triton kernels; this is the CDNA4 design, not a translation).
+//
+// Every tile except possibly the last (packed) takes an unmasked path. The
+// last tile masks lanes past the end of the data; the backward computes
+// those lanes and then removes them with a select, after the arithmetic,
+// so zeros loaded for missing lanes cannot inject tanh(inf * 0) = NaN into
+// the sums (same pull request, Summary, "Padding" bullet).
+//
+// Backward reduction (deterministic, no atomics)
+// ----------------------------------------------
+// Pass 1 keeps float32 accumulators per thread, then reduces them once per
+// workgroup in a fixed order: dalpha by a wavefront butterfly and a fixed
+// sum over the 4 waves; dgamma/dbeta columns through LDS (packed tiles) or
+// directly (row segments, where every column belongs to one thread). Each
+// workgroup writes one partial row [dgamma(Wcols) | dbeta(Wcols) | dalpha]
+// to the workspace. Pass 2 sums the partial rows column by column in a
+// fixed order (16 contiguous segments, then the 16 segment sums in order)
+// and rounds to the parameter dtype.
+#pragma once
+
+#include <type_traits>
+
+#include "dyt_math.hpp"
+
+namespace dyt {
+
+constexpr int kBlock = 256;       // threads per workgroup (4 wave64s)
+constexpr int kTileCap = 4096;    // elements per tile at the largest K
+constexpr int kFinBlock = 1024;   // pass-2 threads: 64 outputs x 16 segments
+constexpr int kFinSegs = kFinBlock / 64;
+
+struct Geo {
+    int64_t total;     // M * N
+    int64_t ntiles;
+    int64_t N;         // row length (elements)
+    int32_t T;         // packed: R*N elements per tile; wide: Wc
+    int32_t R;         // packed: rows per tile; wide: 1
+    int32_t nb;        // wide: column blocks per row; packed: 1
+    int32_t last_len;  // wide: columns in the last block; packed: T
+    int32_t ld;        // floats per workspace partial row
+    int32_t wcols;     // packed: N; wide: Wc (dgamma/dbeta entries per row)
+};
+
+struct FinGeo {
+    int64_t P;         // partial rows
+    int64_t N;
+    int32_t nb;
+    int32_t wc;        // wide: block width
+    int32_t wcols;
+    int32_t ld;
+    int32_t packed;
+};
+
+// ---------------------------------------------------------------- memory IO
+template <typename XT, int V> struct VecIO;
+
+template <> struct VecIO<float, 4> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <> struct VecIO<bf16_t, 8> {
+    static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8]) {
+        const uint4 t = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
+        uint4 t;
+        t.x = pack2_bf16(v[0], v[1]);
+        t.y = pack2_bf16(v[2], v[3]);
+        t.z = pack2_bf16(v[4], v[5]);
+        t.w = pack2_bf16(v[6], v[7]);
+        *reinterpret_cast<uint4*>(p) = t;
+    }
+};
+
+template <typename XT> struct VecIO<XT, 1> {
+    static __device__ __forceinline__ void load(const XT* p, float (&v)[1]) { v[0] = to_f32(p[0]); }
+    static __device__ __forceinline__ void store(XT* p, const float (&v)[1]) { p[0] = from_f32<XT>(v[0]); }
+};
+
+// First n (< V) elements only; the rest read as 0 and are not written.
+template <typename XT, int V>
+__device__ __forceinline__ void load_partial(const XT* p, int n, float (&v)[V]) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = (e < n) ? to_f32(p[e < n ? e : 0]) : 0.0f;
+}
+template <typename XT, int V>
+__device__ __forceinline__ void store_partial(XT* p, int n, const float (&v)[V]) {
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+        if (e < n) p[e] = from_f32<XT>(v[e]);
+}
+
+template <bool ACC>
+__device__ __forceinline__ float dyt_tanh(float u) {
+    if constexpr (ACC) return tanh_accurate(u);
+    else return tanh_fast(u);
+}
+template <bool ACC>
+__device__ __forceinline__ void dyt_tanh_sech2(float u, float& t, float& d) {
+    if constexpr (ACC) tanh_sech2_accurate(u, t, d);
+    else tanh_sech2_fast(u, t, d);
+}
+
+// Column block of this workgroup (row segments) and its length.
+__device__ __forceinline__ void block_columns(const Geo& g, bool packed, int64_t wg,
+                                              int64_t& col_base, int& seg_len) {
+    if (packed) {
+        col_base = 0;
+        seg_len = g.T;
+    } else {
+        const int b = (int)(wg % g.nb);
+        col_base = (int64_t)b * g.T;
+        seg_len = (b == g.nb - 1) ? g.last_len : g.T;
+    }
+}
+
+__device__ __forceinline__ void tile_extent(const Geo& g, bool packed, int64_t t,
+                                            int64_t col_base, int seg_len,
+                                            int64_t& base, int& len) {
+    if (packed) {
+        base = t * g.T;
+        const int64_t rem = g.total - base;
+        len = rem < g.T ? (int)rem : g.T;
+    } else {
+        base = (t / g.nb) * g.N + col_base;
+        len = seg_len;
+    }
+}
+
+// ---------------------------------------------------------------- forward
+// y = gamma * tanh(alpha * x) + beta.
+template <typename XT, typename PT, int V, int K, bool PACKED>
+__global__ void __launch_bounds__(kBlock)
+dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
+               const PT* __restrict__ gamma, const PT* __restrict__ beta,
+               XT* __restrict__ y, const Geo g) {
+    constexpr bool ACC = std::is_same<XT, float>::value;
+    const int tid = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const float alpha = to_f32(alpha_p[0]);
+    int64_t col_base;
+    int seg_len;
+    block_columns(g, PACKED, wg, col_base, seg_len);
+
+    float gm[K][V], bt[K][V];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int o = (k * kBlock + tid) * V + e;
+            gm[k][e] = 0.0f;
+            bt[k][e] = 0.0f;
+            if (o < seg_len) {
+                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : col_base + o;
+                gm[k][e] = to_f32(gamma[c]);
+                bt[k][e] = to_f32(beta[c]);
+            }
+        }
+
+    for (int64_t t = wg; t < g.ntiles; t += gridDim.x) {
+        int64_t base;
+        int len;
+        tile_extent(g, PACKED, t, col_base, seg_len, base, len);
+        const XT* __restrict__ xs = x + base;
+        XT* __restrict__ ys = y + base;
+        if (len == g.T) {
+            float v[K][V];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                if (o < g.T) VecIO<XT, V>::load(xs + o, v[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                if (o < g.T) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        v[k][e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[k][e]), bt[k][e]);
+                    VecIO<XT, V>::store(ys + o, v[k]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                const int n = len - o;
+                if (n <= 0) continue;
+                float v[V];
+                if (n >= V) VecIO<XT, V>::load(xs + o, v);
+                else load_partial<XT, V>(xs + o, n, v);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
+                if (n >= V) VecIO<XT, V>::store(ys + o, v);
+                else store_partial<XT, V>(ys + o, n, v);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- backward
+// Pass 1: dx, plus one float32 partial row per workgroup.
+template <typename XT, typename PT, int V, int K, bool PACKED>
+__global__ void __launch_bounds__(kBlock)
+dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
+                       const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
+                       XT* __restrict__ dx, float* __restrict__ ws, const Geo g) {
+    constexpr bool ACC = std::is_same<XT, float>::value;
+    const int tid = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const float alpha = to_f32(alpha_p[0]);
+    int64_t col_base;
+    int seg_len;
+    block_columns(g, PACKED, wg, col_base, seg_len);
+
+    float gm[K][V], ag[K][V], ab[K][V];
+    float aa = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int o = (k * kBlock + tid) * V + e;
+            ag[k][e] = 0.0f;
+            ab[k][e] = 0.0f;
+            gm[k][e] = 0.0f;
+            if (o < seg_len) {
+                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : col_base + o;
+                gm[k][e] = to_f32(gamma[c]);
+            }
+        }
+
+    for (int64_t t = wg; t < g.ntiles; t += gridDim.x) {
+        int64_t base;
+        int len;
+        tile_extent(g, PACKED, t, col_base, seg_len, base, len);
+        const XT* __restrict__ xs = x + base;
+        const XT* __restrict__ ds = dy + base;
+        XT* __restrict__ os = dx + base;
+        if (len == g.T) {
+            float xv[K][V], dv[K][V];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                if (o < g.T) {
+                    VecIO<XT, V>::load(xs + o, xv[k]);
+                    VecIO<XT, V>::load(ds + o, dv[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                if (o < g.T) {
+                    float out[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float th, sd;
+                        dyt_tanh_sech2<ACC>(alpha * xv[k][e], th, sd);
+                        const float gd = (dv[k][e] * gm[k][e]) * sd;   // dy*gamma*sech^2
+                        out[e] = gd * alpha;
+                        ag[k][e] = __builtin_fmaf(dv[k][e], th, ag[k][e]);
+                        ab[k][e] += dv[k][e];
+                        aa = __builtin_fmaf(gd, xv[k][e], aa);
+                    }
+                    VecIO<XT, V>::store(os + o, out);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int o = (k * kBlock + tid) * V;
+                const int n = len - o;
+                if (n <= 0) continue;
+                float xv[V], dv[V], out[V];
+                if (n >= V) {
+                    VecIO<XT, V>::load(xs + o, xv);
+                    VecIO<XT, V>::load(ds + o, dv);
+                } else {
+                    load_partial<XT, V>(xs + o, n, xv);
+                    load_partial<XT, V>(ds + o, n, dv);
+                }
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float th, sd;
+                    dyt_tanh_sech2<ACC>(alpha * xv[e], th, sd);
+                    const float gd = (dv[e] * gm[k][e]) * sd;
+                    out[e] = gd * alpha;
+                    // Mask after the arithmetic: a lane past the end computed
+                    // on zeros (tanh(inf * 0) = NaN when alpha = inf); the
+                    // select drops whatever it produced.
+                    const bool ok = e < n;
+                    const float cg = dv[e] * th;
+                    const float ca = gd * xv[e];
+                    ag[k][e] += ok ? cg : 0.0f;
+                    ab[k][e] += ok ? dv[e] : 0.0f;
+                    aa += ok ? ca : 0.0f;
+                }
+                if (n >= V) VecIO<XT, V>::store(os + o, out);
+                else store_partial<XT, V>(os + o, n, out);
+            }
+        }
+    }
+
+    // ---- workgroup reduction into one partial row
+    float* __restrict__ wrow = ws + wg * (int64_t)g.ld;
+    __shared__ float red[kBlock / 64];
+    float v = aa;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+
+    if constexpr (PACKED) {
+        __shared__ float sh[K * kBlock * V];
+        __shared__ float sh2[kBlock];
+        const int N = (int)g.N;
+        const int R = g.R;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const int o = (k * kBlock + tid) * V + e;
+                    if (o < g.T) sh[o] = pass ? ab[k][e] : ag[k][e];
+                }
+            __syncthreads();
+            float* __restrict__ dst = wrow + (pass ? g.wcols : 0);
+            if (N <= kBlock) {
+                // groups of N threads; group j sums rows j, j+G, ... in order
+                const int G = kBlock / N;
+                if (tid < G * N) {
+                    const int c = tid % N;
+                    float s = 0.0f;
+                    for (int r = tid / N; r < R; r += G) s += sh[r * N + c];
+                    sh2[tid] = s;
+                }
+                __syncthreads();
+                if (tid < N) {
+                    float s = sh2[tid];
+                    for (int j = 1; j < G; ++j) s += sh2[j * N + tid];
+                    dst[tid] = s;
+                }
+            } else {
+                for (int c = tid; c < N; c += kBlock) {
+                    float s = 0.0f;
+                    for (int r = 0; r < R; ++r) s += sh[r * N + c];
+                    dst[c] = s;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int o = (k * kBlock + tid) * V + e;
+                if (o < seg_len) {
+                    wrow[o] = ag[k][e];
+                    wrow[g.wcols + o] = ab[k][e];
+                }
+            }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float s = red[0];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; ++w) s += red[w];
+        wrow[2 * g.wcols] = s;
+    }
+}
+
+// Pass 2: out[j] = fixed-order sum of the partial rows' column j, rounded to
+// the parameter dtype. Outputs j < N are dgamma, N <= j < 2N dbeta, j = 2N
+// dalpha. Lane = output, wave = one of 16 contiguous row segments.
+template <typename PT>
+__global__ void __launch_bounds__(kFinBlock)
+dyt_bwd_finish_kernel(const float* __restrict__ ws, PT* __restrict__ dgamma,
+                      PT* __restrict__ dbeta, PT* __restrict__ dalpha, const FinGeo f) {
+    const int lane = threadIdx.x & 63;
+    const int seg = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t nout = 2 * f.N + 1;
+    float acc = 0.0f;
+    if (j < nout) {
+        int64_t row0 = 0, step = 1, nrows = f.P, off;
+        if (j < 2 * f.N) {
+            const bool isb = j >= f.N;
+            const int64_t c = isb ? j - f.N : j;
+            if (f.packed) {
+                off = (isb ? f.wcols : 0) + c;
+            } else {
+                const int64_t b = c / f.wc;
+                row0 = b;
+                step = f.nb;
+                nrows = f.P / f.nb;
+                off = (isb ? f.wc : 0) + (c - b * f.wc);
+            }
+        } else {
+            off = 2 * (int64_t)f.wcols;
+        }
+        const int64_t i0 = seg * nrows / kFinSegs;
+        const int64_t i1 = (seg + 1) * nrows / kFinSegs;
+        const int64_t stride = step * f.ld;
+        const float* __restrict__ p = ws + (row0 + i0 * step) * f.ld + off;
+#pragma unroll 8
+        for (int64_t i = i0; i < i1; ++i, p += stride) acc += *p;
+    }
+    __shared__ float red[kFinSegs][64];
+    red[seg][lane] = acc;
+    __syncthreads();
+    if (seg == 0 && j < nout) {
+        float s = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < kFinSegs; ++q) s += red[q][lane];
+        const PT out = from_f32<PT>(s);
+        if (j < f.N) dgamma[j] = out;
+        else if (j < 2 * f.N) dbeta[j - f.N] = out;
+        else dalpha[0] = out;
+    }
+}
+
+}  // namespace dyt

@@ -1,0 +1,158 @@
+// dyt_math.hpp - float32 device math for the DyT kernels (gfx950).
+//
+// The layer needs t = tanh(u) and, in the backward, d = sech^2(u) = 1 - t^2
+// for u = alpha * x. 1 - t*t cancels catastrophically once |u| grows (in
+// float32 it loses 1e-6 relative accuracy near |u| = 2 and a whole bfloat16
+// ulp near |u| = 6), so both quantities are built from e = exp(-2|u|):
+//
+//   tanh|u|  = (1 - e) / (1 + e)          sech^2 u = 4 e / (1 + e)^2
+//
+// which has no cancellation for |u| away from 0. Near 0, 1 - e cancels
+// instead, so small |u| takes a short odd series for tanh (and 1 - t^2,
+// which is then >= 0.87 and exact enough).
+//
+// Two variants, chosen by the storage dtype of x:
+//   * accurate (float32 outputs): e via Cody & Waite's additive range
+//     reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
+//     Functions", 1980) with the hardware 2^x on the reduced argument, a
+//     Newton-refined reciprocal, and the Taylor series of tanh up to u^13
+//     for |u| < 0.35 (coefficients 2^2n (2^2n - 1) B_2n / (2n)!, B the
+//     Bernoulli numbers). About 3-5 float32 ulp on t and on sech^2.
+//   * fast (bfloat16 outputs): e straight from the hardware 2^x and 1/x
+//     (about 1e-5 relative at |u| = 50, far below half a bfloat16 ulp);
+//     tanh u ~= u below 2^-6 (relative error < 1e-4).
+//
+// IEEE behaviour is kept on purpose: u = +-inf gives t = +-1, d = 0; NaN
+// propagates. Branches are selects evaluated after both sides are
+// computed; NaN is never clamped away (v_min/v_max would drop it).
+// float32 subnormals are not flushed (the library is built without
+// fast-math or denormal flushing).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dyt {
+
+// log2(e) and -2*log2(e), rounded to float32.
+constexpr float kLog2e = 0x1.715476p+0f;
+constexpr float kMinus2Log2e = -0x1.715476p+1f;
+// ln 2 split into a float32 head and the float32 rounding of the remainder.
+constexpr float kLn2Hi = 0x1.62e43p-1f;
+constexpr float kLn2Lo = -0x1.05c61p-29f;
+
+__device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// copysign as one bitfield insert: magnitude bits of m, sign bit of s.
+__device__ __forceinline__ float copy_sign(float m, float s) {
+    return __builtin_copysignf(m, s);
+}
+
+// e^z for z <= 0, z possibly -inf or NaN. Cody-Waite: z = k ln2 + r with
+// |r| <= ln2/2; e^z = 2^k * 2^(r log2 e). The fused multiply-adds carry
+// k*ln2 beyond float32 precision. Below -104, e^z rounds to 0 in float32,
+// so z is replaced by -104 there (a select, so NaN stays NaN and -inf maps
+// to an exact 0).
+__device__ __forceinline__ float exp_nonpos_accurate(float z) {
+    z = (z < -104.0f) ? -104.0f : z;
+    const float k = __builtin_rintf(z * kLog2e);
+    float r = __builtin_fmaf(-k, kLn2Hi, z);
+    r = __builtin_fmaf(-k, kLn2Lo, r);
+    const float er = hw_exp2(r * kLog2e);
+    return __builtin_amdgcn_ldexpf(er, (int)k);
+}
+
+// Taylor series of tanh(u)/u - 1 in s = u^2 (terms through s^6, u^13).
+__device__ __forceinline__ float tanh_series_tail(float s) {
+    float p = 0x1.d6d3d0p-9f;                  //  21844/6081075
+    p = __builtin_fmaf(p, s, -0x1.226e36p-7f); // -1382/155925
+    p = __builtin_fmaf(p, s, 0x1.664f48p-6f);  //  62/2835
+    p = __builtin_fmaf(p, s, -0x1.ba1ba2p-5f); // -17/315
+    p = __builtin_fmaf(p, s, 0x1.111112p-3f);  //  2/15
+    p = __builtin_fmaf(p, s, -0x1.555556p-2f); // -1/3
+    return p;
+}
+
+constexpr float kAccurateSmall = 0.35f;
+
+// Accurate tanh(u) and sech^2(u) (float32 outputs).
+__device__ __forceinline__ void tanh_sech2_accurate(float u, float& t, float& d) {
+    const float a = __builtin_fabsf(u);
+    // large |u|
+    const float e = exp_nonpos_accurate(-2.0f * a);
+    const float p = 1.0f + e;
+    float r = hw_rcp(p);
+    r = __builtin_fmaf(r, __builtin_fmaf(-p, r, 1.0f), r);   // Newton step
+    const float tl = (1.0f - e) * r;
+    const float dl = ((4.0f * e) * r) * r;
+    // small |u|
+    const float s = u * u;
+    const float ts = __builtin_fmaf(u * s, tanh_series_tail(s), u);
+    const float ds = __builtin_fmaf(-ts, ts, 1.0f);
+    const bool small = a < kAccurateSmall;
+    t = small ? ts : copy_sign(tl, u);
+    d = small ? ds : dl;
+}
+
+__device__ __forceinline__ float tanh_accurate(float u) {
+    const float a = __builtin_fabsf(u);
+    const float e = exp_nonpos_accurate(-2.0f * a);
+    const float p = 1.0f + e;
+    float r = hw_rcp(p);
+    r = __builtin_fmaf(r, __builtin_fmaf(-p, r, 1.0f), r);
+    const float tl = (1.0f - e) * r;
+    const float s = u * u;
+    const float ts = __builtin_fmaf(u * s, tanh_series_tail(s), u);
+    return (a < kAccurateSmall) ? ts : copy_sign(tl, u);
+}
+
+constexpr float kFastSmall = 0x1p-6f;
+
+// Fast tanh(u) (bfloat16 outputs): e4 = 4 e^{-2|u|} from one hardware 2^x
+// (the factor 4 rides in the exponent), t = (1 - e)/(1 + e).
+__device__ __forceinline__ float tanh_fast(float u) {
+    const float a = __builtin_fabsf(u);
+    const float e4 = hw_exp2(__builtin_fmaf(a, kMinus2Log2e, 2.0f));
+    const float r = hw_rcp(__builtin_fmaf(e4, 0.25f, 1.0f));
+    const float tl = __builtin_fmaf(e4, -0.25f, 1.0f) * r;
+    return (a < kFastSmall) ? u : copy_sign(tl, u);
+}
+
+// Fast tanh and sech^2 for the backward. t only feeds the dgamma sums, where
+// its absolute error (~1e-7 near u = 0) is what matters, so no small branch.
+__device__ __forceinline__ void tanh_sech2_fast(float u, float& t, float& d) {
+    const float a = __builtin_fabsf(u);
+    const float e4 = hw_exp2(__builtin_fmaf(a, kMinus2Log2e, 2.0f));
+    const float r = hw_rcp(__builtin_fmaf(e4, 0.25f, 1.0f));
+    t = copy_sign(__builtin_fmaf(e4, -0.25f, 1.0f) * r, u);
+    d = (e4 * r) * r;
+}
+
+// ------------------------------------------------------------ storage types
+// bfloat16 is carried as its raw 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+    return __builtin_bit_cast(float, (uint32_t)v.bits << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    const b2 r = __builtin_convertvector(v, b2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+    return bf16_t{(uint16_t)(pack2_bf16(v, 0.0f) & 0xffffu)};
+}
+
+}  // namespace dyt

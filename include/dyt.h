@@ -1,0 +1,163 @@
+/*
+ * dyt.h - C ABI of the fused Dynamic Tanh (DyT) layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer, over an M x N row-major activation x with a scalar alpha and
+ * per-column gamma and beta:
+ *
+ *   forward   y[i,j]   = gamma[j] * tanh(alpha * x[i,j]) + beta[j]
+ *   backward  dx[i,j]  = dy[i,j] * gamma[j] * alpha * sech^2(alpha * x[i,j])
+ *             dgamma[j] = sum_i dy[i,j] * tanh(alpha * x[i,j])
+ *             dbeta[j]  = sum_i dy[i,j]
+ *             dalpha    = sum_{i,j} dy[i,j] * gamma[j] * x[i,j] * sech^2(alpha x[i,j])
+ *
+ * with sech^2 = 1 - tanh^2. Source: the Liger-Kernel pull request "fix(dyt):
+ * use a 1D grid and tile small-width rows" (#1616). Its Summary fixes the
+ * behaviour this ABI keeps:
+ *   - "Launch limit": any number of rows is accepted (a flat 1D grid; no
+ *     65,535-block limit on rows).
+ *   - "Small widths": rows of up to 256 columns are packed several to a
+ *     workgroup tile; wider rows keep one row per tile.
+ *   - "Padding": lanes past the end of the data are removed from the
+ *     reductions after the arithmetic, so alpha = +inf cannot inject
+ *     tanh(inf * 0) = NaN into dgamma, dbeta or dalpha.
+ *   - "Precision": dalpha, dgamma and dbeta are returned in the parameter
+ *     dtype; y and dx keep the dtype of x.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *     device). Layout is contiguous row-major; the row stride is N elements.
+ *     alpha, dalpha point to one element; gamma, beta, dgamma, dbeta to N.
+ *   - x, dy, y, dx have the x dtype; alpha, gamma, beta, dalpha, dgamma,
+ *     dbeta have the parameter dtype. Supported dtypes: DYT_F32, DYT_BF16
+ *     for both.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is only enqueued; no call synchronises. Outputs are valid once
+ *     the stream reaches that point; inputs must stay unchanged until then.
+ *   - Ownership: the caller owns every buffer; the library allocates no
+ *     memory and keeps no state beyond immutable tables.
+ *   - Outputs overwrite their buffers (they are not accumulated into) and
+ *     must not overlap any input.
+ *   - Alignment: every pointer must be aligned to its element size. Tensors
+ *     whose x/dy/y/dx pointers are 16-byte aligned use 16-byte vector
+ *     memory access; otherwise an element-wise variant with identical
+ *     results runs. The workspace must be 16-byte aligned.
+ *   - Errors: every call returns DYT_OK (0) or a positive dyt_status.
+ *     Arguments are validated before anything is enqueued, so on error no
+ *     output is written. The library never prints and never throws.
+ *     Faults during kernel execution surface at stream synchronisation.
+ *   - Determinism: results are bitwise reproducible run to run. The
+ *     parameter-gradient sums use a fixed summation order that depends only
+ *     on (M, N, x dtype, alignment class); no floating-point atomics.
+ *   - Arithmetic is float32 throughout (accumulation included); bfloat16
+ *     results are rounded to nearest even. float32 subnormals are kept.
+ */
+#ifndef DYT_H_
+#define DYT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DYT_ABI_VERSION 1
+
+typedef enum dyt_dtype {
+    DYT_F32 = 0,  /* IEEE binary32 */
+    DYT_BF16 = 1  /* bfloat16: 8 exponent bits, 7 fraction bits */
+} dyt_dtype;
+
+typedef enum dyt_status {
+    DYT_OK = 0,
+    DYT_ERR_INVALID_ARG = 1,         /* null pointer with a non-empty extent, M < 0, N < 0,
+                                        size overflow, or an output overlapping an input */
+    DYT_ERR_UNSUPPORTED_DTYPE = 2,   /* dtype code outside dyt_dtype */
+    DYT_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < dyt_backward_workspace_size(...) */
+    DYT_ERR_MISALIGNED = 4,          /* pointer not aligned to its element size, or
+                                        workspace not 16-byte aligned */
+    DYT_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+} dyt_status;
+
+/*
+ * Forward: y = gamma * tanh(alpha * x) + beta.
+ *   x      [M, N] x_dtype, read
+ *   alpha  [1]    param_dtype, read
+ *   gamma  [N]    param_dtype, read
+ *   beta   [N]    param_dtype, read
+ *   y      [M, N] x_dtype, written
+ * M == 0 or N == 0: nothing is enqueued and DYT_OK is returned (pointers may
+ * then be NULL).
+ */
+int dyt_forward(const void* x, const void* alpha, const void* gamma, const void* beta,
+                void* y, int64_t M, int64_t N, int x_dtype, int param_dtype,
+                void* stream);
+
+/*
+ * Bytes of device workspace dyt_backward needs for this problem (a multiple
+ * of 16; 0 when M == 0 or N == 0). Returns 0 as well for invalid arguments,
+ * which dyt_backward then reports. Pure host function.
+ */
+size_t dyt_backward_workspace_size(int64_t M, int64_t N, int x_dtype, int param_dtype);
+
+/*
+ * Backward of the forward above, recomputing tanh(alpha * x) from x.
+ *   x          [M, N] x_dtype, read
+ *   dy         [M, N] x_dtype, read (upstream gradient of y)
+ *   alpha      [1]    param_dtype, read
+ *   gamma      [N]    param_dtype, read
+ *   dx         [M, N] x_dtype, written
+ *   dalpha     [1]    param_dtype, written (always, also when M*N == 0: 0)
+ *   dgamma     [N]    param_dtype, written (zeros when M == 0)
+ *   dbeta      [N]    param_dtype, written (zeros when M == 0)
+ *   workspace  device scratch of workspace_bytes bytes, 16-byte aligned, no
+ *              initial contents required; may be NULL when the required
+ *              size is 0. Contents are undefined afterwards.
+ * Two kernels run in order on the stream: a pass that writes dx and one
+ * float32 partial row of (dgamma, dbeta, dalpha) per workgroup into the
+ * workspace, and a pass that sums those rows in a fixed order and rounds
+ * them to the parameter dtype.
+ */
+int dyt_backward(const void* x, const void* dy, const void* alpha, const void* gamma,
+                 void* dx, void* dalpha, void* dgamma, void* dbeta,
+                 void* workspace, size_t workspace_bytes,
+                 int64_t M, int64_t N, int x_dtype, int param_dtype,
+                 void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* dyt_status_string(int status);
+
+/* DYT_ABI_VERSION of the loaded library. */
+int dyt_abi_version(void);
+
+/*
+ * Launch geometry the library would use (for tests and reports; pure host
+ * function, no HIP calls). vector_aligned != 0 describes 16-byte aligned
+ * x/dy/y/dx pointers. Returns DYT_OK or the status the compute calls would
+ * return for these sizes and dtypes.
+ */
+typedef struct dyt_plan {
+    int32_t packed;        /* 1: tiles of several whole rows (N <= 256); 0: row segments */
+    int32_t vec;           /* elements per vector memory access (16 bytes, or 1) */
+    int32_t slots;         /* vector slots per thread per tile */
+    int32_t block;         /* threads per workgroup */
+    int64_t rows_per_tile; /* packed: rows per tile; wide: 1 */
+    int64_t tile_elems;    /* packed: rows_per_tile * N; wide: columns per row segment */
+    int64_t col_blocks;    /* wide: row segments per row; packed: 1 */
+    int64_t tiles;         /* number of tiles */
+    int64_t fwd_grid;      /* forward workgroups */
+    int64_t bwd_grid;      /* backward pass-1 workgroups = partial rows */
+    int64_t ws_row;        /* floats per partial row */
+    int64_t fin_grid;      /* backward pass-2 workgroups */
+    int64_t ws_bytes;      /* workspace bytes this plan uses */
+} dyt_plan;
+
+int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
+                 dyt_plan* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYT_H_ */

@@ -102,7 +102,7 @@ class ForwardResult:
 
 @dataclass
 class BackwardResult:
-    dx: np.ndarray       # float64 (M, N), unrounded
+    dx: np.ndarray       # float64 (M, N), unrounded (None if not requested)
     dgamma: np.ndarray   # float64 (N,)
     dbeta: np.ndarray    # float64 (N,)
     dalpha: float        # float64 scalar
@@ -134,13 +134,16 @@ def forward(x, alpha, gamma, beta) -> ForwardResult:
     return ForwardResult(y, scale)
 
 
-def backward(x, dy, alpha, gamma) -> BackwardResult:
-    """fp64 backward over a full (M, N) input, processed in row chunks."""
+def backward(x, dy, alpha, gamma, want_dx: bool = True) -> BackwardResult:
+    """fp64 backward over a full (M, N) input, processed in row chunks.
+
+    With want_dx=False only the reductions are kept (dx is None), which
+    bounds memory on large inputs."""
     x = np.asarray(x)
     M, N = x.shape
     a = float(_f64(alpha).reshape(-1)[0])
     g = _f64(gamma).reshape(N)
-    dx = np.empty((M, N), dtype=np.float64)
+    dx = np.empty((M, N), dtype=np.float64) if want_dx else None
     dgamma = np.zeros(N)
     dbeta = np.zeros(N)
     dalpha = 0.0
@@ -151,7 +154,8 @@ def backward(x, dy, alpha, gamma) -> BackwardResult:
         xc = _f64(x[r0:r1])
         dyc = _f64(dy[r0:r1])
         dxc, tg, tb, ta = backward_core(xc, dyc, a, g)
-        dx[r0:r1] = dxc
+        if want_dx:
+            dx[r0:r1] = dxc
         dgamma += tg.sum(axis=0)
         dbeta += tb.sum(axis=0)
         dalpha += float(ta.sum())

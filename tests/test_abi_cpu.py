@@ -1,0 +1,173 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, plans sensible geometry, and rejects invalid arguments
+before touching the HIP runtime (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dyt.h")
+
+
+@pytest.fixture(scope="module")
+def dyt():
+    import __graft_entry__ as ge
+    ge._ensure_built()
+    import bwd_dyt_forward_amd as m
+    return m
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(dyt_[a-z_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted([
+        "dyt_forward", "dyt_backward", "dyt_backward_workspace_size", "dyt_status_string",
+        "dyt_abi_version", "dyt_get_plan"])
+
+
+def test_library_exports_every_declared_symbol(dyt):
+    for name in _declared_functions():
+        assert hasattr(dyt.lib, name), name
+    # and they are real dynamic symbols of the .so
+    out = os.popen(f"nm -D --defined-only {dyt.LIB_FILE}").read()
+    for name in _declared_functions():
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported"
+
+
+def test_no_cpu_fallback_in_product_path():
+    """The package's Python code calls only the C ABI (no oracle, no numpy math)."""
+    pkg = os.path.join(ROOT, "bwd_dyt_forward_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("oracle/", ""), fn
+            assert "torch.tanh" not in src and "np.tanh" not in src, fn
+
+
+def test_version_and_status_strings(dyt):
+    assert dyt.dyt_abi_version() == 1
+    names = [dyt.dyt_status_string(i) for i in range(6)]
+    assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
+                     "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]
+    assert dyt.dyt_status_string(99) == "DYT_ERR_UNKNOWN"
+
+
+CONFIG_SHAPES = [
+    (1024, 64, "f32"), (65537, 16, "bf16"), (100003, 17, "f32"), (100003, 100, "f32"),
+    (100003, 255, "f32"), (32768, 4096, "bf16"), (4194304, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,xdt", CONFIG_SHAPES)
+@pytest.mark.parametrize("vec", [True, False])
+def test_plan_invariants(dyt, M, N, xdt, vec):
+    p = dyt.dyt_get_plan(M, N, xdt, "f32", vec)
+    sx = 4 if xdt == "f32" else 2
+    cap = p["block"] * p["vec"] * p["slots"]
+    assert p["block"] == 256
+    assert p["vec"] == (16 // sx if vec and (p["packed"] or (N * sx) % 16 == 0) else 1)
+    assert 1 <= p["tile_elems"] <= cap <= 4096
+    if p["packed"]:
+        R = p["rows_per_tile"]
+        assert p["tile_elems"] == R * N and p["col_blocks"] == 1
+        assert p["tiles"] == -(-M // R)
+        if p["vec"] > 1:
+            assert (R * N * sx) % 16 == 0, "packed tiles must stay 16-byte aligned"
+    else:
+        assert p["rows_per_tile"] == 1
+        assert p["col_blocks"] * p["tile_elems"] >= N > (p["col_blocks"] - 1) * p["tile_elems"]
+        assert p["tiles"] == M * p["col_blocks"]
+        assert p["bwd_grid"] % p["col_blocks"] == 0 and p["fwd_grid"] % p["col_blocks"] == 0
+    assert 1 <= p["fwd_grid"] <= p["tiles"] and 1 <= p["bwd_grid"] <= p["tiles"]
+    wcols = N if p["packed"] else p["tile_elems"]
+    assert p["ws_row"] >= 2 * wcols + 1 and p["ws_row"] % 4 == 0
+    assert p["ws_bytes"] == p["bwd_grid"] * p["ws_row"] * 4
+    assert p["fin_grid"] == -(-(2 * N + 1) // 64)
+    ws = dyt.dyt_backward_workspace_size(M, N, xdt, "f32")
+    assert ws >= p["ws_bytes"] and ws % 16 == 0
+
+
+def test_plan_uses_1d_grid_beyond_65535_rows(dyt):
+    """More than 65,535 rows: still one grid dimension, tiles cover every row."""
+    p = dyt.dyt_get_plan(65537, 16, "bf16", "f32")
+    assert p["tiles"] * p["rows_per_tile"] >= 65537
+    p = dyt.dyt_get_plan(10 ** 7, 4096, "bf16", "f32")
+    assert p["tiles"] == 10 ** 7 and p["bwd_grid"] <= 4096
+
+
+def test_plan_narrow_rows_are_packed(dyt):
+    for N in (1, 2, 3, 16, 17, 32, 64, 100, 255, 256):
+        p = dyt.dyt_get_plan(100003, N, "bf16", "f32")
+        assert p["packed"] == 1 and p["rows_per_tile"] >= 2, N
+    p = dyt.dyt_get_plan(32768, 4096, "bf16", "f32")
+    assert p["packed"] == 0 and p["col_blocks"] == 1
+    p = dyt.dyt_get_plan(64, 20000, "bf16", "f32")
+    assert p["packed"] == 0 and p["col_blocks"] >= 5
+
+
+def test_workspace_size_empty_and_invalid(dyt):
+    assert dyt.dyt_backward_workspace_size(0, 64, "f32", "f32") == 0
+    assert dyt.dyt_backward_workspace_size(64, 0, "f32", "f32") == 0
+    assert dyt.dyt_backward_workspace_size(-1, 64, "f32", "f32") == 0
+    assert dyt.dyt_backward_workspace_size(4, 4, 7, 0) == 0
+
+
+# ----------------------------------------------------- error paths (no HIP)
+# Pointer values below are never dereferenced: validation fails first.
+A16 = 0x10000          # a 16-byte aligned fake device address
+F32, BF16 = 0, 1
+E_OK, E_ARG, E_DT, E_WS, E_AL = 0, 1, 2, 3, 4
+
+
+def _fwd(dyt, x=A16, a=A16 + 0x100000, g=A16 + 0x200000, b=A16 + 0x300000, y=A16 + 0x400000,
+         M=4, N=4, xdt=F32, pdt=F32):
+    return dyt.lib.dyt_forward(x, a, g, b, y, M, N, xdt, pdt, None)
+
+
+def _bwd(dyt, x=A16, dy=A16 + 0x100000, a=A16 + 0x200000, g=A16 + 0x300000, dx=A16 + 0x400000,
+         da=A16 + 0x500000, dg=A16 + 0x600000, db=A16 + 0x700000, ws=A16 + 0x800000,
+         wsb=1 << 20, M=4, N=4, xdt=F32, pdt=F32):
+    return dyt.lib.dyt_backward(x, dy, a, g, dx, da, dg, db, ws, wsb, M, N, xdt, pdt, None)
+
+
+def test_forward_error_codes(dyt):
+    assert _fwd(dyt, xdt=2) == E_DT
+    assert _fwd(dyt, pdt=-1) == E_DT
+    assert _fwd(dyt, M=-1) == E_ARG
+    assert _fwd(dyt, N=-3) == E_ARG
+    assert _fwd(dyt, M=2 ** 62, N=2 ** 10) == E_ARG                # size overflow
+    for kw in ("x", "a", "g", "b", "y"):
+        assert _fwd(dyt, **{kw: None}) == E_ARG, kw
+    assert _fwd(dyt, x=A16 + 2) == E_AL                            # f32 needs 4-byte alignment
+    assert _fwd(dyt, y=A16 + 1, xdt=BF16) == E_AL
+    assert _fwd(dyt, g=A16 + 0x200002) == E_AL
+    assert _fwd(dyt, y=A16 + 8) == E_ARG                           # y overlaps x
+    assert _fwd(dyt, y=A16 + 0x200000 - 8) == E_ARG                # y overlaps gamma
+    # empty problems enqueue nothing and accept NULL pointers
+    assert _fwd(dyt, x=None, a=None, g=None, b=None, y=None, M=0) == E_OK
+    assert _fwd(dyt, x=None, a=None, g=None, b=None, y=None, N=0) == E_OK
+
+
+def test_backward_error_codes(dyt):
+    need = dyt.dyt_backward_workspace_size(4, 4, F32, F32)
+    assert need > 0
+    assert _bwd(dyt, xdt=5) == E_DT
+    assert _bwd(dyt, M=-1) == E_ARG
+    for kw in ("x", "dy", "a", "g", "dx", "da", "dg", "db", "ws"):
+        assert _bwd(dyt, **{kw: None}) == E_ARG, kw
+    assert _bwd(dyt, wsb=need - 1) == E_WS
+    assert _bwd(dyt, ws=A16 + 0x800004) == E_AL                    # workspace needs 16 bytes
+    assert _bwd(dyt, dx=A16 + 0x400002) == E_AL
+    assert _bwd(dyt, da=A16 + 0x500001, pdt=BF16) == E_AL
+    assert _bwd(dyt, dx=A16 + 0x100000) == E_ARG                   # dx aliases dy
+    assert _bwd(dyt, dg=A16 + 0x700000) == E_ARG                   # dgamma aliases dbeta
+    assert _bwd(dyt, ws=A16) == E_ARG                              # workspace aliases x
+    # dalpha is always written, so it is always required
+    assert _bwd(dyt, da=None, M=0) == E_ARG

@@ -222,3 +222,17 @@ def from_arrays(x, dy, alpha, gamma, beta, x_dtype: str, p_dtype: str,
                   np.ascontiguousarray(gamma, dtype=np.float32),
                   np.ascontiguousarray(beta, dtype=np.float32),
                   x_dtype, p_dtype, {})
+
+
+def custom(M: int, N: int, x_dtype: str = "f32", p_dtype: str = "f32", alpha: float = 0.5,
+           x_sigma: float = 1.0, seed: int = 0) -> Inputs:
+    """Extra shapes for parity sweeps: x, dy ~ N(0, x_sigma), gamma ~ N(1, 0.1),
+    beta ~ N(0, 0.1), same draw order and quantisation as the named workloads."""
+    rng = np.random.default_rng(seed)
+    x = _normal_matrix(rng, M, N, x_sigma, x_dtype)
+    dy = _normal_matrix(rng, M, N, x_sigma, x_dtype)
+    gamma = _param(rng, ("normal", 1.0, 0.1), N, p_dtype)
+    beta = _param(rng, ("normal", 0.0, 0.1), N, p_dtype)
+    a = _quantise(np.array([alpha], dtype=np.float32), p_dtype)
+    return Inputs(f"custom_{M}x{N}_{x_dtype}_{p_dtype}", x, dy, a, gamma, beta, x_dtype, p_dtype,
+                  {"seed": seed})
