@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused DyT layer on one MI355X: one step = forward +
+backward (both passes) over one batch of synthetic input resident in HBM.
+
+Prints ONE JSON line on stdout:
+  value        whole-step effective HBM throughput (GB/s) = algorithmic bytes
+               of forward + backward / measured step time
+  roofline     the dominant kernel (backward pass 1) against the 8 TB/s HBM
+               peak: algorithmic bytes per launch / mean launch duration from
+               HIP events recorded on the launch stream inside the timed loop
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
+               workload, on one pinned host core
+Algorithmic bytes (sx = x dtype size, sp = parameter dtype size):
+  forward   2 M N sx + (2N + 1) sp      backward 3 M N sx + (3N + 2) sp
+  pass 1    3 M N sx + (N + 1) sp       pass 2   (2N + 1) sp
+(workspace traffic of the backward is excluded from the algorithmic bytes).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "c4_32768x4096_bf16"        # the transformer-block shape the 80% target names
+SECONDARY = "c5_4194304x32_bf16_outliers"  # the narrow-row bulk shape the 60% target names
+HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", f)
+                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(M: int, N: int, sx: int, sp: int) -> dict:
+    return {
+        "fwd": 2 * M * N * sx + (2 * N + 1) * sp,
+        "bwd": 3 * M * N * sx + (3 * N + 2) * sp,
+        "pass1": 3 * M * N * sx + (N + 1) * sp,
+        "pass2": (2 * N + 1) * sp,
+    }
+
+
+def measure(dyt, torch, name: str, steps: int, warmup: int) -> dict:
+    import workloads
+    cfg = workloads.CONFIGS[name]
+    t0 = time.perf_counter()
+    inp = workloads.generate(name)
+    log(f"[bench] {name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    xdt, pdt = tdt[inp.x_dtype], tdt[inp.p_dtype]
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp.x).to(dev).to(xdt)
+    dy = torch.from_numpy(inp.dy).to(dev).to(xdt)
+    a = torch.from_numpy(inp.alpha).to(dev).to(pdt)
+    g = torch.from_numpy(inp.gamma).to(dev).to(pdt)
+    b = torch.from_numpy(inp.beta).to(dev).to(pdt)
+    del inp
+    M, N = cfg.M, cfg.N
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dg = torch.empty(N, dtype=pdt, device=dev)
+    db = torch.empty(N, dtype=pdt, device=dev)
+    da = torch.empty(1, dtype=pdt, device=dev)
+    need = dyt.dyt_backward_workspace_size(M, N, xdt, pdt)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dyt.dyt_forward(x, a, g, b, y=y, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        dyt.dyt_backward_partials(x, dy, a, g, dx, ws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    total_ms = start.elapsed_time(end)
+    fwd = [e[0].elapsed_time(e[1]) for e in evs]
+    p1 = [e[1].elapsed_time(e[2]) for e in evs]
+    p2 = [e[2].elapsed_time(e[3]) for e in evs]
+    bwd = [e[1].elapsed_time(e[3]) for e in evs]
+    sx = x.element_size()
+    sp = a.element_size()
+    B = algorithmic_bytes(M, N, sx, sp)
+    ms_step = total_ms / steps
+    res = {
+        "workload": name, "M": M, "N": N, "x_dtype": cfg.x_dtype, "param_dtype": cfg.p_dtype,
+        "ms_per_step": ms_step, "host_s": host_s,
+        "gbps_step": (B["fwd"] + B["bwd"]) / (ms_step * 1e-3) / 1e9,
+        "fwd_us_median": statistics.median(fwd) * 1e3,
+        "bwd_us_median": statistics.median(bwd) * 1e3,
+        "pass1_us_mean": statistics.fmean(p1) * 1e3,
+        "pass2_us_mean": statistics.fmean(p2) * 1e3,
+        "fwd_gbps": B["fwd"] / (statistics.median(fwd) * 1e-3) / 1e9,
+        "bwd_gbps": B["bwd"] / (statistics.median(bwd) * 1e-3) / 1e9,
+        "pass1_gbps": B["pass1"] / (statistics.fmean(p1) * 1e-3) / 1e9,
+        "bytes": B,
+        "workspace_bytes": need,
+        "plan": dyt.dyt_get_plan(M, N, xdt, pdt, True),
+    }
+    res["fwd_frac"] = res["fwd_gbps"] / HBM_PEAK_GBPS
+    res["bwd_frac"] = res["bwd_gbps"] / HBM_PEAK_GBPS
+    del x, dy, y, dx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_calibration(torch, mib: int) -> None:
+    """A plain elementwise kernel of known size (reads and writes mib MiB each)
+    so that HBM byte counters can be scaled; used only by counter runs."""
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written per launch")
+
+
+def cpu_baseline(name: str, seconds: float) -> dict:
+    """The fp64 oracle, as it is, on whole rows of the workload until about
+    `seconds` of CPU time, pinned to one core (numpy ufuncs are single-threaded)."""
+    import workloads
+    from oracle import dyt_oracle
+    cfg = workloads.CONFIGS[name]
+    rows = max(1, (1 << 20) // cfg.N)          # ~1M elements per chunk
+    inp = workloads.generate(name, M=rows)
+    sx = 4 if cfg.x_dtype == "f32" else 2
+    sp = 4 if cfg.p_dtype == "f32" else 2
+    old = os.sched_getaffinity(0)
+    core = min(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            dyt_oracle.forward(inp.x, inp.alpha, inp.gamma, inp.beta)
+            dyt_oracle.backward(inp.x, inp.dy, inp.alpha, inp.gamma)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        os.sched_setaffinity(0, old)
+    B = algorithmic_bytes(rows, cfg.N, sx, sp)
+    gbps = done * (B["fwd"] + B["bwd"]) / el / 1e9
+    return {"value": gbps, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} x ({rows} rows x {cfg.N}) of {name}, forward+backward in fp64, "
+                      f"{el:.1f}s on 1 pinned core"}
+
+
+def load_traffic(kernel: str) -> dict | None:
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", default=SECONDARY, help="second workload reported alongside ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the DyT layer runs on one MI355X here; the row-sharded design is described, not run.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import __graft_entry__ as ge
+    ge._ensure_built()
+    import bwd_dyt_forward_amd as dyt
+
+    main_res = measure(dyt, torch, args.workload, args.steps, args.warmup)
+    log(f"[bench] {json.dumps(main_res)}")
+    sec = None
+    if args.secondary and args.secondary != "none" and args.secondary != args.workload:
+        sec = measure(dyt, torch, args.secondary, args.steps, args.warmup)
+        log(f"[bench] {json.dumps(sec)}")
+    if args.copy_calibration_mib:
+        copy_calibration(torch, args.copy_calibration_mib)
+
+    kernel = "dyt_bwd_partial_kernel"
+    traffic = load_traffic(kernel + ":" + args.workload)
+    rl_bytes = main_res["bytes"]["pass1"]
+    achieved = main_res["pass1_gbps"]
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
+        "kernel": kernel, "algorithmic_bytes_per_launch": rl_bytes,
+        "mean_launch_us": round(main_res["pass1_us_mean"], 2),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+    out = {
+        "metric": "DyT fwd+bwd effective HBM GB/s and % of MI355X peak, per (M,N,dtype)",
+        "value": round(main_res["gbps_step"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": main_res["M"], "N": main_res["N"],
+                   "x_dtype": main_res["x_dtype"], "param_dtype": main_res["param_dtype"],
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(main_res["gbps_step"] / HBM_PEAK_GBPS, 4),
+        "fwd": {"GBps": round(main_res["fwd_gbps"], 1), "frac": round(main_res["fwd_frac"], 4),
+                "us": round(main_res["fwd_us_median"], 2)},
+        "bwd": {"GBps": round(main_res["bwd_gbps"], 1), "frac": round(main_res["bwd_frac"], 4),
+                "us": round(main_res["bwd_us_median"], 2),
+                "pass2_us": round(main_res["pass2_us_mean"], 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if sec:
+        out["secondary"] = {
+            "workload": sec["workload"], "GBps": round(sec["gbps_step"], 1),
+            "frac": round(sec["gbps_step"] / HBM_PEAK_GBPS, 4),
+            "fwd": {"GBps": round(sec["fwd_gbps"], 1), "frac": round(sec["fwd_frac"], 4),
+                    "us": round(sec["fwd_us_median"], 2)},
+            "bwd": {"GBps": round(sec["bwd_gbps"], 1), "frac": round(sec["bwd_frac"], 4),
+                    "us": round(sec["bwd_us_median"], 2)},
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

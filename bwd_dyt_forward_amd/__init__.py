@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     DytError,
     dyt_abi_version,
     dyt_backward,
+    dyt_backward_finish,
+    dyt_backward_partials,
     dyt_backward_workspace_size,
     dyt_forward,
     dyt_get_plan,
@@ -22,6 +24,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "DYT_F32", "DYT_BF16", "DYT_OK", "DytError", "LIB_FILE", "lib",
-    "dyt_forward", "dyt_backward", "dyt_backward_workspace_size",
+    "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
+    "dyt_backward_workspace_size",
     "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
 ]

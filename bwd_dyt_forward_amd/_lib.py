@@ -51,6 +51,9 @@ SIGNATURES = {
     "dyt_backward_workspace_size": (ctypes.c_size_t, [_i64, _i64, _int, _int]),
     "dyt_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                             _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
+                                     _int, _int, _vp]),
+    "dyt_backward_finish": (_int, [_vp, ctypes.c_size_t, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
@@ -61,7 +64,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"DyT HIP library not found at {path}; build it first "
-            "(python -m bwd_dyt_forward_amd.build, or __graft_entry__.build())")
+            "(python bwd_dyt_forward_amd/build.py, or __graft_entry__.build())")
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -168,6 +171,34 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
                           _code(x.dtype), _code(pdt), _stream(stream))
     _check("dyt_backward", st)
     return dx, dalpha, dgamma, dbeta
+
+
+def dyt_backward_partials(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor,
+                          gamma: torch.Tensor, dx: torch.Tensor, workspace: torch.Tensor,
+                          stream=None) -> torch.Tensor:
+    """First backward pass: dx plus the float32 partial rows in workspace."""
+    _check_act("x", x)
+    _check_act("dy", dy)
+    M, N = x.shape
+    _check_params(N, alpha, gamma)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.dyt_backward_partials(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx),
+                                   _ptr(workspace), wbytes, M, N, _code(x.dtype),
+                                   _code(alpha.dtype), _stream(stream))
+    _check("dyt_backward_partials", st)
+    return dx
+
+
+def dyt_backward_finish(workspace: torch.Tensor, M: int, N: int, x_dtype,
+                        dalpha: torch.Tensor, dgamma: torch.Tensor, dbeta: torch.Tensor,
+                        stream=None):
+    """Second backward pass: fixed-order sums of the partial rows."""
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.dyt_backward_finish(_ptr(workspace), wbytes, _ptr(dalpha), _ptr(dgamma), _ptr(dbeta),
+                                 int(M), int(N), _code(x_dtype), _code(dalpha.dtype),
+                                 _stream(stream))
+    _check("dyt_backward_finish", st)
+    return dalpha, dgamma, dbeta
 
 
 def dyt_status_string(status: int) -> str:

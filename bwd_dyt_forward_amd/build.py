@@ -1,6 +1,6 @@
 """Build step: compile the HIP sources into the in-tree C-ABI library.
 
-``python -m bwd_dyt_forward_amd.build`` (or ``build()``) runs hipcc for gfx950
+``python bwd_dyt_forward_amd/build.py`` (or ``build()``) runs hipcc for gfx950
 and writes ``bwd_dyt_forward_amd/libdyt.so``. Cross-compiling needs no GPU.
 """
 from __future__ import annotations

@@ -71,8 +71,12 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // row length limit (int32 in-tile offsets)
 
-// Pure host: validates sizes/dtypes and fills the plan.
-int make_plan(int64_t M, int64_t N, int xdt, int pdt, bool vec_aligned, Plan& p) {
+// Pure host: validates sizes/dtypes and fills the plan. The plan depends
+// only on (M, N, x dtype): tensors whose bases are not 16-byte aligned run
+// the same tiles with the element-wise kernel variant (V = 1, K = 16, whose
+// 4096-element capacity holds any tile), so the partial-row layout - and
+// with it dyt_backward_finish - does not depend on pointer alignment.
+int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
     if (M < 0 || N < 0 || N > kMaxN) return DYT_ERR_INVALID_ARG;
     const int64_t sx = dtype_size(xdt);
@@ -84,30 +88,23 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, bool vec_aligned, Plan& p)
         p.fin_grid = ceil_div(2 * N + 1, 64);
         return DYT_OK;
     }
-    // packed tiles need R >= 2 rows (R a multiple of the rows that keep each
-    // tile 16-byte aligned) within kTileCap elements
-    const int64_t r0 = vec_aligned ? 16 / gcd64(N * sx, 16) : 1;
+    // packed tiles: R >= 2 whole rows, R a multiple of r0 (the rows that keep
+    // each tile 16-byte aligned), within kTileCap elements
+    const int64_t r0 = 16 / gcd64(N * sx, 16);
     const int64_t rcap = (dyt::kTileCap / N) / r0 * r0;
     if (rcap >= 2) {
         p.packed = true;
-        p.vec = vec_aligned ? vmax : 1;
-        const int kmin = vec_aligned ? 1 : 16;
-        const int kbig = vec_aligned ? kmax : 16;
+        p.vec = vmax;
         // largest K (biggest tiles) that still yields DYT_MIN_TILES tiles,
-        // else the smallest K
-        int chosen = kmin;
-        for (int k = kbig; k >= kmin; k /= 2) {
-            const int64_t cap = (int64_t)kBlock * p.vec * k;
-            const int64_t r = (cap / N) / r0 * r0;
-            if (r < 1) continue;
-            if (ceil_div(M, r) >= DYT_MIN_TILES) { chosen = k; break; }
+        // else the smallest K that holds an aligned row group
+        int chosen = 0;
+        for (int k = kmax; k >= 1; k /= 2) {
+            const int64_t r = ((int64_t)kBlock * vmax * k / N) / r0 * r0;
+            if (r < 1) break;
+            chosen = k;
+            if (ceil_div(M, r) >= DYT_MIN_TILES) break;
         }
-        const int64_t cap = (int64_t)kBlock * p.vec * chosen;
-        int64_t r = (cap / N) / r0 * r0;
-        if (r < 1) {   // a smaller K cannot hold an aligned row group: grow back
-            chosen = kbig;
-            r = ((int64_t)kBlock * p.vec * chosen / N) / r0 * r0;
-        }
+        const int64_t r = ((int64_t)kBlock * vmax * chosen / N) / r0 * r0;
         p.slots = chosen;
         p.R = r;
         p.T = r * N;
@@ -119,7 +116,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, bool vec_aligned, Plan& p)
         p.bwd_grid = std::min<int64_t>(p.tiles, DYT_BWD_GRID);
     } else {
         p.packed = false;
-        const bool v = vec_aligned && (N * sx) % 16 == 0;
+        const bool v = (N * sx) % 16 == 0;     // rows start 16-byte aligned
         p.vec = v ? vmax : 1;
         const int kbig = v ? kmax : 16;
         int k = v ? 1 : 16;
@@ -140,6 +137,17 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, bool vec_aligned, Plan& p)
     p.fin_grid = ceil_div(2 * N + 1, 64);
     p.ws_bytes = p.bwd_grid * p.ld * (int64_t)sizeof(float);
     return DYT_OK;
+}
+
+// Kernel variant for the actual pointers: the plan's vector width when every
+// activation pointer is 16-byte aligned, else element-wise access.
+Plan variant_for(const Plan& p, bool vec_aligned) {
+    Plan q = p;
+    if (!vec_aligned && q.vec != 1) {
+        q.vec = 1;
+        q.slots = 16;
+    }
+    return q;
 }
 
 Geo make_geo(const Plan& p, int64_t M, int64_t N) {
@@ -244,6 +252,74 @@ void launch_finish(const Plan& p, int64_t N, const float* ws, void* dg, void* db
 
 int hip_status() { return hipGetLastError() == hipSuccess ? DYT_OK : DYT_ERR_HIP; }
 
+// Shared validation of the backward entry points. Pointers a pass does not
+// use are passed as nullptr with use_* = false.
+int validate_backward(const void* x, const void* dy, const void* alpha, const void* gamma,
+                      void* dx, void* dalpha, void* dgamma, void* dbeta, const void* workspace,
+                      size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int param_dtype,
+                      bool use_pass1, bool use_pass2, Plan& base) {
+    int st = make_plan(M, N, x_dtype, param_dtype, base);
+    if (st != DYT_OK) return st;
+    const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
+    const bool any = M > 0 && N > 0;
+    const bool p1 = use_pass1 && any;
+    if (use_pass2) {
+        if (!dalpha) return DYT_ERR_INVALID_ARG;
+        if (N > 0 && (!dgamma || !dbeta)) return DYT_ERR_INVALID_ARG;
+    }
+    if (p1 && (!x || !dy || !alpha || !gamma || !dx)) return DYT_ERR_INVALID_ARG;
+    const size_t need = (size_t)round_up(base.ws_bytes, 16);
+    if (workspace_bytes < need) return DYT_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0 && !workspace) return DYT_ERR_INVALID_ARG;
+    if (need > 0 && !aligned(workspace, 16)) return DYT_ERR_MISALIGNED;
+    if (use_pass2 && (!aligned(dalpha, sp) || (N > 0 && (!aligned(dgamma, sp) || !aligned(dbeta, sp)))))
+        return DYT_ERR_MISALIGNED;
+    if (p1 && (!aligned(x, sx) || !aligned(dy, sx) || !aligned(dx, sx) || !aligned(alpha, sp) ||
+               !aligned(gamma, sp)))
+        return DYT_ERR_MISALIGNED;
+    // outputs (and the workspace) must not overlap inputs or each other
+    const int64_t mn = p1 ? M * N * sx : 0;
+    const Range outs[5] = {range(dx, mn), range(dalpha, use_pass2 ? sp : 0),
+                           range(dgamma, use_pass2 ? N * sp : 0), range(dbeta, use_pass2 ? N * sp : 0),
+                           range(workspace, (int64_t)need)};
+    const Range ins[4] = {range(x, mn), range(dy, mn), range(alpha, p1 ? sp : 0),
+                          range(gamma, p1 ? N * sp : 0)};
+    for (int a = 0; a < 5; ++a) {
+        if (outs[a].lo == outs[a].hi) continue;
+        for (const Range& i : ins)
+            if (i.lo != i.hi && overlap(outs[a], i)) return DYT_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 5; ++b)
+            if (outs[b].lo != outs[b].hi && overlap(outs[a], outs[b])) return DYT_ERR_INVALID_ARG;
+    }
+    return DYT_OK;
+}
+
+int enqueue_pass1(const Plan& base, const void* x, const void* dy, const void* alpha,
+                  const void* gamma, void* dx, void* workspace, int64_t M, int64_t N,
+                  int x_dtype, int param_dtype, hipStream_t s) {
+    if (M == 0 || N == 0) return DYT_OK;
+    const Plan p = variant_for(base, aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16));
+    const Geo g = make_geo(p, M, N);
+    float* ws = static_cast<float*>(workspace);
+    bool ok;
+    if (x_dtype == DYT_F32)
+        ok = param_dtype == DYT_F32 ? launch_bwd<float, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
+                                    : launch_bwd<float, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
+    else
+        ok = param_dtype == DYT_F32 ? launch_bwd<bf16_t, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
+                                    : launch_bwd<bf16_t, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
+    if (!ok) return DYT_ERR_INVALID_ARG;
+    return hip_status();
+}
+
+int enqueue_pass2(const Plan& base, const void* workspace, void* dalpha, void* dgamma,
+                  void* dbeta, int64_t N, int param_dtype, hipStream_t s) {
+    const float* ws = static_cast<const float*>(workspace);
+    if (param_dtype == DYT_F32) launch_finish<float>(base, N, ws, dgamma, dbeta, dalpha, s);
+    else launch_finish<bf16_t>(base, N, ws, dgamma, dbeta, dalpha, s);
+    return hip_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,9 +341,10 @@ const char* dyt_status_string(int status) {
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
                  dyt_plan* out) {
     if (!out) return DYT_ERR_INVALID_ARG;
-    Plan p;
-    const int st = make_plan(M, N, x_dtype, param_dtype, vector_aligned != 0, p);
+    Plan base;
+    const int st = make_plan(M, N, x_dtype, param_dtype, base);
     if (st != DYT_OK) return st;
+    const Plan p = variant_for(base, vector_aligned != 0);
     out->packed = p.packed ? 1 : 0;
     out->vec = p.vec;
     out->slots = p.slots;
@@ -285,18 +362,15 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
 }
 
 size_t dyt_backward_workspace_size(int64_t M, int64_t N, int x_dtype, int param_dtype) {
-    Plan a, b;
-    if (make_plan(M, N, x_dtype, param_dtype, true, a) != DYT_OK) return 0;
-    if (make_plan(M, N, x_dtype, param_dtype, false, b) != DYT_OK) return 0;
-    return (size_t)round_up(std::max(a.ws_bytes, b.ws_bytes), 16);
+    Plan p;
+    if (make_plan(M, N, x_dtype, param_dtype, p) != DYT_OK) return 0;
+    return (size_t)round_up(p.ws_bytes, 16);
 }
 
 int dyt_forward(const void* x, const void* alpha, const void* gamma, const void* beta, void* y,
                 int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream) {
-    if (!dtype_ok(x_dtype) || !dtype_ok(param_dtype)) return DYT_ERR_UNSUPPORTED_DTYPE;
-    if (M < 0 || N < 0) return DYT_ERR_INVALID_ARG;
-    Plan probe;
-    int st = make_plan(M, N, x_dtype, param_dtype, true, probe);
+    Plan base;
+    int st = make_plan(M, N, x_dtype, param_dtype, base);
     if (st != DYT_OK) return st;
     if (M == 0 || N == 0) return DYT_OK;
     if (!x || !alpha || !gamma || !beta || !y) return DYT_ERR_INVALID_ARG;
@@ -308,10 +382,7 @@ int dyt_forward(const void* x, const void* alpha, const void* gamma, const void*
     if (overlap(ry, range(x, M * N * sx)) || overlap(ry, range(alpha, sp)) ||
         overlap(ry, range(gamma, N * sp)) || overlap(ry, range(beta, N * sp)))
         return DYT_ERR_INVALID_ARG;
-    const bool vec = aligned(x, 16) && aligned(y, 16);
-    Plan p;
-    st = make_plan(M, N, x_dtype, param_dtype, vec, p);
-    if (st != DYT_OK) return st;
+    const Plan p = variant_for(base, aligned(x, 16) && aligned(y, 16));
     const Geo g = make_geo(p, M, N);
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool ok;
@@ -325,65 +396,42 @@ int dyt_forward(const void* x, const void* alpha, const void* gamma, const void*
     return hip_status();
 }
 
+
+int dyt_backward_partials(const void* x, const void* dy, const void* alpha, const void* gamma,
+                          void* dx, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                          int x_dtype, int param_dtype, void* stream) {
+    Plan base;
+    int st = validate_backward(x, dy, alpha, gamma, dx, nullptr, nullptr, nullptr, workspace,
+                               workspace_bytes, M, N, x_dtype, param_dtype, true, false, base);
+    if (st != DYT_OK) return st;
+    return enqueue_pass1(base, x, dy, alpha, gamma, dx, workspace, M, N, x_dtype, param_dtype,
+                         static_cast<hipStream_t>(stream));
+}
+
+int dyt_backward_finish(const void* workspace, size_t workspace_bytes, void* dalpha,
+                        void* dgamma, void* dbeta, int64_t M, int64_t N, int x_dtype,
+                        int param_dtype, void* stream) {
+    Plan base;
+    int st = validate_backward(nullptr, nullptr, nullptr, nullptr, nullptr, dalpha, dgamma, dbeta,
+                               workspace, workspace_bytes, M, N, x_dtype, param_dtype, false, true,
+                               base);
+    if (st != DYT_OK) return st;
+    return enqueue_pass2(base, workspace, dalpha, dgamma, dbeta, N, param_dtype,
+                         static_cast<hipStream_t>(stream));
+}
+
 int dyt_backward(const void* x, const void* dy, const void* alpha, const void* gamma, void* dx,
                  void* dalpha, void* dgamma, void* dbeta, void* workspace,
                  size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int param_dtype,
                  void* stream) {
-    if (!dtype_ok(x_dtype) || !dtype_ok(param_dtype)) return DYT_ERR_UNSUPPORTED_DTYPE;
-    if (M < 0 || N < 0) return DYT_ERR_INVALID_ARG;
-    Plan probe;
-    int st = make_plan(M, N, x_dtype, param_dtype, true, probe);
-    if (st != DYT_OK) return st;
-    const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
-    const bool any = M > 0 && N > 0;
-    if (!dalpha) return DYT_ERR_INVALID_ARG;
-    if (N > 0 && (!dgamma || !dbeta)) return DYT_ERR_INVALID_ARG;
-    if (any && (!x || !dy || !alpha || !gamma || !dx)) return DYT_ERR_INVALID_ARG;
-    const size_t need = dyt_backward_workspace_size(M, N, x_dtype, param_dtype);
-    if (workspace_bytes < need) return DYT_ERR_WORKSPACE_TOO_SMALL;
-    if (need > 0 && !workspace) return DYT_ERR_INVALID_ARG;
-    if (!aligned(dalpha, sp) || (N > 0 && (!aligned(dgamma, sp) || !aligned(dbeta, sp))) ||
-        (need > 0 && !aligned(workspace, 16)))
-        return DYT_ERR_MISALIGNED;
-    if (any && (!aligned(x, sx) || !aligned(dy, sx) || !aligned(dx, sx) || !aligned(alpha, sp) ||
-                !aligned(gamma, sp)))
-        return DYT_ERR_MISALIGNED;
-    // outputs (and the workspace) must not overlap inputs or each other
-    {
-        const int64_t mn = any ? M * N * sx : 0;
-        const Range outs[5] = {range(dx, mn), range(dalpha, sp), range(dgamma, N * sp),
-                               range(dbeta, N * sp), range(workspace, (int64_t)need)};
-        const Range ins[4] = {range(x, mn), range(dy, mn), range(alpha, any ? sp : 0),
-                              range(gamma, any ? N * sp : 0)};
-        for (int a = 0; a < 5; ++a) {
-            if (outs[a].lo == outs[a].hi) continue;
-            for (const Range& i : ins)
-                if (i.lo != i.hi && overlap(outs[a], i)) return DYT_ERR_INVALID_ARG;
-            for (int b = a + 1; b < 5; ++b)
-                if (outs[b].lo != outs[b].hi && overlap(outs[a], outs[b])) return DYT_ERR_INVALID_ARG;
-        }
-    }
-    const bool vec = any && aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16);
-    Plan p;
-    st = make_plan(M, N, x_dtype, param_dtype, vec, p);
+    Plan base;
+    int st = validate_backward(x, dy, alpha, gamma, dx, dalpha, dgamma, dbeta, workspace,
+                               workspace_bytes, M, N, x_dtype, param_dtype, true, true, base);
     if (st != DYT_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float* ws = static_cast<float*>(workspace);
-    if (any) {
-        const Geo g = make_geo(p, M, N);
-        bool ok;
-        if (x_dtype == DYT_F32)
-            ok = param_dtype == DYT_F32 ? launch_bwd<float, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
-                                        : launch_bwd<float, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
-        else
-            ok = param_dtype == DYT_F32 ? launch_bwd<bf16_t, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
-                                        : launch_bwd<bf16_t, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
-        if (!ok) return DYT_ERR_INVALID_ARG;
-        if ((st = hip_status()) != DYT_OK) return st;
-    }
-    if (param_dtype == DYT_F32) launch_finish<float>(p, N, ws, dgamma, dbeta, dalpha, s);
-    else launch_finish<bf16_t>(p, N, ws, dgamma, dbeta, dalpha, s);
-    return hip_status();
+    st = enqueue_pass1(base, x, dy, alpha, gamma, dx, workspace, M, N, x_dtype, param_dtype, s);
+    if (st != DYT_OK) return st;
+    return enqueue_pass2(base, workspace, dalpha, dgamma, dbeta, N, param_dtype, s);
 }
 
 }  // extern "C"

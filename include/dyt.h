@@ -16,8 +16,9 @@
  * behaviour this ABI keeps:
  *   - "Launch limit": any number of rows is accepted (a flat 1D grid; no
  *     65,535-block limit on rows).
- *   - "Small widths": rows of up to 256 columns are packed several to a
- *     workgroup tile; wider rows keep one row per tile.
+ *   - "Small widths": narrow rows are packed several to a workgroup tile
+ *     (whenever two or more fit a 4096-element tile, so every width up to
+ *     256 qualifies); wider rows are cut into row segments, one per tile.
  *   - "Padding": lanes past the end of the data are removed from the
  *     reductions after the arithmetic, so alpha = +inf cannot inject
  *     tanh(inf * 0) = NaN into dgamma, dbeta or dalpha.
@@ -48,7 +49,8 @@
  *     Faults during kernel execution surface at stream synchronisation.
  *   - Determinism: results are bitwise reproducible run to run. The
  *     parameter-gradient sums use a fixed summation order that depends only
- *     on (M, N, x dtype, alignment class); no floating-point atomics.
+ *     on (M, N, x dtype) and on whether x/dy/dx are 16-byte aligned; no
+ *     floating-point atomics.
  *   - Arithmetic is float32 throughout (accumulation included); bfloat16
  *     results are rounded to nearest even. float32 subnormals are kept.
  */
@@ -114,16 +116,36 @@ size_t dyt_backward_workspace_size(int64_t M, int64_t N, int x_dtype, int param_
  *   workspace  device scratch of workspace_bytes bytes, 16-byte aligned, no
  *              initial contents required; may be NULL when the required
  *              size is 0. Contents are undefined afterwards.
- * Two kernels run in order on the stream: a pass that writes dx and one
- * float32 partial row of (dgamma, dbeta, dalpha) per workgroup into the
- * workspace, and a pass that sums those rows in a fixed order and rounds
- * them to the parameter dtype.
+ * Equivalent to dyt_backward_partials followed by dyt_backward_finish on
+ * the same stream (two kernels).
  */
 int dyt_backward(const void* x, const void* dy, const void* alpha, const void* gamma,
                  void* dx, void* dalpha, void* dgamma, void* dbeta,
                  void* workspace, size_t workspace_bytes,
                  int64_t M, int64_t N, int x_dtype, int param_dtype,
                  void* stream);
+
+/*
+ * First backward pass alone: writes dx and, into the workspace, one float32
+ * partial row [dgamma partials | dbeta partials | dalpha partial] per
+ * workgroup (float32 accumulation; lanes past the end of the data are
+ * removed after the arithmetic, so alpha = +inf cannot put
+ * tanh(inf * 0) = NaN into the partials). The row layout depends only on
+ * (M, N, x_dtype), never on pointer alignment. Arguments as dyt_backward.
+ */
+int dyt_backward_partials(const void* x, const void* dy, const void* alpha, const void* gamma,
+                          void* dx, void* workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
+
+/*
+ * Second backward pass alone: sums the partial rows that
+ * dyt_backward_partials(M, N, x_dtype, ...) left in the workspace, column by
+ * column in a fixed order, rounds to param_dtype and writes dgamma, dbeta
+ * and dalpha. Arguments as dyt_backward; the workspace is only read.
+ */
+int dyt_backward_finish(const void* workspace, size_t workspace_bytes,
+                        void* dalpha, void* dgamma, void* dbeta,
+                        int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* dyt_status_string(int status);
@@ -133,9 +155,11 @@ int dyt_abi_version(void);
 
 /*
  * Launch geometry the library would use (for tests and reports; pure host
- * function, no HIP calls). vector_aligned != 0 describes 16-byte aligned
- * x/dy/y/dx pointers. Returns DYT_OK or the status the compute calls would
- * return for these sizes and dtypes.
+ * function, no HIP calls). The tiling, grids and workspace layout depend
+ * only on (M, N, x_dtype); vector_aligned selects which kernel variant is
+ * described (non-zero: 16-byte aligned x/dy/y/dx, vector access; zero:
+ * element-wise access, vec = 1). Returns DYT_OK or the status the compute
+ * calls would return for these sizes and dtypes.
  */
 typedef struct dyt_plan {
     int32_t packed;        /* 1: tiles of several whole rows (N <= 256); 0: row segments */

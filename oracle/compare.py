@@ -99,7 +99,8 @@ class Report:
 def _finish(name, got, ref_cmp, bound) -> Report:
     got = np.asarray(got, dtype=np.float64).reshape(-1)
     ref_cmp = np.asarray(ref_cmp, dtype=np.float64).reshape(-1)
-    bound = np.broadcast_to(np.asarray(bound, dtype=np.float64), got.shape).reshape(-1)
+    bound = np.asarray(bound, dtype=np.float64)
+    bound = bound.reshape(-1) if bound.size == got.size else np.broadcast_to(bound, got.shape)
     rep = Report(name, got.size)
     gnan, rnan = np.isnan(got), np.isnan(ref_cmp)
     rep.nan_mismatch = int(np.count_nonzero(gnan != rnan))

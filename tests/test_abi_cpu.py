@@ -28,8 +28,8 @@ def _declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted([
-        "dyt_forward", "dyt_backward", "dyt_backward_workspace_size", "dyt_status_string",
-        "dyt_abi_version", "dyt_get_plan"])
+        "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
+        "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -73,6 +73,11 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
     cap = p["block"] * p["vec"] * p["slots"]
     assert p["block"] == 256
     assert p["vec"] == (16 // sx if vec and (p["packed"] or (N * sx) % 16 == 0) else 1)
+    # tiling and workspace layout do not depend on the alignment class
+    q = dyt.dyt_get_plan(M, N, xdt, "f32", not vec)
+    for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "fwd_grid",
+                "bwd_grid", "ws_row", "ws_bytes"):
+        assert p[key] == q[key], key
     assert 1 <= p["tile_elems"] <= cap <= 4096
     if p["packed"]:
         R = p["rows_per_tile"]
@@ -91,7 +96,7 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
     assert p["ws_bytes"] == p["bwd_grid"] * p["ws_row"] * 4
     assert p["fin_grid"] == -(-(2 * N + 1) // 64)
     ws = dyt.dyt_backward_workspace_size(M, N, xdt, "f32")
-    assert ws >= p["ws_bytes"] and ws % 16 == 0
+    assert ws == -(-p["ws_bytes"] // 16) * 16
 
 
 def test_plan_uses_1d_grid_beyond_65535_rows(dyt):
@@ -171,3 +176,22 @@ def test_backward_error_codes(dyt):
     assert _bwd(dyt, ws=A16) == E_ARG                              # workspace aliases x
     # dalpha is always written, so it is always required
     assert _bwd(dyt, da=None, M=0) == E_ARG
+
+
+def test_split_backward_error_codes(dyt):
+    L = dyt.lib
+    need = dyt.dyt_backward_workspace_size(4, 4, F32, F32)
+    ws = A16 + 0x800000
+    # pass 1: x, dy, alpha, gamma, dx and workspace required; no param grads involved
+    assert L.dyt_backward_partials(None, A16 + 0x100000, A16 + 0x200000, A16 + 0x300000,
+                                   A16 + 0x400000, ws, need, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_backward_partials(A16, A16 + 0x100000, A16 + 0x200000, A16 + 0x300000,
+                                   A16 + 0x400000, ws, need - 1, 4, 4, F32, F32, None) == E_WS
+    assert L.dyt_backward_partials(A16, A16 + 0x100000, A16 + 0x200000, A16 + 0x300000,
+                                   A16 + 0x100000, ws, need, 4, 4, F32, F32, None) == E_ARG
+    # pass 2: workspace and the three gradient outputs
+    assert L.dyt_backward_finish(ws, need, None, A16, A16 + 64, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_backward_finish(ws, need, A16 + 128, None, A16 + 64, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_backward_finish(ws, need - 16, A16 + 128, A16, A16 + 64, 4, 4, F32, F32, None) == E_WS
+    assert L.dyt_backward_finish(ws, need, A16 + 128, A16, A16 + 8, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_backward_finish(ws, need, A16 + 128, A16, A16 + 64, 4, 4, 9, F32, None) == E_DT

@@ -239,3 +239,24 @@ def test_large_u_float32_keeps_sech2(dyt):
                                 np.zeros(N, np.float32), "f32", "f32")
     outs = run_both(dyt, upload(inp))
     assert_reports("large-u f32", full_reports(inp, *outs))
+
+
+@pytest.mark.parametrize("name,M", [("c5_4194304x32_bf16_outliers", 20001), ("c4_32768x4096_bf16", 40),
+                                    ("c3_100003x17_f32_inf", 3001)])
+def test_split_backward_matches_single_call(dyt, name, M):
+    """dyt_backward_partials + dyt_backward_finish == dyt_backward, bitwise."""
+    d = upload(workloads.generate(name, M=M))
+    _, dx0, da0, dg0, db0 = run_both(dyt, d)
+    x = d["x"]
+    Mx, N = x.shape
+    pdt = d["alpha"].dtype
+    dx = torch.empty_like(x)
+    ws = torch.empty(dyt.dyt_backward_workspace_size(Mx, N, x.dtype, pdt), dtype=torch.uint8, device="cuda")
+    da = torch.empty(1, dtype=pdt, device="cuda")
+    dg = torch.empty(N, dtype=pdt, device="cuda")
+    db = torch.empty(N, dtype=pdt, device="cuda")
+    dyt.dyt_backward_partials(x, d["dy"], d["alpha"], d["gamma"], dx, ws)
+    dyt.dyt_backward_finish(ws, Mx, N, x.dtype, da, dg, db)
+    torch.cuda.synchronize()
+    for u, v in ((dx, dx0), (da, da0), (dg, dg0), (db, db0)):
+        assert np.array_equal(_bits(u), _bits(v))

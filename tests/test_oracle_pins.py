@@ -398,3 +398,11 @@ def test_checkers_accept_and_reject():
     assert not C.check_grad([10.001], [10.0], [1.0], "f32").ok
     assert C.check_grad([1e-3], [0.0], [1000.0], "f32").ok
     assert not C.check_dx(np.array([np.inf]), np.array([1.0]), "f32").ok
+
+
+def test_checkers_accept_2d_bounds():
+    ref = np.arange(12, dtype=np.float64).reshape(3, 4) + 1
+    rep = C.check_y(ref.copy(), ref, np.abs(ref), "f32")
+    assert rep.ok and rep.n == 12
+    rep = C.check_dx(ref * (1 + 1e-5), ref, "f32", np.ones((3, 4)))
+    assert rep.n_fail == 12
