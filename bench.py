@@ -154,6 +154,30 @@ def copy_calibration(torch, mib: int) -> None:
     log(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written per launch")
 
 
+def copy_ceiling(torch, nbytes: int, reps: int = 20) -> float:
+    """Device-to-device copy of nbytes (read nbytes + write nbytes) with the
+    runtime's copy path, as a measured ceiling for streaming kernels (GB/s,
+    counting read + write bytes, median of reps)."""
+    n = nbytes // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (statistics.median(times) * 1e-3) / 1e9
+
+
 def cpu_baseline(name: str, seconds: float) -> dict:
     """The fp64 oracle, as it is, on whole rows of the workload until about
     `seconds` of CPU time, pinned to one core (numpy ufuncs are single-threaded)."""
@@ -236,6 +260,8 @@ def main() -> int:
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)
 
+    ceiling = copy_ceiling(torch, main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] == "bf16" else 4))
+    log(f"[bench] device copy ceiling: {ceiling:.1f} GB/s")
     kernel = "dyt_bwd_partial_kernel"
     traffic = load_traffic(kernel + ":" + args.workload)
     rl_bytes = main_res["bytes"]["pass1"]
@@ -267,6 +293,7 @@ def main() -> int:
                    "x_dtype": main_res["x_dtype"], "param_dtype": main_res["param_dtype"],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(main_res["gbps_step"] / HBM_PEAK_GBPS, 4),
+        "copy_ceiling_GBps": round(ceiling, 1),
         "fwd": {"GBps": round(main_res["fwd_gbps"], 1), "frac": round(main_res["fwd_frac"], 4),
                 "us": round(main_res["fwd_us_median"], 2)},
         "bwd": {"GBps": round(main_res["bwd_gbps"], 1), "frac": round(main_res["bwd_frac"], 4),

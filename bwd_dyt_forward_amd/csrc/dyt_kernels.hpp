@@ -76,22 +76,27 @@ struct FinGeo {
 };
 
 // ---------------------------------------------------------------- memory IO
-template <typename XT, int V> struct VecIO;
+// Raw<XT, V>: the V elements of one access as loaded from memory (one
+// 16-byte vector, or one element). Loads return raw registers so that every
+// load of a tile is issued before any value is needed.
+template <typename XT, int V> struct Raw;
 
-template <> struct VecIO<float, 4> {
-    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
-        const float4 t = *reinterpret_cast<const float4*>(p);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+template <> struct Raw<float, 4> {
+    using T = float4;
+    static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    static __device__ __forceinline__ void unpack(const T& r, float (&v)[4]) {
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
     }
     static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
         *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     }
 };
 
-template <> struct VecIO<bf16_t, 8> {
-    static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8]) {
-        const uint4 t = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+template <> struct Raw<bf16_t, 8> {
+    using T = uint4;
+    static __device__ __forceinline__ T load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ void unpack(const T& r, float (&v)[8]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
@@ -108,8 +113,10 @@ template <> struct VecIO<bf16_t, 8> {
     }
 };
 
-template <typename XT> struct VecIO<XT, 1> {
-    static __device__ __forceinline__ void load(const XT* p, float (&v)[1]) { v[0] = to_f32(p[0]); }
+template <typename XT> struct Raw<XT, 1> {
+    using T = XT;
+    static __device__ __forceinline__ T load(const XT* p) { return *p; }
+    static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) { v[0] = to_f32(r); }
     static __device__ __forceinline__ void store(XT* p, const float (&v)[1]) { p[0] = from_f32<XT>(v[0]); }
 };
 
@@ -126,57 +133,90 @@ __device__ __forceinline__ void store_partial(XT* p, int n, const float (&v)[V])
         if (e < n) p[e] = from_f32<XT>(v[e]);
 }
 
+// ------------------------------------------------------------ tile geometry
+// Per-thread constants of the persistent loop. Slot k of thread tid covers
+// tile offsets o = (k * kBlock + tid) * V + [0, V). A slot is "used" if its
+// whole vector lies inside the workgroup's tiles (packed: o < T; row
+// segments: o < this block's length). Unused slots load a valid address
+// (slot 0's) and discard the result, so the loads carry no branches.
+template <int V, int K>
+struct Slots {
+    int off[K];     // element offset of the slot inside the tile (0 if unused)
+    bool used[K];
+};
+
+template <int V, int K>
+__device__ __forceinline__ Slots<V, K> make_slots(int tid, int seg_len) {
+    Slots<V, K> s;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int o = (k * kBlock + tid) * V;
+        s.used[k] = o < seg_len;
+        s.off[k] = s.used[k] ? o : 0;
+    }
+    return s;
+}
+
+// Tiles handled by workgroup wg: t = wg, wg + G, ...; tiles [0, nfull) are
+// whole, a packed problem whose size is not a multiple of T has one last
+// partial tile (index nfull) that only workgroup nfull % G handles.
+struct TileWalk {
+    int64_t nfull;     // number of whole tiles
+    int64_t base;      // element index of this workgroup's first tile
+    int64_t step;      // elements between consecutive tiles of this workgroup
+    int64_t col_base;  // first column of this workgroup's block
+    int seg_len;       // columns (row segments) or elements (packed) per tile
+    bool tail;         // this workgroup also owns the partial packed tile
+};
+
+__device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G) {
+    TileWalk w;
+    if (packed) {
+        w.nfull = g.total / g.T;
+        w.base = wg * g.T;
+        w.step = G * g.T;
+        w.col_base = 0;
+        w.seg_len = g.T;
+        w.tail = (w.nfull < g.ntiles) && (wg == w.nfull % G);
+    } else {
+        const int b = (int)(wg % g.nb);
+        w.nfull = g.ntiles;
+        w.col_base = (int64_t)b * g.T;
+        w.base = (wg / g.nb) * g.N + w.col_base;
+        w.step = (G / g.nb) * g.N;
+        w.seg_len = (b == g.nb - 1) ? g.last_len : g.T;
+        w.tail = false;
+    }
+    return w;
+}
+
 template <bool ACC>
 __device__ __forceinline__ float dyt_tanh(float u) {
     if constexpr (ACC) return tanh_accurate(u);
     else return tanh_fast(u);
 }
 template <bool ACC>
-__device__ __forceinline__ void dyt_tanh_sech2(float u, float& t, float& d) {
-    if constexpr (ACC) tanh_sech2_accurate(u, t, d);
-    else tanh_sech2_fast(u, t, d);
-}
-
-// Column block of this workgroup (row segments) and its length.
-__device__ __forceinline__ void block_columns(const Geo& g, bool packed, int64_t wg,
-                                              int64_t& col_base, int& seg_len) {
-    if (packed) {
-        col_base = 0;
-        seg_len = g.T;
-    } else {
-        const int b = (int)(wg % g.nb);
-        col_base = (int64_t)b * g.T;
-        seg_len = (b == g.nb - 1) ? g.last_len : g.T;
-    }
-}
-
-__device__ __forceinline__ void tile_extent(const Geo& g, bool packed, int64_t t,
-                                            int64_t col_base, int seg_len,
-                                            int64_t& base, int& len) {
-    if (packed) {
-        base = t * g.T;
-        const int64_t rem = g.total - base;
-        len = rem < g.T ? (int)rem : g.T;
-    } else {
-        base = (t / g.nb) * g.N + col_base;
-        len = seg_len;
-    }
+__device__ __forceinline__ void dyt_tanh_sech2(float xv, float alpha, float& t, float& d) {
+    if constexpr (ACC) tanh_sech2_accurate(xv, alpha, t, d);
+    else tanh_sech2_fast(alpha * xv, t, d);
 }
 
 // ---------------------------------------------------------------- forward
-// y = gamma * tanh(alpha * x) + beta.
+// y = gamma * tanh(alpha * x) + beta. Loads of the next tile are issued
+// before the current tile is computed (register double buffering).
 template <typename XT, typename PT, int V, int K, bool PACKED>
 __global__ void __launch_bounds__(kBlock)
 dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, const PT* __restrict__ beta,
                XT* __restrict__ y, const Geo g) {
+    using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
     const int64_t wg = blockIdx.x;
+    const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    int64_t col_base;
-    int seg_len;
-    block_columns(g, PACKED, wg, col_base, seg_len);
+    const TileWalk w = make_walk(g, PACKED, wg, G);
+    const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
 
     float gm[K][V], bt[K][V];
 #pragma unroll
@@ -186,50 +226,58 @@ dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
             const int o = (k * kBlock + tid) * V + e;
             gm[k][e] = 0.0f;
             bt[k][e] = 0.0f;
-            if (o < seg_len) {
-                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : col_base + o;
+            if (o < w.seg_len) {
+                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : w.col_base + o;
                 gm[k][e] = to_f32(gamma[c]);
                 bt[k][e] = to_f32(beta[c]);
             }
         }
 
-    for (int64_t t = wg; t < g.ntiles; t += gridDim.x) {
-        int64_t base;
-        int len;
-        tile_extent(g, PACKED, t, col_base, seg_len, base, len);
-        const XT* __restrict__ xs = x + base;
-        XT* __restrict__ ys = y + base;
-        if (len == g.T) {
-            float v[K][V];
+    int64_t t = wg;
+    int64_t base = w.base;
+    if (t < w.nfull) {
+        typename R::T cur[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) cur[k] = R::load(x + base + sl.off[k]);
+        for (;;) {
+            const bool more = t + G < w.nfull;
+            const int64_t nbase = more ? base + w.step : base;
+            typename R::T nxt[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) nxt[k] = R::load(x + nbase + sl.off[k]);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                if (o < g.T) VecIO<XT, V>::load(xs + o, v[k]);
-            }
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                if (o < g.T) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        v[k][e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[k][e]), bt[k][e]);
-                    VecIO<XT, V>::store(ys + o, v[k]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                const int n = len - o;
-                if (n <= 0) continue;
                 float v[V];
-                if (n >= V) VecIO<XT, V>::load(xs + o, v);
-                else load_partial<XT, V>(xs + o, n, v);
+                R::unpack(cur[k], v);
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-                if (n >= V) VecIO<XT, V>::store(ys + o, v);
-                else store_partial<XT, V>(ys + o, n, v);
+                if (sl.used[k]) R::store(y + base + sl.off[k], v);
+            }
+            if (!more) break;
+#pragma unroll
+            for (int k = 0; k < K; ++k) cur[k] = nxt[k];
+            t += G;
+            base = nbase;
+        }
+    }
+
+    if (PACKED && w.tail) {
+        const int64_t tb = w.nfull * (int64_t)g.T;
+        const int len = (int)(g.total - tb);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int o = (k * kBlock + tid) * V;
+            const int n = len - o;
+            if (n > 0) {
+                float v[V];
+                if (n >= V) R::unpack(R::load(x + tb + o), v);
+                else load_partial<XT, V>(x + tb + o, n, v);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
+                if (n >= V) R::store(y + tb + o, v);
+                else store_partial<XT, V>(y + tb + o, n, v);
             }
         }
     }
@@ -237,102 +285,125 @@ dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
 
 // ---------------------------------------------------------------- backward
 // Pass 1: dx, plus one float32 partial row per workgroup.
+template <typename XT, int V, int K, bool ACC>
+__device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)[V],
+                                         const float (&gm)[V], float alpha, float (&out)[V],
+                                         float (&ag)[V], float (&ab)[V], float& aa) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float th, sd;
+        dyt_tanh_sech2<ACC>(xv[e], alpha, th, sd);
+        const float gd = (dv[e] * gm[e]) * sd;     // dy * gamma * sech^2
+        out[e] = gd * alpha;
+        ag[e] = __builtin_fmaf(dv[e], th, ag[e]);
+        ab[e] += dv[e];
+        aa = __builtin_fmaf(gd, xv[e], aa);
+    }
+}
+
 template <typename XT, typename PT, int V, int K, bool PACKED>
 __global__ void __launch_bounds__(kBlock)
 dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                        const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
                        XT* __restrict__ dx, float* __restrict__ ws, const Geo g) {
+    using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
     const int64_t wg = blockIdx.x;
+    const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    int64_t col_base;
-    int seg_len;
-    block_columns(g, PACKED, wg, col_base, seg_len);
+    const TileWalk w = make_walk(g, PACKED, wg, G);
+    const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
 
     float gm[K][V], ag[K][V], ab[K][V];
-    float aa = 0.0f;
+    float aa[K];     // dalpha partial per slot: unused slots are dropped at the end
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+    for (int k = 0; k < K; ++k) {
+        aa[k] = 0.0f;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const int o = (k * kBlock + tid) * V + e;
             ag[k][e] = 0.0f;
             ab[k][e] = 0.0f;
             gm[k][e] = 0.0f;
-            if (o < seg_len) {
-                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : col_base + o;
+            if (o < w.seg_len) {
+                const int64_t c = PACKED ? (int64_t)(o % (int)g.N) : w.col_base + o;
                 gm[k][e] = to_f32(gamma[c]);
             }
         }
+    }
 
-    for (int64_t t = wg; t < g.ntiles; t += gridDim.x) {
-        int64_t base;
-        int len;
-        tile_extent(g, PACKED, t, col_base, seg_len, base, len);
-        const XT* __restrict__ xs = x + base;
-        const XT* __restrict__ ds = dy + base;
-        XT* __restrict__ os = dx + base;
-        if (len == g.T) {
-            float xv[K][V], dv[K][V];
+    int64_t t = wg;
+    int64_t base = w.base;
+    if (t < w.nfull) {
+        typename R::T cx[K], cd[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            cx[k] = R::load(x + base + sl.off[k]);
+            cd[k] = R::load(dy + base + sl.off[k]);
+        }
+        for (;;) {
+            const bool more = t + G < w.nfull;
+            const int64_t nbase = more ? base + w.step : base;
+            typename R::T nx[K], nd[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                if (o < g.T) {
-                    VecIO<XT, V>::load(xs + o, xv[k]);
-                    VecIO<XT, V>::load(ds + o, dv[k]);
-                }
+                nx[k] = R::load(x + nbase + sl.off[k]);
+                nd[k] = R::load(dy + nbase + sl.off[k]);
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                if (o < g.T) {
-                    float out[V];
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        float th, sd;
-                        dyt_tanh_sech2<ACC>(alpha * xv[k][e], th, sd);
-                        const float gd = (dv[k][e] * gm[k][e]) * sd;   // dy*gamma*sech^2
-                        out[e] = gd * alpha;
-                        ag[k][e] = __builtin_fmaf(dv[k][e], th, ag[k][e]);
-                        ab[k][e] += dv[k][e];
-                        aa = __builtin_fmaf(gd, xv[k][e], aa);
-                    }
-                    VecIO<XT, V>::store(os + o, out);
-                }
+                float xv[V], dv[V], out[V];
+                R::unpack(cx[k], xv);
+                R::unpack(cd[k], dv);
+                bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
+                if (sl.used[k]) R::store(dx + base + sl.off[k], out);
             }
-        } else {
+            if (!more) break;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const int o = (k * kBlock + tid) * V;
-                const int n = len - o;
-                if (n <= 0) continue;
+                cx[k] = nx[k];
+                cd[k] = nd[k];
+            }
+            t += G;
+            base = nbase;
+        }
+    }
+
+    if (PACKED && w.tail) {
+        const int64_t tb = w.nfull * (int64_t)g.T;
+        const int len = (int)(g.total - tb);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int o = (k * kBlock + tid) * V;
+            const int n = len - o;
+            if (n > 0) {
                 float xv[V], dv[V], out[V];
                 if (n >= V) {
-                    VecIO<XT, V>::load(xs + o, xv);
-                    VecIO<XT, V>::load(ds + o, dv);
+                    R::unpack(R::load(x + tb + o), xv);
+                    R::unpack(R::load(dy + tb + o), dv);
                 } else {
-                    load_partial<XT, V>(xs + o, n, xv);
-                    load_partial<XT, V>(ds + o, n, dv);
+                    load_partial<XT, V>(x + tb + o, n, xv);
+                    load_partial<XT, V>(dy + tb + o, n, dv);
                 }
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     float th, sd;
-                    dyt_tanh_sech2<ACC>(alpha * xv[e], th, sd);
+                    dyt_tanh_sech2<ACC>(xv[e], alpha, th, sd);
                     const float gd = (dv[e] * gm[k][e]) * sd;
                     out[e] = gd * alpha;
-                    // Mask after the arithmetic: a lane past the end computed
-                    // on zeros (tanh(inf * 0) = NaN when alpha = inf); the
-                    // select drops whatever it produced.
+                    // Mask after the arithmetic: a lane past the end computed on
+                    // zeros (tanh(inf * 0) = NaN when alpha = inf); the select
+                    // drops whatever it produced.
                     const bool ok = e < n;
                     const float cg = dv[e] * th;
                     const float ca = gd * xv[e];
                     ag[k][e] += ok ? cg : 0.0f;
                     ab[k][e] += ok ? dv[e] : 0.0f;
-                    aa += ok ? ca : 0.0f;
+                    aa[k] += ok ? ca : 0.0f;
                 }
-                if (n >= V) VecIO<XT, V>::store(os + o, out);
-                else store_partial<XT, V>(os + o, n, out);
+                if (n >= V) R::store(dx + tb + o, out);
+                else store_partial<XT, V>(dx + tb + o, n, out);
             }
         }
     }
@@ -340,7 +411,9 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     // ---- workgroup reduction into one partial row
     float* __restrict__ wrow = ws + wg * (int64_t)g.ld;
     __shared__ float red[kBlock / 64];
-    float v = aa;
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v += sl.used[k] ? aa[k] : 0.0f;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     if ((tid & 63) == 0) red[tid >> 6] = v;
@@ -349,7 +422,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
         __shared__ float sh[K * kBlock * V];
         __shared__ float sh2[kBlock];
         const int N = (int)g.N;
-        const int R = g.R;
+        const int Rr = g.R;
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             __syncthreads();
@@ -363,24 +436,24 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             __syncthreads();
             float* __restrict__ dst = wrow + (pass ? g.wcols : 0);
             if (N <= kBlock) {
-                // groups of N threads; group j sums rows j, j+G, ... in order
-                const int G = kBlock / N;
-                if (tid < G * N) {
+                // groups of N threads; group j sums rows j, j+G2, ... in order
+                const int G2 = kBlock / N;
+                if (tid < G2 * N) {
                     const int c = tid % N;
                     float s = 0.0f;
-                    for (int r = tid / N; r < R; r += G) s += sh[r * N + c];
+                    for (int r = tid / N; r < Rr; r += G2) s += sh[r * N + c];
                     sh2[tid] = s;
                 }
                 __syncthreads();
                 if (tid < N) {
                     float s = sh2[tid];
-                    for (int j = 1; j < G; ++j) s += sh2[j * N + tid];
+                    for (int j = 1; j < G2; ++j) s += sh2[j * N + tid];
                     dst[tid] = s;
                 }
             } else {
                 for (int c = tid; c < N; c += kBlock) {
                     float s = 0.0f;
-                    for (int r = 0; r < R; ++r) s += sh[r * N + c];
+                    for (int r = 0; r < Rr; ++r) s += sh[r * N + c];
                     dst[c] = s;
                 }
             }
@@ -391,7 +464,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int o = (k * kBlock + tid) * V + e;
-                if (o < seg_len) {
+                if (o < w.seg_len) {
                     wrow[o] = ag[k][e];
                     wrow[g.wcols + o] = ab[k][e];
                 }
@@ -401,7 +474,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     if (tid == 0) {
         float s = red[0];
 #pragma unroll
-        for (int w = 1; w < kBlock / 64; ++w) s += red[w];
+        for (int q = 1; q < kBlock / 64; ++q) s += red[q];
         wrow[2 * g.wcols] = s;
     }
 }

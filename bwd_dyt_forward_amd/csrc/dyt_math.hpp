@@ -20,7 +20,8 @@
 //     Bernoulli numbers). About 3-5 float32 ulp on t and on sech^2.
 //   * fast (bfloat16 outputs): e straight from the hardware 2^x and 1/x
 //     (about 1e-5 relative at |u| = 50, far below half a bfloat16 ulp);
-//     tanh u ~= u below 2^-6 (relative error < 1e-4).
+//     in the forward tanh u ~= u below 2^-6 (relative error < 1e-4), in the
+//     backward u - u^3/3 below 2^-5.
 //
 // IEEE behaviour is kept on purpose: u = +-inf gives t = +-1, d = 0; NaN
 // propagates. Branches are selects evaluated after both sides are
@@ -76,16 +77,32 @@ __device__ __forceinline__ float tanh_series_tail(float s) {
 
 constexpr float kAccurateSmall = 0.35f;
 
-// Accurate tanh(u) and sech^2(u) (float32 outputs).
-__device__ __forceinline__ void tanh_sech2_accurate(float u, float& t, float& d) {
+// Accurate tanh(u) and sech^2(u) (float32 outputs) for u = alpha * x.
+// sech^2 has relative condition number 2|u tanh u| in u, so rounding u to
+// float32 alone would cost ~|u| * 1.2e-7 relative error; the product is
+// therefore carried as u + ul (ul = fma(alpha, x, -u), exact), and ul enters
+// the reduced exponent argument. tanh is well conditioned and uses u only.
+__device__ __forceinline__ void tanh_sech2_accurate(float x, float alpha, float& t, float& d) {
+    const float u = alpha * x;
+    const float ul = __builtin_fmaf(alpha, x, -u);
     const float a = __builtin_fabsf(u);
-    // large |u|
-    const float e = exp_nonpos_accurate(-2.0f * a);
+    // large |u|: e = exp(-2|u + ul|) = exp(z + zl), z = -2|u|,
+    // zl = -2 sign(u) ul; Cody-Waite reduction
+    float z = -2.0f * a;
+    float zl = ul * copy_sign(2.0f, -u);
+    const bool under = z < -104.0f;           // e rounds to 0; also u = +-inf
+    z = under ? -104.0f : z;
+    zl = under ? 0.0f : zl;                   // fma(inf, x, -inf) is NaN: drop it
+    const float k = __builtin_rintf(z * kLog2e);
+    float r = __builtin_fmaf(-k, kLn2Hi, z);
+    r = r + zl;
+    r = __builtin_fmaf(-k, kLn2Lo, r);
+    const float e = __builtin_amdgcn_ldexpf(hw_exp2(r * kLog2e), (int)k);
     const float p = 1.0f + e;
-    float r = hw_rcp(p);
-    r = __builtin_fmaf(r, __builtin_fmaf(-p, r, 1.0f), r);   // Newton step
-    const float tl = (1.0f - e) * r;
-    const float dl = ((4.0f * e) * r) * r;
+    float rc = hw_rcp(p);
+    rc = __builtin_fmaf(rc, __builtin_fmaf(-p, rc, 1.0f), rc);   // Newton step
+    const float tl = (1.0f - e) * rc;
+    const float dl = ((4.0f * e) * rc) * rc;
     // small |u|
     const float s = u * u;
     const float ts = __builtin_fmaf(u * s, tanh_series_tail(s), u);
@@ -119,13 +136,18 @@ __device__ __forceinline__ float tanh_fast(float u) {
     return (a < kFastSmall) ? u : copy_sign(tl, u);
 }
 
-// Fast tanh and sech^2 for the backward. t only feeds the dgamma sums, where
-// its absolute error (~1e-7 near u = 0) is what matters, so no small branch.
+// Fast tanh and sech^2 for the backward. t feeds the float32 dgamma sums,
+// which are compared at 1e-5 relative, so small |u| keeps two series terms
+// (u - u^3/3, relative error < 2e-7 below 2^-5) where 1 - e cancels.
+constexpr float kFastSmallBwd = 0x1p-5f;
+
 __device__ __forceinline__ void tanh_sech2_fast(float u, float& t, float& d) {
     const float a = __builtin_fabsf(u);
     const float e4 = hw_exp2(__builtin_fmaf(a, kMinus2Log2e, 2.0f));
     const float r = hw_rcp(__builtin_fmaf(e4, 0.25f, 1.0f));
-    t = copy_sign(__builtin_fmaf(e4, -0.25f, 1.0f) * r, u);
+    const float tl = copy_sign(__builtin_fmaf(e4, -0.25f, 1.0f) * r, u);
+    const float ts = __builtin_fmaf(u * (u * u), -0x1.555556p-2f, u);
+    t = (a < kFastSmallBwd) ? ts : tl;
     d = (e4 * r) * r;
 }
 
