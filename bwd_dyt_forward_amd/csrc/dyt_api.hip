@@ -13,19 +13,30 @@
 #include "dyt.h"
 #include "dyt_kernels.hpp"
 
-// Persistent-grid sizes (workgroups). 256 CUs x 8 (forward) and x 4
-// (backward: up to four persistent workgroups per CU, as the Liger-Kernel
-// DyT pull request's Summary ("Small widths") does for its row-tiled
-// backward). Wide rows use fewer backward workgroups: every one of them
-// writes a full partial row of 2N+1 floats.
+// Persistent-grid sizes (workgroups): one 256-thread workgroup per compute
+// unit of MI355X (256 CUs) for every kernel. Measured on the 32768 x 4096
+// and 4194304 x 32 bfloat16 workloads, one workgroup per CU streamed HBM
+// faster than 2-8 per CU (fewer concurrent streams), and grids that are not
+// a multiple of the CU count lose to load imbalance. The constants are not
+// queried from the device so that the summation order - and every result
+// bit - depends on the problem shape only.
 #ifndef DYT_FWD_GRID
-#define DYT_FWD_GRID 2048
+#define DYT_FWD_GRID 256
 #endif
 #ifndef DYT_BWD_GRID
-#define DYT_BWD_GRID 1024
+#define DYT_BWD_GRID 256
 #endif
 #ifndef DYT_BWD_GRID_WIDE
-#define DYT_BWD_GRID_WIDE 512
+#define DYT_BWD_GRID_WIDE 256
+#endif
+// Tiles per pipeline buffer (loads in flight per wave = U * K per input):
+// the forward has one input stream and needs two tiles in flight, the
+// backward's two input streams already keep enough bytes in flight.
+#ifndef DYT_FWD_U
+#define DYT_FWD_U 2
+#endif
+#ifndef DYT_BWD_U
+#define DYT_BWD_U 1
 #endif
 // Tiles wanted before a packed plan stops shrinking K for more parallelism.
 #ifndef DYT_MIN_TILES
@@ -182,10 +193,10 @@ void launch_fwd_vk(const Plan& p, const Geo& g, const void* x, const void* a, co
                    const void* bt, void* y, hipStream_t s) {
     const dim3 grid((unsigned)p.fwd_grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, true>), grid, block, 0, s,
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, DYT_FWD_U, true>), grid, block, 0, s,
                            (const XT*)x, (const PT*)a, (const PT*)gm, (const PT*)bt, (XT*)y, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, DYT_FWD_U, false>), grid, block, 0, s,
                            (const XT*)x, (const PT*)a, (const PT*)gm, (const PT*)bt, (XT*)y, g);
 }
 
@@ -194,10 +205,10 @@ void launch_bwd_vk(const Plan& p, const Geo& g, const void* x, const void* dy, c
                    const void* gm, void* dx, float* ws, hipStream_t s) {
     const dim3 grid((unsigned)p.bwd_grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, true>), grid, block, 0, s,
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true>), grid, block, 0, s,
                            (const XT*)x, (const XT*)dy, (const PT*)a, (const PT*)gm, (XT*)dx, ws, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false>), grid, block, 0, s,
                            (const XT*)x, (const XT*)dy, (const PT*)a, (const PT*)gm, (XT*)dx, ws, g);
 }
 

@@ -184,33 +184,42 @@ __device__ __forceinline__ Slots<V, K> make_slots(int tid, int seg_len) {
     return s;
 }
 
-// Tiles handled by workgroup wg: t = wg, wg + G, ...; tiles [0, nfull) are
-// whole, a packed problem whose size is not a multiple of T has one last
-// partial tile (index nfull) that only workgroup nfull % G handles.
+// Work of one workgroup. The data is cut into "units" of equal shape:
+// whole tiles (packed) or rows (row segments; the workgroup owns one column
+// block of every row). Units are taken in groups of U adjacent units, so a
+// group is one contiguous run of memory (packed) or U row segments one row
+// apart; groups are dealt round-robin to the gcount workgroups that share a
+// column block: group index gw, gw + gcount, ... Units left over after the
+// last whole group (fewer than U) are dealt the same way one by one, and a
+// packed problem whose size is not a multiple of T has one partial tile
+// (index units) that workgroup units % gcount handles with masks.
 struct TileWalk {
-    int64_t nfull;     // number of whole tiles
-    int64_t base;      // element index of this workgroup's first tile
-    int64_t step;      // elements between consecutive tiles of this workgroup
-    int64_t col_base;  // first column of this workgroup's block
-    int seg_len;       // columns (row segments) or elements (packed) per tile
+    int64_t units;     // whole units
+    int64_t unit;      // elements between consecutive units (T or N)
+    int64_t gw;        // this workgroup's index among those of its column block
+    int64_t gcount;    // workgroups per column block (G / nb)
+    int64_t col_base;  // first column of this workgroup's block (0 when packed)
+    int seg_len;       // elements (packed) or columns (row segments) per tile
     bool tail;         // this workgroup also owns the partial packed tile
 };
 
 __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G) {
     TileWalk w;
     if (packed) {
-        w.nfull = g.total / g.T;
-        w.base = wg * g.T;
-        w.step = G * g.T;
+        w.units = g.total / g.T;
+        w.unit = g.T;
+        w.gw = wg;
+        w.gcount = G;
         w.col_base = 0;
         w.seg_len = g.T;
-        w.tail = (w.nfull < g.ntiles) && (wg == w.nfull % G);
+        w.tail = (w.units * (int64_t)g.T < g.total) && (wg == w.units % G);
     } else {
         const int b = (int)(wg % g.nb);
-        w.nfull = g.ntiles;
+        w.units = g.ntiles / g.nb;   // rows
+        w.unit = g.N;
+        w.gw = wg / g.nb;
+        w.gcount = G / g.nb;
         w.col_base = (int64_t)b * g.T;
-        w.base = (wg / g.nb) * g.N + w.col_base;
-        w.step = (G / g.nb) * g.N;
         w.seg_len = (b == g.nb - 1) ? g.last_len : g.T;
         w.tail = false;
     }
@@ -228,35 +237,41 @@ __device__ __forceinline__ void dyt_tanh_sech2(float xv, float alpha, float& t, 
     else tanh_sech2_fast(alpha * xv, t, d);
 }
 
-// One tile's loads (all K slots, raw registers) and the forward arithmetic
-// and stores of a loaded tile.
-template <typename XT, int V, int K>
-__device__ __forceinline__ void fwd_load(const XT* __restrict__ x, int64_t base,
-                                         const Slots<V, K>& sl, typename Raw<XT, V>::T (&r)[K]) {
+// Loads of U consecutive tiles of this workgroup (all K slots, raw
+// registers; tile j sits at base + j * step) and the forward arithmetic and
+// stores of such a loaded group.
+template <typename XT, int V, int K, int U>
+__device__ __forceinline__ void fwd_load(const XT* __restrict__ x, int64_t base, int64_t step,
+                                         const Slots<V, K>& sl,
+                                         typename Raw<XT, V>::T (&r)[U][K]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) r[k] = Raw<XT, V>::load(x + base + sl.off[k]);
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) r[j][k] = Raw<XT, V>::load(x + base + j * step + sl.off[k]);
 }
 
-template <typename XT, int V, int K, bool ACC>
-__device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&r)[K], XT* __restrict__ y,
-                                         int64_t base, const Slots<V, K>& sl,
-                                         const float (&gm)[K][V], const float (&bt)[K][V],
-                                         float alpha) {
+template <typename XT, int V, int K, int U, bool ACC>
+__device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&r)[U][K],
+                                         XT* __restrict__ y, int64_t base, int64_t step,
+                                         const Slots<V, K>& sl, const float (&gm)[K][V],
+                                         const float (&bt)[K][V], float alpha) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        float v[V];
-        Raw<XT, V>::unpack(r[k], v);
+    for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-        Raw<XT, V>::store(y + base + sl.off[k], v);
-    }
+        for (int k = 0; k < K; ++k) {
+            float v[V];
+            Raw<XT, V>::unpack(r[j][k], v);
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
+            Raw<XT, V>::store(y + base + j * step + sl.off[k], v);
+        }
 }
 
 // ---------------------------------------------------------------- forward
 // y = gamma * tanh(alpha * x) + beta. Loads of the next tile are issued
 // before the current tile is computed (register double buffering).
-template <typename XT, typename PT, int V, int K, bool PACKED>
+template <typename XT, typename PT, int V, int K, int U, bool PACKED>
 __global__ void __launch_bounds__(kBlock)
 dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, const PT* __restrict__ beta,
@@ -281,35 +296,45 @@ dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
             bt[k][e] = to_f32(beta[c]);
         }
 
-    // Persistent loop, two tiles per iteration in two register buffers (A and
-    // B): the loads of one tile are in flight while the other is computed.
-    // Each step's loads are pinned above the compute that follows them by a
-    // scheduling barrier. A last A load past this workgroup's tiles re-reads
-    // the previous tile (valid memory, never computed).
-    const int64_t iters = wg < w.nfull ? (w.nfull - wg + G - 1) / G : 0;
+    // Persistent loop over this workgroup's groups of U adjacent units,
+    // alternating between two register buffers (A and B): the loads of one
+    // group are in flight while the other group is computed. Each step's
+    // loads are pinned above the compute that follows them by a scheduling
+    // barrier. A last A load past this workgroup's groups re-reads the
+    // previous group (valid memory, never computed).
+    const int64_t ng = w.units / U;
+    const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
+    const int64_t gstep = w.gcount * U * w.unit;
     if (iters > 0) {
-        typename R::T ra[K], rb[K];
-        int64_t base_a = w.base;
-        fwd_load<XT, V, K>(x, base_a, sl, ra);
+        typename R::T ra[U][K], rb[U][K];
+        int64_t base_a = w.col_base + w.gw * U * w.unit;
+        fwd_load<XT, V, K, U>(x, base_a, w.unit, sl, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t base_b = base_a + w.step;
-            fwd_load<XT, V, K>(x, base_b, sl, rb);
+            const int64_t base_b = base_a + gstep;
+            fwd_load<XT, V, K, U>(x, base_b, w.unit, sl, rb);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, ACC>(ra, y, base_a, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC>(ra, y, base_a, w.unit, sl, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + w.step : base_b;
-            fwd_load<XT, V, K>(x, base_n, sl, ra);
+            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
+            fwd_load<XT, V, K, U>(x, base_n, w.unit, sl, ra);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, ACC>(rb, y, base_b, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC>(rb, y, base_b, w.unit, sl, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
             base_a = base_n;
         }
-        if (iters & 1) fwd_tile<XT, V, K, ACC>(ra, y, base_a, sl, gm, bt, alpha);
+        if (iters & 1) fwd_tile<XT, V, K, U, ACC>(ra, y, base_a, w.unit, sl, gm, bt, alpha);
+    }
+    // units after the last whole group (fewer than U in total)
+    for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
+        typename R::T r1[1][K];
+        const int64_t base_r = w.col_base + u * w.unit;
+        fwd_load<XT, V, K, 1>(x, base_r, w.unit, sl, r1);
+        fwd_tile<XT, V, K, 1, ACC>(r1, y, base_r, w.unit, sl, gm, bt, alpha);
     }
 
     if (PACKED && w.tail) {
-        const int64_t tb = w.nfull * (int64_t)g.T;
+        const int64_t tb = w.units * (int64_t)g.T;
         const int len = (int)(g.total - tb);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -347,35 +372,40 @@ __device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)
     }
 }
 
-template <typename XT, int V, int K>
+template <typename XT, int V, int K, int U>
 __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __restrict__ dy,
-                                         int64_t base, const Slots<V, K>& sl,
-                                         typename Raw<XT, V>::T (&rx)[K],
-                                         typename Raw<XT, V>::T (&rd)[K]) {
+                                         int64_t base, int64_t step, const Slots<V, K>& sl,
+                                         typename Raw<XT, V>::T (&rx)[U][K],
+                                         typename Raw<XT, V>::T (&rd)[U][K]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        rx[k] = Raw<XT, V>::load(x + base + sl.off[k]);
-        rd[k] = Raw<XT, V>::load(dy + base + sl.off[k]);
-    }
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            rx[j][k] = Raw<XT, V>::load(x + base + j * step + sl.off[k]);
+            rd[j][k] = Raw<XT, V>::load(dy + base + j * step + sl.off[k]);
+        }
 }
 
-template <typename XT, int V, int K, bool ACC>
-__device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[K],
-                                         const typename Raw<XT, V>::T (&rd)[K],
-                                         XT* __restrict__ dx, int64_t base, const Slots<V, K>& sl,
-                                         const float (&gm)[K][V], float alpha, float (&ag)[K][V],
-                                         float (&ab)[K][V], float (&aa)[K]) {
+template <typename XT, int V, int K, int U, bool ACC>
+__device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
+                                         const typename Raw<XT, V>::T (&rd)[U][K],
+                                         XT* __restrict__ dx, int64_t base, int64_t step,
+                                         const Slots<V, K>& sl, const float (&gm)[K][V],
+                                         float alpha, float (&ag)[K][V], float (&ab)[K][V],
+                                         float (&aa)[K]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        float xv[V], dv[V], out[V];
-        Raw<XT, V>::unpack(rx[k], xv);
-        Raw<XT, V>::unpack(rd[k], dv);
-        bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
-        Raw<XT, V>::store(dx + base + sl.off[k], out);
-    }
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float xv[V], dv[V], out[V];
+            Raw<XT, V>::unpack(rx[j][k], xv);
+            Raw<XT, V>::unpack(rd[j][k], dv);
+            bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
+            Raw<XT, V>::store(dx + base + j * step + sl.off[k], out);
+        }
 }
 
-template <typename XT, typename PT, int V, int K, bool PACKED>
+template <typename XT, typename PT, int V, int K, int U, bool PACKED>
 __global__ void __launch_bounds__(kBlock)
 dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                        const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
@@ -404,31 +434,40 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
         }
     }
 
-    // Same two-buffer persistent loop as the forward.
-    const int64_t iters = wg < w.nfull ? (w.nfull - wg + G - 1) / G : 0;
+    // Same two-buffer persistent loop over groups of U adjacent units as the
+    // forward.
+    const int64_t ng = w.units / U;
+    const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
+    const int64_t gstep = w.gcount * U * w.unit;
     if (iters > 0) {
-        typename R::T xa[K], da[K], xb[K], db[K];
-        int64_t base_a = w.base;
-        bwd_load<XT, V, K>(x, dy, base_a, sl, xa, da);
+        typename R::T xa[U][K], da[U][K], xb[U][K], db[U][K];
+        int64_t base_a = w.col_base + w.gw * U * w.unit;
+        bwd_load<XT, V, K, U>(x, dy, base_a, w.unit, sl, xa, da);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t base_b = base_a + w.step;
-            bwd_load<XT, V, K>(x, dy, base_b, sl, xb, db);
+            const int64_t base_b = base_a + gstep;
+            bwd_load<XT, V, K, U>(x, dy, base_b, w.unit, sl, xb, db);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, ACC>(xa, da, dx, base_a, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC>(xa, da, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + w.step : base_b;
-            bwd_load<XT, V, K>(x, dy, base_n, sl, xa, da);
+            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
+            bwd_load<XT, V, K, U>(x, dy, base_n, w.unit, sl, xa, da);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, ACC>(xb, db, dx, base_b, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC>(xb, db, dx, base_b, w.unit, sl, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             base_a = base_n;
         }
-        if (iters & 1) bwd_tile<XT, V, K, ACC>(xa, da, dx, base_a, sl, gm, alpha, ag, ab, aa);
+        if (iters & 1) bwd_tile<XT, V, K, U, ACC>(xa, da, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
+    }
+    for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
+        typename R::T x1[1][K], d1[1][K];
+        const int64_t base_r = w.col_base + u * w.unit;
+        bwd_load<XT, V, K, 1>(x, dy, base_r, w.unit, sl, x1, d1);
+        bwd_tile<XT, V, K, 1, ACC>(x1, d1, dx, base_r, w.unit, sl, gm, alpha, ag, ab, aa);
     }
 
     if (PACKED && w.tail) {
-        const int64_t tb = w.nfull * (int64_t)g.T;
+        const int64_t tb = w.units * (int64_t)g.T;
         const int len = (int)(g.total - tb);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
