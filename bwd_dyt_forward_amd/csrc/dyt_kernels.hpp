@@ -17,12 +17,14 @@
 //    width Wc. The grid size is a multiple of nb, so a workgroup always sees
 //    the same column block.
 //
-// The grid is one-dimensional and persistent: workgroup w processes tiles
-// w, w + G, w + 2G, ... (G = gridDim.x). Rows never map to a grid
-// dimension, so there is no 65,535 limit on M (the Liger-Kernel pull
-// request "fix(dyt): use a 1D grid and tile small-width rows", Summary,
-// "Launch limit" and "Small widths" bullets, describes both problems for
-// its Triton kernels; this is the CDNA4 design, not a translation).
+// The grid is one-dimensional and persistent (one workgroup per CU): groups
+// of U adjacent tiles are dealt round-robin to the workgroups, and each
+// workgroup pipelines its groups through two register buffers. Rows never
+// map to a grid dimension, so there is no 65,535 limit on M (the
+// Liger-Kernel pull request "fix(dyt): use a 1D grid and tile small-width
+// rows", Summary, "Launch limit" and "Small widths" bullets, describes both
+// problems for its Triton kernels; this is the CDNA4 design, not a
+// translation).
 //
 // Every tile except possibly the last (packed) takes an unmasked path. The
 // last tile masks lanes past the end of the data; the backward computes
