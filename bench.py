@@ -43,10 +43,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel and launch sources with comments and blank space
+    removed, so that counter figures stay attached to the code they measured."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
