@@ -50,8 +50,14 @@
 
 namespace dyt {
 
-constexpr int kBlock = 256;       // threads per workgroup (4 wave64s)
-constexpr int kTileCap = 4096;    // elements per tile at the largest K
+#ifndef DYT_BLOCK
+#define DYT_BLOCK 256
+#endif
+#ifndef DYT_TILE_CAP
+#define DYT_TILE_CAP 4096
+#endif
+constexpr int kBlock = DYT_BLOCK;       // threads per workgroup (wave64s x 64)
+constexpr int kTileCap = DYT_TILE_CAP;  // elements per tile at the largest K
 constexpr int kFinBlock = 1024;   // pass-2 threads: 64 outputs x 16 segments
 constexpr int kFinSegs = kFinBlock / 64;
 
@@ -87,26 +93,46 @@ struct FinGeo {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef DYT_FWD_NT
+#define DYT_FWD_NT 1
+#endif
+#ifndef DYT_BWD_NT
+#define DYT_BWD_NT 1
+#endif
+template <bool NT, typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void stream_store(T v, T* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 template <typename XT, int V> struct Raw;
 
 template <> struct Raw<float, 4> {
     using T = f32x4;
+    template <bool NT = true>
     static __device__ __forceinline__ T load(const float* p) {
-        return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        return stream_load<NT>(reinterpret_cast<const f32x4*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[4]) {
         v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
     }
+    template <bool NT = true>
     static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
         const f32x4 t = {v[0], v[1], v[2], v[3]};
-        __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+        stream_store<NT>(t, reinterpret_cast<f32x4*>(p));
     }
 };
 
 template <> struct Raw<bf16_t, 8> {
     using T = u32x4;
+    template <bool NT = true>
     static __device__ __forceinline__ T load(const bf16_t* p) {
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return stream_load<NT>(reinterpret_cast<const u32x4*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[8]) {
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -116,32 +142,37 @@ template <> struct Raw<bf16_t, 8> {
             v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
         }
     }
+    template <bool NT = true>
     static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
         const u32x4 t = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
                          pack2_bf16(v[6], v[7])};
-        __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+        stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
     }
 };
 
 template <> struct Raw<float, 1> {
     using T = float;
-    static __device__ __forceinline__ T load(const float* p) { return __builtin_nontemporal_load(p); }
+    template <bool NT = true>
+    static __device__ __forceinline__ T load(const float* p) { return stream_load<NT>(p); }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) { v[0] = r; }
+    template <bool NT = true>
     static __device__ __forceinline__ void store(float* p, const float (&v)[1]) {
-        __builtin_nontemporal_store(v[0], p);
+        stream_store<NT>(v[0], p);
     }
 };
 
 template <> struct Raw<bf16_t, 1> {
     using T = uint16_t;
+    template <bool NT = true>
     static __device__ __forceinline__ T load(const bf16_t* p) {
-        return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+        return stream_load<NT>(reinterpret_cast<const uint16_t*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) {
         v[0] = __builtin_bit_cast(float, (uint32_t)r << 16);
     }
+    template <bool NT = true>
     static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[1]) {
-        __builtin_nontemporal_store(from_f32<bf16_t>(v[0]).bits, reinterpret_cast<uint16_t*>(p));
+        stream_store<NT>(from_f32<bf16_t>(v[0]).bits, reinterpret_cast<uint16_t*>(p));
     }
 };
 
@@ -249,7 +280,7 @@ __device__ __forceinline__ void fwd_load(const XT* __restrict__ x, int64_t base,
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int k = 0; k < K; ++k) r[j][k] = Raw<XT, V>::load(x + base + j * step + sl.off[k]);
+        for (int k = 0; k < K; ++k) r[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(x + base + j * step + sl.off[k]);
 }
 
 template <typename XT, int V, int K, int U, bool ACC>
@@ -266,7 +297,7 @@ __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&r)[U][K]
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-            Raw<XT, V>::store(y + base + j * step + sl.off[k], v);
+            Raw<XT, V>::template store<DYT_FWD_NT>(y + base + j * step + sl.off[k], v);
         }
 }
 
@@ -383,8 +414,8 @@ __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __r
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            rx[j][k] = Raw<XT, V>::load(x + base + j * step + sl.off[k]);
-            rd[j][k] = Raw<XT, V>::load(dy + base + j * step + sl.off[k]);
+            rx[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(x + base + j * step + sl.off[k]);
+            rd[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dy + base + j * step + sl.off[k]);
         }
 }
 
@@ -403,7 +434,7 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
             Raw<XT, V>::unpack(rx[j][k], xv);
             Raw<XT, V>::unpack(rd[j][k], dv);
             bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
-            Raw<XT, V>::store(dx + base + j * step + sl.off[k], out);
+            Raw<XT, V>::template store<DYT_BWD_NT>(dx + base + j * step + sl.off[k], out);
         }
 }
 
@@ -610,8 +641,17 @@ dyt_bwd_finish_kernel(const float* __restrict__ ws, PT* __restrict__ dgamma,
         const int64_t i1 = (seg + 1) * nrows / kFinSegs;
         const int64_t stride = step * f.ld;
         const float* __restrict__ p = ws + (row0 + i0 * step) * f.ld + off;
-#pragma unroll 8
-        for (int64_t i = i0; i < i1; ++i, p += stride) acc += *p;
+        // 16 loads in flight per step (one round trip for the usual 256
+        // partial rows), summed in row order
+        int64_t i = i0;
+        for (; i + 16 <= i1; i += 16, p += 16 * stride) {
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = p[q * stride];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc += v[q];
+        }
+        for (; i < i1; ++i, p += stride) acc += *p;
     }
     __shared__ float red[kFinSegs][64];
     red[seg][lane] = acc;
