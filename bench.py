@@ -216,6 +216,48 @@ def cpu_baseline(name: str, seconds: float) -> dict:
                       f"{el:.1f}s on 1 pinned core"}
 
 
+def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
+    """Every workload shape: steady-state forward / backward times (HIP events,
+    means over `steps` continuous steps after `warmup`), written as Markdown."""
+    import workloads
+    floor_x = torch.zeros(1, 8, dtype=torch.float32, device="cuda")
+    floor_p = torch.ones(8, device="cuda")
+    a1 = torch.ones(1, device="cuda")
+    y1 = torch.empty_like(floor_x)
+    for _ in range(20):
+        dyt.dyt_forward(floor_x, a1, floor_p, floor_p, y=y1)
+    torch.cuda.synchronize()
+    fl = []
+    for _ in range(50):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dyt.dyt_forward(floor_x, a1, floor_p, floor_p, y=y1)
+        e1.record()
+        e1.synchronize()
+        fl.append(e0.elapsed_time(e1) * 1e3)
+    floor_us = statistics.median(fl)
+    rows = [f"Launch floor (1 x 8 forward, event to event): {floor_us:.1f} us", "",
+            "| workload | M x N | x/params | fwd us | fwd GB/s | fwd % | bwd us | bwd GB/s | bwd % | "
+            "step GB/s | step % | plan |",
+            "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
+    for name in workloads.config_names():
+        r = measure(dyt, torch, name, steps, warmup)
+        B = r["bytes"]
+        step_us = r["fwd_us_median"] + r["bwd_us_median"]
+        sgbps = (B["fwd"] + B["bwd"]) / (step_us * 1e-6) / 1e9
+        pl = r["plan"]
+        plan = (f"{'packed R=' + str(pl['rows_per_tile']) if pl['packed'] else 'rows nb=' + str(pl['col_blocks'])}"
+                f", V={pl['vec']} K={pl['slots']}, tiles {pl['tiles']}")
+        rows.append(f"| {name} | {r['M']} x {r['N']} | {r['x_dtype']}/{r['param_dtype']} | "
+                    f"{r['fwd_us_median']:.1f} | {r['fwd_gbps']:.0f} | {100 * r['fwd_frac']:.1f} | "
+                    f"{r['bwd_us_median']:.1f} | {r['bwd_gbps']:.0f} | {100 * r['bwd_frac']:.1f} | "
+                    f"{sgbps:.0f} | {100 * sgbps / HBM_PEAK_GBPS:.1f} | {plan} |")
+        log(rows[-1])
+    with open(path, "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
 def load_traffic(kernel: str) -> dict | None:
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -240,6 +282,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--all-configs", metavar="FILE", default=None,
+                    help="also time every workload shape and write a Markdown table to FILE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -265,6 +309,8 @@ def main() -> int:
         log(f"[bench] {json.dumps(sec)}")
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)
+    if args.all_configs:
+        report_all(dyt, torch, args.all_configs)
 
     ceiling = copy_ceiling(torch, main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] == "bf16" else 4))
     log(f"[bench] device copy ceiling: {ceiling:.1f} GB/s")

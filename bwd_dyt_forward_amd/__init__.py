@@ -22,7 +22,10 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
+from .module import DyT, DyTFunction, dyt  # noqa: E402,F401
+
 __all__ = [
+    "DyT", "DyTFunction", "dyt",
     "DYT_F32", "DYT_BF16", "DYT_OK", "DytError", "LIB_FILE", "lib",
     "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
     "dyt_backward_workspace_size",

@@ -1,0 +1,73 @@
+"""PyTorch autograd function and module for the DyT layer over the C ABI.
+
+``DyT(num_features)`` is a drop-in layer computing
+``y = weight * tanh(alpha * x) + bias`` over the last dimension of x, with
+scalar ``alpha`` and per-feature ``weight`` (gamma) and ``bias`` (beta), as
+the Liger-Kernel pull request "fix(dyt): use a 1D grid and tile small-width
+rows" treats it (Summary: y keeps x's dtype, the parameter gradients come
+back in the parameters' dtype). Forward and backward run in the HIP library;
+this module only reshapes to [M, N] and wires autograd.
+"""
+from __future__ import annotations
+
+import torch
+from torch import nn
+
+from . import _lib
+
+
+def _rows(t: torch.Tensor) -> torch.Tensor:
+    """[..., N] -> contiguous [M, N] (a view when t is already contiguous)."""
+    t = t.contiguous()
+    return t.view(-1, t.shape[-1])
+
+
+class DyTFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves x (the backward recomputes tanh from x)."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
+                beta: torch.Tensor) -> torch.Tensor:
+        x2 = _rows(x)
+        y = _lib.dyt_forward(x2, alpha, gamma, beta)
+        ctx.save_for_backward(x2, alpha, gamma)
+        ctx.x_shape = x.shape
+        return y.view(x.shape)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, alpha, gamma = ctx.saved_tensors
+        dy2 = _rows(dy.to(x2.dtype))
+        dx, dalpha, dgamma, dbeta = _lib.dyt_backward(x2, dy2, alpha, gamma)
+        return dx.view(ctx.x_shape), dalpha, dgamma, dbeta
+
+
+def dyt(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor) -> torch.Tensor:
+    """Functional form with autograd support."""
+    return DyTFunction.apply(x, alpha, gamma, beta)
+
+
+class DyT(nn.Module):
+    """Dynamic Tanh layer: ``weight * tanh(alpha * x) + bias`` over the last dim.
+
+    ``alpha_init`` defaults to 0.5; ``weight`` starts at 1 and ``bias`` at 0.
+    Parameters live in ``dtype`` (float32 or bfloat16); inputs may be float32
+    or bfloat16 independently of it.
+    """
+
+    def __init__(self, num_features: int, alpha_init: float = 0.5, dtype=torch.float32,
+                 device=None):
+        super().__init__()
+        kw = {"dtype": dtype, "device": device}
+        self.num_features = num_features
+        self.alpha = nn.Parameter(torch.full((1,), float(alpha_init), **kw))
+        self.weight = nn.Parameter(torch.ones(num_features, **kw))
+        self.bias = nn.Parameter(torch.zeros(num_features, **kw))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.num_features:
+            raise ValueError(f"expected last dimension {self.num_features}, got {x.shape[-1]}")
+        return DyTFunction.apply(x, self.alpha, self.weight, self.bias)
+
+    def extra_repr(self) -> str:
+        return f"{self.num_features}, alpha={float(self.alpha.detach().float().cpu()[0]):.4g}"

@@ -195,3 +195,12 @@ def test_split_backward_error_codes(dyt):
     assert L.dyt_backward_finish(ws, need - 16, A16 + 128, A16, A16 + 64, 4, 4, F32, F32, None) == E_WS
     assert L.dyt_backward_finish(ws, need, A16 + 128, A16, A16 + 8, 4, 4, F32, F32, None) == E_ARG
     assert L.dyt_backward_finish(ws, need, A16 + 128, A16, A16 + 64, 4, 4, 9, F32, None) == E_DT
+
+
+def test_module_constructs_on_cpu(dyt):
+    """The nn.Module drop-in builds its parameters without a GPU."""
+    layer = dyt.DyT(16, alpha_init=0.25)
+    assert layer.alpha.shape == (1,) and float(layer.alpha[0]) == 0.25
+    assert layer.weight.shape == (16,) and bool((layer.weight == 1).all())
+    assert layer.bias.shape == (16,) and not layer.bias.any()
+    assert "16" in repr(layer)
