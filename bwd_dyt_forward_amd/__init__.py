@@ -7,6 +7,7 @@ The Python functions below carry the ABI's names and only marshal tensors.
 """
 from ._lib import (  # noqa: F401
     DYT_BF16,
+    DYT_F16,
     DYT_F32,
     DYT_OK,
     LIB_FILE,
@@ -26,7 +27,7 @@ from .module import DyT, DyTFunction, dyt  # noqa: E402,F401
 
 __all__ = [
     "DyT", "DyTFunction", "dyt",
-    "DYT_F32", "DYT_BF16", "DYT_OK", "DytError", "LIB_FILE", "lib",
+    "DYT_F32", "DYT_BF16", "DYT_F16", "DYT_OK", "DytError", "LIB_FILE", "lib",
     "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
     "dyt_backward_workspace_size",
     "dyt_status_string", "dyt_abi_version", "dyt_get_plan",

@@ -18,9 +18,10 @@ from .build import LIB_PATH
 
 DYT_F32 = 0
 DYT_BF16 = 1
+DYT_F16 = 2
 DYT_OK = 0
 
-_TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16}
+_TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16, torch.float16: DYT_F16}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
 
 
@@ -86,7 +87,7 @@ def _code(dtype) -> int:
     if isinstance(dtype, int):
         return dtype
     if isinstance(dtype, str):
-        return {"f32": DYT_F32, "bf16": DYT_BF16}[dtype]
+        return {"f32": DYT_F32, "bf16": DYT_BF16, "f16": DYT_F16}[dtype]
     try:
         return _TORCH_TO_CODE[dtype]
     except KeyError:

@@ -67,8 +67,19 @@ struct Plan {
     int64_t ws_bytes = 0;
 };
 
-bool dtype_ok(int d) { return d == DYT_F32 || d == DYT_BF16; }
+bool dtype_ok(int d) { return d == DYT_F32 || d == DYT_BF16 || d == DYT_F16; }
 int64_t dtype_size(int d) { return d == DYT_F32 ? 4 : 2; }
+
+// Calls f.template operator()<T>() with T the storage type of dtype code d.
+template <typename F>
+bool with_dtype(int d, F&& f) {
+    switch (d) {
+        case DYT_F32: return f(float{});
+        case DYT_BF16: return f(dyt::bf16_t{});
+        case DYT_F16: return f(dyt::f16_t{});
+        default: return false;
+    }
+}
 int64_t gcd64(int64_t a, int64_t b) {
     while (b) {
         const int64_t t = a % b;
@@ -312,13 +323,11 @@ int enqueue_pass1(const Plan& base, const void* x, const void* dy, const void* a
     const Plan p = variant_for(base, aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16));
     const Geo g = make_geo(p, M, N);
     float* ws = static_cast<float*>(workspace);
-    bool ok;
-    if (x_dtype == DYT_F32)
-        ok = param_dtype == DYT_F32 ? launch_bwd<float, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
-                                    : launch_bwd<float, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
-    else
-        ok = param_dtype == DYT_F32 ? launch_bwd<bf16_t, float>(p, g, x, dy, alpha, gamma, dx, ws, s)
-                                    : launch_bwd<bf16_t, bf16_t>(p, g, x, dy, alpha, gamma, dx, ws, s);
+    const bool ok = with_dtype(x_dtype, [&](auto xt) {
+        return with_dtype(param_dtype, [&](auto pt) {
+            return launch_bwd<decltype(xt), decltype(pt)>(p, g, x, dy, alpha, gamma, dx, ws, s);
+        });
+    });
     if (!ok) return DYT_ERR_INVALID_ARG;
     return hip_status();
 }
@@ -326,8 +335,10 @@ int enqueue_pass1(const Plan& base, const void* x, const void* dy, const void* a
 int enqueue_pass2(const Plan& base, const void* workspace, void* dalpha, void* dgamma,
                   void* dbeta, int64_t N, int param_dtype, hipStream_t s) {
     const float* ws = static_cast<const float*>(workspace);
-    if (param_dtype == DYT_F32) launch_finish<float>(base, N, ws, dgamma, dbeta, dalpha, s);
-    else launch_finish<bf16_t>(base, N, ws, dgamma, dbeta, dalpha, s);
+    with_dtype(param_dtype, [&](auto pt) {
+        launch_finish<decltype(pt)>(base, N, ws, dgamma, dbeta, dalpha, s);
+        return true;
+    });
     return hip_status();
 }
 
@@ -396,13 +407,11 @@ int dyt_forward(const void* x, const void* alpha, const void* gamma, const void*
     const Plan p = variant_for(base, aligned(x, 16) && aligned(y, 16));
     const Geo g = make_geo(p, M, N);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    bool ok;
-    if (x_dtype == DYT_F32)
-        ok = param_dtype == DYT_F32 ? launch_fwd<float, float>(p, g, x, alpha, gamma, beta, y, s)
-                                    : launch_fwd<float, bf16_t>(p, g, x, alpha, gamma, beta, y, s);
-    else
-        ok = param_dtype == DYT_F32 ? launch_fwd<bf16_t, float>(p, g, x, alpha, gamma, beta, y, s)
-                                    : launch_fwd<bf16_t, bf16_t>(p, g, x, alpha, gamma, beta, y, s);
+    const bool ok = with_dtype(x_dtype, [&](auto xt) {
+        return with_dtype(param_dtype, [&](auto pt) {
+            return launch_fwd<decltype(xt), decltype(pt)>(p, g, x, alpha, gamma, beta, y, s);
+        });
+    });
     if (!ok) return DYT_ERR_INVALID_ARG;   // no kernel instance for this plan (not reachable)
     return hip_status();
 }

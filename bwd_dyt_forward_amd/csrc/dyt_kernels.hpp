@@ -150,6 +150,43 @@ template <> struct Raw<bf16_t, 8> {
     }
 };
 
+template <> struct Raw<f16_t, 8> {
+    using T = u32x4;
+    template <bool NT = true>
+    static __device__ __forceinline__ T load(const f16_t* p) {
+        return stream_load<NT>(reinterpret_cast<const u32x4*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const T& r, float (&v)[8]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+            v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+        }
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store(f16_t* p, const float (&v)[8]) {
+        const u32x4 t = {pack2_f16(v[0], v[1]), pack2_f16(v[2], v[3]), pack2_f16(v[4], v[5]),
+                         pack2_f16(v[6], v[7])};
+        stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
+    }
+};
+
+template <> struct Raw<f16_t, 1> {
+    using T = uint16_t;
+    template <bool NT = true>
+    static __device__ __forceinline__ T load(const f16_t* p) {
+        return stream_load<NT>(reinterpret_cast<const uint16_t*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) {
+        v[0] = (float)__builtin_bit_cast(_Float16, r);
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store(f16_t* p, const float (&v)[1]) {
+        stream_store<NT>(from_f32<f16_t>(v[0]).bits, reinterpret_cast<uint16_t*>(p));
+    }
+};
+
 template <> struct Raw<float, 1> {
     using T = float;
     template <bool NT = true>

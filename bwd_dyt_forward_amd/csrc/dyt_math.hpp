@@ -157,9 +157,17 @@ struct bf16_t {
     uint16_t bits;
 };
 
+// IEEE binary16 is carried as its raw 16-bit pattern as well.
+struct f16_t {
+    uint16_t bits;
+};
+
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) {
     return __builtin_bit_cast(float, (uint32_t)v.bits << 16);
+}
+__device__ __forceinline__ float to_f32(f16_t v) {
+    return (float)__builtin_bit_cast(_Float16, v.bits);
 }
 
 // float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
@@ -171,10 +179,22 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// float32 -> float16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack2_f16(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    const h2 r = __builtin_convertvector(v, h2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
     return bf16_t{(uint16_t)(pack2_bf16(v, 0.0f) & 0xffffu)};
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v) {
+    return f16_t{__builtin_bit_cast(uint16_t, (_Float16)v)};
 }
 
 }  // namespace dyt

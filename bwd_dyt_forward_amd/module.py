@@ -51,8 +51,8 @@ class DyT(nn.Module):
     """Dynamic Tanh layer: ``weight * tanh(alpha * x) + bias`` over the last dim.
 
     ``alpha_init`` defaults to 0.5; ``weight`` starts at 1 and ``bias`` at 0.
-    Parameters live in ``dtype`` (float32 or bfloat16); inputs may be float32
-    or bfloat16 independently of it.
+    Parameters live in ``dtype`` (float32, bfloat16 or float16); inputs may be
+    any of the three independently of it.
     """
 
     def __init__(self, num_features: int, alpha_init: float = 0.5, dtype=torch.float32,

@@ -31,7 +31,7 @@
  *     alpha, dalpha point to one element; gamma, beta, dgamma, dbeta to N.
  *   - x, dy, y, dx have the x dtype; alpha, gamma, beta, dalpha, dgamma,
  *     dbeta have the parameter dtype. Supported dtypes: DYT_F32, DYT_BF16
- *     for both.
+ *     and DYT_F16 for both, in any combination.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is only enqueued; no call synchronises. Outputs are valid once
  *     the stream reaches that point; inputs must stay unchanged until then.
@@ -52,7 +52,8 @@
  *     on (M, N, x dtype) and on whether x/dy/dx are 16-byte aligned; no
  *     floating-point atomics.
  *   - Arithmetic is float32 throughout (accumulation included); bfloat16
- *     results are rounded to nearest even. float32 subnormals are kept.
+ *     and float16 results are rounded to nearest even (values beyond the
+ *     float16 range become +-inf). float32 subnormals are kept.
  */
 #ifndef DYT_H_
 #define DYT_H_
@@ -68,7 +69,8 @@ extern "C" {
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
-    DYT_BF16 = 1  /* bfloat16: 8 exponent bits, 7 fraction bits */
+    DYT_BF16 = 1, /* bfloat16: 8 exponent bits, 7 fraction bits */
+    DYT_F16 = 2   /* IEEE binary16: 5 exponent bits, 10 fraction bits */
 } dyt_dtype;
 
 typedef enum dyt_status {

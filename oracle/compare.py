@@ -15,6 +15,8 @@ match exactly):
   intermediate float32 underflow of sech^2 (|alpha x| > ~43.7, where
   float32 keeps fewer than 24 bits): floor = 2^-149 * (1 + 4 |dy gamma alpha|).
 * dx, bfloat16: |dx_gpu - rne_bf16(dx*)| <= 1 ulp_bf16(|dx*|).
+* float16 outputs follow the bfloat16 rules with float16 rounding and ulps
+  (11 significant bits, subnormal spacing 2^-24, overflow to +-inf).
 * dgamma, dbeta, dalpha (float32 accumulation):
   |g_gpu - g*| <= 1e-5 * max(|g*|, RSS_g) + 2^-149, RSS_g the root sum of
   squares of the summed terms (random-sign sums are compared at the scale
@@ -28,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "rne_bf16", "ulp_bf16", "rne", "Report",
+    "rne_bf16", "ulp_bf16", "rne_f16", "ulp_f16", "rne", "ulp", "Report",
     "check_y", "check_dx", "check_grad",
 ]
 
@@ -67,12 +69,52 @@ def ulp_bf16(v) -> np.ndarray:
     return u.reshape(a0.shape)
 
 
+def rne_f16(v) -> np.ndarray:
+    """Round float64 values to IEEE binary16 (11 significant bits, subnormal
+    spacing 2^-24, largest finite 65504), round-to-nearest-even, in one step
+    on the scaled integer grid (no intermediate float32 rounding); values that
+    round past 65504 become +-inf."""
+    v0 = np.asarray(v, dtype=np.float64)
+    v = np.atleast_1d(v0)
+    out = v.copy()
+    fin = np.isfinite(v)
+    a = np.abs(v[fin])
+    _, e = np.frexp(a)
+    sp = np.maximum(e - 11, -24)
+    q = np.rint(np.ldexp(a, -sp))
+    r = np.ldexp(q, sp)
+    r[r >= 65520.0] = np.inf          # 65504 + half its spacing rounds to even = inf
+    out[fin] = np.copysign(r, v[fin])
+    return out.reshape(v0.shape)
+
+
+def ulp_f16(v) -> np.ndarray:
+    """Spacing of float16 values at magnitude |v| (2^-24 below 2^-14)."""
+    a0 = np.abs(np.asarray(v, dtype=np.float64))
+    a = np.atleast_1d(a0)
+    _, e = np.frexp(a)
+    e = np.where(a == 0, -14, e)
+    u = np.ldexp(np.ones_like(a), np.maximum(e - 11, -24))
+    u[~np.isfinite(a)] = np.inf
+    return u.reshape(a0.shape)
+
+
 def rne(v, dtype: str) -> np.ndarray:
     """Round float64 values to the given storage dtype (RNE), as float64."""
     if dtype == "f32":
         return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "bf16":
         return rne_bf16(v)
+    if dtype == "f16":
+        return rne_f16(v)
+    raise ValueError(dtype)
+
+
+def ulp(v, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return ulp_bf16(v)
+    if dtype == "f16":
+        return ulp_f16(v)
     raise ValueError(dtype)
 
 
@@ -129,9 +171,9 @@ def check_y(got, y_ref, scale, dtype: str, name: str = "y") -> Report:
     scale = np.asarray(scale, dtype=np.float64)
     if dtype == "f32":
         return _finish(name, got, y_ref, 1e-6 * scale)
-    if dtype == "bf16":
-        return _finish(name, got, rne_bf16(y_ref),
-                       ulp_bf16(np.maximum(np.abs(y_ref), scale)))
+    if dtype in ("bf16", "f16"):
+        return _finish(name, got, rne(y_ref, dtype),
+                       ulp(np.maximum(np.abs(y_ref), scale), dtype))
     raise ValueError(dtype)
 
 
@@ -144,8 +186,8 @@ def check_dx(got, dx_ref, dtype: str, dy_gamma_alpha=None, name: str = "dx") -> 
     if dtype == "f32":
         k = 0.0 if dy_gamma_alpha is None else 4.0 * np.abs(np.asarray(dy_gamma_alpha, np.float64))
         return _finish(name, got, dx_ref, 1e-6 * np.abs(dx_ref) + _F32_TINY * (1.0 + k))
-    if dtype == "bf16":
-        return _finish(name, got, rne_bf16(dx_ref), ulp_bf16(dx_ref))
+    if dtype in ("bf16", "f16"):
+        return _finish(name, got, rne(dx_ref, dtype), ulp(dx_ref, dtype))
     raise ValueError(dtype)
 
 
@@ -155,6 +197,6 @@ def check_grad(got, g_ref, rss, dtype: str, name: str = "grad") -> Report:
     got = np.atleast_1d(np.asarray(got, dtype=np.float64))
     if dtype == "f32":
         return _finish(name, got, g_ref, 1e-5 * np.maximum(np.abs(g_ref), rss) + _F32_TINY)
-    if dtype == "bf16":
-        return _finish(name, got, rne_bf16(g_ref), ulp_bf16(g_ref) + 1e-5 * rss)
+    if dtype in ("bf16", "f16"):
+        return _finish(name, got, rne(g_ref, dtype), ulp(g_ref, dtype) + 1e-5 * rss)
     raise ValueError(dtype)

@@ -9,7 +9,7 @@ import torch
 
 from oracle import compare, dyt_oracle
 
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def log(msg: str) -> None:

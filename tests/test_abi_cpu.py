@@ -62,6 +62,7 @@ def test_version_and_status_strings(dyt):
 CONFIG_SHAPES = [
     (1024, 64, "f32"), (65537, 16, "bf16"), (100003, 17, "f32"), (100003, 100, "f32"),
     (100003, 255, "f32"), (32768, 4096, "bf16"), (4194304, 32, "bf16"),
+    (65537, 16, "f16"), (32768, 4096, "f16"), (1031, 300, "f16"),
 ]
 
 
@@ -69,7 +70,7 @@ CONFIG_SHAPES = [
 @pytest.mark.parametrize("vec", [True, False])
 def test_plan_invariants(dyt, M, N, xdt, vec):
     p = dyt.dyt_get_plan(M, N, xdt, "f32", vec)
-    sx = 4 if xdt == "f32" else 2
+    sx = 4 if xdt == "f32" else 2       # bf16 and f16 are both 2 bytes
     cap = p["block"] * p["vec"] * p["slots"]
     assert p["block"] == 256
     assert p["vec"] == (16 // sx if vec and (p["packed"] or (N * sx) % 16 == 0) else 1)
@@ -143,7 +144,7 @@ def _bwd(dyt, x=A16, dy=A16 + 0x100000, a=A16 + 0x200000, g=A16 + 0x300000, dx=A
 
 
 def test_forward_error_codes(dyt):
-    assert _fwd(dyt, xdt=2) == E_DT
+    assert _fwd(dyt, xdt=3) == E_DT
     assert _fwd(dyt, pdt=-1) == E_DT
     assert _fwd(dyt, M=-1) == E_ARG
     assert _fwd(dyt, N=-3) == E_ARG

@@ -17,7 +17,7 @@ def dyt():
     return m
 
 
-@pytest.mark.parametrize("xdt,pdt", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("xdt,pdt", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")])
 @pytest.mark.parametrize("shape", [(4, 129, 64), (3, 5, 4096), (1000, 17)])
 def test_module_forward_backward_matches_oracle(dyt, xdt, pdt, shape):
     log(f"[module] shape={shape} x={xdt} p={pdt}")

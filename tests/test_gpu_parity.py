@@ -66,6 +66,9 @@ SWEEP = [
     (7, 4100, "bf16", "f32", 0.5), (5, 8192, "bf16", "f32", 0.5), (3, 20000, "f32", "f32", 0.3),
     (301, 64, "f32", "bf16", 0.5), (300, 4096, "bf16", "bf16", 0.5), (1031, 17, "bf16", "bf16", 2.0),
     (4099, 8, "f32", "f32", 3.0), (1, 7, "f32", "f32", 0.5),
+    # float16 activations and/or parameters
+    (65537, 16, "f16", "f32", 0.8), (37, 4096, "f16", "f32", 0.5), (1031, 300, "f16", "f16", 1.5),
+    (513, 17, "f32", "f16", 0.9), (257, 64, "bf16", "f16", 0.7), (9, 4100, "f16", "bf16", 0.5),
 ]
 
 

@@ -406,3 +406,26 @@ def test_checkers_accept_2d_bounds():
     assert rep.ok and rep.n == 12
     rep = C.check_dx(ref * (1 + 1e-5), ref, "f32", np.ones((3, 4)))
     assert rep.n_fail == 12
+
+
+def test_rne_f16_matches_torch_for_float32_inputs():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    v = np.concatenate([
+        (rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000)).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65504.0, 65519.0, 65520.0,
+                  2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 6e-8, np.inf, -np.inf], dtype=np.float32),
+    ]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float16).to(torch.float64).numpy()
+    got = C.rne_f16(v.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_rne_f16_direct_rounding_and_ulp():
+    assert C.rne_f16(1 + 2.0 ** -11) == 1.0                      # tie to even
+    assert C.rne_f16(1 + 2.0 ** -11 + 2.0 ** -40) == 1 + 2.0 ** -10
+    assert C.rne_f16(65520.0) == np.inf and C.rne_f16(65519.99) == 65504.0
+    assert C.rne_f16(2.0 ** -25) == 0.0 and C.rne_f16(3 * 2.0 ** -25) == 2.0 ** -23
+    assert C.ulp_f16(1.0) == 2.0 ** -10 and C.ulp_f16(0.0) == 2.0 ** -24
+    assert C.ulp_f16(2.0 ** -15) == 2.0 ** -24 and C.ulp_f16(1000.0) == 0.5

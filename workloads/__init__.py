@@ -41,8 +41,8 @@ class Config:
     name: str
     M: int
     N: int
-    x_dtype: str          # "f32" | "bf16"
-    p_dtype: str          # "f32" | "bf16"
+    x_dtype: str          # "f32" | "bf16" | "f16"
+    p_dtype: str          # "f32" | "bf16" | "f16"
     x_sigma: float        # standard deviation of x and dy
     alpha: float
     gamma: tuple          # ("normal", mean, sd) | ("uniform", lo, hi)
@@ -137,6 +137,8 @@ def _quantise(a32: np.ndarray, dtype: str) -> np.ndarray:
         return a32
     if dtype == "bf16":
         return _bits_to_f32(bf16_round_bits(a32))
+    if dtype == "f16":
+        return np.asarray(a32, dtype=np.float32).astype(np.float16).astype(np.float32)
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
@@ -215,8 +217,8 @@ def from_arrays(x, dy, alpha, gamma, beta, x_dtype: str, p_dtype: str,
     x = np.ascontiguousarray(x, dtype=np.float32)
     dy = np.ascontiguousarray(dy, dtype=np.float32)
     for arr, dt in ((x, x_dtype), (dy, x_dtype)):
-        if dt == "bf16" and not np.array_equal(_quantise(arr, "bf16"), arr, equal_nan=True):
-            raise ValueError("values not representable in bf16")
+        if dt != "f32" and not np.array_equal(_quantise(arr, dt), arr, equal_nan=True):
+            raise ValueError(f"values not representable in {dt}")
     return Inputs(name, x, dy,
                   np.ascontiguousarray(alpha, dtype=np.float32).reshape(1),
                   np.ascontiguousarray(gamma, dtype=np.float32),
