@@ -15,6 +15,12 @@ Algorithmic bytes (sx = x dtype size, sp = parameter dtype size):
   pass 1    3 M N sx + (N + 1) sp       pass 2   (2N + 1) sp
 (workspace traffic of the backward is excluded from the algorithmic bytes).
 
+Timing: W warm-up steps (extended by untimed steps until 0.3 s have passed,
+because the GPU clocks ramp for the first ~100 steps after idle), then three
+timed regions of K steps each: A without events inside (the reported value
+and ms_per_step), B with events around backward pass 1 (the roofline
+figure), C with events around every kernel (forward/backward breakdown).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -33,6 +39,7 @@ sys.path.insert(0, ROOT)
 HEADLINE = "c4_32768x4096_bf16"        # the transformer-block shape the 80% target names
 SECONDARY = "c5_4194304x32_bf16_outliers"  # the narrow-row bulk shape the 60% target names
 HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, vendor figure
+SETTLE_S = 0.3                         # minimum untimed warm-up wall time
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", f)
                   for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp")]
@@ -140,25 +147,40 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False)
         ev[1].record(stream)
         dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db, stream=stream)
 
-    for _ in range(warmup):
+    # Warm-up: `warmup` steps, extended by untimed steps until SETTLE_S of
+    # wall time has passed. On MI355X the first ~100 steps after idle run up
+    # to 1.6x slower while the clocks ramp; 0.3 s is several times that.
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t0 < SETTLE_S:
         step()
+        n_warm += 1
+        if n_warm % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # Timed region: `steps` whole steps; the only events inside bracket the
-    # dominant kernel (backward pass 1) for the roofline figure.
-    p1ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+
+    # Timed region A (the reported value): `steps` whole steps, no events
+    # inside (each event record costs ~3 us of step time on this GPU).
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     h0 = time.perf_counter()
     start.record(stream)
-    for i in range(steps):
-        step_p1_events(p1ev[i])
+    for _ in range(steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - h0
     total_ms = start.elapsed_time(end)
+
+    # Timed region B (roofline): the same steps with events around the
+    # dominant kernel (backward pass 1) on its launch stream.
+    p1ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step_p1_events(p1ev[i])
+    torch.cuda.synchronize()
     p1 = [e[0].elapsed_time(e[1]) for e in p1ev]
-    # Breakdown (separate loop, events around every kernel).
+
+    # Timed region C (breakdown): events around every kernel.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
@@ -172,7 +194,7 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False)
     ms_step = total_ms / steps
     res = {
         "workload": name, "M": M, "N": N, "x_dtype": cfg.x_dtype, "param_dtype": cfg.p_dtype,
-        "ms_per_step": ms_step, "host_s": host_s,
+        "ms_per_step": ms_step, "host_s": host_s, "warmup_steps_run": n_warm,
         "gbps_step": (B["fwd"] + B["bwd"]) / (ms_step * 1e-3) / 1e9,
         "fwd_us_median": statistics.median(fwd) * 1e3,
         "bwd_us_median": statistics.median(bwd) * 1e3,
@@ -391,6 +413,7 @@ def main() -> int:
         "ms_per_step": round(main_res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
+        "warmup_steps_run": main_res["warmup_steps_run"],
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
