@@ -585,56 +585,118 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     if ((tid & 63) == 0) red[tid >> 6] = v;
 
     if constexpr (PACKED) {
-        __shared__ float sh[K * kBlock * V];
-        __shared__ float sh2[kBlock];
+        // Column sums over the tile's R rows, dgamma and dbeta together. The
+        // tile goes to LDS as laid out in memory (element o = row o / N,
+        // column o mod N). With N <= block size, thread (j, c) = (tid / N,
+        // tid mod N) sums rows j, j + G2, j + 2 G2, ... of column c in that
+        // order (G2 = block / N groups), then thread c adds the G2 group sums
+        // in group order; wider packed rows sum all R rows per column in row
+        // order. Loads are issued eight at a time ahead of the additions,
+        // which keep their fixed order (bitwise the same as one at a time).
+        constexpr int kTile = K * kBlock * V;
+        __shared__ float4 shg4[kTile / 4], shb4[kTile / 4];
+        __shared__ float s2g[kBlock], s2b[kBlock];
+        float* const shg = reinterpret_cast<float*>(shg4);
+        float* const shb = reinterpret_cast<float*>(shb4);
         const int N = (int)g.N;
         const int Rr = g.R;
+        const int T = g.T;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int k = 0; k < K; ++k) {
+            const int o = (k * kBlock + tid) * V;
+            if constexpr (V % 4 == 0) {
+                if (o + V <= T) {
+#pragma unroll
+                    for (int e = 0; e < V; e += 4) {
+                        shg4[(o + e) / 4] = make_float4(ag[k][e], ag[k][e + 1], ag[k][e + 2], ag[k][e + 3]);
+                        shb4[(o + e) / 4] = make_float4(ab[k][e], ab[k][e + 1], ab[k][e + 2], ab[k][e + 3]);
+                    }
+                    continue;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (o + e < T) {
+                    shg[o + e] = ag[k][e];
+                    shb[o + e] = ab[k][e];
+                }
+        }
+        __syncthreads();
+        // sa += a[(first + i * step) * stride] for i = 0 .. count-1 in that
+        // order (sb likewise from b)
+        auto ordered_sum = [](const float* __restrict__ a, const float* __restrict__ b, int first,
+                              int step, int count, int stride, float& sa, float& sb) {
+            for (int i0 = 0; i0 < count; i0 += 8) {
+                float va[8], vb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int idx = (i0 + i < count) ? (first + (i0 + i) * step) * stride : 0;
+                    va[i] = a[idx];
+                    vb[i] = b[idx];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i0 + i < count) {
+                        sa += va[i];
+                        sb += vb[i];
+                    }
+            }
+        };
+        if (N <= kBlock) {
+            const int G2 = kBlock / N;
+            if (tid < G2 * N) {
+                const int c = tid % N;
+                const int j = tid / N;
+                const int nrow = j < Rr ? (Rr - j + G2 - 1) / G2 : 0;
+                float sg = 0.0f, sb = 0.0f;
+                ordered_sum(shg + c, shb + c, j, G2, nrow, N, sg, sb);
+                s2g[tid] = sg;
+                s2b[tid] = sb;
+            }
             __syncthreads();
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const int o = (k * kBlock + tid) * V + e;
-                    if (o < g.T) sh[o] = pass ? ab[k][e] : ag[k][e];
-                }
-            __syncthreads();
-            float* __restrict__ dst = wrow + (pass ? g.wcols : 0);
-            if (N <= kBlock) {
-                // groups of N threads; group j sums rows j, j+G2, ... in order
-                const int G2 = kBlock / N;
-                if (tid < G2 * N) {
-                    const int c = tid % N;
-                    float s = 0.0f;
-                    for (int r = tid / N; r < Rr; r += G2) s += sh[r * N + c];
-                    sh2[tid] = s;
-                }
-                __syncthreads();
-                if (tid < N) {
-                    float s = sh2[tid];
-                    for (int j = 1; j < G2; ++j) s += sh2[j * N + tid];
-                    dst[tid] = s;
-                }
-            } else {
-                for (int c = tid; c < N; c += kBlock) {
-                    float s = 0.0f;
-                    for (int r = 0; r < Rr; ++r) s += sh[r * N + c];
-                    dst[c] = s;
-                }
+            if (tid < N) {
+                float sg = s2g[tid], sb = s2b[tid];
+                ordered_sum(s2g + tid, s2b + tid, 1, 1, G2 - 1, N, sg, sb);
+                wrow[tid] = sg;
+                wrow[g.wcols + tid] = sb;
+            }
+        } else {
+            for (int c = tid; c < N; c += kBlock) {
+                float sg = 0.0f, sb = 0.0f;
+                ordered_sum(shg + c, shb + c, 0, 1, Rr, N, sg, sb);
+                wrow[c] = sg;
+                wrow[g.wcols + c] = sb;
             }
         }
     } else {
+        // Each thread owns V consecutive columns per slot: whole in-range
+        // groups go out as 16-byte stores (the partial row, ld and the column
+        // block width are all multiples of 4 floats, the workspace 16-byte
+        // aligned); only the ragged end of the last column block is written
+        // element by element. Element-wise stores here, lanes 4*V bytes
+        // apart, cost about 2% of the pass at N = 4096.
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < K; ++k) {
+            const int o = (k * kBlock + tid) * V;
+            if constexpr (V % 4 == 0) {
+                if (o + V <= w.seg_len) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const int o = (k * kBlock + tid) * V + e;
-                if (o < w.seg_len) {
-                    wrow[o] = ag[k][e];
-                    wrow[g.wcols + o] = ab[k][e];
+                    for (int e = 0; e < V; e += 4) {
+                        *reinterpret_cast<float4*>(wrow + o + e) =
+                            make_float4(ag[k][e], ag[k][e + 1], ag[k][e + 2], ag[k][e + 3]);
+                        *reinterpret_cast<float4*>(wrow + g.wcols + o + e) =
+                            make_float4(ab[k][e], ab[k][e + 1], ab[k][e + 2], ab[k][e + 3]);
+                    }
+                    continue;
                 }
             }
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (o + e < w.seg_len) {
+                    wrow[o + e] = ag[k][e];
+                    wrow[g.wcols + o + e] = ab[k][e];
+                }
+        }
     }
     __syncthreads();
     if (tid == 0) {

@@ -91,6 +91,8 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
         assert p["col_blocks"] * p["tile_elems"] >= N > (p["col_blocks"] - 1) * p["tile_elems"]
         assert p["tiles"] == M * p["col_blocks"]
         assert p["bwd_grid"] % p["col_blocks"] == 0 and p["fwd_grid"] % p["col_blocks"] == 0
+        # pass 1 writes whole column groups of its partial row as 16-byte stores
+        assert p["tile_elems"] % 4 == 0 and p["tile_elems"] % p["vec"] == 0
     assert 1 <= p["fwd_grid"] <= p["tiles"] and 1 <= p["bwd_grid"] <= p["tiles"]
     wcols = N if p["packed"] else p["tile_elems"]
     assert p["ws_row"] >= 2 * wcols + 1 and p["ws_row"] % 4 == 0
