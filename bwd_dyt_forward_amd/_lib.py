@@ -55,6 +55,11 @@ SIGNATURES = {
     "dyt_backward_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
                                      _int, _int, _vp]),
     "dyt_backward_finish": (_int, [_vp, ctypes.c_size_t, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
+    "dyt_forward_residual": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_residual": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_residual_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                              _i64, _i64, _int, _int, _vp]),
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
@@ -200,6 +205,81 @@ def dyt_backward_finish(workspace: torch.Tensor, M: int, N: int, x_dtype,
                                  _stream(stream))
     _check("dyt_backward_finish", st)
     return dalpha, dgamma, dbeta
+
+
+def _same(name: str, t: torch.Tensor, ref: torch.Tensor) -> None:
+    _check_act(name, t)
+    if t.shape != ref.shape or t.dtype != ref.dtype:
+        raise ValueError(f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+
+
+def dyt_forward_residual(x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor,
+                         gamma: torch.Tensor, beta: torch.Tensor, h: torch.Tensor | None = None,
+                         y: torch.Tensor | None = None, stream=None):
+    """h = x + r (rounded to x's dtype), y = gamma * tanh(alpha * h) + beta; returns (h, y)."""
+    _check_act("x", x)
+    _same("r", r, x)
+    M, N = x.shape
+    _check_params(N, alpha, gamma, beta)
+    if h is None:
+        h = torch.empty_like(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.dyt_forward_residual(_ptr(x), _ptr(r), _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(h),
+                                  _ptr(y), M, N, _code(x.dtype), _code(alpha.dtype),
+                                  _stream(stream))
+    _check("dyt_forward_residual", st)
+    return h, y
+
+
+def dyt_backward_residual(h: torch.Tensor, dy: torch.Tensor, dres: torch.Tensor,
+                          alpha: torch.Tensor, gamma: torch.Tensor, dh: torch.Tensor | None = None,
+                          dalpha: torch.Tensor | None = None, dgamma: torch.Tensor | None = None,
+                          dbeta: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          stream=None):
+    """dh = dres + (DyT backward of dy at h); returns (dh, dalpha, dgamma, dbeta)."""
+    _check_act("h", h)
+    _same("dy", dy, h)
+    _same("dres", dres, h)
+    M, N = h.shape
+    _check_params(N, alpha, gamma)
+    pdt = alpha.dtype
+    dev = h.device
+    if dh is None:
+        dh = torch.empty_like(h)
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=pdt, device=dev)
+    if dgamma is None:
+        dgamma = torch.empty(N, dtype=pdt, device=dev)
+    if dbeta is None:
+        dbeta = torch.empty(N, dtype=pdt, device=dev)
+    need = dyt_backward_workspace_size(M, N, h.dtype, pdt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.dyt_backward_residual(_ptr(h), _ptr(dy), _ptr(dres), _ptr(alpha), _ptr(gamma),
+                                   _ptr(dh), _ptr(dalpha), _ptr(dgamma), _ptr(dbeta),
+                                   _ptr(workspace), wbytes, M, N, _code(h.dtype), _code(pdt),
+                                   _stream(stream))
+    _check("dyt_backward_residual", st)
+    return dh, dalpha, dgamma, dbeta
+
+
+def dyt_backward_residual_partials(h: torch.Tensor, dy: torch.Tensor, dres: torch.Tensor,
+                                   alpha: torch.Tensor, gamma: torch.Tensor, dh: torch.Tensor,
+                                   workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """First pass of the residual backward: dh plus the partial rows in workspace."""
+    _check_act("h", h)
+    _same("dy", dy, h)
+    _same("dres", dres, h)
+    M, N = h.shape
+    _check_params(N, alpha, gamma)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.dyt_backward_residual_partials(_ptr(h), _ptr(dy), _ptr(dres), _ptr(alpha),
+                                            _ptr(gamma), _ptr(dh), _ptr(workspace), wbytes, M, N,
+                                            _code(h.dtype), _code(alpha.dtype), _stream(stream))
+    _check("dyt_backward_residual_partials", st)
+    return dh
 
 
 def dyt_status_string(status: int) -> str:

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "dyt.h"
 #include "dyt_kernels.hpp"
@@ -37,6 +38,11 @@
 #endif
 #ifndef DYT_BWD_U
 #define DYT_BWD_U 1
+#endif
+// The residual forward streams two inputs and two outputs: one tile per
+// buffer, like the backward.
+#ifndef DYT_FWD_RES_U
+#define DYT_FWD_RES_U 1
 #endif
 // Tiles wanted before a packed plan stops shrinking K for more parallelism.
 #ifndef DYT_MIN_TILES
@@ -199,62 +205,86 @@ Range range(const void* p, int64_t bytes) {
 }
 
 // ------------------------------------------------------------- dispatch
-template <typename XT, typename PT, int V, int K>
-void launch_fwd_vk(const Plan& p, const Geo& g, const void* x, const void* a, const void* gm,
-                   const void* bt, void* y, hipStream_t s) {
+// Device pointers of one launch; r/h (forward) and dres (backward) are null
+// unless the residual add is fused.
+struct FwdPtrs {
+    const void* x;
+    const void* r;
+    const void* alpha;
+    const void* gamma;
+    const void* beta;
+    void* y;
+    void* h;
+};
+struct BwdPtrs {
+    const void* x;
+    const void* dy;
+    const void* dres;
+    const void* alpha;
+    const void* gamma;
+    void* dx;
+    float* ws;
+};
+
+template <typename XT, typename PT, int V, int K, bool RES>
+void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
+    constexpr int U = RES ? DYT_FWD_RES_U : DYT_FWD_U;
     const dim3 grid((unsigned)p.fwd_grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, DYT_FWD_U, true>), grid, block, 0, s,
-                           (const XT*)x, (const PT*)a, (const PT*)gm, (const PT*)bt, (XT*)y, g);
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES>), grid, block, 0, s,
+                           (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
+                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, DYT_FWD_U, false>), grid, block, 0, s,
-                           (const XT*)x, (const PT*)a, (const PT*)gm, (const PT*)bt, (XT*)y, g);
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, false, RES>), grid, block, 0, s,
+                           (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
+                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
 }
 
-template <typename XT, typename PT, int V, int K>
-void launch_bwd_vk(const Plan& p, const Geo& g, const void* x, const void* dy, const void* a,
-                   const void* gm, void* dx, float* ws, hipStream_t s) {
+template <typename XT, typename PT, int V, int K, bool RES>
+void launch_bwd_vk(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
     const dim3 grid((unsigned)p.bwd_grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true>), grid, block, 0, s,
-                           (const XT*)x, (const XT*)dy, (const PT*)a, (const PT*)gm, (XT*)dx, ws, g);
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true, RES>), grid,
+                           block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
+                           (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false>), grid, block, 0, s,
-                           (const XT*)x, (const XT*)dy, (const PT*)a, (const PT*)gm, (XT*)dx, ws, g);
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false, RES>), grid,
+                           block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
+                           (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
 }
 
 // Kernel instances: vector access at K in {1, 2, ..., 4096 / (256 V)}, and
-// the element-wise variant (V = 1) at K = 16.
-template <typename XT, typename PT>
-bool launch_fwd(const Plan& p, const Geo& g, const void* x, const void* a, const void* gm,
-                const void* bt, void* y, hipStream_t s) {
+// the element-wise variant (V = 1) at K = 16. dispatch_vk calls launch(V, K),
+// both as integral constants, for the instance the plan selects.
+template <typename XT, typename L>
+bool dispatch_vk(const Plan& p, L&& launch) {
     constexpr int VV = 16 / sizeof(XT);
-    if (p.vec == 1 && p.slots == 16) { launch_fwd_vk<XT, PT, 1, 16>(p, g, x, a, gm, bt, y, s); return true; }
+    if (p.vec == 1 && p.slots == 16) return launch(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
     if (p.vec != VV) return false;
     switch (p.slots) {
-        case 1: launch_fwd_vk<XT, PT, VV, 1>(p, g, x, a, gm, bt, y, s); return true;
-        case 2: launch_fwd_vk<XT, PT, VV, 2>(p, g, x, a, gm, bt, y, s); return true;
+        case 1: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 1>{});
+        case 2: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 2>{});
         case 4:
-            if constexpr (VV == 4) { launch_fwd_vk<XT, PT, VV, 4>(p, g, x, a, gm, bt, y, s); return true; }
+            if constexpr (VV == 4) return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 4>{});
             return false;
         default: return false;
     }
 }
 
-template <typename XT, typename PT>
-bool launch_bwd(const Plan& p, const Geo& g, const void* x, const void* dy, const void* a,
-                const void* gm, void* dx, float* ws, hipStream_t s) {
-    constexpr int VV = 16 / sizeof(XT);
-    if (p.vec == 1 && p.slots == 16) { launch_bwd_vk<XT, PT, 1, 16>(p, g, x, dy, a, gm, dx, ws, s); return true; }
-    if (p.vec != VV) return false;
-    switch (p.slots) {
-        case 1: launch_bwd_vk<XT, PT, VV, 1>(p, g, x, dy, a, gm, dx, ws, s); return true;
-        case 2: launch_bwd_vk<XT, PT, VV, 2>(p, g, x, dy, a, gm, dx, ws, s); return true;
-        case 4:
-            if constexpr (VV == 4) { launch_bwd_vk<XT, PT, VV, 4>(p, g, x, dy, a, gm, dx, ws, s); return true; }
-            return false;
-        default: return false;
-    }
+template <typename XT, typename PT, bool RES>
+bool launch_fwd(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
+    return dispatch_vk<XT>(p, [&](auto v, auto k) {
+        launch_fwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES>(p, g, a, s);
+        return true;
+    });
+}
+
+template <typename XT, typename PT, bool RES>
+bool launch_bwd(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
+    return dispatch_vk<XT>(p, [&](auto v, auto k) {
+        launch_bwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES>(p, g, a, s);
+        return true;
+    });
 }
 
 template <typename PT>
@@ -276,10 +306,11 @@ int hip_status() { return hipGetLastError() == hipSuccess ? DYT_OK : DYT_ERR_HIP
 
 // Shared validation of the backward entry points. Pointers a pass does not
 // use are passed as nullptr with use_* = false.
-int validate_backward(const void* x, const void* dy, const void* alpha, const void* gamma,
-                      void* dx, void* dalpha, void* dgamma, void* dbeta, const void* workspace,
-                      size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int param_dtype,
-                      bool use_pass1, bool use_pass2, Plan& base) {
+int validate_backward(const void* x, const void* dy, const void* dres, bool use_dres,
+                      const void* alpha, const void* gamma, void* dx, void* dalpha, void* dgamma,
+                      void* dbeta, const void* workspace, size_t workspace_bytes, int64_t M,
+                      int64_t N, int x_dtype, int param_dtype, bool use_pass1, bool use_pass2,
+                      Plan& base) {
     int st = make_plan(M, N, x_dtype, param_dtype, base);
     if (st != DYT_OK) return st;
     const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
@@ -289,7 +320,7 @@ int validate_backward(const void* x, const void* dy, const void* alpha, const vo
         if (!dalpha) return DYT_ERR_INVALID_ARG;
         if (N > 0 && (!dgamma || !dbeta)) return DYT_ERR_INVALID_ARG;
     }
-    if (p1 && (!x || !dy || !alpha || !gamma || !dx)) return DYT_ERR_INVALID_ARG;
+    if (p1 && (!x || !dy || !alpha || !gamma || !dx || (use_dres && !dres))) return DYT_ERR_INVALID_ARG;
     const size_t need = (size_t)round_up(base.ws_bytes, 16);
     if (workspace_bytes < need) return DYT_ERR_WORKSPACE_TOO_SMALL;
     if (need > 0 && !workspace) return DYT_ERR_INVALID_ARG;
@@ -297,15 +328,15 @@ int validate_backward(const void* x, const void* dy, const void* alpha, const vo
     if (use_pass2 && (!aligned(dalpha, sp) || (N > 0 && (!aligned(dgamma, sp) || !aligned(dbeta, sp)))))
         return DYT_ERR_MISALIGNED;
     if (p1 && (!aligned(x, sx) || !aligned(dy, sx) || !aligned(dx, sx) || !aligned(alpha, sp) ||
-               !aligned(gamma, sp)))
+               !aligned(gamma, sp) || (use_dres && !aligned(dres, sx))))
         return DYT_ERR_MISALIGNED;
     // outputs (and the workspace) must not overlap inputs or each other
     const int64_t mn = p1 ? M * N * sx : 0;
     const Range outs[5] = {range(dx, mn), range(dalpha, use_pass2 ? sp : 0),
                            range(dgamma, use_pass2 ? N * sp : 0), range(dbeta, use_pass2 ? N * sp : 0),
                            range(workspace, (int64_t)need)};
-    const Range ins[4] = {range(x, mn), range(dy, mn), range(alpha, p1 ? sp : 0),
-                          range(gamma, p1 ? N * sp : 0)};
+    const Range ins[5] = {range(x, mn), range(dy, mn), range(dres, use_dres ? mn : 0),
+                          range(alpha, p1 ? sp : 0), range(gamma, p1 ? N * sp : 0)};
     for (int a = 0; a < 5; ++a) {
         if (outs[a].lo == outs[a].hi) continue;
         for (const Range& i : ins)
@@ -316,16 +347,18 @@ int validate_backward(const void* x, const void* dy, const void* alpha, const vo
     return DYT_OK;
 }
 
-int enqueue_pass1(const Plan& base, const void* x, const void* dy, const void* alpha,
-                  const void* gamma, void* dx, void* workspace, int64_t M, int64_t N,
-                  int x_dtype, int param_dtype, hipStream_t s) {
+int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int x_dtype,
+                  int param_dtype, hipStream_t s) {
     if (M == 0 || N == 0) return DYT_OK;
-    const Plan p = variant_for(base, aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16));
+    const bool res = a.dres != nullptr;
+    const Plan p = variant_for(base, aligned(a.x, 16) && aligned(a.dy, 16) && aligned(a.dx, 16) &&
+                                         (!res || aligned(a.dres, 16)));
     const Geo g = make_geo(p, M, N);
-    float* ws = static_cast<float*>(workspace);
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return with_dtype(param_dtype, [&](auto pt) {
-            return launch_bwd<decltype(xt), decltype(pt)>(p, g, x, dy, alpha, gamma, dx, ws, s);
+            using XT = decltype(xt);
+            using PT = decltype(pt);
+            return res ? launch_bwd<XT, PT, true>(p, g, a, s) : launch_bwd<XT, PT, false>(p, g, a, s);
         });
     });
     if (!ok) return DYT_ERR_INVALID_ARG;
@@ -340,6 +373,58 @@ int enqueue_pass2(const Plan& base, const void* workspace, void* dalpha, void* d
         return true;
     });
     return hip_status();
+}
+
+// Forward with or without the fused residual add: validation, then launch.
+int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, int param_dtype,
+                 hipStream_t s) {
+    Plan base;
+    int st = make_plan(M, N, x_dtype, param_dtype, base);
+    if (st != DYT_OK) return st;
+    if (M == 0 || N == 0) return DYT_OK;
+    if (!a.x || !a.alpha || !a.gamma || !a.beta || !a.y || (res && (!a.r || !a.h)))
+        return DYT_ERR_INVALID_ARG;
+    const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
+    if (!aligned(a.x, sx) || !aligned(a.y, sx) || !aligned(a.alpha, sp) || !aligned(a.gamma, sp) ||
+        !aligned(a.beta, sp) || (res && (!aligned(a.r, sx) || !aligned(a.h, sx))))
+        return DYT_ERR_MISALIGNED;
+    // outputs must not overlap inputs or each other
+    const int64_t mn = M * N * sx;
+    const Range outs[2] = {range(a.y, mn), range(a.h, res ? mn : 0)};
+    const Range ins[5] = {range(a.x, mn), range(a.r, res ? mn : 0), range(a.alpha, sp),
+                          range(a.gamma, N * sp), range(a.beta, N * sp)};
+    for (const Range& o : outs) {
+        if (o.lo == o.hi) continue;
+        for (const Range& i : ins)
+            if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
+    }
+    if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
+    const Plan p = variant_for(base, aligned(a.x, 16) && aligned(a.y, 16) &&
+                                         (!res || (aligned(a.r, 16) && aligned(a.h, 16))));
+    const Geo g = make_geo(p, M, N);
+    const bool ok = with_dtype(x_dtype, [&](auto xt) {
+        return with_dtype(param_dtype, [&](auto pt) {
+            using XT = decltype(xt);
+            using PT = decltype(pt);
+            return res ? launch_fwd<XT, PT, true>(p, g, a, s) : launch_fwd<XT, PT, false>(p, g, a, s);
+        });
+    });
+    if (!ok) return DYT_ERR_INVALID_ARG;   // no kernel instance for this plan (not reachable)
+    return hip_status();
+}
+
+// Both passes, with or without the residual gradient (res: a.dres is used).
+int backward_impl(const BwdPtrs& a, bool res, void* dalpha, void* dgamma, void* dbeta,
+                  size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int param_dtype,
+                  hipStream_t s) {
+    Plan base;
+    int st = validate_backward(a.x, a.dy, a.dres, res, a.alpha, a.gamma, a.dx, dalpha, dgamma,
+                               dbeta, a.ws, workspace_bytes, M, N, x_dtype, param_dtype, true,
+                               true, base);
+    if (st != DYT_OK) return st;
+    st = enqueue_pass1(base, a, M, N, x_dtype, param_dtype, s);
+    if (st != DYT_OK) return st;
+    return enqueue_pass2(base, a.ws, dalpha, dgamma, dbeta, N, param_dtype, s);
 }
 
 }  // namespace
@@ -391,50 +476,49 @@ size_t dyt_backward_workspace_size(int64_t M, int64_t N, int x_dtype, int param_
 
 int dyt_forward(const void* x, const void* alpha, const void* gamma, const void* beta, void* y,
                 int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream) {
-    Plan base;
-    int st = make_plan(M, N, x_dtype, param_dtype, base);
-    if (st != DYT_OK) return st;
-    if (M == 0 || N == 0) return DYT_OK;
-    if (!x || !alpha || !gamma || !beta || !y) return DYT_ERR_INVALID_ARG;
-    const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
-    if (!aligned(x, sx) || !aligned(y, sx) || !aligned(alpha, sp) || !aligned(gamma, sp) ||
-        !aligned(beta, sp))
-        return DYT_ERR_MISALIGNED;
-    const Range ry = range(y, M * N * sx);
-    if (overlap(ry, range(x, M * N * sx)) || overlap(ry, range(alpha, sp)) ||
-        overlap(ry, range(gamma, N * sp)) || overlap(ry, range(beta, N * sp)))
-        return DYT_ERR_INVALID_ARG;
-    const Plan p = variant_for(base, aligned(x, 16) && aligned(y, 16));
-    const Geo g = make_geo(p, M, N);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool ok = with_dtype(x_dtype, [&](auto xt) {
-        return with_dtype(param_dtype, [&](auto pt) {
-            return launch_fwd<decltype(xt), decltype(pt)>(p, g, x, alpha, gamma, beta, y, s);
-        });
-    });
-    if (!ok) return DYT_ERR_INVALID_ARG;   // no kernel instance for this plan (not reachable)
-    return hip_status();
+    return forward_impl(FwdPtrs{x, nullptr, alpha, gamma, beta, y, nullptr}, false, M, N, x_dtype,
+                        param_dtype, static_cast<hipStream_t>(stream));
 }
 
+int dyt_forward_residual(const void* x, const void* r, const void* alpha, const void* gamma,
+                         const void* beta, void* h, void* y, int64_t M, int64_t N, int x_dtype,
+                         int param_dtype, void* stream) {
+    return forward_impl(FwdPtrs{x, r, alpha, gamma, beta, y, h}, true, M, N, x_dtype, param_dtype,
+                        static_cast<hipStream_t>(stream));
+}
 
 int dyt_backward_partials(const void* x, const void* dy, const void* alpha, const void* gamma,
                           void* dx, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
                           int x_dtype, int param_dtype, void* stream) {
     Plan base;
-    int st = validate_backward(x, dy, alpha, gamma, dx, nullptr, nullptr, nullptr, workspace,
-                               workspace_bytes, M, N, x_dtype, param_dtype, true, false, base);
+    int st = validate_backward(x, dy, nullptr, false, alpha, gamma, dx, nullptr, nullptr, nullptr,
+                               workspace, workspace_bytes, M, N, x_dtype, param_dtype, true, false,
+                               base);
     if (st != DYT_OK) return st;
-    return enqueue_pass1(base, x, dy, alpha, gamma, dx, workspace, M, N, x_dtype, param_dtype,
-                         static_cast<hipStream_t>(stream));
+    return enqueue_pass1(base, BwdPtrs{x, dy, nullptr, alpha, gamma, dx, static_cast<float*>(workspace)},
+                         M, N, x_dtype, param_dtype, static_cast<hipStream_t>(stream));
+}
+
+int dyt_backward_residual_partials(const void* h, const void* dy, const void* dres,
+                                   const void* alpha, const void* gamma, void* dh, void* workspace,
+                                   size_t workspace_bytes, int64_t M, int64_t N, int x_dtype,
+                                   int param_dtype, void* stream) {
+    Plan base;
+    int st = validate_backward(h, dy, dres, true, alpha, gamma, dh, nullptr, nullptr, nullptr,
+                               workspace, workspace_bytes, M, N, x_dtype, param_dtype, true, false,
+                               base);
+    if (st != DYT_OK) return st;
+    return enqueue_pass1(base, BwdPtrs{h, dy, dres, alpha, gamma, dh, static_cast<float*>(workspace)},
+                         M, N, x_dtype, param_dtype, static_cast<hipStream_t>(stream));
 }
 
 int dyt_backward_finish(const void* workspace, size_t workspace_bytes, void* dalpha,
                         void* dgamma, void* dbeta, int64_t M, int64_t N, int x_dtype,
                         int param_dtype, void* stream) {
     Plan base;
-    int st = validate_backward(nullptr, nullptr, nullptr, nullptr, nullptr, dalpha, dgamma, dbeta,
-                               workspace, workspace_bytes, M, N, x_dtype, param_dtype, false, true,
-                               base);
+    int st = validate_backward(nullptr, nullptr, nullptr, false, nullptr, nullptr, nullptr, dalpha,
+                               dgamma, dbeta, workspace, workspace_bytes, M, N, x_dtype,
+                               param_dtype, false, true, base);
     if (st != DYT_OK) return st;
     return enqueue_pass2(base, workspace, dalpha, dgamma, dbeta, N, param_dtype,
                          static_cast<hipStream_t>(stream));
@@ -444,14 +528,18 @@ int dyt_backward(const void* x, const void* dy, const void* alpha, const void* g
                  void* dalpha, void* dgamma, void* dbeta, void* workspace,
                  size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int param_dtype,
                  void* stream) {
-    Plan base;
-    int st = validate_backward(x, dy, alpha, gamma, dx, dalpha, dgamma, dbeta, workspace,
-                               workspace_bytes, M, N, x_dtype, param_dtype, true, true, base);
-    if (st != DYT_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = enqueue_pass1(base, x, dy, alpha, gamma, dx, workspace, M, N, x_dtype, param_dtype, s);
-    if (st != DYT_OK) return st;
-    return enqueue_pass2(base, workspace, dalpha, dgamma, dbeta, N, param_dtype, s);
+    return backward_impl(BwdPtrs{x, dy, nullptr, alpha, gamma, dx, static_cast<float*>(workspace)},
+                         false, dalpha, dgamma, dbeta, workspace_bytes, M, N, x_dtype, param_dtype,
+                         static_cast<hipStream_t>(stream));
+}
+
+int dyt_backward_residual(const void* h, const void* dy, const void* dres, const void* alpha,
+                          const void* gamma, void* dh, void* dalpha, void* dgamma, void* dbeta,
+                          void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                          int x_dtype, int param_dtype, void* stream) {
+    return backward_impl(BwdPtrs{h, dy, dres, alpha, gamma, dh, static_cast<float*>(workspace)},
+                         true, dalpha, dgamma, dbeta, workspace_bytes, M, N, x_dtype, param_dtype,
+                         static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -111,6 +111,9 @@ __device__ __forceinline__ void stream_store(T v, T* p) {
 }
 
 template <typename XT, int V> struct Raw;
+// Each Raw<XT, V> has: load (raw registers), unpack (to float32), pack (float32
+// to raw registers, rounding to nearest even), store_raw, and store = pack +
+// store_raw. pack followed by unpack yields the values as stored.
 
 template <> struct Raw<float, 4> {
     using T = f32x4;
@@ -121,10 +124,17 @@ template <> struct Raw<float, 4> {
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[4]) {
         v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
     }
+    static __device__ __forceinline__ T pack(const float (&v)[4]) {
+        const f32x4 t = {v[0], v[1], v[2], v[3]};
+        return t;
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(float* p, const T& t) {
+        stream_store<NT>(t, reinterpret_cast<f32x4*>(p));
+    }
     template <bool NT = true>
     static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
-        const f32x4 t = {v[0], v[1], v[2], v[3]};
-        stream_store<NT>(t, reinterpret_cast<f32x4*>(p));
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -142,11 +152,18 @@ template <> struct Raw<bf16_t, 8> {
             v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
         }
     }
-    template <bool NT = true>
-    static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
+    static __device__ __forceinline__ T pack(const float (&v)[8]) {
         const u32x4 t = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
                          pack2_bf16(v[6], v[7])};
+        return t;
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(bf16_t* p, const T& t) {
         stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -164,11 +181,18 @@ template <> struct Raw<f16_t, 8> {
             v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
         }
     }
-    template <bool NT = true>
-    static __device__ __forceinline__ void store(f16_t* p, const float (&v)[8]) {
+    static __device__ __forceinline__ T pack(const float (&v)[8]) {
         const u32x4 t = {pack2_f16(v[0], v[1]), pack2_f16(v[2], v[3]), pack2_f16(v[4], v[5]),
                          pack2_f16(v[6], v[7])};
+        return t;
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(f16_t* p, const T& t) {
         stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
+    }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store(f16_t* p, const float (&v)[8]) {
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -181,9 +205,14 @@ template <> struct Raw<f16_t, 1> {
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) {
         v[0] = (float)__builtin_bit_cast(_Float16, r);
     }
+    static __device__ __forceinline__ T pack(const float (&v)[1]) { return from_f32<f16_t>(v[0]).bits; }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(f16_t* p, const T& t) {
+        stream_store<NT>(t, reinterpret_cast<uint16_t*>(p));
+    }
     template <bool NT = true>
     static __device__ __forceinline__ void store(f16_t* p, const float (&v)[1]) {
-        stream_store<NT>(from_f32<f16_t>(v[0]).bits, reinterpret_cast<uint16_t*>(p));
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -192,9 +221,12 @@ template <> struct Raw<float, 1> {
     template <bool NT = true>
     static __device__ __forceinline__ T load(const float* p) { return stream_load<NT>(p); }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) { v[0] = r; }
+    static __device__ __forceinline__ T pack(const float (&v)[1]) { return v[0]; }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(float* p, const T& t) { stream_store<NT>(t, p); }
     template <bool NT = true>
     static __device__ __forceinline__ void store(float* p, const float (&v)[1]) {
-        stream_store<NT>(v[0], p);
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -207,9 +239,14 @@ template <> struct Raw<bf16_t, 1> {
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[1]) {
         v[0] = __builtin_bit_cast(float, (uint32_t)r << 16);
     }
+    static __device__ __forceinline__ T pack(const float (&v)[1]) { return from_f32<bf16_t>(v[0]).bits; }
+    template <bool NT = true>
+    static __device__ __forceinline__ void store_raw(bf16_t* p, const T& t) {
+        stream_store<NT>(t, reinterpret_cast<uint16_t*>(p));
+    }
     template <bool NT = true>
     static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[1]) {
-        stream_store<NT>(from_f32<bf16_t>(v[0]).bits, reinterpret_cast<uint16_t*>(p));
+        store_raw<NT>(p, pack(v));
     }
 };
 
@@ -309,43 +346,74 @@ __device__ __forceinline__ void dyt_tanh_sech2(float xv, float alpha, float& t, 
 
 // Loads of U consecutive tiles of this workgroup (all K slots, raw
 // registers; tile j sits at base + j * step) and the forward arithmetic and
-// stores of such a loaded group.
-template <typename XT, int V, int K, int U>
-__device__ __forceinline__ void fwd_load(const XT* __restrict__ x, int64_t base, int64_t step,
-                                         const Slots<V, K>& sl,
-                                         typename Raw<XT, V>::T (&r)[U][K]) {
-#pragma unroll
-    for (int j = 0; j < U; ++j)
-#pragma unroll
-        for (int k = 0; k < K; ++k) r[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(x + base + j * step + sl.off[k]);
-}
-
-template <typename XT, int V, int K, int U, bool ACC>
-__device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&r)[U][K],
-                                         XT* __restrict__ y, int64_t base, int64_t step,
-                                         const Slots<V, K>& sl, const float (&gm)[K][V],
-                                         const float (&bt)[K][V], float alpha) {
+// stores of such a loaded group. With RES the residual r is loaded beside x,
+// h = x + r is rounded to the storage type and stored, and y is computed
+// from the stored h.
+template <typename XT, int V, int K, int U, bool RES>
+__device__ __forceinline__ void fwd_load(const XT* __restrict__ x, const XT* __restrict__ r,
+                                         int64_t base, int64_t step, const Slots<V, K>& sl,
+                                         typename Raw<XT, V>::T (&rx)[U][K],
+                                         typename Raw<XT, V>::T (&rr)[U][K]) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
+            rx[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(x + base + j * step + sl.off[k]);
+            if constexpr (RES)
+                rr[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(r + base + j * step + sl.off[k]);
+        }
+}
+
+// v = x (+ r, rounded to XT and stored to h when RES)
+template <typename XT, int V, bool RES>
+__device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
+                                          const typename Raw<XT, V>::T& rr, XT* __restrict__ h,
+                                          float (&v)[V]) {
+    using R = Raw<XT, V>;
+    R::unpack(rx, v);
+    if constexpr (RES) {
+        float rv[V];
+        R::unpack(rr, rv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] += rv[e];
+        const typename R::T hr = R::pack(v);
+        R::template store_raw<DYT_FWD_NT>(h, hr);
+        R::unpack(hr, v);
+    }
+}
+
+template <typename XT, int V, int K, int U, bool ACC, bool RES>
+__device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
+                                         const typename Raw<XT, V>::T (&rr)[U][K],
+                                         XT* __restrict__ y, XT* __restrict__ h, int64_t base,
+                                         int64_t step, const Slots<V, K>& sl,
+                                         const float (&gm)[K][V], const float (&bt)[K][V],
+                                         float alpha) {
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t at = base + j * step + sl.off[k];
             float v[V];
-            Raw<XT, V>::unpack(r[j][k], v);
+            fwd_input<XT, V, RES>(rx[j][k], rr[j][k], h + at, v);
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-            Raw<XT, V>::template store<DYT_FWD_NT>(y + base + j * step + sl.off[k], v);
+            Raw<XT, V>::template store<DYT_FWD_NT>(y + at, v);
         }
 }
 
 // ---------------------------------------------------------------- forward
-// y = gamma * tanh(alpha * x) + beta. Loads of the next tile are issued
-// before the current tile is computed (register double buffering).
-template <typename XT, typename PT, int V, int K, int U, bool PACKED>
+// y = gamma * tanh(alpha * x) + beta; with RES (residual add fused in front)
+// h = x + r and y = gamma * tanh(alpha * h) + beta. Loads of the next tile
+// are issued before the current tile is computed (register double
+// buffering). r and h are unused (null) without RES.
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES>
 __global__ void __launch_bounds__(kBlock)
-dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
-               const PT* __restrict__ gamma, const PT* __restrict__ beta,
-               XT* __restrict__ y, const Geo g) {
+dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
+               const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
+               const PT* __restrict__ beta, XT* __restrict__ y, XT* __restrict__ h,
+               const Geo g) {
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -376,31 +444,31 @@ dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
     const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
     const int64_t gstep = w.gcount * U * w.unit;
     if (iters > 0) {
-        typename R::T ra[U][K], rb[U][K];
+        typename R::T xa[U][K], xb[U][K], ra[U][K], rb[U][K];
         int64_t base_a = w.col_base + w.gw * U * w.unit;
-        fwd_load<XT, V, K, U>(x, base_a, w.unit, sl, ra);
+        fwd_load<XT, V, K, U, RES>(x, r, base_a, w.unit, sl, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
             const int64_t base_b = base_a + gstep;
-            fwd_load<XT, V, K, U>(x, base_b, w.unit, sl, rb);
+            fwd_load<XT, V, K, U, RES>(x, r, base_b, w.unit, sl, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC>(ra, y, base_a, w.unit, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, base_a, w.unit, sl, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
-            fwd_load<XT, V, K, U>(x, base_n, w.unit, sl, ra);
+            fwd_load<XT, V, K, U, RES>(x, r, base_n, w.unit, sl, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC>(rb, y, base_b, w.unit, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES>(xb, rb, y, h, base_b, w.unit, sl, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
             base_a = base_n;
         }
-        if (iters & 1) fwd_tile<XT, V, K, U, ACC>(ra, y, base_a, w.unit, sl, gm, bt, alpha);
+        if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, base_a, w.unit, sl, gm, bt, alpha);
     }
     // units after the last whole group (fewer than U in total)
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
-        typename R::T r1[1][K];
+        typename R::T x1[1][K], r1[1][K];
         const int64_t base_r = w.col_base + u * w.unit;
-        fwd_load<XT, V, K, 1>(x, base_r, w.unit, sl, r1);
-        fwd_tile<XT, V, K, 1, ACC>(r1, y, base_r, w.unit, sl, gm, bt, alpha);
+        fwd_load<XT, V, K, 1, RES>(x, r, base_r, w.unit, sl, x1, r1);
+        fwd_tile<XT, V, K, 1, ACC, RES>(x1, r1, y, h, base_r, w.unit, sl, gm, bt, alpha);
     }
 
     if (PACKED && w.tail) {
@@ -412,8 +480,20 @@ dyt_fwd_kernel(const XT* __restrict__ x, const PT* __restrict__ alpha_p,
             const int n = len - o;
             if (n > 0) {
                 float v[V];
-                if (n >= V) R::unpack(R::load(x + tb + o), v);
-                else load_partial<XT, V>(x + tb + o, n, v);
+                if (n >= V) {
+                    typename R::T rr{};
+                    if constexpr (RES) rr = R::load(r + tb + o);
+                    fwd_input<XT, V, RES>(R::load(x + tb + o), rr, h + tb + o, v);
+                } else {
+                    load_partial<XT, V>(x + tb + o, n, v);
+                    if constexpr (RES) {
+                        float rv[V];
+                        load_partial<XT, V>(r + tb + o, n, rv);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) v[e] = to_f32(from_f32<XT>(v[e] + rv[e]));
+                        store_partial<XT, V>(h + tb + o, n, v);
+                    }
+                }
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
@@ -442,23 +522,30 @@ __device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)
     }
 }
 
-template <typename XT, int V, int K, int U>
+// With RES the residual gradient dres is loaded beside x and dy and added
+// (in float32) to dx before the one rounding to the storage type.
+template <typename XT, int V, int K, int U, bool RES>
 __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __restrict__ dy,
-                                         int64_t base, int64_t step, const Slots<V, K>& sl,
+                                         const XT* __restrict__ dres, int64_t base, int64_t step,
+                                         const Slots<V, K>& sl,
                                          typename Raw<XT, V>::T (&rx)[U][K],
-                                         typename Raw<XT, V>::T (&rd)[U][K]) {
+                                         typename Raw<XT, V>::T (&rd)[U][K],
+                                         typename Raw<XT, V>::T (&rr)[U][K]) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             rx[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(x + base + j * step + sl.off[k]);
             rd[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dy + base + j * step + sl.off[k]);
+            if constexpr (RES)
+                rr[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dres + base + j * step + sl.off[k]);
         }
 }
 
-template <typename XT, int V, int K, int U, bool ACC>
+template <typename XT, int V, int K, int U, bool ACC, bool RES>
 __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
                                          const typename Raw<XT, V>::T (&rd)[U][K],
+                                         const typename Raw<XT, V>::T (&rr)[U][K],
                                          XT* __restrict__ dx, int64_t base, int64_t step,
                                          const Slots<V, K>& sl, const float (&gm)[K][V],
                                          float alpha, float (&ag)[K][V], float (&ab)[K][V],
@@ -471,15 +558,23 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
             Raw<XT, V>::unpack(rx[j][k], xv);
             Raw<XT, V>::unpack(rd[j][k], dv);
             bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
+            if constexpr (RES) {
+                float rv[V];
+                Raw<XT, V>::unpack(rr[j][k], rv);
+#pragma unroll
+                for (int e = 0; e < V; ++e) out[e] += rv[e];
+            }
             Raw<XT, V>::template store<DYT_BWD_NT>(dx + base + j * step + sl.off[k], out);
         }
 }
 
-template <typename XT, typename PT, int V, int K, int U, bool PACKED>
+// x is the layer input (h of the residual forward); dres and RES as above.
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES>
 __global__ void __launch_bounds__(kBlock)
 dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
-                       const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
-                       XT* __restrict__ dx, float* __restrict__ ws, const Geo g) {
+                       const XT* __restrict__ dres, const PT* __restrict__ alpha_p,
+                       const PT* __restrict__ gamma, XT* __restrict__ dx,
+                       float* __restrict__ ws, const Geo g) {
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -510,30 +605,31 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
     const int64_t gstep = w.gcount * U * w.unit;
     if (iters > 0) {
-        typename R::T xa[U][K], da[U][K], xb[U][K], db[U][K];
+        typename R::T xa[U][K], da[U][K], ra[U][K], xb[U][K], db[U][K], rb[U][K];
         int64_t base_a = w.col_base + w.gw * U * w.unit;
-        bwd_load<XT, V, K, U>(x, dy, base_a, w.unit, sl, xa, da);
+        bwd_load<XT, V, K, U, RES>(x, dy, dres, base_a, w.unit, sl, xa, da, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
             const int64_t base_b = base_a + gstep;
-            bwd_load<XT, V, K, U>(x, dy, base_b, w.unit, sl, xb, db);
+            bwd_load<XT, V, K, U, RES>(x, dy, dres, base_b, w.unit, sl, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC>(xa, da, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
-            bwd_load<XT, V, K, U>(x, dy, base_n, w.unit, sl, xa, da);
+            bwd_load<XT, V, K, U, RES>(x, dy, dres, base_n, w.unit, sl, xa, da, ra);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC>(xb, db, dx, base_b, w.unit, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES>(xb, db, rb, dx, base_b, w.unit, sl, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             base_a = base_n;
         }
-        if (iters & 1) bwd_tile<XT, V, K, U, ACC>(xa, da, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
+        if (iters & 1)
+            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
     }
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
-        typename R::T x1[1][K], d1[1][K];
+        typename R::T x1[1][K], d1[1][K], r1[1][K];
         const int64_t base_r = w.col_base + u * w.unit;
-        bwd_load<XT, V, K, 1>(x, dy, base_r, w.unit, sl, x1, d1);
-        bwd_tile<XT, V, K, 1, ACC>(x1, d1, dx, base_r, w.unit, sl, gm, alpha, ag, ab, aa);
+        bwd_load<XT, V, K, 1, RES>(x, dy, dres, base_r, w.unit, sl, x1, d1, r1);
+        bwd_tile<XT, V, K, 1, ACC, RES>(x1, d1, r1, dx, base_r, w.unit, sl, gm, alpha, ag, ab, aa);
     }
 
     if (PACKED && w.tail) {
@@ -544,13 +640,15 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int o = (k * kBlock + tid) * V;
             const int n = len - o;
             if (n > 0) {
-                float xv[V], dv[V], out[V];
+                float xv[V], dv[V], rv[V], out[V];
                 if (n >= V) {
                     R::unpack(R::load(x + tb + o), xv);
                     R::unpack(R::load(dy + tb + o), dv);
+                    if constexpr (RES) R::unpack(R::load(dres + tb + o), rv);
                 } else {
                     load_partial<XT, V>(x + tb + o, n, xv);
                     load_partial<XT, V>(dy + tb + o, n, dv);
+                    if constexpr (RES) load_partial<XT, V>(dres + tb + o, n, rv);
                 }
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -558,6 +656,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                     dyt_tanh_sech2<ACC>(xv[e], alpha, th, sd);
                     const float gd = (dv[e] * gm[k][e]) * sd;
                     out[e] = gd * alpha;
+                    if constexpr (RES) out[e] += rv[e];
                     // Mask after the arithmetic: a lane past the end computed on
                     // zeros (tanh(inf * 0) = NaN when alpha = inf); the select
                     // drops whatever it produced.

@@ -71,3 +71,55 @@ class DyT(nn.Module):
 
     def extra_repr(self) -> str:
         return f"{self.num_features}, alpha={float(self.alpha.detach().float().cpu()[0]):.4g}"
+
+
+class DyTResidualFunction(torch.autograd.Function):
+    """Autograd wrapper of the residual-fused layer: (x, r) -> (h = x + r, y = DyT(h)).
+
+    The backward receives the gradients of both outputs and returns
+    dh = grad_h + DyT-backward(grad_y) for x and for r (one fused kernel when
+    both are present).
+    """
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
+                beta: torch.Tensor):
+        x2 = _rows(x)
+        r2 = _rows(r.to(x.dtype))
+        h, y = _lib.dyt_forward_residual(x2, r2, alpha, gamma, beta)
+        ctx.save_for_backward(h, alpha, gamma)
+        ctx.set_materialize_grads(False)   # an unused output's gradient arrives as None
+        ctx.x_shape = x.shape
+        return h.view(x.shape), y.view(x.shape)
+
+    @staticmethod
+    def backward(ctx, grad_h: torch.Tensor | None, grad_y: torch.Tensor | None):
+        h, alpha, gamma = ctx.saved_tensors
+        shape = ctx.x_shape
+        if grad_y is None:
+            dh = _rows(grad_h.to(h.dtype))
+            return dh.view(shape), dh.view(shape), None, None, None
+        dy2 = _rows(grad_y.to(h.dtype))
+        if grad_h is None:
+            dh, dalpha, dgamma, dbeta = _lib.dyt_backward(h, dy2, alpha, gamma)
+        else:
+            dres = _rows(grad_h.to(h.dtype))
+            dh, dalpha, dgamma, dbeta = _lib.dyt_backward_residual(h, dy2, dres, alpha, gamma)
+        return dh.view(shape), dh.view(shape), dalpha, dgamma, dbeta
+
+
+def dyt_residual(x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
+                 beta: torch.Tensor):
+    """(h, y) = (x + r, DyT(x + r)) with autograd support."""
+    return DyTResidualFunction.apply(x, r, alpha, gamma, beta)
+
+
+class DyTResidual(DyT):
+    """DyT with the residual add fused in front: ``forward(x, r)`` returns
+    ``(h, y)`` with ``h = x + r`` (the new residual stream, in x's dtype) and
+    ``y = weight * tanh(alpha * h) + bias``."""
+
+    def forward(self, x: torch.Tensor, r: torch.Tensor):  # type: ignore[override]
+        if x.shape[-1] != self.num_features or r.shape != x.shape:
+            raise ValueError(f"expected x and r of equal shape with last dimension {self.num_features}")
+        return DyTResidualFunction.apply(x, r, self.alpha, self.weight, self.bias)

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 1
+#define DYT_ABI_VERSION 2
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -149,6 +149,63 @@ int dyt_backward_finish(const void* workspace, size_t workspace_bytes,
                         void* dalpha, void* dgamma, void* dbeta,
                         int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
 
+/*
+ * Residual add fused with the layer (forward): the pre-norm block pattern
+ * h = x + r ("x" the residual stream, "r" the branch output added to it)
+ * followed by DyT of h, in one pass over memory:
+ *
+ *   h[i,j] = x[i,j] + r[i,j]            (rounded once to x_dtype)
+ *   y[i,j] = gamma[j] * tanh(alpha * h[i,j]) + beta[j]
+ *
+ * y is computed from h as stored (rounded), so the pair (h, y) equals an
+ * add followed by dyt_forward(h) bit for bit. It moves 4 M x N tensors
+ * instead of the 5 of the two separate steps; the deepmd-kit pull request
+ * "perf(pt): fuse the mixing-stack per-layer backward chain" (Motivation)
+ * describes the HBM round trip of an intermediate that such fusion removes.
+ *   x, r   [M, N] x_dtype, read
+ *   alpha, gamma, beta as dyt_forward
+ *   h      [M, N] x_dtype, written
+ *   y      [M, N] x_dtype, written
+ * h and y must not overlap each other or any input (no in-place h = x).
+ * Other conventions, and M == 0 or N == 0, as dyt_forward.
+ */
+int dyt_forward_residual(const void* x, const void* r, const void* alpha, const void* gamma,
+                         const void* beta, void* h, void* y, int64_t M, int64_t N,
+                         int x_dtype, int param_dtype, void* stream);
+
+/*
+ * Backward of dyt_forward_residual: with dy the gradient of y and dres the
+ * gradient reaching h through the residual stream,
+ *
+ *   dh[i,j] = dres[i,j] + dy[i,j] * gamma[j] * alpha * sech^2(alpha * h[i,j])
+ *
+ * (added in float32, rounded once to x_dtype) is the gradient of both x and
+ * r; dgamma, dbeta and dalpha are those of dyt_backward(h, dy) - bit for bit
+ * the same values, from the same partial rows. 4 M x N tensors move instead
+ * of the 6 of dyt_backward followed by a separate add.
+ *   h      [M, N] x_dtype, read (the h written by the forward)
+ *   dy     [M, N] x_dtype, read
+ *   dres   [M, N] x_dtype, read
+ *   dh     [M, N] x_dtype, written
+ * Other arguments, workspace (same size as dyt_backward's) and conventions
+ * as dyt_backward; dh must not overlap any input.
+ */
+int dyt_backward_residual(const void* h, const void* dy, const void* dres, const void* alpha,
+                          const void* gamma, void* dh, void* dalpha, void* dgamma, void* dbeta,
+                          void* workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
+
+/*
+ * First pass of dyt_backward_residual alone: writes dh and the partial rows
+ * (identical to those of dyt_backward_partials(h, dy, ...)); finish with
+ * dyt_backward_finish. Arguments as dyt_backward_residual.
+ */
+int dyt_backward_residual_partials(const void* h, const void* dy, const void* dres,
+                                   const void* alpha, const void* gamma, void* dh,
+                                   void* workspace, size_t workspace_bytes,
+                                   int64_t M, int64_t N, int x_dtype, int param_dtype,
+                                   void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* dyt_status_string(int status);
 
@@ -164,7 +221,7 @@ int dyt_abi_version(void);
  * calls would return for these sizes and dtypes.
  */
 typedef struct dyt_plan {
-    int32_t packed;        /* 1: tiles of several whole rows (N <= 256); 0: row segments */
+    int32_t packed;        /* 1: tiles of >= 2 whole rows (N <= 2048); 0: row segments */
     int32_t vec;           /* elements per vector memory access (16 bytes, or 1) */
     int32_t slots;         /* vector slots per thread per tile */
     int32_t block;         /* threads per workgroup */

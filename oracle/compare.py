@@ -17,6 +17,9 @@ match exactly):
 * dx, bfloat16: |dx_gpu - rne_bf16(dx*)| <= 1 ulp_bf16(|dx*|).
 * float16 outputs follow the bfloat16 rules with float16 rounding and ulps
   (11 significant bits, subnormal spacing 2^-24, overflow to +-inf).
+* dh of the residual backward (dres + dx, one rounding): the y rules with
+  the scale S_dh = |dres| + |dx*|, plus the float32 dx underflow floor.
+* h of the residual forward (x + r rounded once): exact, bit for bit.
 * dgamma, dbeta, dalpha (float32 accumulation):
   |g_gpu - g*| <= 1e-5 * max(|g*|, RSS_g) + 2^-149, RSS_g the root sum of
   squares of the summed terms (random-sign sums are compared at the scale
@@ -31,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "rne_bf16", "ulp_bf16", "rne_f16", "ulp_f16", "rne", "ulp", "Report",
-    "check_y", "check_dx", "check_grad",
+    "check_y", "check_dx", "check_grad", "check_dh", "check_exact",
 ]
 
 _BF16_OVERFLOW = 2.0 ** 128
@@ -200,3 +203,22 @@ def check_grad(got, g_ref, rss, dtype: str, name: str = "grad") -> Report:
     if dtype in ("bf16", "f16"):
         return _finish(name, got, rne(g_ref, dtype), ulp(g_ref, dtype) + 1e-5 * rss)
     raise ValueError(dtype)
+
+
+def check_dh(got, dh_ref, scale, dtype: str, dy_gamma_alpha=None, name: str = "dh") -> Report:
+    """dh = dres + dx: a sum that can cancel, judged at its condition scale
+    |dres| + |dx*| (like y), with dx's float32 underflow floor."""
+    dh_ref = np.asarray(dh_ref, dtype=np.float64)
+    scale = np.asarray(scale, dtype=np.float64)
+    if dtype == "f32":
+        k = 0.0 if dy_gamma_alpha is None else 4.0 * np.abs(np.asarray(dy_gamma_alpha, np.float64))
+        return _finish(name, got, dh_ref, 1e-6 * scale + _F32_TINY * (1.0 + k))
+    if dtype in ("bf16", "f16"):
+        return _finish(name, got, rne(dh_ref, dtype), ulp(np.maximum(np.abs(dh_ref), scale), dtype))
+    raise ValueError(dtype)
+
+
+def check_exact(got, ref, name: str = "h") -> Report:
+    """Bit-for-bit equality of values (NaN where NaN; -0 and +0 compared as
+    values; zero tolerance)."""
+    return _finish(name, got, ref, 0.0)

@@ -39,6 +39,21 @@ u = inf * 0 = NaN, which then propagates (the hazard the "Padding" bullet
 describes for padded lanes; padded lanes are not part of the problem and
 never enter this oracle).
 
+Residual add fused in front of the layer (the pre-norm block pattern; a
+fusion of two neighbouring steps, not something the DyT pull request
+describes): for a residual stream x and a branch output r of the same shape
+
+    h = x + r            (rounded once to the storage dtype of x)
+    y = DyT(h)           (from h as stored)
+
+and, with dres the gradient reaching h through the residual stream,
+
+    dh = dres + dx(h, dy)     (the gradient of both x and r)
+
+with dgamma, dbeta, dalpha those of the layer at input h. The sum x + r is
+formed in float64 and rounded once (round to nearest even): for float32,
+bfloat16 and float16 inputs this is the correctly rounded sum in that dtype.
+
 Sums are taken with numpy's pairwise float64 summation over row chunks.
 The oracle returns unrounded float64 results and, for the tolerance
 checks, the per-element condition scale of y (|gamma t| + |beta|) and the
@@ -50,9 +65,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .compare import rne as _rne
+
 __all__ = [
     "forward", "backward", "forward_core", "backward_core",
     "forward_at", "backward_dx_at", "ForwardResult", "BackwardResult",
+    "residual_sum", "forward_residual", "backward_residual", "backward_dh_at",
 ]
 
 _CHUNK_ELEMS = 1 << 22
@@ -184,3 +202,34 @@ def backward_dx_at(x_vals, dy_vals, cols, alpha, gamma):
     g = _f64(gamma)[cols]
     dx, _, _, _ = backward_core(_f64(x_vals), _f64(dy_vals), a, g)
     return dx
+
+
+# ----------------------------------------------------------- residual add
+
+def residual_sum(x, r, x_dtype: str) -> np.ndarray:
+    """h = x + r, formed in float64 and rounded once to x_dtype (RNE)."""
+    return _rne(_f64(x) + _f64(r), x_dtype)
+
+
+def forward_residual(x, r, alpha, gamma, beta, x_dtype: str):
+    """Residual add, then the layer on h as stored: returns (h, ForwardResult of h)."""
+    h = residual_sum(x, r, x_dtype)
+    return h, forward(h, alpha, gamma, beta)
+
+
+def backward_residual(h, dy, dres, alpha, gamma, want_dh: bool = True):
+    """Gradient of the residual-fused layer: returns (dh, BackwardResult of the
+    layer at input h), dh = dres + dx in float64 (None unless want_dh), and
+    the scale |dres| + |dx| of dh."""
+    res = backward(h, dy, alpha, gamma, want_dx=want_dh)
+    if not want_dh:
+        return None, res, None
+    d = _f64(dres)
+    return d + res.dx, res, np.abs(d) + np.abs(res.dx)
+
+
+def backward_dh_at(h_vals, dy_vals, dres_vals, cols, alpha, gamma):
+    """dh at sampled elements, one by one: returns (dh, scale |dres| + |dx|)."""
+    dx = backward_dx_at(h_vals, dy_vals, cols, alpha, gamma)
+    d = _f64(dres_vals)
+    return d + dx, np.abs(d) + np.abs(dx)

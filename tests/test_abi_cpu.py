@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted([
         "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
-        "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan"])
+        "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
+        "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -52,7 +53,7 @@ def test_no_cpu_fallback_in_product_path():
 
 
 def test_version_and_status_strings(dyt):
-    assert dyt.dyt_abi_version() == 1
+    assert dyt.dyt_abi_version() == 2
     names = [dyt.dyt_status_string(i) for i in range(6)]
     assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
                      "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]
@@ -200,6 +201,50 @@ def test_split_backward_error_codes(dyt):
     assert L.dyt_backward_finish(ws, need, A16 + 128, A16, A16 + 64, 4, 4, 9, F32, None) == E_DT
 
 
+def _fres(dyt, x=A16, r=A16 + 0x100000, a=A16 + 0x200000, g=A16 + 0x300000, b=A16 + 0x400000,
+          h=A16 + 0x500000, y=A16 + 0x600000, M=4, N=4, xdt=F32, pdt=F32):
+    return dyt.lib.dyt_forward_residual(x, r, a, g, b, h, y, M, N, xdt, pdt, None)
+
+
+def _bres(dyt, h=A16, dy=A16 + 0x100000, dres=A16 + 0x200000, a=A16 + 0x300000,
+          g=A16 + 0x400000, dh=A16 + 0x500000, da=A16 + 0x600000, dg=A16 + 0x700000,
+          db=A16 + 0x800000, ws=A16 + 0x900000, wsb=1 << 20, M=4, N=4, xdt=F32, pdt=F32):
+    return dyt.lib.dyt_backward_residual(h, dy, dres, a, g, dh, da, dg, db, ws, wsb, M, N, xdt, pdt,
+                                         None)
+
+
+def test_residual_forward_error_codes(dyt):
+    assert _fres(dyt, xdt=3) == E_DT
+    assert _fres(dyt, M=-1) == E_ARG
+    for kw in ("x", "r", "a", "g", "b", "h", "y"):
+        assert _fres(dyt, **{kw: None}) == E_ARG, kw
+    assert _fres(dyt, r=A16 + 0x100002) == E_AL
+    assert _fres(dyt, h=A16 + 0x500001, xdt=BF16) == E_AL
+    assert _fres(dyt, h=A16) == E_ARG                              # h aliases x (no in-place)
+    assert _fres(dyt, h=A16 + 0x100000) == E_ARG                   # h aliases r
+    assert _fres(dyt, y=A16 + 0x500000) == E_ARG                   # y aliases h
+    assert _fres(dyt, y=A16 + 0x100008) == E_ARG                   # y overlaps r
+    assert _fres(dyt, x=None, r=None, a=None, g=None, b=None, h=None, y=None, M=0) == E_OK
+
+
+def test_residual_backward_error_codes(dyt):
+    need = dyt.dyt_backward_workspace_size(4, 4, F32, F32)
+    assert _bres(dyt, xdt=5) == E_DT
+    for kw in ("h", "dy", "dres", "a", "g", "dh", "da", "dg", "db", "ws"):
+        assert _bres(dyt, **{kw: None}) == E_ARG, kw
+    assert _bres(dyt, wsb=need - 1) == E_WS
+    assert _bres(dyt, dres=A16 + 0x200002) == E_AL
+    assert _bres(dyt, dh=A16 + 0x200000) == E_ARG                  # dh aliases dres (no in-place)
+    assert _bres(dyt, ws=A16 + 0x200000) == E_ARG                  # workspace aliases dres
+    L = dyt.lib
+    assert L.dyt_backward_residual_partials(A16, A16 + 0x100000, None, A16 + 0x300000,
+                                            A16 + 0x400000, A16 + 0x500000, A16 + 0x900000, need,
+                                            4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_backward_residual_partials(A16, A16 + 0x100000, A16 + 0x200000, A16 + 0x300000,
+                                            A16 + 0x400000, A16 + 0x200000, A16 + 0x900000, need,
+                                            4, 4, F32, F32, None) == E_ARG
+
+
 def test_module_constructs_on_cpu(dyt):
     """The nn.Module drop-in builds its parameters without a GPU."""
     layer = dyt.DyT(16, alpha_init=0.25)
@@ -207,3 +252,8 @@ def test_module_constructs_on_cpu(dyt):
     assert layer.weight.shape == (16,) and bool((layer.weight == 1).all())
     assert layer.bias.shape == (16,) and not layer.bias.any()
     assert "16" in repr(layer)
+
+
+def test_residual_module_constructs_on_cpu(dyt):
+    layer = dyt.DyTResidual(8, alpha_init=0.5)
+    assert layer.weight.shape == (8,) and isinstance(layer, dyt.DyT)

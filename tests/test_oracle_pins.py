@@ -262,11 +262,90 @@ def pin_sampled_matches_full(o):
     assert np.array_equal(dxs, bw.dx.reshape(-1))
 
 
+# --- residual add fused in front of the layer (h = x + r rounded once, y from h)
+
+def pin_residual_zero_branch(o):
+    """r = +-0: h is x itself and y is the plain layer's y."""
+    rng = np.random.default_rng(21)
+    x = C.rne_bf16(rng.standard_normal((5, 7)))
+    g, b = 1 + rng.standard_normal(7) * 0.1, rng.standard_normal(7) * 0.1
+    for z in (0.0, -0.0):
+        h, f = o.forward_residual(x, np.full((5, 7), z), [0.7], g, b, "bf16")
+        assert np.array_equal(h, x)
+        assert np.array_equal(f.y, o.forward(x, [0.7], g, b).y)
+
+
+def pin_residual_integer_sums(o):
+    """Integer-valued x and r: h is the exact integer sum (Python ints)."""
+    rng = np.random.default_rng(22)
+    xi = rng.integers(-100, 101, (6, 5))
+    ri = rng.integers(-100, 101, (6, 5))
+    for dt in ("f32", "bf16", "f16"):
+        h, _ = o.forward_residual(xi.astype(np.float64), ri.astype(np.float64), [0.5], np.ones(5),
+                                  np.zeros(5), dt)
+        want = [[int(a) + int(c) for a, c in zip(ra, rr)] for ra, rr in zip(xi.tolist(), ri.tolist())]
+        # |sum| <= 200 has at most 8 significant bits: exact in every dtype
+        assert h.tolist() == want
+
+
+def pin_residual_rounding_ties(o):
+    """Hand-worked round-to-nearest-even of x + r, and y taken from h as stored."""
+    cases = [  # (dtype, x, r, h)
+        ("bf16", 1.0, 2.0 ** -8, 1.0),                          # tie, even is 1.0
+        ("bf16", 1.0, 3 * 2.0 ** -8, 1.015625),                 # tie between 1+2^-7 and 1+2^-6
+        ("bf16", 1.0, 2.0 ** -8 + 2.0 ** -20, 1.0078125),       # just above the tie
+        ("f16", 1.0, 2.0 ** -11, 1.0),
+        ("f16", 1.0, 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),
+        ("f32", 1.0, 2.0 ** -24, 1.0),
+        ("f32", 1.0, 3 * 2.0 ** -24, 1.0 + 2.0 ** -22),
+        ("bf16", 2.0 ** 100, 2.0 ** -100, 2.0 ** 100),          # beyond float64's exact sum
+        ("f16", 65504.0, 16.0, np.inf),                         # rounds past the largest f16
+    ]
+    for dt, xv, rv, hv in cases:
+        h, f = o.forward_residual(np.array([[xv]]), np.array([[rv]]), [1.0], [1.0], [0.0], dt)
+        assert h[0, 0] == hv, (dt, xv, rv, h[0, 0], hv)
+        if np.isfinite(hv):
+            assert math.isclose(f.y[0, 0], math.tanh(hv), rel_tol=1e-14)
+
+
+def pin_residual_backward_composition(o):
+    """dh = dres + dx: dres = 0 gives dx, dy = 0 gives dres with zero grads,
+    and central differences of L(h) = sum(dres*h) + sum(dy*y(h)) give dh."""
+    rng = np.random.default_rng(23)
+    h = rng.standard_normal((3, 4))
+    dy = rng.standard_normal((3, 4))
+    dres = rng.standard_normal((3, 4))
+    g, b, a = 1 + rng.standard_normal(4) * 0.1, rng.standard_normal(4) * 0.1, 0.8
+    dh0, bw0, _ = o.backward_residual(h, dy, np.zeros((3, 4)), [a], g)
+    assert np.array_equal(dh0, o.backward(h, dy, [a], g).dx)
+    dh1, bw1, sc1 = o.backward_residual(h, np.zeros((3, 4)), dres, [a], g)
+    assert np.array_equal(dh1, dres) and np.array_equal(sc1, np.abs(dres))
+    assert not bw1.dgamma.any() and not bw1.dbeta.any() and bw1.dalpha == 0.0
+    dh, bw, _ = o.backward_residual(h, dy, dres, [a], g)
+    assert np.array_equal(bw.dgamma, bw0.dgamma) and bw.dalpha == bw0.dalpha
+
+    def loss(hh):
+        return math.fsum((dres * hh).ravel()) + math.fsum((dy * (g * np.tanh(a * hh) + b)).ravel())
+    eps = 1e-6
+    for i in range(3):
+        for j in range(4):
+            hp, hm = h.copy(), h.copy()
+            hp[i, j] += eps
+            hm[i, j] -= eps
+            fd = (loss(hp) - loss(hm)) / (2 * eps)
+            assert math.isclose(dh[i, j], fd, rel_tol=1e-7, abs_tol=1e-8), (i, j, dh[i, j], fd)
+    rows, cols = np.divmod(np.arange(12), 4)
+    dhs, scs = o.backward_dh_at(h[rows, cols], dy[rows, cols], dres[rows, cols], cols, [a], g)
+    assert np.array_equal(dhs, dh.reshape(-1))
+
+
 PINS = [
     pin_alpha_zero_gives_beta, pin_unit_affine_is_library_tanh, pin_rational_points,
     pin_complex_step, pin_central_differences, pin_integer_sums_alpha_inf,
     pin_integer_sums_alpha_zero, pin_ieee_alpha_inf_table, pin_large_u_sech2_not_cancelled,
     pin_odd_symmetry, pin_bruteforce_sums, pin_empty, pin_sampled_matches_full,
+    pin_residual_zero_branch, pin_residual_integer_sums, pin_residual_rounding_ties,
+    pin_residual_backward_composition,
 ]
 
 
@@ -298,7 +377,30 @@ def _bw_variant(dx=None, tg=None, ta=None, tb=None):
     return {"backward_core": core}
 
 
+def _res_y_from_unrounded(x, r, alpha, gamma, beta, x_dtype):
+    h = O.residual_sum(x, r, x_dtype)
+    return h, O.forward(np.asarray(x, np.float64) + np.asarray(r, np.float64), alpha, gamma, beta)
+
+
+def _res_h_difference(x, r, alpha, gamma, beta, x_dtype):
+    h = C.rne(np.asarray(x, np.float64) - np.asarray(r, np.float64), x_dtype)
+    return h, O.forward(h, alpha, gamma, beta)
+
+
+def _res_dh_variant(fn):
+    def bres(h, dy, dres, alpha, gamma, want_dh=True):
+        res = O.backward(h, dy, alpha, gamma, want_dx=want_dh)
+        d = np.asarray(dres, np.float64)
+        return fn(d, res.dx), res, np.abs(d) + np.abs(res.dx)
+    return {"backward_residual": bres}
+
+
 MUTANTS = {
+    "res_y_from_unrounded_h": {"forward_residual": _res_y_from_unrounded},
+    "res_h_is_difference": {"forward_residual": _res_h_difference},
+    "res_dh_without_dres": _res_dh_variant(lambda d, dx: dx),
+    "res_dh_minus_dres": _res_dh_variant(lambda d, dx: dx - d),
+    "res_dh_without_dx": _res_dh_variant(lambda d, dx: d + 0 * dx),
     "fwd_alpha_dropped": _mut_forward(lambda x, a, g, b: g * np.tanh(x) + b),
     "fwd_beta_sign": _mut_forward(lambda x, a, g, b: g * np.tanh(a * x) - b),
     "fwd_gamma_beta_swapped": _mut_forward(lambda x, a, g, b: b * np.tanh(a * x) + g),

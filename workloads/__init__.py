@@ -238,3 +238,15 @@ def custom(M: int, N: int, x_dtype: str = "f32", p_dtype: str = "f32", alpha: fl
     a = _quantise(np.array([alpha], dtype=np.float32), p_dtype)
     return Inputs(f"custom_{M}x{N}_{x_dtype}_{p_dtype}", x, dy, a, gamma, beta, x_dtype, p_dtype,
                   {"seed": seed})
+
+
+def residual_pair(M: int, N: int, x_dtype: str, seed: int, sigma: float = 1.0):
+    """Extra tensors of the residual-fused layer: r (the branch output added
+    to the residual stream x) and dres (the gradient reaching h through the
+    residual stream), both ~ N(0, sigma) in x_dtype, drawn in that order from
+    their own generator (seed + 1000003) so the layer's own inputs stay those
+    of the workload."""
+    rng = np.random.default_rng(seed + 1000003)
+    r = _normal_matrix(rng, M, N, sigma, x_dtype)
+    dres = _normal_matrix(rng, M, N, sigma, x_dtype)
+    return r, dres
