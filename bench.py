@@ -15,6 +15,10 @@ Algorithmic bytes (sx = x dtype size, sp = parameter dtype size):
   pass 1    3 M N sx + (N + 1) sp       pass 2   (2N + 1) sp
 (workspace traffic of the backward is excluded from the algorithmic bytes).
 
+With the residual add fused in front (h = x + r, y = DyT(h); backward
+dh = dres + dx), the line also carries "residual": fused and unfused
+(torch.add beside the plain layer) times on the same shape.
+
 Timing: W warm-up steps (extended by untimed steps until 0.3 s have passed,
 because the GPU clocks ramp for the first ~100 steps after idle), then three
 timed regions of K steps each: A without events inside (the reported value
@@ -218,6 +222,73 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False)
     return res
 
 
+def measure_residual(dyt, torch, name: str, reps: int = 40, rounds: int = 3) -> dict:
+    """The residual-fused layer against the same work unfused, on the
+    workload's shape: forward h = x + r, y = DyT(h) (fused: one kernel;
+    unfused: torch.add then dyt_forward) and backward dh = dres + dx (fused:
+    dyt_backward_residual; unfused: dyt_backward then torch.add). Each sample
+    is `reps` back-to-back calls between two events (no events inside);
+    medians over `rounds` interleaved rounds. Inputs are drawn on the device
+    from a seeded generator (N(0, 1) in the workload's x dtype)."""
+    import workloads
+    cfg = workloads.CONFIGS[name]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    xdt, pdt = tdt[cfg.x_dtype], tdt[cfg.p_dtype]
+    M, N = cfg.M, cfg.N
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    mk = lambda: torch.randn(M, N, device="cuda", generator=gen).to(xdt)
+    x, r, dy, dres = mk(), mk(), mk(), mk()
+    h, y, dh = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    a = torch.full((1,), 0.5, device="cuda").to(pdt)
+    g = (1 + 0.02 * torch.randn(N, device="cuda", generator=gen)).to(pdt)
+    b = torch.zeros(N, device="cuda").to(pdt)
+    da, dg, db = torch.empty_like(a), torch.empty_like(g), torch.empty_like(b)
+    ws = torch.empty(max(16, dyt.dyt_backward_workspace_size(M, N, xdt, pdt)), dtype=torch.uint8,
+                     device="cuda")
+    ops = {
+        "fwd_fused": lambda: dyt.dyt_forward_residual(x, r, a, g, b, h=h, y=y),
+        "fwd_unfused": lambda: (torch.add(x, r, out=h), dyt.dyt_forward(h, a, g, b, y=y)),
+        "bwd_fused": lambda: dyt.dyt_backward_residual(h, dy, dres, a, g, dh=dh, dalpha=da, dgamma=dg,
+                                                       dbeta=db, workspace=ws),
+        "bwd_unfused": lambda: (dyt.dyt_backward(h, dy, a, g, dx=dh, dalpha=da, dgamma=dg, dbeta=db,
+                                                 workspace=ws), torch.add(dh, dres, out=dh)),
+    }
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(20):
+            ops["fwd_fused"]()
+        torch.cuda.synchronize()
+    samples = {k: [] for k in ops}
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(rounds):
+        for k, f in ops.items():
+            for _ in range(5):
+                f()
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            e1.synchronize()
+            samples[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = {k: statistics.median(v) for k, v in samples.items()}
+    sx, sp = x.element_size(), a.element_size()
+    fwd_bytes = 4 * M * N * sx + (2 * N + 1) * sp          # read x, r; write h, y
+    bwd_bytes = 4 * M * N * sx + (3 * N + 2) * sp          # read h, dy, dres; write dh
+    del x, r, dy, dres, h, y, dh, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": name,
+        "unfused": "torch.add then dyt_forward; dyt_backward then torch.add",
+        "fwd": {"fused_us": round(us["fwd_fused"], 2), "unfused_us": round(us["fwd_unfused"], 2),
+                "speedup": round(us["fwd_unfused"] / us["fwd_fused"], 3),
+                "fused_GBps": round(fwd_bytes / (us["fwd_fused"] * 1e-6) / 1e9, 1)},
+        "bwd": {"fused_us": round(us["bwd_fused"], 2), "unfused_us": round(us["bwd_unfused"], 2),
+                "speedup": round(us["bwd_unfused"] / us["bwd_fused"], 3),
+                "fused_GBps": round(bwd_bytes / (us["bwd_fused"] * 1e-6) / 1e9, 1)},
+    }
+
+
 def copy_calibration(torch, mib: int) -> None:
     """A plain elementwise kernel of known size (reads and writes mib MiB each)
     so that HBM byte counters can be scaled; used only by counter runs."""
@@ -357,6 +428,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--no-residual", action="store_true",
+                    help="skip the residual-fused vs unfused comparison")
     ap.add_argument("--all-configs", metavar="FILE", default=None,
                     help="also time every workload shape and write a Markdown table to FILE")
     args = ap.parse_args()
@@ -382,6 +455,10 @@ def main() -> int:
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         sec = measure(dyt, torch, args.secondary, args.steps, args.warmup)
         log(f"[bench] {json.dumps(sec)}")
+    resid = None
+    if not args.no_residual:
+        resid = measure_residual(dyt, torch, args.workload)
+        log(f"[bench] residual: {json.dumps(resid)}")
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)
     if args.all_configs:
@@ -439,6 +516,8 @@ def main() -> int:
             "bwd": {"GBps": round(sec["bwd_gbps"], 1), "frac": round(sec["bwd_frac"], 4),
                     "us": round(sec["bwd_us_median"], 2)},
         }
+    if resid:
+        out["residual"] = resid
     print(json.dumps(out), flush=True)
     return 0
 

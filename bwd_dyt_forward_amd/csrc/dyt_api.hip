@@ -39,11 +39,9 @@
 #ifndef DYT_BWD_U
 #define DYT_BWD_U 1
 #endif
-// The residual forward streams two inputs and two outputs: one tile per
-// buffer, like the backward.
-#ifndef DYT_FWD_RES_U
-#define DYT_FWD_RES_U 1
-#endif
+// The residual forward (two inputs, two outputs) uses the forward's U as
+// well: on 32768 x 4096 and 4194304 x 32 bf16 U = 2 measured 0.2-0.8%
+// faster than U = 1.
 // Tiles wanted before a packed plan stops shrinking K for more parallelism.
 #ifndef DYT_MIN_TILES
 #define DYT_MIN_TILES 1024
@@ -228,7 +226,7 @@ struct BwdPtrs {
 
 template <typename XT, typename PT, int V, int K, bool RES>
 void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
-    constexpr int U = RES ? DYT_FWD_RES_U : DYT_FWD_U;
+    constexpr int U = DYT_FWD_U;
     const dim3 grid((unsigned)p.fwd_grid), block(kBlock);
     if (p.packed)
         hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES>), grid, block, 0, s,
