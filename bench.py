@@ -10,6 +10,10 @@ Prints ONE JSON line on stdout:
                HIP events recorded on the launch stream inside the timed loop
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
                workload, on one pinned host core
+  stream_ceiling  measured ceilings on the same tensor size: a plain 16-byte
+               nontemporal copy and a 2-in/1-out stream (reference kernels in
+               libdyt_streamref.so), with the forward's and pass 1's fraction
+               of them
 Algorithmic bytes (sx = x dtype size, sp = parameter dtype size):
   forward   2 M N sx + (2N + 1) sp      backward 3 M N sx + (3N + 2) sp
   pass 1    3 M N sx + (N + 1) sp       pass 2   (2N + 1) sp
@@ -106,7 +110,44 @@ def graph_step_us(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt, 
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False) -> dict:
+def cold_times(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt, iters, B) -> dict:
+    """Cold-cache timing: before each timed launch a 1 GiB buffer is written
+    (four times the 256 MB MALL, far above the L2s), then HIP events bracket
+    the forward, and after another flush the backward (pass 1 + pass 2).
+    Median, 10th and 90th percentile over `iters` repetitions (microseconds)."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fwd, bwd = [], []
+    for i in range(iters + 3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.zero_()
+        ev[0].record()
+        dyt.dyt_forward(x, a, g, b, y=y)
+        ev[1].record()
+        flush.zero_()
+        ev[2].record()
+        dyt.dyt_backward_partials(x, dy, a, g, dx, ws)
+        dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db)
+        ev[3].record()
+        ev[3].synchronize()
+        if i >= 3:          # the first repetitions warm the code paths
+            fwd.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            bwd.append(ev[2].elapsed_time(ev[3]) * 1e3)
+    del flush
+    torch.cuda.empty_cache()
+
+    def q(v, f):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    out = {}
+    for k, v, nb in (("fwd", fwd, B["fwd"]), ("bwd", bwd, B["bwd"])):
+        med = statistics.median(v)
+        out[k] = {"p50_us": med, "p10_us": q(v, 0.1), "p90_us": q(v, 0.9),
+                  "gbps": nb / (med * 1e-6) / 1e9}
+    return out
+
+
+def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
+            cold_iters: int = 0) -> dict:
     import workloads
     cfg = workloads.CONFIGS[name]
     t0 = time.perf_counter()
@@ -213,6 +254,9 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False)
     }
     res["fwd_frac"] = res["fwd_gbps"] / HBM_PEAK_GBPS
     res["bwd_frac"] = res["bwd_gbps"] / HBM_PEAK_GBPS
+    if cold_iters:
+        res["cold"] = cold_times(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt,
+                                 cold_iters, B)
     if graph:
         gus = graph_step_us(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt)
         res["graph_step_us"] = gus
@@ -289,6 +333,53 @@ def measure_residual(dyt, torch, name: str, reps: int = 40, rounds: int = 3) -> 
     }
 
 
+def stream_ceilings(torch, nbytes: int, reps: int = 40, rounds: int = 3) -> dict:
+    """Measured streaming ceilings on tensors of nbytes each, from the
+    reference kernels in libdyt_streamref.so (16-byte nontemporal streams at
+    their best measured launch shapes): a copy (the forward's 1 read + 1
+    write) and a 2-in/1-out stream (backward pass 1's traffic). GB/s count
+    every byte read and written; medians of `rounds` samples of `reps`
+    back-to-back launches after a settling warm-up."""
+    import ctypes
+    sys.path.insert(0, os.path.join(ROOT, "bwd_dyt_forward_amd"))
+    import build as dyt_build
+    lib = ctypes.CDLL(dyt_build.STREAM_REF_PATH, mode=ctypes.RTLD_LOCAL)
+    lib.stream_ref_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.stream_ref_2in1out.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p]
+    nbytes -= nbytes % 16
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    ops = {"copy": lambda: lib.stream_ref_copy(a.data_ptr(), c.data_ptr(), nbytes, s),
+           "2in1out": lambda: lib.stream_ref_2in1out(a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, s)}
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(20):
+            if ops["copy"]() != 0:
+                raise RuntimeError("stream_ref_copy rejected its arguments")
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    us = {k: [] for k in ops}
+    for _ in range(rounds):
+        for k, f in ops.items():
+            if f() != 0:
+                raise RuntimeError(f"stream_ref {k} failed")
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            e1.synchronize()
+            us[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * nbytes / (statistics.median(us["copy"]) * 1e-6) / 1e9, 1),
+            "two_in_one_out_GBps": round(3 * nbytes / (statistics.median(us["2in1out"]) * 1e-6) / 1e9, 1),
+            "tensor_bytes": nbytes}
+
+
 def copy_calibration(torch, mib: int) -> None:
     """A plain elementwise kernel of known size (reads and writes mib MiB each)
     so that HBM byte counters can be scaled; used only by counter runs."""
@@ -357,6 +448,49 @@ def cpu_baseline(name: str, seconds: float) -> dict:
                       f"{el:.1f}s on 1 pinned core"}
 
 
+def oracle_times(name: str, max_elems: int = 1 << 20, runs: int = 3) -> dict:
+    """The fp64 oracle, as it is, per direction on a bounded sample of the
+    workload (whole rows, at most max_elems elements), pinned to one host
+    core; median of `runs` runs, GB/s of the sample's algorithmic bytes."""
+    import workloads
+    from oracle import dyt_oracle
+    cfg = workloads.CONFIGS[name]
+    rows = min(cfg.M, max(1, max_elems // cfg.N))
+    inp = workloads.generate(name, M=rows)
+    sx = 4 if cfg.x_dtype == "f32" else 2
+    sp = 4 if cfg.p_dtype == "f32" else 2
+    B = algorithmic_bytes(rows, cfg.N, sx, sp)
+    old = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old)})
+    try:
+        tf, tb = [], []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            dyt_oracle.forward(inp.x, inp.alpha, inp.gamma, inp.beta)
+            tf.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            dyt_oracle.backward(inp.x, inp.dy, inp.alpha, inp.gamma)
+            tb.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, old)
+    return {"rows": rows, "fwd_gbps": B["fwd"] / statistics.median(tf) / 1e9,
+            "bwd_gbps": B["bwd"] / statistics.median(tb) / 1e9}
+
+
+def host_description() -> str:
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return (f"{model}; os.cpu_count() = {os.cpu_count()}, "
+            f"affinity = {len(os.sched_getaffinity(0))} cores; oracle runs pinned to 1 core")
+
+
 def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
     """Every workload shape: steady-state forward / backward times (HIP events,
     means over `steps` continuous steps after `warmup`), written as Markdown."""
@@ -386,8 +520,24 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
             "| workload | M x N | x/params | fwd us | fwd GB/s | fwd % | bwd us | bwd GB/s | bwd % | "
             "step GB/s | step % | graph step us | graph GB/s | graph % | plan |",
             "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
+    cold_rows = ["", "Cold cache (SURVEY timing protocol): a 1 GiB buffer is written before each timed "
+                 "launch; HIP events around the forward and around pass 1 + pass 2; median [p10, p90] over "
+                 "30 repetitions. CPU oracle: the fp64 oracle as it is, per direction, on a sample of whole "
+                 "rows (at most 2^20 elements), median of 3 runs on one pinned core of the host: "
+                 + host_description() + ".", "",
+                 "| workload | cold fwd us [p10, p90] | cold fwd GB/s | cold bwd us [p10, p90] | cold bwd GB/s | "
+                 "oracle rows | oracle fwd GB/s | oracle bwd GB/s |",
+                 "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for name in workloads.config_names():
-        r = measure(dyt, torch, name, steps, warmup, graph=True)
+        r = measure(dyt, torch, name, steps, warmup, graph=True, cold_iters=30)
+        c = r["cold"]
+        o = oracle_times(name)
+        cold_rows.append(
+            f"| {name} | {c['fwd']['p50_us']:.1f} [{c['fwd']['p10_us']:.1f}, {c['fwd']['p90_us']:.1f}] | "
+            f"{c['fwd']['gbps']:.0f} | {c['bwd']['p50_us']:.1f} [{c['bwd']['p10_us']:.1f}, "
+            f"{c['bwd']['p90_us']:.1f}] | {c['bwd']['gbps']:.0f} | {o['rows']} | {o['fwd_gbps']:.3f} | "
+            f"{o['bwd_gbps']:.3f} |")
+        log(cold_rows[-1])
         B = r["bytes"]
         step_us = r["fwd_us_median"] + r["bwd_us_median"]
         sgbps = (B["fwd"] + B["bwd"]) / (step_us * 1e-6) / 1e9
@@ -401,7 +551,7 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
                     f"{r['graph_step_gbps']:.0f} | {100 * r['graph_step_gbps'] / HBM_PEAK_GBPS:.1f} | {plan} |")
         log(rows[-1])
     with open(path, "w") as f:
-        f.write("\n".join(rows) + "\n")
+        f.write("\n".join(rows + cold_rows) + "\n")
 
 
 def load_traffic(kernel: str) -> dict | None:
@@ -464,8 +614,13 @@ def main() -> int:
     if args.all_configs:
         report_all(dyt, torch, args.all_configs)
 
-    ceiling = copy_ceiling(torch, main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] == "bf16" else 4))
+    tensor_bytes = main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] in ("bf16", "f16") else 4)
+    ceiling = copy_ceiling(torch, tensor_bytes)
     log(f"[bench] device copy ceiling: {ceiling:.1f} GB/s")
+    streams = stream_ceilings(torch, tensor_bytes)
+    streams["fwd_frac_of_copy"] = round(main_res["fwd_gbps"] / streams["copy_GBps"], 4)
+    streams["pass1_frac_of_2in1out"] = round(main_res["pass1_gbps"] / streams["two_in_one_out_GBps"], 4)
+    log(f"[bench] stream ceilings: {json.dumps(streams)}")
     kernel = "dyt_bwd_partial_kernel"
     traffic = load_traffic(kernel + ":" + args.workload)
     rl_bytes = main_res["bytes"]["pass1"]
@@ -499,6 +654,7 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "frac_of_peak": round(main_res["gbps_step"] / HBM_PEAK_GBPS, 4),
         "copy_ceiling_GBps": round(ceiling, 1),
+        "stream_ceiling": streams,
         "fwd": {"GBps": round(main_res["fwd_gbps"], 1), "frac": round(main_res["fwd_frac"], 4),
                 "us": round(main_res["fwd_us_median"], 2)},
         "bwd": {"GBps": round(main_res["bwd_gbps"], 1), "frac": round(main_res["bwd_frac"], 4),

@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "dyt_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "dyt_kernels.hpp"), os.path.join(CSRC, "dyt_math.hpp"),
                      os.path.join(INCLUDE, "dyt.h")]
+# Reference streaming kernels for bench.py's measured ceilings (not part of
+# the DyT ABI; nothing in the package loads them).
+STREAM_REF_SOURCE = os.path.join(CSRC, "stream_ref.hip")
+STREAM_REF_PATH = os.path.join(PKG_DIR, "libdyt_streamref.so")
 
 ARCH = "gfx950"
 
@@ -38,11 +42,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the DyT library needs ROCm's hipcc to build")
 
 
-def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile the library; returns its path. Always recompiles."""
+def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False,
+          with_stream_ref: bool = True) -> str:
+    """Compile the library (and, by default, the reference streaming kernels
+    next to the default library path); returns the library's path. Always
+    recompiles."""
+    _compile(out, SOURCES, extra_flags, verbose)
+    if with_stream_ref and out == LIB_PATH:
+        _compile(STREAM_REF_PATH, [STREAM_REF_SOURCE], None, verbose)
+    return out
+
+
+def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbose: bool) -> None:
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra_flags or []),
-           "-o", tmp, *SOURCES]
+           "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,7 +67,6 @@ def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bo
     if verbose and msgs.strip():
         print(msgs)
     os.replace(tmp, out)
-    return out
 
 
 def is_stale(path: str = LIB_PATH) -> bool:
