@@ -50,7 +50,7 @@ HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, vendor figure
 SETTLE_S = 0.3                         # minimum untimed warm-up wall time
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", f)
-                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp")]
+                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp", "dyt_tune_table.inc")]
 
 
 def log(*a):
@@ -251,6 +251,7 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
         "bytes": B,
         "workspace_bytes": need,
         "plan": dyt.dyt_get_plan(M, N, xdt, pdt, True),
+        "fwd_plan": dyt.dyt_get_forward_plan(M, N, xdt, pdt, True),
     }
     res["fwd_frac"] = res["fwd_gbps"] / HBM_PEAK_GBPS
     res["bwd_frac"] = res["bwd_gbps"] / HBM_PEAK_GBPS
@@ -541,9 +542,11 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         B = r["bytes"]
         step_us = r["fwd_us_median"] + r["bwd_us_median"]
         sgbps = (B["fwd"] + B["bwd"]) / (step_us * 1e-6) / 1e9
-        pl = r["plan"]
-        plan = (f"{'packed R=' + str(pl['rows_per_tile']) if pl['packed'] else 'rows nb=' + str(pl['col_blocks'])}"
-                f", V={pl['vec']} K={pl['slots']}, tiles {pl['tiles']}")
+        def desc(pl, grid):
+            return (f"{'packed R=' + str(pl['rows_per_tile']) if pl['packed'] else 'rows nb=' + str(pl['col_blocks'])}"
+                    f", V={pl['vec']} K={pl['slots']}, {pl['tiles']} tiles, grid {grid}")
+        plan = (f"fwd: {desc(r['fwd_plan'], r['fwd_plan']['fwd_grid'])}; "
+                f"bwd: {desc(r['plan'], r['plan']['bwd_grid'])}")
         rows.append(f"| {name} | {r['M']} x {r['N']} | {r['x_dtype']}/{r['param_dtype']} | "
                     f"{r['fwd_us_median']:.1f} | {r['fwd_gbps']:.0f} | {100 * r['fwd_frac']:.1f} | "
                     f"{r['bwd_us_median']:.1f} | {r['bwd_gbps']:.0f} | {100 * r['bwd_frac']:.1f} | "

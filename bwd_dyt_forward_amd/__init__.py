@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     dyt_backward_workspace_size,
     dyt_forward,
     dyt_forward_residual,
+    dyt_get_forward_plan,
     dyt_get_plan,
     dyt_status_string,
     lib,
@@ -35,5 +36,5 @@ __all__ = [
     "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
     "dyt_backward_workspace_size", "dyt_forward_residual", "dyt_backward_residual",
     "dyt_backward_residual_partials",
-    "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
+    "dyt_status_string", "dyt_abi_version", "dyt_get_plan", "dyt_get_forward_plan",
 ]

@@ -63,6 +63,7 @@ SIGNATURES = {
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
+    "dyt_get_forward_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
 }
 
 
@@ -291,8 +292,18 @@ def dyt_abi_version() -> int:
 
 
 def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_aligned: bool = True) -> dict:
+    """The backward's plan (tiles, grid, workspace layout) and the forward's grid."""
     p = DytPlan()
     st = lib.dyt_get_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
                           1 if vector_aligned else 0, ctypes.byref(p))
     _check("dyt_get_plan", st)
+    return {name: getattr(p, name) for name, _ in DytPlan._fields_}
+
+
+def dyt_get_forward_plan(M: int, N: int, x_dtype, param_dtype, vector_aligned: bool = True) -> dict:
+    """The forward's plan (its tiles and grid; backward-only fields are 0)."""
+    p = DytPlan()
+    st = lib.dyt_get_forward_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
+                                  1 if vector_aligned else 0, ctypes.byref(p))
+    _check("dyt_get_forward_plan", st)
     return {name: getattr(p, name) for name, _ in DytPlan._fields_}

@@ -18,6 +18,7 @@ LIB_NAME = "libdyt.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "dyt_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "dyt_kernels.hpp"), os.path.join(CSRC, "dyt_math.hpp"),
+                     os.path.join(CSRC, "dyt_tune_table.inc"),
                      os.path.join(INCLUDE, "dyt.h")]
 # Reference streaming kernels for bench.py's measured ceilings (not part of
 # the DyT ABI; nothing in the package loads them).

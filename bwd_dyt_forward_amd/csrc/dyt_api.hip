@@ -14,8 +14,8 @@
 #include "dyt.h"
 #include "dyt_kernels.hpp"
 
-// Persistent-grid sizes (workgroups): one 256-thread workgroup per compute
-// unit of MI355X (256 CUs) for every kernel. Measured on the 32768 x 4096
+// Default persistent-grid sizes (workgroups): one 256-thread workgroup per
+// compute unit of MI355X (256 CUs). Measured on the 32768 x 4096
 // and 4194304 x 32 bfloat16 workloads, one workgroup per CU streamed HBM
 // faster than 2-8 per CU (fewer concurrent streams), and grids that are not
 // a multiple of the CU count lose to load imbalance. The constants are not
@@ -26,9 +26,6 @@
 #endif
 #ifndef DYT_BWD_GRID
 #define DYT_BWD_GRID 256
-#endif
-#ifndef DYT_BWD_GRID_WIDE
-#define DYT_BWD_GRID_WIDE 256
 #endif
 // Tiles per pipeline buffer (loads in flight per wave = U * K per input):
 // the forward has one input stream and needs two tiles in flight, the
@@ -46,8 +43,58 @@
 #ifndef DYT_MIN_TILES
 #define DYT_MIN_TILES 1024
 #endif
+// Largest K for row segments (0: the tile capacity's).
+#ifndef DYT_WIDE_KCAP
+#define DYT_WIDE_KCAP 0
+#endif
+// The constants above are the defaults; the measured table below overrides
+// them per (x dtype, row length) unless built with DYT_TUNE_TABLE=0 (the
+// tuner's candidate builds).
+#ifndef DYT_TUNE_TABLE
+#define DYT_TUNE_TABLE 1
+#endif
 
 namespace {
+
+// One row of the offline-measured tile table (bwd_dyt_forward_amd/tune.py
+// writes dyt_tune_table.inc): for x dtype `xdt`, row lengths
+// n_lo <= N <= n_hi and problem sizes e_lo <= M * N <= e_hi, one setting
+// each for the forward, the backward and the residual forward.
+// A packed plan takes the largest K that still yields min_tiles tiles, row
+// segments use at most kcap slots (0: no cap), and the grid has `grid`
+// workgroups. The forward's tiling is independent of the backward's (it has
+// no workspace), so the two are tuned separately. A static table keeps each
+// plan a pure function of the shape: the summation order, and every result
+// bit, never depends on a run-time measurement.
+struct TuneDir {
+    int64_t min_tiles;
+    int kcap;
+    int grid;
+};
+struct TuneEntry {
+    int xdt;
+    int64_t n_lo, n_hi;
+    int64_t e_lo, e_hi;
+    TuneDir fwd, bwd, res_fwd;   // plain forward, backward (both kinds), residual forward
+};
+
+// Which kernel a plan is for. The backward with and without the residual
+// gradient share one plan, so their parameter gradients are bitwise equal.
+enum class Dir { Fwd, Bwd, ResFwd };
+
+const TuneEntry kTuneTable[] = {
+#include "dyt_tune_table.inc"
+};
+
+TuneDir tune_for(int xdt, int64_t M, int64_t N, Dir d) {
+    if (DYT_TUNE_TABLE) {
+        const int64_t elems = M * N;
+        for (const TuneEntry& e : kTuneTable)
+            if (e.xdt == xdt && e.n_lo <= N && N <= e.n_hi && e.e_lo <= elems && elems <= e.e_hi)
+                return d == Dir::Fwd ? e.fwd : d == Dir::Bwd ? e.bwd : e.res_fwd;
+    }
+    return TuneDir{DYT_MIN_TILES, DYT_WIDE_KCAP, d == Dir::Bwd ? DYT_BWD_GRID : DYT_FWD_GRID};
+}
 
 using dyt::Geo;
 using dyt::FinGeo;
@@ -63,8 +110,7 @@ struct Plan {
     int64_t nb = 1;
     int64_t last_len = 0;
     int64_t tiles = 0;
-    int64_t fwd_grid = 0;
-    int64_t bwd_grid = 0;
+    int64_t grid = 0;      // workgroups of this direction's kernel (pass 1 for the backward)
     int64_t ld = 0;
     int64_t wcols = 0;
     int64_t fin_grid = 1;
@@ -102,7 +148,7 @@ constexpr int64_t kMaxN = (int64_t)1 << 30;   // row length limit (int32 in-tile
 // the same tiles with the element-wise kernel variant (V = 1, K = 16, whose
 // 4096-element capacity holds any tile), so the partial-row layout - and
 // with it dyt_backward_finish - does not depend on pointer alignment.
-int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
+int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
     if (M < 0 || N < 0 || N > kMaxN) return DYT_ERR_INVALID_ARG;
     const int64_t sx = dtype_size(xdt);
@@ -110,6 +156,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
     p = Plan();
     const int vmax = (int)(16 / sx);           // elements per 16 bytes
     const int kmax = dyt::kTileCap / (kBlock * vmax);
+    const TuneDir tune = tune_for(xdt, M, N, dir);
     if (M == 0 || N == 0) {
         p.fin_grid = ceil_div(2 * N + 1, 64);
         return DYT_OK;
@@ -128,7 +175,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
             const int64_t r = ((int64_t)kBlock * vmax * k / N) / r0 * r0;
             if (r < 1) break;
             chosen = k;
-            if (ceil_div(M, r) >= DYT_MIN_TILES) break;
+            if (ceil_div(M, r) >= tune.min_tiles) break;
         }
         const int64_t r = ((int64_t)kBlock * vmax * chosen / N) / r0 * r0;
         p.slots = chosen;
@@ -138,13 +185,12 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
         p.last_len = p.T;
         p.tiles = ceil_div(M, r);
         p.wcols = N;
-        p.fwd_grid = std::min<int64_t>(p.tiles, DYT_FWD_GRID);
-        p.bwd_grid = std::min<int64_t>(p.tiles, DYT_BWD_GRID);
+        p.grid = std::min<int64_t>(p.tiles, tune.grid);
     } else {
         p.packed = false;
         const bool v = (N * sx) % 16 == 0;     // rows start 16-byte aligned
         p.vec = v ? vmax : 1;
-        const int kbig = v ? kmax : 16;
+        const int kbig = v ? (tune.kcap > 0 ? std::min(kmax, tune.kcap) : kmax) : 16;
         int k = v ? 1 : 16;
         while (k < kbig && (int64_t)kBlock * p.vec * k < N) k *= 2;
         p.slots = k;
@@ -156,12 +202,11 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Plan& p) {
         p.R = 1;
         p.tiles = M * p.nb;
         p.wcols = p.T;
-        p.fwd_grid = p.nb * std::min<int64_t>(M, std::max<int64_t>(1, DYT_FWD_GRID / p.nb));
-        p.bwd_grid = p.nb * std::min<int64_t>(M, std::max<int64_t>(1, DYT_BWD_GRID_WIDE / p.nb));
+        p.grid = p.nb * std::min<int64_t>(M, std::max<int64_t>(1, tune.grid / p.nb));
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
-    p.ws_bytes = p.bwd_grid * p.ld * (int64_t)sizeof(float);
+    p.ws_bytes = p.grid * p.ld * (int64_t)sizeof(float);
     return DYT_OK;
 }
 
@@ -227,7 +272,7 @@ struct BwdPtrs {
 template <typename XT, typename PT, int V, int K, bool RES>
 void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
     constexpr int U = DYT_FWD_U;
-    const dim3 grid((unsigned)p.fwd_grid), block(kBlock);
+    const dim3 grid((unsigned)p.grid), block(kBlock);
     if (p.packed)
         hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES>), grid, block, 0, s,
                            (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
@@ -240,7 +285,7 @@ void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s)
 
 template <typename XT, typename PT, int V, int K, bool RES>
 void launch_bwd_vk(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
-    const dim3 grid((unsigned)p.bwd_grid), block(kBlock);
+    const dim3 grid((unsigned)p.grid), block(kBlock);
     if (p.packed)
         hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true, RES>), grid,
                            block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
@@ -289,7 +334,7 @@ template <typename PT>
 void launch_finish(const Plan& p, int64_t N, const float* ws, void* dg, void* db, void* da,
                    hipStream_t s) {
     FinGeo f;
-    f.P = p.bwd_grid;
+    f.P = p.grid;
     f.N = N;
     f.nb = (int32_t)p.nb;
     f.wc = (int32_t)p.T;
@@ -309,7 +354,7 @@ int validate_backward(const void* x, const void* dy, const void* dres, bool use_
                       void* dbeta, const void* workspace, size_t workspace_bytes, int64_t M,
                       int64_t N, int x_dtype, int param_dtype, bool use_pass1, bool use_pass2,
                       Plan& base) {
-    int st = make_plan(M, N, x_dtype, param_dtype, base);
+    int st = make_plan(M, N, x_dtype, param_dtype, Dir::Bwd, base);
     if (st != DYT_OK) return st;
     const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
     const bool any = M > 0 && N > 0;
@@ -377,7 +422,7 @@ int enqueue_pass2(const Plan& base, const void* workspace, void* dalpha, void* d
 int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, int param_dtype,
                  hipStream_t s) {
     Plan base;
-    int st = make_plan(M, N, x_dtype, param_dtype, base);
+    int st = make_plan(M, N, x_dtype, param_dtype, res ? Dir::ResFwd : Dir::Fwd, base);
     if (st != DYT_OK) return st;
     if (M == 0 || N == 0) return DYT_OK;
     if (!a.x || !a.alpha || !a.gamma || !a.beta || !a.y || (res && (!a.r || !a.h)))
@@ -425,6 +470,17 @@ int backward_impl(const BwdPtrs& a, bool res, void* dalpha, void* dgamma, void* 
     return enqueue_pass2(base, a.ws, dalpha, dgamma, dbeta, N, param_dtype, s);
 }
 
+void fill_plan(const Plan& p, dyt_plan* out) {
+    out->packed = p.packed ? 1 : 0;
+    out->vec = p.vec;
+    out->slots = p.slots;
+    out->block = kBlock;
+    out->rows_per_tile = p.R;
+    out->tile_elems = p.T;
+    out->col_blocks = p.nb;
+    out->tiles = p.tiles;
+}
+
 }  // namespace
 
 extern "C" {
@@ -446,29 +502,40 @@ const char* dyt_status_string(int status) {
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
                  dyt_plan* out) {
     if (!out) return DYT_ERR_INVALID_ARG;
-    Plan base;
-    const int st = make_plan(M, N, x_dtype, param_dtype, base);
+    Plan base, fbase;
+    int st = make_plan(M, N, x_dtype, param_dtype, Dir::Bwd, base);
+    if (st != DYT_OK) return st;
+    st = make_plan(M, N, x_dtype, param_dtype, Dir::Fwd, fbase);
     if (st != DYT_OK) return st;
     const Plan p = variant_for(base, vector_aligned != 0);
-    out->packed = p.packed ? 1 : 0;
-    out->vec = p.vec;
-    out->slots = p.slots;
-    out->block = kBlock;
-    out->rows_per_tile = p.R;
-    out->tile_elems = p.T;
-    out->col_blocks = p.nb;
-    out->tiles = p.tiles;
-    out->fwd_grid = p.fwd_grid;
-    out->bwd_grid = p.bwd_grid;
+    fill_plan(p, out);
+    out->fwd_grid = fbase.grid;
+    out->bwd_grid = p.grid;
     out->ws_row = p.ld;
     out->fin_grid = p.fin_grid;
     out->ws_bytes = p.ws_bytes;
     return DYT_OK;
 }
 
+int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
+                         dyt_plan* out) {
+    if (!out) return DYT_ERR_INVALID_ARG;
+    Plan base;
+    const int st = make_plan(M, N, x_dtype, param_dtype, Dir::Fwd, base);
+    if (st != DYT_OK) return st;
+    const Plan p = variant_for(base, vector_aligned != 0);
+    fill_plan(p, out);
+    out->fwd_grid = p.grid;
+    out->bwd_grid = 0;
+    out->ws_row = 0;
+    out->fin_grid = 0;
+    out->ws_bytes = 0;
+    return DYT_OK;
+}
+
 size_t dyt_backward_workspace_size(int64_t M, int64_t N, int x_dtype, int param_dtype) {
     Plan p;
-    if (make_plan(M, N, x_dtype, param_dtype, p) != DYT_OK) return 0;
+    if (make_plan(M, N, x_dtype, param_dtype, Dir::Bwd, p) != DYT_OK) return 0;
     return (size_t)round_up(p.ws_bytes, 16);
 }
 

@@ -214,11 +214,14 @@ int dyt_abi_version(void);
 
 /*
  * Launch geometry the library would use (for tests and reports; pure host
- * function, no HIP calls). The tiling, grids and workspace layout depend
- * only on (M, N, x_dtype); vector_aligned selects which kernel variant is
- * described (non-zero: 16-byte aligned x/dy/y/dx, vector access; zero:
- * element-wise access, vec = 1). Returns DYT_OK or the status the compute
- * calls would return for these sizes and dtypes.
+ * function, no HIP calls). dyt_get_plan describes the backward (pass 1 tiles,
+ * grid and workspace layout; fwd_grid is the forward's grid), which depends
+ * only on (M, N, x_dtype). Both directions take their tile size and grid
+ * from a static table measured offline per (x dtype, row-length range), so
+ * every plan is a pure function of the shape. vector_aligned selects which
+ * kernel variant is described (non-zero: 16-byte aligned x/dy/y/dx, vector
+ * access; zero: element-wise access, vec = 1). Returns DYT_OK or the status
+ * the compute calls would return for these sizes and dtypes.
  */
 typedef struct dyt_plan {
     int32_t packed;        /* 1: tiles of >= 2 whole rows (N <= 2048); 0: row segments */
@@ -238,6 +241,15 @@ typedef struct dyt_plan {
 
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
                  dyt_plan* out);
+
+/*
+ * The forward's geometry: the forward (plain and residual) tiles the problem
+ * independently of the backward (it has no workspace), from its own row of
+ * the tile table. Same struct; fwd_grid is the forward's grid and the
+ * backward-only fields (bwd_grid, ws_row, fin_grid, ws_bytes) are 0.
+ */
+int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype,
+                         int vector_aligned, dyt_plan* out);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,8 @@ def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted([
         "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
-        "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials"])
+        "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
+        "dyt_get_forward_plan"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -109,6 +110,51 @@ def test_plan_uses_1d_grid_beyond_65535_rows(dyt):
     assert p["tiles"] * p["rows_per_tile"] >= 65537
     p = dyt.dyt_get_plan(10 ** 7, 4096, "bf16", "f32")
     assert p["tiles"] == 10 ** 7 and p["bwd_grid"] <= 4096
+
+
+@pytest.mark.parametrize("M,N,xdt", CONFIG_SHAPES + [(7, 5000, "f32"), (3, 20000, "bf16"), (1, 1, "f16")])
+@pytest.mark.parametrize("vec", [True, False])
+def test_forward_plan_invariants(dyt, M, N, xdt, vec):
+    """The forward tiles independently of the backward, with the same rules."""
+    p = dyt.dyt_get_forward_plan(M, N, xdt, "f32", vec)
+    b = dyt.dyt_get_plan(M, N, xdt, "f32", vec)
+    sx = 4 if xdt == "f32" else 2
+    assert p["fwd_grid"] == b["fwd_grid"] and p["ws_bytes"] == 0 and p["bwd_grid"] == 0
+    assert p["packed"] == b["packed"] and p["vec"] == b["vec"]
+    assert 1 <= p["tile_elems"] <= p["block"] * p["vec"] * p["slots"] <= 4096
+    if p["packed"]:
+        R = p["rows_per_tile"]
+        assert p["tile_elems"] == R * N and p["tiles"] == -(-M // R)
+        if p["vec"] > 1:
+            assert (R * N * sx) % 16 == 0
+    else:
+        assert p["col_blocks"] * p["tile_elems"] >= N > (p["col_blocks"] - 1) * p["tile_elems"]
+        assert p["tiles"] == M * p["col_blocks"] and p["fwd_grid"] % p["col_blocks"] == 0
+    assert 1 <= p["fwd_grid"] <= p["tiles"]
+
+
+def test_tile_table_covers_every_dtype_width_and_size():
+    """Every (x dtype, N, M*N) resolves to exactly one row of the measured table."""
+    import re
+    src = open(os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", "dyt_tune_table.inc")).read()
+    rows = re.findall(r"\{(DYT_\w+), (\d+), (\d+), (\d+), (\d+), \{(\d+), (\d+), (\d+)\}, "
+                      r"\{(\d+), (\d+), (\d+)\}, \{(\d+), (\d+), (\d+)\}\}", src)
+    assert rows
+    for dt in ("DYT_F32", "DYT_BF16", "DYT_F16"):
+        mine = [r for r in rows if r[0] == dt]
+        spans = sorted({(int(r[1]), int(r[2])) for r in mine})
+        assert spans[0][0] == 1 and spans[-1][1] >= 1 << 30
+        for (a, b), (c, d) in zip(spans, spans[1:]):
+            assert c == b + 1, (dt, b, c)
+        for lo, hi in spans:
+            sizes = sorted((int(r[3]), int(r[4])) for r in mine if (int(r[1]), int(r[2])) == (lo, hi))
+            assert sizes[0][0] <= 1 and sizes[-1][1] >= 1 << 62
+            for (a, b), (c, d) in zip(sizes, sizes[1:]):
+                assert c == b + 1, (dt, lo, b, c)
+    for r in rows:
+        v = list(map(int, r[5:]))
+        for mt, kc, g in (v[0:3], v[3:6], v[6:9]):
+            assert mt >= 1 and kc in (0, 1, 2, 4) and 64 <= g <= 4096
 
 
 def test_plan_narrow_rows_are_packed(dyt):
