@@ -68,6 +68,8 @@ CANDIDATES = {
     "g_mt1024_k0_fg1024": (1024, 0, 1024, 256),
     "h_mt4096_k2_fg1024": (4096, 2, 1024, 256),
     "i_mt16384_k1_fg1024": (16384, 1, 1024, 256),
+    "j_mt1M_k1_g512": (1 << 20, 1, 512, 512),
+    "k_mt1M_k1_fg1024": (1 << 20, 1, 1024, 256),
 }
 
 
@@ -218,7 +220,7 @@ def cmd_emit(path: str) -> None:
     cands = {k: tuple(v) for k, v in data["candidates"].items()}
     dflt = data["default"]
     lines = HEADER + [f"// measured: {os.path.basename(path)}; note = representative shapes, chosen "
-                      "candidate (a-i, see tune.py) and its times relative to the default a "
+                      "candidate (a-k, see tune.py) and its times relative to the default a "
                       "(forward; backward; residual forward)"]
     groups = {}
     for d in DTYPES:
