@@ -56,6 +56,9 @@ SIGNATURES = {
                                      _int, _int, _vp]),
     "dyt_backward_finish": (_int, [_vp, ctypes.c_size_t, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
     "dyt_forward_residual": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp]),
+    "dyt_forward_strided": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_strided": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _i64, _i64, _int, _int, _vp]),
     "dyt_backward_residual": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _i64, _i64, _int, _int, _vp]),
     "dyt_backward_residual_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
@@ -112,11 +115,21 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _check_act(name: str, t: torch.Tensor) -> None:
+def _check_act(name: str, t: torch.Tensor, strided: bool = False) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.dim() != 2 or not t.is_contiguous():
+    if strided:
+        if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1) or \
+                (t.size(0) > 1 and t.stride(0) < t.size(1)):
+            raise ValueError(f"{name} must be a 2-D [M, N] tensor with unit column stride and "
+                             "row stride >= N")
+    elif t.dim() != 2 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous 2-D [M, N] tensor")
+
+
+def _pitch(t: torch.Tensor) -> int:
+    """Row pitch in elements (N for a single row or a contiguous tensor)."""
+    return t.stride(0) if t.size(0) > 1 else t.size(1)
 
 
 def _check_params(N: int, alpha, *vecs) -> None:
@@ -132,15 +145,26 @@ def _check_params(N: int, alpha, *vecs) -> None:
 
 def dyt_forward(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
                 y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y = gamma * tanh(alpha * x) + beta on the HIP stream (async)."""
-    _check_act("x", x)
+    """y = gamma * tanh(alpha * x) + beta on the HIP stream (async). x and y
+    may be row-strided 2-D views (unit column stride); a new y is contiguous."""
+    _check_act("x", x, strided=True)
     M, N = x.shape
     _check_params(N, alpha, gamma, beta)
     if y is None:
-        y = torch.empty_like(x)
-    st = lib.dyt_forward(_ptr(x), _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(y), M, N,
-                         _code(x.dtype), _code(alpha.dtype), _stream(stream))
-    _check("dyt_forward", st)
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _check_act("y", y, strided=True)
+        if y.shape != x.shape or y.dtype != x.dtype:
+            raise ValueError("y must match x in shape and dtype")
+    ldx, ldy = _pitch(x), _pitch(y)
+    if ldx == N and ldy == N:
+        st = lib.dyt_forward(_ptr(x), _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(y), M, N,
+                             _code(x.dtype), _code(alpha.dtype), _stream(stream))
+        _check("dyt_forward", st)
+    else:
+        st = lib.dyt_forward_strided(_ptr(x), ldx, _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(y),
+                                     ldy, M, N, _code(x.dtype), _code(alpha.dtype), _stream(stream))
+        _check("dyt_forward_strided", st)
     return y
 
 
@@ -152,9 +176,11 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
                  dx: torch.Tensor | None = None, dalpha: torch.Tensor | None = None,
                  dgamma: torch.Tensor | None = None, dbeta: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None, stream=None):
-    """Returns (dx, dalpha, dgamma, dbeta); enqueued on the HIP stream (async)."""
-    _check_act("x", x)
-    _check_act("dy", dy)
+    """Returns (dx, dalpha, dgamma, dbeta); enqueued on the HIP stream (async).
+    x, dy and dx may be row-strided 2-D views (unit column stride); a new dx
+    is contiguous."""
+    _check_act("x", x, strided=True)
+    _check_act("dy", dy, strided=True)
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
     M, N = x.shape
@@ -162,7 +188,11 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
     pdt = alpha.dtype
     dev = x.device
     if dx is None:
-        dx = torch.empty_like(x)
+        dx = torch.empty((M, N), dtype=x.dtype, device=dev)
+    else:
+        _check_act("dx", dx, strided=True)
+        if dx.shape != x.shape or dx.dtype != x.dtype:
+            raise ValueError("dx must match x in shape and dtype")
     if dalpha is None:
         dalpha = torch.empty(1, dtype=pdt, device=dev)
     if dgamma is None:
@@ -173,10 +203,18 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() * workspace.element_size()
-    st = lib.dyt_backward(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx), _ptr(dalpha),
-                          _ptr(dgamma), _ptr(dbeta), _ptr(workspace), wbytes, M, N,
-                          _code(x.dtype), _code(pdt), _stream(stream))
-    _check("dyt_backward", st)
+    ldx, lddy, lddx = _pitch(x), _pitch(dy), _pitch(dx)
+    if ldx == N and lddy == N and lddx == N:
+        st = lib.dyt_backward(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx), _ptr(dalpha),
+                              _ptr(dgamma), _ptr(dbeta), _ptr(workspace), wbytes, M, N,
+                              _code(x.dtype), _code(pdt), _stream(stream))
+        _check("dyt_backward", st)
+    else:
+        st = lib.dyt_backward_strided(_ptr(x), ldx, _ptr(dy), lddy, _ptr(alpha), _ptr(gamma),
+                                      _ptr(dx), lddx, _ptr(dalpha), _ptr(dgamma), _ptr(dbeta),
+                                      _ptr(workspace), wbytes, M, N, _code(x.dtype), _code(pdt),
+                                      _stream(stream))
+        _check("dyt_backward_strided", st)
     return dx, dalpha, dgamma, dbeta
 
 

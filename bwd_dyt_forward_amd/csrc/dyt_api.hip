@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <type_traits>
 
 #include "dyt.h"
@@ -232,6 +233,7 @@ Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     g.last_len = (int32_t)p.last_len;
     g.ld = (int32_t)p.ld;
     g.wcols = (int32_t)p.wcols;
+    g.pitch[0] = g.pitch[1] = g.pitch[2] = N;
     return g;
 }
 
@@ -250,6 +252,8 @@ Range range(const void* p, int64_t bytes) {
 // ------------------------------------------------------------- dispatch
 // Device pointers of one launch; r/h (forward) and dres (backward) are null
 // unless the residual add is fused.
+// Row pitches (elements; 0 = N, contiguous) of x and y (forward) or x, dy
+// and dx (backward) for the strided entry points.
 struct FwdPtrs {
     const void* x;
     const void* r;
@@ -258,6 +262,7 @@ struct FwdPtrs {
     const void* beta;
     void* y;
     void* h;
+    int64_t ldx, ldy;
 };
 struct BwdPtrs {
     const void* x;
@@ -267,32 +272,61 @@ struct BwdPtrs {
     const void* gamma;
     void* dx;
     float* ws;
+    int64_t ldx, lddy, lddx;
 };
 
-template <typename XT, typename PT, int V, int K, bool RES>
+int64_t pitch_or(int64_t ld, int64_t N) { return ld == 0 ? N : ld; }
+
+// Bytes a row-pitched M x N tensor spans (0 when empty).
+int64_t span_bytes(int64_t M, int64_t N, int64_t ld, int64_t sx) {
+    return (M > 0 && N > 0) ? ((M - 1) * ld + N) * sx : 0;
+}
+
+// Pitches valid: each at least N and small enough that every element offset
+// fits in int64 (checked like M * N).
+bool pitches_ok(int64_t M, int64_t N, std::initializer_list<int64_t> lds) {
+    for (int64_t ld : lds)
+        if (ld < N || (M > 0 && ld > INT64_MAX / M / 16)) return false;
+    return true;
+}
+
+// The vector kernels need every base 16-byte aligned; a strided launch also
+// needs every row start aligned (pitch * sx multiple of 16) and, for packed
+// tiles, slots that never straddle two rows (N a multiple of the vector width).
+bool vector_ok(const Plan& p, int64_t N, int64_t sx, bool strided,
+               std::initializer_list<const void*> ptrs, std::initializer_list<int64_t> lds) {
+    for (const void* q : ptrs)
+        if (q && (uintptr_t)q % 16 != 0) return false;
+    if (!strided) return true;
+    for (int64_t ld : lds)
+        if ((ld * sx) % 16 != 0) return false;
+    return !p.packed || N % (16 / sx) == 0;
+}
+
+template <typename XT, typename PT, int V, int K, bool RES, bool STRIDED>
 void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
     constexpr int U = DYT_FWD_U;
     const dim3 grid((unsigned)p.grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES>), grid, block, 0, s,
-                           (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
-                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES, STRIDED>), grid, block, 0,
+                           s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
+                           (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, false, RES>), grid, block, 0, s,
-                           (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
-                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
+        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, false, RES, STRIDED>), grid, block, 0,
+                           s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
+                           (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
 }
 
-template <typename XT, typename PT, int V, int K, bool RES>
+template <typename XT, typename PT, int V, int K, bool RES, bool STRIDED>
 void launch_bwd_vk(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
     const dim3 grid((unsigned)p.grid), block(kBlock);
     if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true, RES>), grid,
-                           block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true, RES, STRIDED>),
+                           grid, block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
                            (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
     else
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false, RES>), grid,
-                           block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
+        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false, RES, STRIDED>),
+                           grid, block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
                            (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
 }
 
@@ -314,18 +348,18 @@ bool dispatch_vk(const Plan& p, L&& launch) {
     }
 }
 
-template <typename XT, typename PT, bool RES>
+template <typename XT, typename PT, bool RES, bool STRIDED>
 bool launch_fwd(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
     return dispatch_vk<XT>(p, [&](auto v, auto k) {
-        launch_fwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES>(p, g, a, s);
+        launch_fwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES, STRIDED>(p, g, a, s);
         return true;
     });
 }
 
-template <typename XT, typename PT, bool RES>
+template <typename XT, typename PT, bool RES, bool STRIDED>
 bool launch_bwd(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
     return dispatch_vk<XT>(p, [&](auto v, auto k) {
-        launch_bwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES>(p, g, a, s);
+        launch_bwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES, STRIDED>(p, g, a, s);
         return true;
     });
 }
@@ -353,7 +387,7 @@ int validate_backward(const void* x, const void* dy, const void* dres, bool use_
                       const void* alpha, const void* gamma, void* dx, void* dalpha, void* dgamma,
                       void* dbeta, const void* workspace, size_t workspace_bytes, int64_t M,
                       int64_t N, int x_dtype, int param_dtype, bool use_pass1, bool use_pass2,
-                      Plan& base) {
+                      Plan& base, int64_t ldx = 0, int64_t lddy = 0, int64_t lddx = 0) {
     int st = make_plan(M, N, x_dtype, param_dtype, Dir::Bwd, base);
     if (st != DYT_OK) return st;
     const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
@@ -364,6 +398,10 @@ int validate_backward(const void* x, const void* dy, const void* dres, bool use_
         if (N > 0 && (!dgamma || !dbeta)) return DYT_ERR_INVALID_ARG;
     }
     if (p1 && (!x || !dy || !alpha || !gamma || !dx || (use_dres && !dres))) return DYT_ERR_INVALID_ARG;
+    ldx = pitch_or(ldx, N);
+    lddy = pitch_or(lddy, N);
+    lddx = pitch_or(lddx, N);
+    if (!pitches_ok(M, N, {ldx, lddy, lddx})) return DYT_ERR_INVALID_ARG;
     const size_t need = (size_t)round_up(base.ws_bytes, 16);
     if (workspace_bytes < need) return DYT_ERR_WORKSPACE_TOO_SMALL;
     if (need > 0 && !workspace) return DYT_ERR_INVALID_ARG;
@@ -374,12 +412,15 @@ int validate_backward(const void* x, const void* dy, const void* dres, bool use_
                !aligned(gamma, sp) || (use_dres && !aligned(dres, sx))))
         return DYT_ERR_MISALIGNED;
     // outputs (and the workspace) must not overlap inputs or each other
-    const int64_t mn = p1 ? M * N * sx : 0;
-    const Range outs[5] = {range(dx, mn), range(dalpha, use_pass2 ? sp : 0),
+    // (strided tensors: over the bytes from their first to their last element)
+    const int64_t mx = p1 ? span_bytes(M, N, ldx, sx) : 0;
+    const Range outs[5] = {range(dx, p1 ? span_bytes(M, N, lddx, sx) : 0),
+                           range(dalpha, use_pass2 ? sp : 0),
                            range(dgamma, use_pass2 ? N * sp : 0), range(dbeta, use_pass2 ? N * sp : 0),
                            range(workspace, (int64_t)need)};
-    const Range ins[5] = {range(x, mn), range(dy, mn), range(dres, use_dres ? mn : 0),
-                          range(alpha, p1 ? sp : 0), range(gamma, p1 ? N * sp : 0)};
+    const Range ins[5] = {range(x, mx), range(dy, p1 ? span_bytes(M, N, lddy, sx) : 0),
+                          range(dres, use_dres ? mx : 0), range(alpha, p1 ? sp : 0),
+                          range(gamma, p1 ? N * sp : 0)};
     for (int a = 0; a < 5; ++a) {
         if (outs[a].lo == outs[a].hi) continue;
         for (const Range& i : ins)
@@ -394,14 +435,22 @@ int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int 
                   int param_dtype, hipStream_t s) {
     if (M == 0 || N == 0) return DYT_OK;
     const bool res = a.dres != nullptr;
-    const Plan p = variant_for(base, aligned(a.x, 16) && aligned(a.dy, 16) && aligned(a.dx, 16) &&
-                                         (!res || aligned(a.dres, 16)));
-    const Geo g = make_geo(p, M, N);
+    const int64_t ldx = pitch_or(a.ldx, N), lddy = pitch_or(a.lddy, N), lddx = pitch_or(a.lddx, N);
+    const bool strided = ldx != N || lddy != N || lddx != N;
+    const int64_t sx = dtype_size(x_dtype);
+    const Plan p = variant_for(base, vector_ok(base, N, sx, strided, {a.x, a.dy, a.dx, a.dres},
+                                               {ldx, lddy, lddx}));
+    Geo g = make_geo(p, M, N);
+    g.pitch[0] = ldx;
+    g.pitch[1] = lddy;
+    g.pitch[2] = lddx;
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return with_dtype(param_dtype, [&](auto pt) {
             using XT = decltype(xt);
             using PT = decltype(pt);
-            return res ? launch_bwd<XT, PT, true>(p, g, a, s) : launch_bwd<XT, PT, false>(p, g, a, s);
+            if (res) return launch_bwd<XT, PT, true, false>(p, g, a, s);
+            return strided ? launch_bwd<XT, PT, false, true>(p, g, a, s)
+                           : launch_bwd<XT, PT, false, false>(p, g, a, s);
         });
     });
     if (!ok) return DYT_ERR_INVALID_ARG;
@@ -427,14 +476,19 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     if (M == 0 || N == 0) return DYT_OK;
     if (!a.x || !a.alpha || !a.gamma || !a.beta || !a.y || (res && (!a.r || !a.h)))
         return DYT_ERR_INVALID_ARG;
+    const int64_t ldx = pitch_or(a.ldx, N), ldy = pitch_or(a.ldy, N);
+    if (!pitches_ok(M, N, {ldx, ldy})) return DYT_ERR_INVALID_ARG;
+    const bool strided = ldx != N || ldy != N;
+    if (strided && res) return DYT_ERR_INVALID_ARG;   // not offered by any entry point
     const int64_t sx = dtype_size(x_dtype), sp = dtype_size(param_dtype);
     if (!aligned(a.x, sx) || !aligned(a.y, sx) || !aligned(a.alpha, sp) || !aligned(a.gamma, sp) ||
         !aligned(a.beta, sp) || (res && (!aligned(a.r, sx) || !aligned(a.h, sx))))
         return DYT_ERR_MISALIGNED;
-    // outputs must not overlap inputs or each other
-    const int64_t mn = M * N * sx;
-    const Range outs[2] = {range(a.y, mn), range(a.h, res ? mn : 0)};
-    const Range ins[5] = {range(a.x, mn), range(a.r, res ? mn : 0), range(a.alpha, sp),
+    // outputs must not overlap inputs or each other (strided tensors: over the
+    // bytes from their first to their last element)
+    const int64_t mx = span_bytes(M, N, ldx, sx), my = span_bytes(M, N, ldy, sx);
+    const Range outs[2] = {range(a.y, my), range(a.h, res ? my : 0)};
+    const Range ins[5] = {range(a.x, mx), range(a.r, res ? mx : 0), range(a.alpha, sp),
                           range(a.gamma, N * sp), range(a.beta, N * sp)};
     for (const Range& o : outs) {
         if (o.lo == o.hi) continue;
@@ -442,14 +496,17 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
-    const Plan p = variant_for(base, aligned(a.x, 16) && aligned(a.y, 16) &&
-                                         (!res || (aligned(a.r, 16) && aligned(a.h, 16))));
-    const Geo g = make_geo(p, M, N);
+    const Plan p = variant_for(base, vector_ok(base, N, sx, strided, {a.x, a.y, a.r, a.h}, {ldx, ldy}));
+    Geo g = make_geo(p, M, N);
+    g.pitch[0] = ldx;
+    g.pitch[1] = ldy;
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return with_dtype(param_dtype, [&](auto pt) {
             using XT = decltype(xt);
             using PT = decltype(pt);
-            return res ? launch_fwd<XT, PT, true>(p, g, a, s) : launch_fwd<XT, PT, false>(p, g, a, s);
+            if (res) return launch_fwd<XT, PT, true, false>(p, g, a, s);
+            return strided ? launch_fwd<XT, PT, false, true>(p, g, a, s)
+                           : launch_fwd<XT, PT, false, false>(p, g, a, s);
         });
     });
     if (!ok) return DYT_ERR_INVALID_ARG;   // no kernel instance for this plan (not reachable)
@@ -463,7 +520,7 @@ int backward_impl(const BwdPtrs& a, bool res, void* dalpha, void* dgamma, void* 
     Plan base;
     int st = validate_backward(a.x, a.dy, a.dres, res, a.alpha, a.gamma, a.dx, dalpha, dgamma,
                                dbeta, a.ws, workspace_bytes, M, N, x_dtype, param_dtype, true,
-                               true, base);
+                               true, base, a.ldx, a.lddy, a.lddx);
     if (st != DYT_OK) return st;
     st = enqueue_pass1(base, a, M, N, x_dtype, param_dtype, s);
     if (st != DYT_OK) return st;
@@ -543,6 +600,26 @@ int dyt_forward(const void* x, const void* alpha, const void* gamma, const void*
                 int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream) {
     return forward_impl(FwdPtrs{x, nullptr, alpha, gamma, beta, y, nullptr}, false, M, N, x_dtype,
                         param_dtype, static_cast<hipStream_t>(stream));
+}
+
+int dyt_forward_strided(const void* x, int64_t ldx, const void* alpha, const void* gamma,
+                        const void* beta, void* y, int64_t ldy, int64_t M, int64_t N, int x_dtype,
+                        int param_dtype, void* stream) {
+    if (ldx <= 0 || ldy <= 0) return DYT_ERR_INVALID_ARG;
+    return forward_impl(FwdPtrs{x, nullptr, alpha, gamma, beta, y, nullptr, ldx, ldy}, false, M, N,
+                        x_dtype, param_dtype, static_cast<hipStream_t>(stream));
+}
+
+int dyt_backward_strided(const void* x, int64_t ldx, const void* dy, int64_t lddy,
+                         const void* alpha, const void* gamma, void* dx, int64_t lddx,
+                         void* dalpha, void* dgamma, void* dbeta, void* workspace,
+                         size_t workspace_bytes, int64_t M, int64_t N, int x_dtype,
+                         int param_dtype, void* stream) {
+    if (ldx <= 0 || lddy <= 0 || lddx <= 0) return DYT_ERR_INVALID_ARG;
+    return backward_impl(BwdPtrs{x, dy, nullptr, alpha, gamma, dx, static_cast<float*>(workspace),
+                                 ldx, lddy, lddx},
+                         false, dalpha, dgamma, dbeta, workspace_bytes, M, N, x_dtype,
+                         param_dtype, static_cast<hipStream_t>(stream));
 }
 
 int dyt_forward_residual(const void* x, const void* r, const void* alpha, const void* gamma,

@@ -71,6 +71,9 @@ struct Geo {
     int32_t last_len;  // wide: columns in the last block; packed: T
     int32_t ld;        // floats per workspace partial row
     int32_t wcols;     // packed: N; wide: Wc (dgamma/dbeta entries per row)
+    // Row pitches (elements) of the activations of a strided launch: forward
+    // x (and r), y (and h); backward x (and dres), dy, dx. N when contiguous.
+    int64_t pitch[3];
 };
 
 struct FinGeo {
@@ -333,6 +336,46 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t
     return w;
 }
 
+// Addressing of one tensor in this workgroup's walk: unit u starts at
+// element col_base + u * upitch, and slot k lies `off[k]` elements after it.
+// Contiguous tensors share one Addr (upitch = T or N, off = the slot's tile
+// offset). A tensor with row pitch ld (strided launch) has upitch = R * ld
+// (packed) or ld (row segments), and a packed slot at tile offset o lies at
+// (o / N) * ld + o mod N: with N a multiple of V the slot's V elements stay
+// in one row.
+template <int K, bool STRIDED>
+struct Addr {
+    using Off = typename std::conditional<STRIDED, int64_t, int>::type;
+    int64_t upitch;
+    Off off[K];
+};
+
+template <int V, int K, bool PACKED, bool STRIDED>
+__device__ __forceinline__ Addr<K, STRIDED> make_addr(const Slots<V, K>& sl, const TileWalk& w,
+                                                      const Geo& g, int64_t ld) {
+    Addr<K, STRIDED> a;
+    if constexpr (!STRIDED) {
+        a.upitch = w.unit;
+#pragma unroll
+        for (int k = 0; k < K; ++k) a.off[k] = sl.off[k];
+    } else {
+        a.upitch = PACKED ? (int64_t)g.R * ld : ld;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int o = sl.off[k];
+            a.off[k] = PACKED ? (int64_t)(o / (int)g.N) * ld + o % (int)g.N : (int64_t)o;
+        }
+    }
+    return a;
+}
+
+// Offset of tile offset o (a natural slot position, for the masked tail).
+template <bool PACKED, bool STRIDED>
+__device__ __forceinline__ int64_t tile_off(int o, const Geo& g, int64_t ld) {
+    if constexpr (STRIDED && PACKED) return (int64_t)(o / (int)g.N) * ld + o % (int)g.N;
+    else return o;
+}
+
 template <bool ACC>
 __device__ __forceinline__ float dyt_tanh(float u) {
     if constexpr (ACC) return tanh_accurate(u);
@@ -345,22 +388,22 @@ __device__ __forceinline__ void dyt_tanh_sech2(float xv, float alpha, float& t, 
 }
 
 // Loads of U consecutive tiles of this workgroup (all K slots, raw
-// registers; tile j sits at base + j * step) and the forward arithmetic and
-// stores of such a loaded group. With RES the residual r is loaded beside x,
-// h = x + r is rounded to the storage type and stored, and y is computed
-// from the stored h.
-template <typename XT, int V, int K, int U, bool RES>
+// registers; tile j of the input sits at bi + j * pi) and the forward
+// arithmetic and stores of such a loaded group (outputs at bo + j * po).
+// With RES the residual r is loaded beside x, h = x + r is rounded to the
+// storage type and stored, and y is computed from the stored h.
+template <typename XT, int V, int K, int U, bool RES, typename AD>
 __device__ __forceinline__ void fwd_load(const XT* __restrict__ x, const XT* __restrict__ r,
-                                         int64_t base, int64_t step, const Slots<V, K>& sl,
+                                         int64_t bi, const AD& ai,
                                          typename Raw<XT, V>::T (&rx)[U][K],
                                          typename Raw<XT, V>::T (&rr)[U][K]) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            rx[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(x + base + j * step + sl.off[k]);
-            if constexpr (RES)
-                rr[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(r + base + j * step + sl.off[k]);
+            const int64_t at = bi + j * ai.upitch + ai.off[k];
+            rx[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(x + at);
+            if constexpr (RES) rr[j][k] = Raw<XT, V>::template load<DYT_FWD_NT>(r + at);
         }
 }
 
@@ -382,18 +425,17 @@ __device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
     }
 }
 
-template <typename XT, int V, int K, int U, bool ACC, bool RES>
+template <typename XT, int V, int K, int U, bool ACC, bool RES, typename AD>
 __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
                                          const typename Raw<XT, V>::T (&rr)[U][K],
-                                         XT* __restrict__ y, XT* __restrict__ h, int64_t base,
-                                         int64_t step, const Slots<V, K>& sl,
-                                         const float (&gm)[K][V], const float (&bt)[K][V],
-                                         float alpha) {
+                                         XT* __restrict__ y, XT* __restrict__ h, int64_t bo,
+                                         const AD& ao, const float (&gm)[K][V],
+                                         const float (&bt)[K][V], float alpha) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int64_t at = base + j * step + sl.off[k];
+            const int64_t at = bo + j * ao.upitch + ao.off[k];
             float v[V];
             fwd_input<XT, V, RES>(rx[j][k], rr[j][k], h + at, v);
 #pragma unroll
@@ -407,13 +449,15 @@ __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 // y = gamma * tanh(alpha * x) + beta; with RES (residual add fused in front)
 // h = x + r and y = gamma * tanh(alpha * h) + beta. Loads of the next tile
 // are issued before the current tile is computed (register double
-// buffering). r and h are unused (null) without RES.
-template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES>
+// buffering). r and h are unused (null) without RES. STRIDED: x and y have
+// row pitches g.pitch[0] and g.pitch[1] (no RES).
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED>
 __global__ void __launch_bounds__(kBlock)
 dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
                const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
                const PT* __restrict__ beta, XT* __restrict__ y, XT* __restrict__ h,
                const Geo g) {
+    static_assert(!(RES && STRIDED), "the residual layer takes contiguous tensors");
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -422,6 +466,8 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const float alpha = to_f32(alpha_p[0]);
     const TileWalk w = make_walk(g, PACKED, wg, G);
     const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
+    const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
+    const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
 
     float gm[K][V], bt[K][V];
 #pragma unroll
@@ -442,63 +488,69 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     // previous group (valid memory, never computed).
     const int64_t ng = w.units / U;
     const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
-    const int64_t gstep = w.gcount * U * w.unit;
+    const int64_t ustep = w.gcount * U;          // units between this workgroup's groups
+    const int64_t gsi = ustep * ai.upitch, gso = ustep * ao.upitch;
     if (iters > 0) {
         typename R::T xa[U][K], xb[U][K], ra[U][K], rb[U][K];
-        int64_t base_a = w.col_base + w.gw * U * w.unit;
-        fwd_load<XT, V, K, U, RES>(x, r, base_a, w.unit, sl, xa, ra);
+        int64_t bia = w.col_base + w.gw * U * ai.upitch;   // input / output bases of group A
+        int64_t boa = w.col_base + w.gw * U * ao.upitch;
+        fwd_load<XT, V, K, U, RES>(x, r, bia, ai, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t base_b = base_a + gstep;
-            fwd_load<XT, V, K, U, RES>(x, r, base_b, w.unit, sl, xb, rb);
+            const int64_t bib = bia + gsi, bob = boa + gso;
+            fwd_load<XT, V, K, U, RES>(x, r, bib, ai, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, base_a, w.unit, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, boa, ao, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
-            fwd_load<XT, V, K, U, RES>(x, r, base_n, w.unit, sl, xa, ra);
+            const bool more = 2 * pi + 2 < iters;
+            const int64_t bin = more ? bib + gsi : bib, bon = more ? bob + gso : bob;
+            fwd_load<XT, V, K, U, RES>(x, r, bin, ai, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC, RES>(xb, rb, y, h, base_b, w.unit, sl, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES>(xb, rb, y, h, bob, ao, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
-            base_a = base_n;
+            bia = bin;
+            boa = bon;
         }
-        if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, base_a, w.unit, sl, gm, bt, alpha);
+        if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, boa, ao, gm, bt, alpha);
     }
     // units after the last whole group (fewer than U in total)
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
         typename R::T x1[1][K], r1[1][K];
-        const int64_t base_r = w.col_base + u * w.unit;
-        fwd_load<XT, V, K, 1, RES>(x, r, base_r, w.unit, sl, x1, r1);
-        fwd_tile<XT, V, K, 1, ACC, RES>(x1, r1, y, h, base_r, w.unit, sl, gm, bt, alpha);
+        fwd_load<XT, V, K, 1, RES>(x, r, w.col_base + u * ai.upitch, ai, x1, r1);
+        fwd_tile<XT, V, K, 1, ACC, RES>(x1, r1, y, h, w.col_base + u * ao.upitch, ao, gm, bt, alpha);
     }
 
     if (PACKED && w.tail) {
-        const int64_t tb = w.units * (int64_t)g.T;
-        const int len = (int)(g.total - tb);
+        const int64_t ti = w.units * ai.upitch;   // the partial tile, input side
+        const int64_t to = w.units * ao.upitch;   // and output side
+        const int len = (int)(g.total - w.units * (int64_t)g.T);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int o = (k * kBlock + tid) * V;
             const int n = len - o;
             if (n > 0) {
+                const int64_t oi = ti + tile_off<PACKED, STRIDED>(o, g, g.pitch[0]);
+                const int64_t oo = to + tile_off<PACKED, STRIDED>(o, g, g.pitch[1]);
                 float v[V];
                 if (n >= V) {
                     typename R::T rr{};
-                    if constexpr (RES) rr = R::load(r + tb + o);
-                    fwd_input<XT, V, RES>(R::load(x + tb + o), rr, h + tb + o, v);
+                    if constexpr (RES) rr = R::load(r + oi);
+                    fwd_input<XT, V, RES>(R::load(x + oi), rr, h + oo, v);
                 } else {
-                    load_partial<XT, V>(x + tb + o, n, v);
+                    load_partial<XT, V>(x + oi, n, v);
                     if constexpr (RES) {
                         float rv[V];
-                        load_partial<XT, V>(r + tb + o, n, rv);
+                        load_partial<XT, V>(r + oi, n, rv);
 #pragma unroll
                         for (int e = 0; e < V; ++e) v[e] = to_f32(from_f32<XT>(v[e] + rv[e]));
-                        store_partial<XT, V>(h + tb + o, n, v);
+                        store_partial<XT, V>(h + oo, n, v);
                     }
                 }
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-                if (n >= V) R::store(y + tb + o, v);
-                else store_partial<XT, V>(y + tb + o, n, v);
+                if (n >= V) R::store(y + oo, v);
+                else store_partial<XT, V>(y + oo, n, v);
             }
         }
     }
@@ -523,11 +575,12 @@ __device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)
 }
 
 // With RES the residual gradient dres is loaded beside x and dy and added
-// (in float32) to dx before the one rounding to the storage type.
-template <typename XT, int V, int K, int U, bool RES>
+// (in float32) to dx before the one rounding to the storage type. x (and
+// dres) are addressed by ax, dy by ad, dx by ao; unit bases bx, bd, bo.
+template <typename XT, int V, int K, int U, bool RES, typename AD>
 __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __restrict__ dy,
-                                         const XT* __restrict__ dres, int64_t base, int64_t step,
-                                         const Slots<V, K>& sl,
+                                         const XT* __restrict__ dres, int64_t bx, const AD& ax,
+                                         int64_t bd, const AD& ad,
                                          typename Raw<XT, V>::T (&rx)[U][K],
                                          typename Raw<XT, V>::T (&rd)[U][K],
                                          typename Raw<XT, V>::T (&rr)[U][K]) {
@@ -535,21 +588,20 @@ __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __r
     for (int j = 0; j < U; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            rx[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(x + base + j * step + sl.off[k]);
-            rd[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dy + base + j * step + sl.off[k]);
-            if constexpr (RES)
-                rr[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dres + base + j * step + sl.off[k]);
+            const int64_t atx = bx + j * ax.upitch + ax.off[k];
+            rx[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(x + atx);
+            rd[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dy + bd + j * ad.upitch + ad.off[k]);
+            if constexpr (RES) rr[j][k] = Raw<XT, V>::template load<DYT_BWD_NT>(dres + atx);
         }
 }
 
-template <typename XT, int V, int K, int U, bool ACC, bool RES>
+template <typename XT, int V, int K, int U, bool ACC, bool RES, typename AD>
 __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
                                          const typename Raw<XT, V>::T (&rd)[U][K],
                                          const typename Raw<XT, V>::T (&rr)[U][K],
-                                         XT* __restrict__ dx, int64_t base, int64_t step,
-                                         const Slots<V, K>& sl, const float (&gm)[K][V],
-                                         float alpha, float (&ag)[K][V], float (&ab)[K][V],
-                                         float (&aa)[K]) {
+                                         XT* __restrict__ dx, int64_t bo, const AD& ao,
+                                         const float (&gm)[K][V], float alpha,
+                                         float (&ag)[K][V], float (&ab)[K][V], float (&aa)[K]) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -564,17 +616,20 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 #pragma unroll
                 for (int e = 0; e < V; ++e) out[e] += rv[e];
             }
-            Raw<XT, V>::template store<DYT_BWD_NT>(dx + base + j * step + sl.off[k], out);
+            Raw<XT, V>::template store<DYT_BWD_NT>(dx + bo + j * ao.upitch + ao.off[k], out);
         }
 }
 
 // x is the layer input (h of the residual forward); dres and RES as above.
-template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES>
+// STRIDED: x, dy, dx have row pitches g.pitch[0], g.pitch[1], g.pitch[2]
+// (no RES). The tiling - and so every partial row - is the contiguous one.
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED>
 __global__ void __launch_bounds__(kBlock)
 dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                        const XT* __restrict__ dres, const PT* __restrict__ alpha_p,
                        const PT* __restrict__ gamma, XT* __restrict__ dx,
                        float* __restrict__ ws, const Geo g) {
+    static_assert(!(RES && STRIDED), "the residual layer takes contiguous tensors");
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -583,6 +638,9 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const float alpha = to_f32(alpha_p[0]);
     const TileWalk w = make_walk(g, PACKED, wg, G);
     const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
+    const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
+    const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;
+    const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[2]) : ax;
 
     float gm[K][V], ag[K][V], ab[K][V];
     float aa[K];     // dalpha partial per slot: unused slots are dropped at the end
@@ -603,52 +661,59 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     // forward.
     const int64_t ng = w.units / U;
     const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
-    const int64_t gstep = w.gcount * U * w.unit;
+    const int64_t ustep = w.gcount * U;
+    const int64_t cb = w.col_base;
+    const int64_t gsx = ustep * ax.upitch, gsd = ustep * ad.upitch, gso = ustep * ao.upitch;
     if (iters > 0) {
         typename R::T xa[U][K], da[U][K], ra[U][K], xb[U][K], db[U][K], rb[U][K];
-        int64_t base_a = w.col_base + w.gw * U * w.unit;
-        bwd_load<XT, V, K, U, RES>(x, dy, dres, base_a, w.unit, sl, xa, da, ra);
+        const int64_t u0 = w.gw * U;
+        int64_t bxa = cb + u0 * ax.upitch, bda = cb + u0 * ad.upitch, boa = cb + u0 * ao.upitch;
+        bwd_load<XT, V, K, U, RES>(x, dy, dres, bxa, ax, bda, ad, xa, da, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t base_b = base_a + gstep;
-            bwd_load<XT, V, K, U, RES>(x, dy, dres, base_b, w.unit, sl, xb, db, rb);
+            const int64_t bxb = bxa + gsx, bdb = bda + gsd, bob = boa + gso;
+            bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, boa, ao, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t base_n = (2 * pi + 2 < iters) ? base_b + gstep : base_b;
-            bwd_load<XT, V, K, U, RES>(x, dy, dres, base_n, w.unit, sl, xa, da, ra);
+            const bool more = 2 * pi + 2 < iters;
+            const int64_t bxn = more ? bxb + gsx : bxb, bdn = more ? bdb + gsd : bdb;
+            const int64_t bon = more ? bob + gso : bob;
+            bwd_load<XT, V, K, U, RES>(x, dy, dres, bxn, ax, bdn, ad, xa, da, ra);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES>(xb, db, rb, dx, base_b, w.unit, sl, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES>(xb, db, rb, dx, bob, ao, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
-            base_a = base_n;
+            bxa = bxn;
+            bda = bdn;
+            boa = bon;
         }
-        if (iters & 1)
-            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, base_a, w.unit, sl, gm, alpha, ag, ab, aa);
+        if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, boa, ao, gm, alpha, ag, ab, aa);
     }
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
         typename R::T x1[1][K], d1[1][K], r1[1][K];
-        const int64_t base_r = w.col_base + u * w.unit;
-        bwd_load<XT, V, K, 1, RES>(x, dy, dres, base_r, w.unit, sl, x1, d1, r1);
-        bwd_tile<XT, V, K, 1, ACC, RES>(x1, d1, r1, dx, base_r, w.unit, sl, gm, alpha, ag, ab, aa);
+        bwd_load<XT, V, K, 1, RES>(x, dy, dres, cb + u * ax.upitch, ax, cb + u * ad.upitch, ad, x1, d1, r1);
+        bwd_tile<XT, V, K, 1, ACC, RES>(x1, d1, r1, dx, cb + u * ao.upitch, ao, gm, alpha, ag, ab, aa);
     }
 
     if (PACKED && w.tail) {
-        const int64_t tb = w.units * (int64_t)g.T;
-        const int len = (int)(g.total - tb);
+        const int len = (int)(g.total - w.units * (int64_t)g.T);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int o = (k * kBlock + tid) * V;
             const int n = len - o;
             if (n > 0) {
+                const int64_t ox = w.units * ax.upitch + tile_off<PACKED, STRIDED>(o, g, g.pitch[0]);
+                const int64_t od = w.units * ad.upitch + tile_off<PACKED, STRIDED>(o, g, g.pitch[1]);
+                const int64_t oo = w.units * ao.upitch + tile_off<PACKED, STRIDED>(o, g, g.pitch[2]);
                 float xv[V], dv[V], rv[V], out[V];
                 if (n >= V) {
-                    R::unpack(R::load(x + tb + o), xv);
-                    R::unpack(R::load(dy + tb + o), dv);
-                    if constexpr (RES) R::unpack(R::load(dres + tb + o), rv);
+                    R::unpack(R::load(x + ox), xv);
+                    R::unpack(R::load(dy + od), dv);
+                    if constexpr (RES) R::unpack(R::load(dres + ox), rv);
                 } else {
-                    load_partial<XT, V>(x + tb + o, n, xv);
-                    load_partial<XT, V>(dy + tb + o, n, dv);
-                    if constexpr (RES) load_partial<XT, V>(dres + tb + o, n, rv);
+                    load_partial<XT, V>(x + ox, n, xv);
+                    load_partial<XT, V>(dy + od, n, dv);
+                    if constexpr (RES) load_partial<XT, V>(dres + ox, n, rv);
                 }
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
@@ -667,8 +732,8 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                     ab[k][e] += ok ? dv[e] : 0.0f;
                     aa[k] += ok ? ca : 0.0f;
                 }
-                if (n >= V) R::store(dx + tb + o, out);
-                else store_partial<XT, V>(dx + tb + o, n, out);
+                if (n >= V) R::store(dx + oo, out);
+                else store_partial<XT, V>(dx + oo, n, out);
             }
         }
     }

@@ -17,7 +17,22 @@ from . import _lib
 
 
 def _rows(t: torch.Tensor) -> torch.Tensor:
-    """[..., N] -> contiguous [M, N] (a view when t is already contiguous)."""
+    """[..., N] -> [M, N] with unit column stride and a row pitch >= N: a view
+    when the leading dimensions flatten into one row stride (contiguous
+    tensors, or rows sliced out of a wider buffer), else a contiguous copy."""
+    n = t.shape[-1]
+    if t.dim() >= 1 and (n <= 1 or t.stride(-1) == 1):
+        try:
+            v = t.view(-1, n)
+        except RuntimeError:
+            v = None
+        if v is not None and (v.size(0) <= 1 or v.stride(0) >= n) and (n <= 1 or v.stride(1) == 1):
+            return v
+    return t.contiguous().view(-1, n)
+
+
+def _dense_rows(t: torch.Tensor) -> torch.Tensor:
+    """[..., N] -> contiguous [M, N] (the residual-fused calls take dense rows)."""
     t = t.contiguous()
     return t.view(-1, t.shape[-1])
 
@@ -84,8 +99,8 @@ class DyTResidualFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
                 beta: torch.Tensor):
-        x2 = _rows(x)
-        r2 = _rows(r.to(x.dtype))
+        x2 = _dense_rows(x)
+        r2 = _dense_rows(r.to(x.dtype))
         h, y = _lib.dyt_forward_residual(x2, r2, alpha, gamma, beta)
         ctx.save_for_backward(h, alpha, gamma)
         ctx.set_materialize_grads(False)   # an unused output's gradient arrives as None
@@ -97,13 +112,13 @@ class DyTResidualFunction(torch.autograd.Function):
         h, alpha, gamma = ctx.saved_tensors
         shape = ctx.x_shape
         if grad_y is None:
-            dh = _rows(grad_h.to(h.dtype))
+            dh = _dense_rows(grad_h.to(h.dtype))
             return dh.view(shape), dh.view(shape), None, None, None
-        dy2 = _rows(grad_y.to(h.dtype))
+        dy2 = _dense_rows(grad_y.to(h.dtype))
         if grad_h is None:
             dh, dalpha, dgamma, dbeta = _lib.dyt_backward(h, dy2, alpha, gamma)
         else:
-            dres = _rows(grad_h.to(h.dtype))
+            dres = _dense_rows(grad_h.to(h.dtype))
             dh, dalpha, dgamma, dbeta = _lib.dyt_backward_residual(h, dy2, dres, alpha, gamma)
         return dh.view(shape), dh.view(shape), dalpha, dgamma, dbeta
 

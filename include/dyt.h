@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers (memory of the current HIP
- *     device). Layout is contiguous row-major; the row stride is N elements.
+ *     device). Layout is contiguous row-major; the row stride is N elements
+ *     (the *_strided entry points take explicit row strides).
  *     alpha, dalpha point to one element; gamma, beta, dgamma, dbeta to N.
  *   - x, dy, y, dx have the x dtype; alpha, gamma, beta, dalpha, dgamma,
  *     dbeta have the parameter dtype. Supported dtypes: DYT_F32, DYT_BF16
@@ -148,6 +149,34 @@ int dyt_backward_partials(const void* x, const void* dy, const void* alpha, cons
 int dyt_backward_finish(const void* workspace, size_t workspace_bytes,
                         void* dalpha, void* dgamma, void* dbeta,
                         int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
+
+/*
+ * Row-strided activations: the same forward and backward over tensors whose
+ * rows are `ld` elements apart (ld >= N), e.g. an M x N block of a wider
+ * buffer, so no copy is needed. Element (i, j) of x lives at x[i * ldx + j]
+ * (likewise y with ldy, dy with lddy, dx with lddx). The 16-byte vector
+ * kernels run when every base and every ld * sizeof(x) is a multiple of 16
+ * (and, for rows short enough to be packed, N is a multiple of
+ * 16 / sizeof(x)); otherwise the element-wise variant does. The tiling is
+ * that of the contiguous call, so with the same kernel variant every partial
+ * row and the gradients' summation order are too: the results equal those of
+ * dyt_forward / dyt_backward on contiguous copies bit for bit (y and dx do
+ * for either variant; the gradients' rounding can differ between the two
+ * variants, within the stated tolerance). ld = N is the contiguous case.
+ * Outputs must not overlap inputs anywhere between their first and last
+ * element. Other arguments and conventions as dyt_forward / dyt_backward
+ * (workspace size from dyt_backward_workspace_size(M, N, ...)); ld <= 0 or
+ * ld < N is DYT_ERR_INVALID_ARG.
+ */
+int dyt_forward_strided(const void* x, int64_t ldx, const void* alpha, const void* gamma,
+                        const void* beta, void* y, int64_t ldy, int64_t M, int64_t N,
+                        int x_dtype, int param_dtype, void* stream);
+
+int dyt_backward_strided(const void* x, int64_t ldx, const void* dy, int64_t lddy,
+                         const void* alpha, const void* gamma, void* dx, int64_t lddx,
+                         void* dalpha, void* dgamma, void* dbeta,
+                         void* workspace, size_t workspace_bytes,
+                         int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
 
 /*
  * Residual add fused with the layer (forward): the pre-norm block pattern

@@ -31,7 +31,7 @@ def test_header_declares_expected_entry_points():
         "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
         "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
-        "dyt_get_forward_plan"])
+        "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -257,6 +257,28 @@ def _bres(dyt, h=A16, dy=A16 + 0x100000, dres=A16 + 0x200000, a=A16 + 0x300000,
           db=A16 + 0x800000, ws=A16 + 0x900000, wsb=1 << 20, M=4, N=4, xdt=F32, pdt=F32):
     return dyt.lib.dyt_backward_residual(h, dy, dres, a, g, dh, da, dg, db, ws, wsb, M, N, xdt, pdt,
                                          None)
+
+
+def test_strided_error_codes(dyt):
+    L = dyt.lib
+    x, a, g, b, y = A16, A16 + 0x100000, A16 + 0x200000, A16 + 0x300000, A16 + 0x400000
+    # pitch below N or not positive
+    assert L.dyt_forward_strided(x, 3, a, g, b, y, 4, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_forward_strided(x, 4, a, g, b, y, 0, 4, 4, F32, F32, None) == E_ARG
+    # a strided x whose span reaches y: overlap (4 rows of pitch 0x10000 floats)
+    assert L.dyt_forward_strided(x, 0x10000, a, g, b, A16 + 0x80000, 4, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_forward_strided(x + 2, 8, a, g, b, y, 4, 4, 4, F32, F32, None) == E_AL
+    assert L.dyt_forward_strided(None, 8, a, g, b, y, 4, 4, 4, F32, F32, None) == E_ARG
+    assert L.dyt_forward_strided(None, 8, None, None, None, None, 4, 0, 4, F32, F32, None) == E_OK
+    need = dyt.dyt_backward_workspace_size(4, 4, F32, F32)
+    args = [A16, 8, A16 + 0x100000, 8, A16 + 0x200000, A16 + 0x300000, A16 + 0x400000, 8,
+            A16 + 0x500000, A16 + 0x600000, A16 + 0x700000, A16 + 0x800000, need, 4, 4, F32, F32, None]
+    bad = list(args); bad[3] = 2
+    assert L.dyt_backward_strided(*bad) == E_ARG                     # dy pitch < N
+    bad = list(args); bad[6] = A16 + 0x100010
+    assert L.dyt_backward_strided(*bad) == E_ARG                     # dx inside dy's span
+    bad = list(args); bad[12] = need - 1
+    assert L.dyt_backward_strided(*bad) == E_WS
 
 
 def test_residual_forward_error_codes(dyt):
