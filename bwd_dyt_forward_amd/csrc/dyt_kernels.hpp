@@ -493,17 +493,18 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     if (iters > 0) {
         typename R::T xa[U][K], xb[U][K], ra[U][K], rb[U][K];
         int64_t bia = w.col_base + w.gw * U * ai.upitch;   // input / output bases of group A
-        int64_t boa = w.col_base + w.gw * U * ao.upitch;
+        int64_t boa = STRIDED ? w.col_base + w.gw * U * ao.upitch : bia;
         fwd_load<XT, V, K, U, RES>(x, r, bia, ai, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t bib = bia + gsi, bob = boa + gso;
+            const int64_t bib = bia + gsi, bob = STRIDED ? boa + gso : bib;
             fwd_load<XT, V, K, U, RES>(x, r, bib, ai, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
             fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, boa, ao, gm, bt, alpha);
             __builtin_amdgcn_sched_barrier(0);
             const bool more = 2 * pi + 2 < iters;
-            const int64_t bin = more ? bib + gsi : bib, bon = more ? bob + gso : bob;
+            const int64_t bin = more ? bib + gsi : bib;
+            const int64_t bon = STRIDED ? (more ? bob + gso : bob) : bin;
             fwd_load<XT, V, K, U, RES>(x, r, bin, ai, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
             fwd_tile<XT, V, K, U, ACC, RES>(xb, rb, y, h, bob, ao, gm, bt, alpha);
@@ -667,18 +668,22 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     if (iters > 0) {
         typename R::T xa[U][K], da[U][K], ra[U][K], xb[U][K], db[U][K], rb[U][K];
         const int64_t u0 = w.gw * U;
-        int64_t bxa = cb + u0 * ax.upitch, bda = cb + u0 * ad.upitch, boa = cb + u0 * ao.upitch;
+        // without row pitches all three operands share one offset
+        int64_t bxa = cb + u0 * ax.upitch;
+        int64_t bda = STRIDED ? cb + u0 * ad.upitch : bxa, boa = STRIDED ? cb + u0 * ao.upitch : bxa;
         bwd_load<XT, V, K, U, RES>(x, dy, dres, bxa, ax, bda, ad, xa, da, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t bxb = bxa + gsx, bdb = bda + gsd, bob = boa + gso;
+            const int64_t bxb = bxa + gsx;
+            const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
             bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, boa, ao, gm, alpha, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             const bool more = 2 * pi + 2 < iters;
-            const int64_t bxn = more ? bxb + gsx : bxb, bdn = more ? bdb + gsd : bdb;
-            const int64_t bon = more ? bob + gso : bob;
+            const int64_t bxn = more ? bxb + gsx : bxb;
+            const int64_t bdn = STRIDED ? (more ? bdb + gsd : bdb) : bxn;
+            const int64_t bon = STRIDED ? (more ? bob + gso : bob) : bxn;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxn, ax, bdn, ad, xa, da, ra);
             __builtin_amdgcn_sched_barrier(0);
             bwd_tile<XT, V, K, U, ACC, RES>(xb, db, rb, dx, bob, ao, gm, alpha, ag, ab, aa);
