@@ -50,7 +50,8 @@ HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, vendor figure
 SETTLE_S = 0.3                         # minimum untimed warm-up wall time
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", f)
-                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp", "dyt_tune_table.inc")]
+                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp", "dyt_tune_table.inc",
+                            "dyt_launch.hpp", "dyt_launch_impl.hpp")]
 
 
 def log(*a):

@@ -329,19 +329,19 @@ def dyt_abi_version() -> int:
     return int(lib.dyt_abi_version())
 
 
-def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_aligned: bool = True) -> dict:
+def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_access: bool = True) -> dict:
     """The backward's plan (tiles, grid, workspace layout) and the forward's grid."""
     p = DytPlan()
     st = lib.dyt_get_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
-                          1 if vector_aligned else 0, ctypes.byref(p))
+                          1 if vector_access else 0, ctypes.byref(p))
     _check("dyt_get_plan", st)
     return {name: getattr(p, name) for name, _ in DytPlan._fields_}
 
 
-def dyt_get_forward_plan(M: int, N: int, x_dtype, param_dtype, vector_aligned: bool = True) -> dict:
+def dyt_get_forward_plan(M: int, N: int, x_dtype, param_dtype, vector_access: bool = True) -> dict:
     """The forward's plan (its tiles and grid; backward-only fields are 0)."""
     p = DytPlan()
     st = lib.dyt_get_forward_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
-                                  1 if vector_aligned else 0, ctypes.byref(p))
+                                  1 if vector_access else 0, ctypes.byref(p))
     _check("dyt_get_forward_plan", st)
     return {name: getattr(p, name) for name, _ in DytPlan._fields_}

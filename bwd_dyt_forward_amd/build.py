@@ -9,6 +9,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
@@ -16,10 +18,13 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libdyt.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "dyt_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "dyt_kernels.hpp"), os.path.join(CSRC, "dyt_math.hpp"),
-                     os.path.join(CSRC, "dyt_tune_table.inc"),
-                     os.path.join(INCLUDE, "dyt.h")]
+# Host logic and the kernel instances per x dtype and direction: separate
+# translation units, compiled in parallel.
+SOURCES = [os.path.join(CSRC, "dyt_api.hip")] + [
+    os.path.join(CSRC, f"dyt_launch_{d}_{t}.hip") for d in ("fwd", "bwd") for t in ("f32", "bf16", "f16")]
+DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in (
+    "dyt_kernels.hpp", "dyt_math.hpp", "dyt_launch.hpp", "dyt_launch_impl.hpp",
+    "dyt_tune_table.inc")] + [os.path.join(INCLUDE, "dyt.h")]
 # Reference streaming kernels for bench.py's measured ceilings (not part of
 # the DyT ABI; nothing in the package loads them).
 STREAM_REF_SOURCE = os.path.join(CSRC, "stream_ref.hip")
@@ -31,9 +36,11 @@ ARCH = "gfx950"
 # (x subnormal with alpha = inf gives +-gamma + beta, not NaN). Packed fp32
 # VALU ops are disabled for the device pass.
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# parallel compilations (at most 16: the share of a GPU machine's CPUs)
+JOBS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
 
 
 def hipcc() -> str:
@@ -54,10 +61,7 @@ def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bo
     return out
 
 
-def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbose: bool) -> None:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra_flags or []),
-           "-o", tmp, *sources]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,8 +70,20 @@ def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbos
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
-        print(msgs)
-    os.replace(tmp, out)
+        print(msgs, flush=True)
+
+
+def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbose: bool) -> None:
+    """Each source to an object (in parallel), then one shared library."""
+    flags = [*HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra_flags or [])]
+    with tempfile.TemporaryDirectory(prefix="dyt_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources]
+        with ThreadPoolExecutor(max_workers=min(JOBS, len(sources))) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *flags, "-c", "-o", so[1], so[0]], verbose),
+                        zip(sources, objs)))
+        tmp = out + ".tmp"
+        _run([hipcc(), *flags, "-shared", "-o", tmp, *objs], verbose)
+        os.replace(tmp, out)
 
 
 def is_stale(path: str = LIB_PATH) -> bool:

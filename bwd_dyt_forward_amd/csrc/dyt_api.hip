@@ -1,9 +1,10 @@
 // dyt_api.hip - C ABI of the fused DyT layer (declared in include/dyt.h):
 // argument validation, launch planning and kernel dispatch on gfx950.
 //
-// The plan is a pure function of (M, N, dtypes, 16-byte alignment class), so
-// the order of every floating-point sum, and with it every result bit, is
-// reproducible run to run and device to device.
+// The plan is a pure function of (M, N, dtypes), so the order of every
+// floating-point sum, and with it every result bit, is reproducible run to
+// run and device to device. The kernel instances are launched from
+// dyt_launch_{fwd,bwd}_<dtype>.hip (see dyt_launch.hpp).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -13,7 +14,7 @@
 #include <type_traits>
 
 #include "dyt.h"
-#include "dyt_kernels.hpp"
+#include "dyt_launch.hpp"
 
 // Default persistent-grid sizes (workgroups): one 256-thread workgroup per
 // compute unit of MI355X (256 CUs). Measured on the 32768 x 4096
@@ -28,18 +29,6 @@
 #ifndef DYT_BWD_GRID
 #define DYT_BWD_GRID 256
 #endif
-// Tiles per pipeline buffer (loads in flight per wave = U * K per input):
-// the forward has one input stream and needs two tiles in flight, the
-// backward's two input streams already keep enough bytes in flight.
-#ifndef DYT_FWD_U
-#define DYT_FWD_U 2
-#endif
-#ifndef DYT_BWD_U
-#define DYT_BWD_U 1
-#endif
-// The residual forward (two inputs, two outputs) uses the forward's U as
-// well: on 32768 x 4096 and 4194304 x 32 bf16 U = 2 measured 0.2-0.8%
-// faster than U = 1.
 // Tiles wanted before a packed plan stops shrinking K for more parallelism.
 #ifndef DYT_MIN_TILES
 #define DYT_MIN_TILES 1024
@@ -98,25 +87,13 @@ TuneDir tune_for(int xdt, int64_t M, int64_t N, Dir d) {
 }
 
 using dyt::Geo;
+using dyt::host::BwdPtrs;
+using dyt::host::FwdPtrs;
+using dyt::host::Plan;
 using dyt::FinGeo;
 using dyt::bf16_t;
 using dyt::kBlock;
 
-struct Plan {
-    bool packed = true;
-    int vec = 1;
-    int slots = 1;
-    int64_t R = 1;
-    int64_t T = 0;
-    int64_t nb = 1;
-    int64_t last_len = 0;
-    int64_t tiles = 0;
-    int64_t grid = 0;      // workgroups of this direction's kernel (pass 1 for the backward)
-    int64_t ld = 0;
-    int64_t wcols = 0;
-    int64_t fin_grid = 1;
-    int64_t ws_bytes = 0;
-};
 
 bool dtype_ok(int d) { return d == DYT_F32 || d == DYT_BF16 || d == DYT_F16; }
 int64_t dtype_size(int d) { return d == DYT_F32 ? 4 : 2; }
@@ -145,10 +122,12 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // row length limit (int32 in-tile offsets)
 
 // Pure host: validates sizes/dtypes and fills the plan. The plan depends
-// only on (M, N, x dtype): tensors whose bases are not 16-byte aligned run
-// the same tiles with the element-wise kernel variant (V = 1, K = 16, whose
-// 4096-element capacity holds any tile), so the partial-row layout - and
-// with it dyt_backward_finish - does not depend on pointer alignment.
+// only on (M, N, x dtype); pointer alignment and row pitches never change
+// it. The one launch that cannot use 16-byte vectors (row-strided packed
+// rows whose length is not a multiple of V) runs the same tiles with the
+// element-wise kernel variant (V = 1, K = 16, whose 4096-element capacity
+// holds any tile), so the partial-row layout - and with it
+// dyt_backward_finish - is the same for every launch of a shape.
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
     if (M < 0 || N < 0 || N > kMaxN) return DYT_ERR_INVALID_ARG;
@@ -162,8 +141,8 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         p.fin_grid = ceil_div(2 * N + 1, 64);
         return DYT_OK;
     }
-    // packed tiles: R >= 2 whole rows, R a multiple of r0 (the rows that keep
-    // each tile 16-byte aligned), within kTileCap elements
+    // packed tiles: R >= 2 whole rows, R a multiple of r0 (the rows that make
+    // R * N a multiple of V), within kTileCap elements
     const int64_t r0 = 16 / gcd64(N * sx, 16);
     const int64_t rcap = (dyt::kTileCap / N) / r0 * r0;
     if (rcap >= 2) {
@@ -188,11 +167,12 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         p.wcols = N;
         p.grid = std::min<int64_t>(p.tiles, tune.grid);
     } else {
+        // row segments: vectors from each row's start; with N not a multiple
+        // of V the kernels shift each row's last vector back (RAG)
         p.packed = false;
-        const bool v = (N * sx) % 16 == 0;     // rows start 16-byte aligned
-        p.vec = v ? vmax : 1;
-        const int kbig = v ? (tune.kcap > 0 ? std::min(kmax, tune.kcap) : kmax) : 16;
-        int k = v ? 1 : 16;
+        p.vec = vmax;
+        const int kbig = tune.kcap > 0 ? std::min(kmax, tune.kcap) : kmax;
+        int k = 1;
         while (k < kbig && (int64_t)kBlock * p.vec * k < N) k *= 2;
         p.slots = k;
         const int64_t cap = (int64_t)kBlock * p.vec * k;
@@ -211,11 +191,11 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     return DYT_OK;
 }
 
-// Kernel variant for the actual pointers: the plan's vector width when every
-// activation pointer is 16-byte aligned, else element-wise access.
-Plan variant_for(const Plan& p, bool vec_aligned) {
+// Kernel variant of a launch: the plan's vector width, or element-wise
+// access (see vector_ok).
+Plan variant_for(const Plan& p, bool vector) {
     Plan q = p;
-    if (!vec_aligned && q.vec != 1) {
+    if (!vector && q.vec != 1) {
         q.vec = 1;
         q.slots = 16;
     }
@@ -250,30 +230,6 @@ Range range(const void* p, int64_t bytes) {
 }
 
 // ------------------------------------------------------------- dispatch
-// Device pointers of one launch; r/h (forward) and dres (backward) are null
-// unless the residual add is fused.
-// Row pitches (elements; 0 = N, contiguous) of x and y (forward) or x, dy
-// and dx (backward) for the strided entry points.
-struct FwdPtrs {
-    const void* x;
-    const void* r;
-    const void* alpha;
-    const void* gamma;
-    const void* beta;
-    void* y;
-    void* h;
-    int64_t ldx, ldy;
-};
-struct BwdPtrs {
-    const void* x;
-    const void* dy;
-    const void* dres;
-    const void* alpha;
-    const void* gamma;
-    void* dx;
-    float* ws;
-    int64_t ldx, lddy, lddx;
-};
 
 int64_t pitch_or(int64_t ld, int64_t N) { return ld == 0 ? N : ld; }
 
@@ -290,79 +246,13 @@ bool pitches_ok(int64_t M, int64_t N, std::initializer_list<int64_t> lds) {
     return true;
 }
 
-// The vector kernels need every base 16-byte aligned; a strided launch also
-// needs every row start aligned (pitch * sx multiple of 16) and, for packed
-// tiles, slots that never straddle two rows (N a multiple of the vector width).
-bool vector_ok(const Plan& p, int64_t N, int64_t sx, bool strided,
-               std::initializer_list<const void*> ptrs, std::initializer_list<int64_t> lds) {
-    for (const void* q : ptrs)
-        if (q && (uintptr_t)q % 16 != 0) return false;
-    if (!strided) return true;
-    for (int64_t ld : lds)
-        if ((ld * sx) % 16 != 0) return false;
-    return !p.packed || N % (16 / sx) == 0;
+// The vector kernels take any element-aligned base and any row pitch; only a
+// row-strided launch of packed tiles needs N to be a multiple of the vector
+// width, so that no slot straddles the gap between two rows.
+bool vector_ok(const Plan& p, int64_t N, int64_t sx, bool strided) {
+    return !(strided && p.packed && N % (16 / sx) != 0);
 }
 
-template <typename XT, typename PT, int V, int K, bool RES, bool STRIDED>
-void launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
-    constexpr int U = DYT_FWD_U;
-    const dim3 grid((unsigned)p.grid), block(kBlock);
-    if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, true, RES, STRIDED>), grid, block, 0,
-                           s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
-                           (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
-    else
-        hipLaunchKernelGGL((dyt::dyt_fwd_kernel<XT, PT, V, K, U, false, RES, STRIDED>), grid, block, 0,
-                           s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
-                           (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, g);
-}
-
-template <typename XT, typename PT, int V, int K, bool RES, bool STRIDED>
-void launch_bwd_vk(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
-    const dim3 grid((unsigned)p.grid), block(kBlock);
-    if (p.packed)
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, true, RES, STRIDED>),
-                           grid, block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
-                           (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
-    else
-        hipLaunchKernelGGL((dyt::dyt_bwd_partial_kernel<XT, PT, V, K, DYT_BWD_U, false, RES, STRIDED>),
-                           grid, block, 0, s, (const XT*)a.x, (const XT*)a.dy, (const XT*)a.dres,
-                           (const PT*)a.alpha, (const PT*)a.gamma, (XT*)a.dx, a.ws, g);
-}
-
-// Kernel instances: vector access at K in {1, 2, ..., 4096 / (256 V)}, and
-// the element-wise variant (V = 1) at K = 16. dispatch_vk calls launch(V, K),
-// both as integral constants, for the instance the plan selects.
-template <typename XT, typename L>
-bool dispatch_vk(const Plan& p, L&& launch) {
-    constexpr int VV = 16 / sizeof(XT);
-    if (p.vec == 1 && p.slots == 16) return launch(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
-    if (p.vec != VV) return false;
-    switch (p.slots) {
-        case 1: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 1>{});
-        case 2: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 2>{});
-        case 4:
-            if constexpr (VV == 4) return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 4>{});
-            return false;
-        default: return false;
-    }
-}
-
-template <typename XT, typename PT, bool RES, bool STRIDED>
-bool launch_fwd(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
-    return dispatch_vk<XT>(p, [&](auto v, auto k) {
-        launch_fwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES, STRIDED>(p, g, a, s);
-        return true;
-    });
-}
-
-template <typename XT, typename PT, bool RES, bool STRIDED>
-bool launch_bwd(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s) {
-    return dispatch_vk<XT>(p, [&](auto v, auto k) {
-        launch_bwd_vk<XT, PT, decltype(v)::value, decltype(k)::value, RES, STRIDED>(p, g, a, s);
-        return true;
-    });
-}
 
 template <typename PT>
 void launch_finish(const Plan& p, int64_t N, const float* ws, void* dg, void* db, void* da,
@@ -438,20 +328,13 @@ int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int 
     const int64_t ldx = pitch_or(a.ldx, N), lddy = pitch_or(a.lddy, N), lddx = pitch_or(a.lddx, N);
     const bool strided = ldx != N || lddy != N || lddx != N;
     const int64_t sx = dtype_size(x_dtype);
-    const Plan p = variant_for(base, vector_ok(base, N, sx, strided, {a.x, a.dy, a.dx, a.dres},
-                                               {ldx, lddy, lddx}));
+    const Plan p = variant_for(base, vector_ok(base, N, sx, strided));
     Geo g = make_geo(p, M, N);
     g.pitch[0] = ldx;
     g.pitch[1] = lddy;
     g.pitch[2] = lddx;
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
-        return with_dtype(param_dtype, [&](auto pt) {
-            using XT = decltype(xt);
-            using PT = decltype(pt);
-            if (res) return launch_bwd<XT, PT, true, false>(p, g, a, s);
-            return strided ? launch_bwd<XT, PT, false, true>(p, g, a, s)
-                           : launch_bwd<XT, PT, false, false>(p, g, a, s);
-        });
+        return dyt::host::launch_backward<decltype(xt)>(param_dtype, res, strided, p, g, a, s);
     });
     if (!ok) return DYT_ERR_INVALID_ARG;
     return hip_status();
@@ -496,18 +379,12 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
-    const Plan p = variant_for(base, vector_ok(base, N, sx, strided, {a.x, a.y, a.r, a.h}, {ldx, ldy}));
+    const Plan p = variant_for(base, vector_ok(base, N, sx, strided));
     Geo g = make_geo(p, M, N);
     g.pitch[0] = ldx;
     g.pitch[1] = ldy;
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
-        return with_dtype(param_dtype, [&](auto pt) {
-            using XT = decltype(xt);
-            using PT = decltype(pt);
-            if (res) return launch_fwd<XT, PT, true, false>(p, g, a, s);
-            return strided ? launch_fwd<XT, PT, false, true>(p, g, a, s)
-                           : launch_fwd<XT, PT, false, false>(p, g, a, s);
-        });
+        return dyt::host::launch_forward<decltype(xt)>(param_dtype, res, strided, p, g, a, s);
     });
     if (!ok) return DYT_ERR_INVALID_ARG;   // no kernel instance for this plan (not reachable)
     return hip_status();
@@ -556,7 +433,7 @@ const char* dyt_status_string(int status) {
     }
 }
 
-int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
+int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,
                  dyt_plan* out) {
     if (!out) return DYT_ERR_INVALID_ARG;
     Plan base, fbase;
@@ -564,7 +441,7 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
     if (st != DYT_OK) return st;
     st = make_plan(M, N, x_dtype, param_dtype, Dir::Fwd, fbase);
     if (st != DYT_OK) return st;
-    const Plan p = variant_for(base, vector_aligned != 0);
+    const Plan p = variant_for(base, vector_access != 0);
     fill_plan(p, out);
     out->fwd_grid = fbase.grid;
     out->bwd_grid = p.grid;
@@ -574,13 +451,13 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
     return DYT_OK;
 }
 
-int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
+int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,
                          dyt_plan* out) {
     if (!out) return DYT_ERR_INVALID_ARG;
     Plan base;
     const int st = make_plan(M, N, x_dtype, param_dtype, Dir::Fwd, base);
     if (st != DYT_OK) return st;
-    const Plan p = variant_for(base, vector_aligned != 0);
+    const Plan p = variant_for(base, vector_access != 0);
     fill_plan(p, out);
     out->fwd_grid = p.grid;
     out->bwd_grid = 0;

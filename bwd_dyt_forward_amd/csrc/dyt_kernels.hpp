@@ -8,14 +8,23 @@
 //
 //  * packed tiles (several whole rows; used whenever two or more rows fit a
 //    4096-element tile): tile t is the contiguous run of R rows starting at
-//    row t*R, i.e. elements [t*R*N, (t+1)*R*N). R*N*sizeof(x) is a multiple
-//    of 16, so every tile starts 16-byte aligned and the element at tile
-//    offset o always sits in column o mod N. Each thread therefore owns the
-//    same columns in every tile: its gamma/beta values live in registers for
-//    the whole kernel and its backward accumulators are per (slot, lane).
+//    row t*R, i.e. elements [t*R*N, (t+1)*R*N). R*N is a multiple of V, so
+//    the element at tile offset o always sits in column o mod N and a
+//    vector never needs columns from two rows' worth of parameters in a
+//    different order. Each thread therefore owns the same columns in every
+//    tile: its gamma/beta values live in registers for the whole kernel and
+//    its backward accumulators are per (slot, lane).
 //  * row segments (wide rows): tile t is row t / nb, column block t % nb of
-//    width Wc. The grid size is a multiple of nb, so a workgroup always sees
-//    the same column block.
+//    width Wc (a multiple of V). The grid size is a multiple of nb, so a
+//    workgroup always sees the same column block. When N is not a multiple
+//    of V, the last vector of every row is shifted back to end at the row's
+//    end (see Slots).
+//
+// Memory accesses assume only element alignment: gfx9 and later GPUs run
+// global memory instructions in unaligned mode under ROCm (the compiler
+// assumes it for HSA code objects and emits the same 16-byte instructions),
+// so tensors at any element-aligned address, and rows of any length or
+// pitch, take the 16-byte vector path.
 //
 // The grid is one-dimensional and persistent (one workgroup per CU): groups
 // of U adjacent tiles are dealt round-robin to the workgroups, and each
@@ -95,6 +104,9 @@ struct FinGeo {
 // MI355X this lifts a plain 16-byte copy from ~5.7 to ~6.4 TB/s.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// The same vectors as seen in memory: only element alignment is assumed.
+typedef uint32_t u32x4_m __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4_m __attribute__((ext_vector_type(4), aligned(4)));
 
 #ifndef DYT_FWD_NT
 #define DYT_FWD_NT 1
@@ -112,6 +124,29 @@ __device__ __forceinline__ void stream_store(T v, T* p) {
     if constexpr (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
+// 16-byte vectors at element-aligned addresses. Not deduced from the pointer
+// type: template deduction would drop the reduced alignment of the typedef
+// and the access would be declared 16-byte aligned.
+template <bool NT>
+__device__ __forceinline__ u32x4 stream_load_v(const u32x4_m* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ f32x4 stream_load_v(const f32x4_m* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void stream_store_v(u32x4 v, u32x4_m* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void stream_store_v(f32x4 v, f32x4_m* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 template <typename XT, int V> struct Raw;
 // Each Raw<XT, V> has: load (raw registers), unpack (to float32), pack (float32
@@ -122,7 +157,7 @@ template <> struct Raw<float, 4> {
     using T = f32x4;
     template <bool NT = true>
     static __device__ __forceinline__ T load(const float* p) {
-        return stream_load<NT>(reinterpret_cast<const f32x4*>(p));
+        return stream_load_v<NT>(reinterpret_cast<const f32x4_m*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[4]) {
         v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
@@ -133,7 +168,7 @@ template <> struct Raw<float, 4> {
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store_raw(float* p, const T& t) {
-        stream_store<NT>(t, reinterpret_cast<f32x4*>(p));
+        stream_store_v<NT>(t, reinterpret_cast<f32x4_m*>(p));
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
@@ -145,7 +180,7 @@ template <> struct Raw<bf16_t, 8> {
     using T = u32x4;
     template <bool NT = true>
     static __device__ __forceinline__ T load(const bf16_t* p) {
-        return stream_load<NT>(reinterpret_cast<const u32x4*>(p));
+        return stream_load_v<NT>(reinterpret_cast<const u32x4_m*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[8]) {
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -162,7 +197,7 @@ template <> struct Raw<bf16_t, 8> {
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store_raw(bf16_t* p, const T& t) {
-        stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
+        stream_store_v<NT>(t, reinterpret_cast<u32x4_m*>(p));
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
@@ -174,7 +209,7 @@ template <> struct Raw<f16_t, 8> {
     using T = u32x4;
     template <bool NT = true>
     static __device__ __forceinline__ T load(const f16_t* p) {
-        return stream_load<NT>(reinterpret_cast<const u32x4*>(p));
+        return stream_load_v<NT>(reinterpret_cast<const u32x4_m*>(p));
     }
     static __device__ __forceinline__ void unpack(const T& r, float (&v)[8]) {
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -191,7 +226,7 @@ template <> struct Raw<f16_t, 8> {
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store_raw(f16_t* p, const T& t) {
-        stream_store<NT>(t, reinterpret_cast<u32x4*>(p));
+        stream_store_v<NT>(t, reinterpret_cast<u32x4_m*>(p));
     }
     template <bool NT = true>
     static __device__ __forceinline__ void store(f16_t* p, const float (&v)[8]) {
@@ -269,27 +304,50 @@ __device__ __forceinline__ void store_partial(XT* p, int n, const float (&v)[V])
 // ------------------------------------------------------------ tile geometry
 // Per-thread constants of the persistent loop. Slot k of thread tid covers
 // tile offsets o = (k * kBlock + tid) * V + [0, V). A slot is "used" if its
-// vector lies inside the workgroup's tiles (packed: o < T; row segments:
-// o < this block's length). An unused slot is pointed at tile offset 0 and
-// given the parameters of columns 0..V-1 of the tile, so it recomputes the
-// first vector and rewrites exactly the bytes its owner writes there. Loads
+// vector starts inside the workgroup's tiles (packed: o < T; row segments:
+// o < this block's length). An unused slot is pointed at the tile's first
+// whole vector (offset 0, or the shifted one below when a row segment is
+// shorter than V) and given that vector's parameters, so it recomputes it
+// and rewrites exactly the bytes its owner writes there. A
+// used slot that would run past the end of a row segment (N not a multiple
+// of V) is shifted back to end there: its first `lo` elements belong to the
+// slot before it (or, in a segment shorter than V, to the previous column
+// block), are recomputed from the same data and parameters, and so rewrite
+// the same bytes; the backward leaves them out of its sums. Loads
 // and stores therefore carry no branches, and the compiler can keep the
 // next tile's loads in flight across this tile's stores (a conditional
 // store makes it wait for every outstanding access at the loop back-edge).
 template <int V, int K>
 struct Slots {
     int off[K];     // element offset of the slot inside the tile (0 if unused)
+    int lo[K];      // elements of the slot before this one's own (shifted slot), else 0
     bool used[K];
 };
 
-template <int V, int K>
+// SHIFT: row segments whose length may not be a multiple of V.
+template <int V, int K, bool SHIFT>
 __device__ __forceinline__ Slots<V, K> make_slots(int tid, int seg_len) {
     Slots<V, K> s;
+    // 1 <= seg_len <= kTileCap; the clamp only tells the compiler the range
+    // of the offsets. A segment shorter than V (the last of several column
+    // blocks) has its one vector reach back into the previous block of the
+    // same row: columns another workgroup owns and writes identically.
+    const int last = min(max(seg_len - V, 1 - V), kTileCap - V);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int o = (k * kBlock + tid) * V;
         s.used[k] = o < seg_len;
-        s.off[k] = s.used[k] ? o : 0;
+        if constexpr (!SHIFT) {       // segment length a multiple of V
+            s.off[k] = s.used[k] ? o : 0;
+            s.lo[k] = 0;
+        } else {
+            // unused slots recompute the segment's first whole vector: the
+            // one at offset 0, or the shifted one if the segment is shorter
+            // than V (offset 0 would then run past the row's end)
+            const bool full = o + V <= seg_len;
+            s.off[k] = !s.used[k] ? min(last, 0) : full ? o : last;
+            s.lo[k] = s.used[k] && !full ? o - last : 0;
+        }
     }
     return s;
 }
@@ -450,14 +508,17 @@ __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 // h = x + r and y = gamma * tanh(alpha * h) + beta. Loads of the next tile
 // are issued before the current tile is computed (register double
 // buffering). r and h are unused (null) without RES. STRIDED: x and y have
-// row pitches g.pitch[0] and g.pitch[1] (no RES).
-template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED>
+// row pitches g.pitch[0] and g.pitch[1] (no RES). RAG: row segments whose
+// length N is not a multiple of V (shifted slots).
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED,
+          bool RAG>
 __global__ void __launch_bounds__(kBlock)
 dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
                const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
                const PT* __restrict__ beta, XT* __restrict__ y, XT* __restrict__ h,
                const Geo g) {
     static_assert(!(RES && STRIDED), "the residual layer takes contiguous tensors");
+    static_assert(!(RAG && PACKED), "packed tiles hold whole vectors");
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -465,7 +526,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
     const TileWalk w = make_walk(g, PACKED, wg, G);
-    const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
+    const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
 
@@ -559,10 +620,14 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 
 // ---------------------------------------------------------------- backward
 // Pass 1: dx, plus one float32 partial row per workgroup.
-template <typename XT, int V, int K, bool ACC>
+// RAG (row segments with N not a multiple of V): elements e < lo of a
+// shifted slot are another slot's; they stay out of dalpha here and out of
+// the partial row at the end (dgamma/dbeta: not written).
+template <typename XT, int V, int K, bool ACC, bool RAG>
 __device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)[V],
-                                         const float (&gm)[V], float alpha, float (&out)[V],
-                                         float (&ag)[V], float (&ab)[V], float& aa) {
+                                         const float (&gm)[V], float alpha, int lo,
+                                         float (&out)[V], float (&ag)[V], float (&ab)[V],
+                                         float& aa) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         float th, sd;
@@ -571,7 +636,8 @@ __device__ __forceinline__ void bwd_slot(const float (&xv)[V], const float (&dv)
         out[e] = gd * alpha;
         ag[e] = __builtin_fmaf(dv[e], th, ag[e]);
         ab[e] += dv[e];
-        aa = __builtin_fmaf(gd, xv[e], aa);
+        if constexpr (RAG) aa = __builtin_fmaf(e >= lo ? gd : 0.0f, xv[e], aa);
+        else aa = __builtin_fmaf(gd, xv[e], aa);
     }
 }
 
@@ -596,12 +662,12 @@ __device__ __forceinline__ void bwd_load(const XT* __restrict__ x, const XT* __r
         }
 }
 
-template <typename XT, int V, int K, int U, bool ACC, bool RES, typename AD>
+template <typename XT, int V, int K, int U, bool ACC, bool RES, bool RAG, typename AD>
 __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
                                          const typename Raw<XT, V>::T (&rd)[U][K],
                                          const typename Raw<XT, V>::T (&rr)[U][K],
                                          XT* __restrict__ dx, int64_t bo, const AD& ao,
-                                         const float (&gm)[K][V], float alpha,
+                                         const float (&gm)[K][V], float alpha, const int (&lo)[K],
                                          float (&ag)[K][V], float (&ab)[K][V], float (&aa)[K]) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
@@ -610,7 +676,7 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
             float xv[V], dv[V], out[V];
             Raw<XT, V>::unpack(rx[j][k], xv);
             Raw<XT, V>::unpack(rd[j][k], dv);
-            bwd_slot<XT, V, K, ACC>(xv, dv, gm[k], alpha, out, ag[k], ab[k], aa[k]);
+            bwd_slot<XT, V, K, ACC, RAG>(xv, dv, gm[k], alpha, lo[k], out, ag[k], ab[k], aa[k]);
             if constexpr (RES) {
                 float rv[V];
                 Raw<XT, V>::unpack(rr[j][k], rv);
@@ -624,13 +690,16 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 // x is the layer input (h of the residual forward); dres and RES as above.
 // STRIDED: x, dy, dx have row pitches g.pitch[0], g.pitch[1], g.pitch[2]
 // (no RES). The tiling - and so every partial row - is the contiguous one.
-template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED>
+// RAG: row segments whose length N is not a multiple of V (shifted slots).
+template <typename XT, typename PT, int V, int K, int U, bool PACKED, bool RES, bool STRIDED,
+          bool RAG>
 __global__ void __launch_bounds__(kBlock)
 dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                        const XT* __restrict__ dres, const PT* __restrict__ alpha_p,
                        const PT* __restrict__ gamma, XT* __restrict__ dx,
                        float* __restrict__ ws, const Geo g) {
     static_assert(!(RES && STRIDED), "the residual layer takes contiguous tensors");
+    static_assert(!(RAG && PACKED), "packed tiles hold whole vectors");
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     const int tid = threadIdx.x;
@@ -638,7 +707,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
     const TileWalk w = make_walk(g, PACKED, wg, G);
-    const Slots<V, K> sl = make_slots<V, K>(tid, w.seg_len);
+    const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[2]) : ax;
@@ -678,7 +747,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, boa, ao, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             const bool more = 2 * pi + 2 < iters;
             const int64_t bxn = more ? bxb + gsx : bxb;
@@ -686,18 +755,19 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int64_t bon = STRIDED ? (more ? bob + gso : bob) : bxn;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxn, ax, bdn, ad, xa, da, ra);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES>(xb, db, rb, dx, bob, ao, gm, alpha, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa);
             __builtin_amdgcn_sched_barrier(0);
             bxa = bxn;
             bda = bdn;
             boa = bon;
         }
-        if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES>(xa, da, ra, dx, boa, ao, gm, alpha, ag, ab, aa);
+        if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
     }
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
         typename R::T x1[1][K], d1[1][K], r1[1][K];
         bwd_load<XT, V, K, 1, RES>(x, dy, dres, cb + u * ax.upitch, ax, cb + u * ad.upitch, ad, x1, d1, r1);
-        bwd_tile<XT, V, K, 1, ACC, RES>(x1, d1, r1, dx, cb + u * ao.upitch, ao, gm, alpha, ag, ab, aa);
+        bwd_tile<XT, V, K, 1, ACC, RES, RAG>(x1, d1, r1, dx, cb + u * ao.upitch, ao, gm, alpha, sl.lo, ag,
+                                             ab, aa);
     }
 
     if (PACKED && w.tail) {
@@ -859,12 +929,24 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
                     continue;
                 }
             }
+            if constexpr (RAG) {
+                // the slot's registers hold columns off + e; a shifted slot
+                // writes only its own ones (e >= lo)
+                if (!sl.used[k]) continue;
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                if (o + e < w.seg_len) {
-                    wrow[o + e] = ag[k][e];
-                    wrow[g.wcols + o + e] = ab[k][e];
-                }
+                for (int e = 0; e < V; ++e)
+                    if (e >= sl.lo[k]) {
+                        wrow[sl.off[k] + e] = ag[k][e];
+                        wrow[g.wcols + sl.off[k] + e] = ab[k][e];
+                    }
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    if (o + e < w.seg_len) {
+                        wrow[o + e] = ag[k][e];
+                        wrow[g.wcols + o + e] = ab[k][e];
+                    }
+            }
         }
     }
     __syncthreads();

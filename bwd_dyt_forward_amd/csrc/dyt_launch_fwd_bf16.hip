@@ -1,0 +1,8 @@
+// dyt_launch_fwd_bf16.hip - the forward kernel instances for bf16_t activations.
+#include "dyt_launch_impl.hpp"
+
+namespace dyt {
+namespace host {
+template bool launch_forward<bf16_t>(int, bool, bool, const Plan&, const Geo&, const FwdPtrs&, hipStream_t);
+}  // namespace host
+}  // namespace dyt

@@ -40,18 +40,19 @@
  *     memory and keeps no state beyond immutable tables.
  *   - Outputs overwrite their buffers (they are not accumulated into) and
  *     must not overlap any input.
- *   - Alignment: every pointer must be aligned to its element size. Tensors
- *     whose x/dy/y/dx pointers are 16-byte aligned use 16-byte vector
- *     memory access; otherwise an element-wise variant with identical
- *     results runs. The workspace must be 16-byte aligned.
+ *   - Alignment: every pointer must be aligned to its element size; the
+ *     workspace must be 16-byte aligned. Activations at any element-aligned
+ *     address, and rows of any length, use 16-byte vector memory access
+ *     (gfx9 and later GPUs run global memory instructions in unaligned mode
+ *     under ROCm), so alignment never changes the results.
  *   - Errors: every call returns DYT_OK (0) or a positive dyt_status.
  *     Arguments are validated before anything is enqueued, so on error no
  *     output is written. The library never prints and never throws.
  *     Faults during kernel execution surface at stream synchronisation.
  *   - Determinism: results are bitwise reproducible run to run. The
  *     parameter-gradient sums use a fixed summation order that depends only
- *     on (M, N, x dtype) and on whether x/dy/dx are 16-byte aligned; no
- *     floating-point atomics.
+ *     on (M, N, x dtype) (and, for the row-strided entry points, on whether
+ *     they take the element-wise variant); no floating-point atomics.
  *   - Arithmetic is float32 throughout (accumulation included); bfloat16
  *     and float16 results are rounded to nearest even (values beyond the
  *     float16 range become +-inf). float32 subnormals are kept.
@@ -66,7 +67,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 2
+#define DYT_ABI_VERSION 3
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -154,15 +155,15 @@ int dyt_backward_finish(const void* workspace, size_t workspace_bytes,
  * Row-strided activations: the same forward and backward over tensors whose
  * rows are `ld` elements apart (ld >= N), e.g. an M x N block of a wider
  * buffer, so no copy is needed. Element (i, j) of x lives at x[i * ldx + j]
- * (likewise y with ldy, dy with lddy, dx with lddx). The 16-byte vector
- * kernels run when every base and every ld * sizeof(x) is a multiple of 16
- * (and, for rows short enough to be packed, N is a multiple of
- * 16 / sizeof(x)); otherwise the element-wise variant does. The tiling is
- * that of the contiguous call, so with the same kernel variant every partial
- * row and the gradients' summation order are too: the results equal those of
- * dyt_forward / dyt_backward on contiguous copies bit for bit (y and dx do
- * for either variant; the gradients' rounding can differ between the two
- * variants, within the stated tolerance). ld = N is the contiguous case.
+ * (likewise y with ldy, dy with lddy, dx with lddx). Any pitch takes the
+ * 16-byte vector kernels, except rows short enough to be packed several to
+ * a tile (N <= 2048) whose length N is not a multiple of 16 / sizeof(x):
+ * those run the element-wise variant. The tiling is that of the contiguous
+ * call, so with the vector kernels every partial row and the gradients'
+ * summation order are too: the results equal those of dyt_forward /
+ * dyt_backward on contiguous copies bit for bit. With the element-wise
+ * variant y and dx still do; the gradients' rounding can differ, within the
+ * stated tolerance. ld = N is the contiguous case.
  * Outputs must not overlap inputs anywhere between their first and last
  * element. Other arguments and conventions as dyt_forward / dyt_backward
  * (workspace size from dyt_backward_workspace_size(M, N, ...)); ld <= 0 or
@@ -247,10 +248,12 @@ int dyt_abi_version(void);
  * grid and workspace layout; fwd_grid is the forward's grid), which depends
  * only on (M, N, x_dtype). Both directions take their tile size and grid
  * from a static table measured offline per (x dtype, row-length range), so
- * every plan is a pure function of the shape. vector_aligned selects which
- * kernel variant is described (non-zero: 16-byte aligned x/dy/y/dx, vector
- * access; zero: element-wise access, vec = 1). Returns DYT_OK or the status
- * the compute calls would return for these sizes and dtypes.
+ * every plan is a pure function of the shape. vector_access selects which
+ * kernel variant is described (non-zero: 16-byte vector access, which every
+ * launch uses except the row-strided packed case named at
+ * dyt_forward_strided; zero: that element-wise variant, vec = 1, same tiles
+ * and workspace). Returns DYT_OK or the status the compute calls would
+ * return for these sizes and dtypes.
  */
 typedef struct dyt_plan {
     int32_t packed;        /* 1: tiles of >= 2 whole rows (N <= 2048); 0: row segments */
@@ -268,7 +271,7 @@ typedef struct dyt_plan {
     int64_t ws_bytes;      /* workspace bytes this plan uses */
 } dyt_plan;
 
-int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_aligned,
+int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,
                  dyt_plan* out);
 
 /*
@@ -278,7 +281,7 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
  * backward-only fields (bwd_grid, ws_row, fin_grid, ws_bytes) are 0.
  */
 int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype,
-                         int vector_aligned, dyt_plan* out);
+                         int vector_access, dyt_plan* out);
 
 #ifdef __cplusplus
 }

@@ -54,7 +54,7 @@ def test_no_cpu_fallback_in_product_path():
 
 
 def test_version_and_status_strings(dyt):
-    assert dyt.dyt_abi_version() == 2
+    assert dyt.dyt_abi_version() == 3
     names = [dyt.dyt_status_string(i) for i in range(6)]
     assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
                      "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]
@@ -68,6 +68,10 @@ CONFIG_SHAPES = [
 ]
 
 
+RAGGED_SHAPES = [(5, 4095, "bf16"), (3, 10001, "bf16"), (2, 2051, "f32"), (9, 3001, "f16"),
+                 (40, 4097, "f32"), (9, 20003, "bf16")]
+
+
 @pytest.mark.parametrize("M,N,xdt", CONFIG_SHAPES)
 @pytest.mark.parametrize("vec", [True, False])
 def test_plan_invariants(dyt, M, N, xdt, vec):
@@ -75,8 +79,8 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
     sx = 4 if xdt == "f32" else 2       # bf16 and f16 are both 2 bytes
     cap = p["block"] * p["vec"] * p["slots"]
     assert p["block"] == 256
-    assert p["vec"] == (16 // sx if vec and (p["packed"] or (N * sx) % 16 == 0) else 1)
-    # tiling and workspace layout do not depend on the alignment class
+    assert p["vec"] == (16 // sx if vec else 1)
+    # tiling and workspace layout do not depend on the kernel variant
     q = dyt.dyt_get_plan(M, N, xdt, "f32", not vec)
     for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "fwd_grid",
                 "bwd_grid", "ws_row", "ws_bytes"):
@@ -86,8 +90,8 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
         R = p["rows_per_tile"]
         assert p["tile_elems"] == R * N and p["col_blocks"] == 1
         assert p["tiles"] == -(-M // R)
-        if p["vec"] > 1:
-            assert (R * N * sx) % 16 == 0, "packed tiles must stay 16-byte aligned"
+        # every tile starts at the same column phase of a 16-byte vector
+        assert (R * N * sx) % 16 == 0
     else:
         assert p["rows_per_tile"] == 1
         assert p["col_blocks"] * p["tile_elems"] >= N > (p["col_blocks"] - 1) * p["tile_elems"]
@@ -112,7 +116,8 @@ def test_plan_uses_1d_grid_beyond_65535_rows(dyt):
     assert p["tiles"] == 10 ** 7 and p["bwd_grid"] <= 4096
 
 
-@pytest.mark.parametrize("M,N,xdt", CONFIG_SHAPES + [(7, 5000, "f32"), (3, 20000, "bf16"), (1, 1, "f16")])
+@pytest.mark.parametrize("M,N,xdt", CONFIG_SHAPES + RAGGED_SHAPES + [(7, 5000, "f32"), (3, 20000, "bf16"),
+                                                     (1, 1, "f16")])
 @pytest.mark.parametrize("vec", [True, False])
 def test_forward_plan_invariants(dyt, M, N, xdt, vec):
     """The forward tiles independently of the backward, with the same rules."""
@@ -125,12 +130,36 @@ def test_forward_plan_invariants(dyt, M, N, xdt, vec):
     if p["packed"]:
         R = p["rows_per_tile"]
         assert p["tile_elems"] == R * N and p["tiles"] == -(-M // R)
-        if p["vec"] > 1:
-            assert (R * N * sx) % 16 == 0
+        assert (R * N * sx) % 16 == 0
     else:
         assert p["col_blocks"] * p["tile_elems"] >= N > (p["col_blocks"] - 1) * p["tile_elems"]
         assert p["tiles"] == M * p["col_blocks"] and p["fwd_grid"] % p["col_blocks"] == 0
     assert 1 <= p["fwd_grid"] <= p["tiles"]
+
+
+@pytest.mark.parametrize("M,N,xdt", RAGGED_SHAPES)
+def test_ragged_rows_take_the_vector_kernels(dyt, M, N, xdt):
+    """Rows whose length is not a multiple of the vector width are cut into
+    whole-vector column blocks (the kernels shift each row's last vector)."""
+    v = 4 if xdt == "f32" else 8
+    for p in (dyt.dyt_get_plan(M, N, xdt, "f32"), dyt.dyt_get_forward_plan(M, N, xdt, "f32")):
+        assert not p["packed"] and p["vec"] == v and N % v != 0
+        assert p["tile_elems"] % v == 0 and p["tile_elems"] <= p["block"] * v * p["slots"]
+        last = N - (p["col_blocks"] - 1) * p["tile_elems"]
+        assert 1 <= last <= p["tile_elems"]
+
+
+@pytest.mark.parametrize("M,N,xdt", [(3, 261121, "f32"), (3, 522241, "bf16"), (2, 522242, "f16")])
+def test_short_last_block_shapes(dyt, M, N, xdt):
+    """The GPU tests' shapes whose last column block is shorter than one
+    vector in the backward or forward plan (the shifted vector then reaches
+    into the previous block)."""
+    v = 4 if xdt == "f32" else 8
+    lasts = []
+    for p in (dyt.dyt_get_plan(M, N, xdt, "f32"), dyt.dyt_get_forward_plan(M, N, xdt, "f32")):
+        assert not p["packed"]
+        lasts.append(N - (p["col_blocks"] - 1) * p["tile_elems"])
+    assert min(lasts) >= 1 and any(last < v for last in lasts)
 
 
 def test_tile_table_covers_every_dtype_width_and_size():

@@ -60,7 +60,7 @@ def test_parity_full_size_sampled(dyt, name):
 
 
 SWEEP = [
-    # (M, N, x dtype, param dtype, alpha): packed, wide, multi-block, element-wise paths
+    # (M, N, x dtype, param dtype, alpha): packed, wide, multi-block and ragged-row paths
     (257, 1, "f32", "f32", 0.7), (513, 3, "bf16", "f32", 1.1), (97, 250, "bf16", "f32", 0.5),
     (41, 300, "bf16", "f32", 0.5), (33, 1000, "f32", "f32", 0.9), (9, 2049, "bf16", "f32", 0.5),
     (7, 4100, "bf16", "f32", 0.5), (5, 8192, "bf16", "f32", 0.5), (3, 20000, "f32", "f32", 0.3),

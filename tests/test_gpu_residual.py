@@ -4,8 +4,8 @@ and its backward dh = dres + dx with the layer's parameter gradients.
 Parity: h bit for bit against the oracle's rounded sum; y, dh and the
 gradients within the oracle tolerances (oracle/compare.py). Properties
 (bitwise): a zero branch reproduces the plain forward, a zero residual
-gradient the plain backward, the split backward the single call, and the
-element-wise variant (unaligned bases) the vector path."""
+gradient the plain backward, the split backward the single call, and
+unaligned bases the aligned call."""
 import numpy as np
 import pytest
 import torch
@@ -112,7 +112,7 @@ def test_split_equals_single_call_and_unaligned_equals_vector(dyt, M, N, xdt):
     da2, dg2, db2 = torch.empty_like(da), torch.empty_like(dg), torch.empty_like(db)
     dyt.dyt_backward_residual_partials(h, d["dy"], d["dres"], d["alpha"], d["gamma"], dh2, ws)
     dyt.dyt_backward_finish(ws, M, N, xdt, da2, dg2, db2)
-    # element-wise variant: every activation one element off 16-byte alignment
+    # every activation one element off 16-byte alignment: same kernels
     def off(t):
         buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
         v = buf[1:].view(t.shape)
@@ -122,13 +122,13 @@ def test_split_equals_single_call_and_unaligned_equals_vector(dyt, M, N, xdt):
     hu, yu = off(torch.zeros_like(h)), off(torch.zeros_like(y))
     dyt.dyt_forward_residual(xu, ru, d["alpha"], d["gamma"], d["beta"], h=hu, y=yu)
     dhu = off(torch.zeros_like(dh))
-    dyt.dyt_backward_residual(hu, dyu, dresu, d["alpha"], d["gamma"], dh=dhu)
+    _, dau, dgu, dbu = dyt.dyt_backward_residual(hu, dyu, dresu, d["alpha"], d["gamma"], dh=dhu)
     torch.cuda.synchronize()
     assert hu.data_ptr() % 16 != 0
     assert np.array_equal(_bits(dh2), _bits(dh))
     for a, b in ((da2, da), (dg2, dg), (db2, db)):
         assert np.array_equal(_bits(a), _bits(b))
-    for a, b in ((hu, h), (yu, y), (dhu, dh)):
+    for a, b in ((hu, h), (yu, y), (dhu, dh), (dau, da), (dgu, dg), (dbu, db)):
         assert np.array_equal(_bits(a), _bits(b))
     assert_reports(f"residual {M}x{N}", _reports(inp, r, dres, h, y, dh, da, dg, db))
 

@@ -1,8 +1,8 @@
 """Row-strided activations (dyt_forward_strided / dyt_backward_strided):
 results equal the contiguous calls bit for bit (same tiling, same partial
-rows), on both tile layouts, with 16-byte-aligned pitches (vector kernels)
-and odd pitches (element-wise kernels); the gaps between rows are never
-written."""
+rows), on both tile layouts and with pitches of any alignment; packed rows
+whose length is not a multiple of the vector width take the element-wise
+kernels. The gaps between rows are never written."""
 import numpy as np
 import pytest
 import torch
@@ -42,36 +42,38 @@ def _strided(src: torch.Tensor, pad: int, fill=CANARY) -> torch.Tensor:
 SHAPES = [  # (M, N, x dtype, param dtype, pads for x / dy / outputs)
     (2049, 32, "bf16", "f32", (8, 16, 24)),        # packed, vector kernels
     (1031, 17, "f32", "f32", (3, 1, 7)),           # packed, element-wise (N % V != 0)
-    (333, 100, "f16", "f16", (4, 12, 28)),         # packed, vector kernels
-    (301, 64, "bf16", "bf16", (1, 8, 8)),          # odd pitch: element-wise
-    (65, 4096, "bf16", "f32", (64, 8, 128)),       # row segments, vector kernels
+    (333, 100, "f16", "f16", (4, 12, 28)),         # packed, element-wise (N % V != 0)
+    (301, 64, "bf16", "bf16", (1, 8, 8)),          # packed, odd pitch: vector kernels
+    (65, 4096, "bf16", "f32", (64, 8, 128)),       # row segments
     (9, 20000, "f32", "f32", (4, 0, 12)),          # row segments, several column blocks
-    (7, 5000, "f32", "bf16", (1, 2, 3)),           # row segments, element-wise
+    (7, 5000, "f32", "bf16", (1, 2, 3)),           # row segments, odd pitches
+    (11, 4099, "bf16", "f32", (5, 1, 2)),          # row segments, N % V != 0
 ]
 
 
-def _misaligned(src: torch.Tensor) -> torch.Tensor:
-    """Contiguous copy whose base is one element past a 16-byte boundary (the
-    element-wise kernels run on it)."""
-    M, N = src.shape
-    buf = torch.empty(M * N + 1, dtype=src.dtype, device=src.device)
-    v = buf[1:].view(M, N)
-    v.copy_(src)
-    return v
+def _vector_kernels(N: int, sx: int, packed: bool) -> bool:
+    """The documented rule: every pitch takes the 16-byte kernels except
+    packed rows whose length is not a multiple of the vector width."""
+    return not packed or N % (16 // sx) == 0
 
 
-def _vector_eligible(N: int, sx: int, packed: bool, lds) -> bool:
-    """The documented rule for the 16-byte kernels on row-strided operands
-    (bases here are always 16-byte aligned)."""
-    return all((ld * sx) % 16 == 0 for ld in lds) and (not packed or N % (16 // sx) == 0)
+def _strided_run(dyt, x, dy, a, g, b, pads):
+    px, pd, po = pads
+    pdx = po + 8 if po else 0
+    xs, dys = _strided(x, px), _strided(dy, pd)
+    ys = _strided(torch.zeros_like(x), po)
+    dxs = _strided(torch.zeros_like(x), pdx)
+    dyt.dyt_forward(xs, a, g, b, y=ys)
+    _, da, dg, db = dyt.dyt_backward(xs, dys, a, g, dx=dxs)
+    return ys, dxs, da, dg, db, po, pdx
 
 
 @pytest.mark.parametrize("M,N,xdt,pdt,pads", SHAPES)
 def test_strided_equals_contiguous(dyt, M, N, xdt, pdt, pads):
-    """Same tiling and kernel variant as the contiguous call, so the same bits.
-    Where a pitch rules out the vector kernels, the contiguous reference runs
-    the element-wise ones too (misaligned base); y and dx never depend on the
-    variant."""
+    """Same tiling as the contiguous call. With the vector kernels every
+    output is the contiguous call's bit for bit; with the element-wise ones
+    (packed rows, N not a multiple of the vector width) y and dx are, the
+    gradients match another strided launch bit for bit and the oracle."""
     log(f"[strided] M={M} N={N} x={xdt} p={pdt} pads={pads}")
     inp = workloads.custom(M, N, xdt, pdt, alpha=0.7, seed=M * 31 + N)
     xt, pt = TORCH_DT[xdt], TORCH_DT[pdt]
@@ -82,25 +84,22 @@ def test_strided_equals_contiguous(dyt, M, N, xdt, pdt, pads):
     a = torch.from_numpy(inp.alpha).to(dev).to(pt)
     g = torch.from_numpy(inp.gamma).to(dev).to(pt)
     b = torch.from_numpy(inp.beta).to(dev).to(pt)
-    px, pd, po = pads
-    pdx = po + 8 if po else 0
-    fplan = dyt.dyt_get_forward_plan(M, N, xdt, pdt)
-    bplan = dyt.dyt_get_plan(M, N, xdt, pdt)
-    fvec = _vector_eligible(N, sx, fplan["packed"], (N + px, N + po))
-    bvec = _vector_eligible(N, sx, bplan["packed"], (N + px, N + pd, N + pdx))
-    y0 = dyt.dyt_forward(x if fvec else _misaligned(x), a, g, b)
-    dx0, da0, dg0, db0 = dyt.dyt_backward(x if bvec else _misaligned(x), dy, a, g)
-    xs, dys = _strided(x, px), _strided(dy, pd)
-    ys = _strided(torch.zeros_like(x), po)
-    dxs = _strided(torch.zeros_like(x), pdx)
-    assert xs.stride(0) == N + px and (po == 0 or ys.stride(0) == N + po)
-    dyt.dyt_forward(xs, a, g, b, y=ys)
-    _, da, dg, db = dyt.dyt_backward(xs, dys, a, g, dx=dxs)
+    packed = bool(dyt.dyt_get_plan(M, N, xdt, pdt)["packed"])
+    assert packed == bool(dyt.dyt_get_forward_plan(M, N, xdt, pdt)["packed"])
+    vec = _vector_kernels(N, sx, packed)
+    y0 = dyt.dyt_forward(x, a, g, b)
+    dx0, da0, dg0, db0 = dyt.dyt_backward(x, dy, a, g)
+    ys, dxs, da, dg, db, po, pdx = _strided_run(dyt, x, dy, a, g, b, pads)
     torch.cuda.synchronize()
-    log(f"[strided] vector kernels: forward {fvec}, backward {bvec}")
+    log(f"[strided] vector kernels: {vec}")
     assert np.array_equal(_bits(ys), _bits(y0))
     assert np.array_equal(_bits(dxs), _bits(dx0))
-    for u, v in ((da, da0), (dg, dg0), (db, db0)):
+    if vec:
+        refs = (da0, dg0, db0)
+    else:
+        _, _, *refs, _, _ = _strided_run(dyt, x, dy, a, g, b, tuple(q + 5 for q in pads))
+        torch.cuda.synchronize()
+    for u, v in zip((da, dg, db), refs):
         assert np.array_equal(_bits(u), _bits(v))
     # the gaps between rows are untouched
     for out, pad in ((ys, po), (dxs, pdx)):
