@@ -121,13 +121,79 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 constexpr int64_t kMaxN = (int64_t)1 << 30;   // row length limit (int32 in-tile offsets)
 
+// Tiling helpers: packed tiles of r whole rows, or row segments in nb column
+// blocks, with k vector slots per thread.
+void fill_packed(Plan& p, int64_t M, int64_t N, int vec, int k, int64_t r, int64_t grid) {
+    p.packed = true;
+    p.vec = vec;
+    p.slots = k;
+    p.R = r;
+    p.T = r * N;
+    p.nb = 1;
+    p.last_len = p.T;
+    p.tiles = ceil_div(M, r);
+    p.wcols = N;
+    p.grid = std::min<int64_t>(p.tiles, grid);
+}
+
+void fill_segments(Plan& p, int64_t M, int64_t N, int vec, int k, int64_t grid) {
+    const int64_t cap = (int64_t)kBlock * vec * k;
+    p.packed = false;
+    p.vec = vec;
+    p.slots = k;
+    p.nb = ceil_div(N, cap);
+    p.T = round_up(ceil_div(N, p.nb), vec);
+    while (p.nb > 1 && (p.nb - 1) * p.T >= N) --p.nb;   // no empty last block
+    p.last_len = N - (p.nb - 1) * p.T;
+    p.R = 1;
+    p.tiles = M * p.nb;
+    p.wcols = p.T;
+    p.grid = p.nb * std::min<int64_t>(M, std::max<int64_t>(1, grid / p.nb));
+}
+
+// Fraction of the vector slots that carry data (row segments: averaged over
+// the column blocks).
+double occupancy(const Plan& p, int64_t N) {
+    const double cap = (double)kBlock * p.vec * p.slots;
+    return p.packed ? (double)p.T / cap : (double)N / ((double)p.nb * cap);
+}
+
 // Pure host: validates sizes/dtypes and fills the plan. The plan depends
 // only on (M, N, x dtype); pointer alignment and row pitches never change
 // it. The one launch that cannot use 16-byte vectors (row-strided packed
 // rows whose length is not a multiple of V) runs the same tiles with the
-// element-wise kernel variant (V = 1, K = 16, whose 4096-element capacity
-// holds any tile), so the partial-row layout - and with it
-// dyt_backward_finish - is the same for every launch of a shape.
+// element-wise kernel variant (V = 1, K = 16 or 32: a capacity that holds
+// the tile), so the partial-row layout - and with it dyt_backward_finish -
+// is the same for every launch of a shape.
+//
+// The default tiling uses tiles of up to kTileCap elements with K a power of
+// two (the measured tile table picks K and the grid). Widths that fill those
+// tiles poorly (fewer than DYT_OCC_MIN of the slots carry data, e.g. rows of
+// 2,560 or 5,120 bf16 elements; DYT_OCC_MIN_FWD for the forward) are
+// re-tiled for occupancy: K = 2 .. 4 slots
+// (tiles up to kTileMax elements), packed rows or row segments, whichever
+// fills the most slots (ties: the bigger tile), if that beats the default by
+// DYT_OCC_GAIN. Backward throughput follows slot occupancy almost linearly
+// on MI355X (wasted slots still load and compute); measured at 2^27
+// elements, re-tiling lifts the backward by 10-35% at N = 2,560 ... 6,144
+// (bf16) and 2,560 ... 5,120 (f32) and never lost beyond noise, while
+// re-tiling to K = 1 (tiles of 256 vectors) lost up to 19%, hence
+// DYT_OCC_KMIN. Widths that fill the default tiles keep the measured plan.
+#ifndef DYT_OCC_MIN
+#define DYT_OCC_MIN 0.9
+#endif
+// The forward (half the arithmetic per byte) is re-tiled only below this
+// occupancy: from 0.63 and less it gained up to 26% (f32 rows of 2,560 to
+// 5,120), while bf16 rows of 1,500 (0.73 -> 0.98) lost 4%.
+#ifndef DYT_OCC_MIN_FWD
+#define DYT_OCC_MIN_FWD 0.7
+#endif
+#ifndef DYT_OCC_GAIN
+#define DYT_OCC_GAIN 0.05
+#endif
+#ifndef DYT_OCC_KMIN
+#define DYT_OCC_KMIN 2
+#endif
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
     if (M < 0 || N < 0 || N > kMaxN) return DYT_ERR_INVALID_ARG;
@@ -146,8 +212,6 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     const int64_t r0 = 16 / gcd64(N * sx, 16);
     const int64_t rcap = (dyt::kTileCap / N) / r0 * r0;
     if (rcap >= 2) {
-        p.packed = true;
-        p.vec = vmax;
         // largest K (biggest tiles) that still yields DYT_MIN_TILES tiles,
         // else the smallest K that holds an aligned row group
         int chosen = 0;
@@ -158,32 +222,37 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
             if (ceil_div(M, r) >= tune.min_tiles) break;
         }
         const int64_t r = ((int64_t)kBlock * vmax * chosen / N) / r0 * r0;
-        p.slots = chosen;
-        p.R = r;
-        p.T = r * N;
-        p.nb = 1;
-        p.last_len = p.T;
-        p.tiles = ceil_div(M, r);
-        p.wcols = N;
-        p.grid = std::min<int64_t>(p.tiles, tune.grid);
+        fill_packed(p, M, N, vmax, chosen, r, tune.grid);
     } else {
         // row segments: vectors from each row's start; with N not a multiple
         // of V the kernels shift each row's last vector back (RAG)
-        p.packed = false;
-        p.vec = vmax;
         const int kbig = tune.kcap > 0 ? std::min(kmax, tune.kcap) : kmax;
         int k = 1;
-        while (k < kbig && (int64_t)kBlock * p.vec * k < N) k *= 2;
-        p.slots = k;
-        const int64_t cap = (int64_t)kBlock * p.vec * k;
-        p.nb = ceil_div(N, cap);
-        p.T = round_up(ceil_div(N, p.nb), p.vec);
-        while (p.nb > 1 && (p.nb - 1) * p.T >= N) --p.nb;   // no empty last block
-        p.last_len = N - (p.nb - 1) * p.T;
-        p.R = 1;
-        p.tiles = M * p.nb;
-        p.wcols = p.T;
-        p.grid = p.nb * std::min<int64_t>(M, std::max<int64_t>(1, tune.grid / p.nb));
+        while (k < kbig && (int64_t)kBlock * vmax * k < N) k *= 2;
+        fill_segments(p, M, N, vmax, k, tune.grid);
+    }
+    const double occ = occupancy(p, N);
+    if (occ < (dir == Dir::Bwd ? DYT_OCC_MIN : DYT_OCC_MIN_FWD)) {
+        const int kalt = std::min(dyt::kSlotsMax, dyt::kTileMax / (kBlock * vmax));
+        const int khi = tune.kcap > 0 ? std::min(kalt, std::max(tune.kcap, (int)p.slots)) : kalt;
+        Plan best = p;
+        double best_occ = occ;
+        for (int k = DYT_OCC_KMIN; k <= khi; ++k) {
+            const int64_t cap = (int64_t)kBlock * vmax * k;
+            Plan c;
+            const int64_t r = (cap / N) / r0 * r0;
+            if (r >= 2) {
+                fill_packed(c, M, N, vmax, k, r, tune.grid);
+            } else {
+                fill_segments(c, M, N, vmax, k, tune.grid);
+            }
+            const double co = occupancy(c, N);
+            if (co > best_occ + 1e-9 || (co > best_occ - 1e-9 && c.T > best.T)) {
+                best = c;
+                best_occ = co;
+            }
+        }
+        if (best_occ >= occ + DYT_OCC_GAIN) p = best;
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
@@ -197,7 +266,7 @@ Plan variant_for(const Plan& p, bool vector) {
     Plan q = p;
     if (!vector && q.vec != 1) {
         q.vec = 1;
-        q.slots = 16;
+        q.slots = q.T <= 16 * kBlock ? 16 : 32;
     }
     return q;
 }

@@ -66,7 +66,9 @@ namespace dyt {
 #define DYT_TILE_CAP 4096
 #endif
 constexpr int kBlock = DYT_BLOCK;       // threads per workgroup (wave64s x 64)
-constexpr int kTileCap = DYT_TILE_CAP;  // elements per tile at the largest K
+constexpr int kTileCap = DYT_TILE_CAP;  // elements per tile of the default tiling
+constexpr int kTileMax = 8192;          // largest tile of any plan (occupancy re-tiling)
+constexpr int kSlotsMax = 4;            // largest K of the vector kernels
 constexpr int kFinBlock = 1024;   // pass-2 threads: 64 outputs x 16 segments
 constexpr int kFinSegs = kFinBlock / 64;
 
@@ -328,11 +330,11 @@ struct Slots {
 template <int V, int K, bool SHIFT>
 __device__ __forceinline__ Slots<V, K> make_slots(int tid, int seg_len) {
     Slots<V, K> s;
-    // 1 <= seg_len <= kTileCap; the clamp only tells the compiler the range
+    // 1 <= seg_len <= kTileMax; the clamp only tells the compiler the range
     // of the offsets. A segment shorter than V (the last of several column
     // blocks) has its one vector reach back into the previous block of the
     // same row: columns another workgroup owns and writes identically.
-    const int last = min(max(seg_len - V, 1 - V), kTileCap - V);
+    const int last = min(max(seg_len - V, 1 - V), kTileMax - V);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int o = (k * kBlock + tid) * V;

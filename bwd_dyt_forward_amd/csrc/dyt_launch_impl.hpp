@@ -70,21 +70,25 @@ bool launch_bwd_vk(const Plan& p, const Geo& g, const BwdPtrs& a, hipStream_t s)
     return true;
 }
 
-// Kernel instances: vector access at K in {1, 2, ..., 4096 / (256 V)}, and
-// the element-wise variant (V = 1) at K = 16 (packed, row-strided only).
-// dispatch_vk calls launch(V, K), both as integral constants, for the
-// instance the plan selects.
+// Kernel instances: vector access at K = 1 .. 4, and the element-wise
+// variant (V = 1) at K = 16 or 32 (packed, row-strided only). dispatch_vk
+// calls launch(V, K), both as integral constants, for the instance the plan
+// selects.
 template <typename XT, typename L>
 bool dispatch_vk(const Plan& p, L&& launch) {
     constexpr int VV = 16 / sizeof(XT);
-    if (p.vec == 1 && p.slots == 16) return launch(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
+    using I = std::integral_constant<int, VV>;
+    if (p.vec == 1) {
+        if (p.slots == 16) return launch(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
+        if (p.slots == 32) return launch(std::integral_constant<int, 1>{}, std::integral_constant<int, 32>{});
+        return false;
+    }
     if (p.vec != VV) return false;
     switch (p.slots) {
-        case 1: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 1>{});
-        case 2: return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 2>{});
-        case 4:
-            if constexpr (VV == 4) return launch(std::integral_constant<int, VV>{}, std::integral_constant<int, 4>{});
-            return false;
+        case 1: return launch(I{}, std::integral_constant<int, 1>{});
+        case 2: return launch(I{}, std::integral_constant<int, 2>{});
+        case 3: return launch(I{}, std::integral_constant<int, 3>{});
+        case 4: return launch(I{}, std::integral_constant<int, 4>{});
         default: return false;
     }
 }

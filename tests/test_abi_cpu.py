@@ -85,7 +85,8 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
     for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "fwd_grid",
                 "bwd_grid", "ws_row", "ws_bytes"):
         assert p[key] == q[key], key
-    assert 1 <= p["tile_elems"] <= cap <= 4096
+    assert 1 <= p["tile_elems"] <= cap <= 8192
+    assert p["slots"] in ((1, 2, 3, 4) if vec else (16, 32))
     if p["packed"]:
         R = p["rows_per_tile"]
         assert p["tile_elems"] == R * N and p["col_blocks"] == 1
@@ -126,7 +127,7 @@ def test_forward_plan_invariants(dyt, M, N, xdt, vec):
     sx = 4 if xdt == "f32" else 2
     assert p["fwd_grid"] == b["fwd_grid"] and p["ws_bytes"] == 0 and p["bwd_grid"] == 0
     assert p["packed"] == b["packed"] and p["vec"] == b["vec"]
-    assert 1 <= p["tile_elems"] <= p["block"] * p["vec"] * p["slots"] <= 4096
+    assert 1 <= p["tile_elems"] <= p["block"] * p["vec"] * p["slots"] <= 8192
     if p["packed"]:
         R = p["rows_per_tile"]
         assert p["tile_elems"] == R * N and p["tiles"] == -(-M // R)
@@ -160,6 +161,37 @@ def test_short_last_block_shapes(dyt, M, N, xdt):
         assert not p["packed"]
         lasts.append(N - (p["col_blocks"] - 1) * p["tile_elems"])
     assert min(lasts) >= 1 and any(last < v for last in lasts)
+
+
+def _occ(p, N):
+    cap = p["block"] * p["vec"] * p["slots"]
+    return p["tile_elems"] / cap if p["packed"] else N / (p["col_blocks"] * cap)
+
+
+# (M, N, x dtype, layout, K) of the backward and forward plans after
+# occupancy re-tiling (the GPU tests run these shapes)
+RETILED = [(301, 1500, "bf16", "packed", 3), (1100, 5120, "bf16", "segments", 3),
+           (2000, 2560, "bf16", "packed", 4), (1700, 2560, "f32", "segments", 3),
+           (2100, 4104, "f32", "segments", 3), (1400, 3072, "bf16", "packed", 3)]
+
+
+@pytest.mark.parametrize("M,N,xdt,layout,k", RETILED)
+def test_occupancy_retiling(dyt, M, N, xdt, layout, k):
+    """Widths that fill the default tiles poorly are re-tiled: K >= 2 slots,
+    at least as many slots carrying data as the default tiling would."""
+    p = dyt.dyt_get_plan(M, N, xdt, "f32")
+    assert p["slots"] == k and bool(p["packed"]) == (layout == "packed")
+    assert _occ(p, N) >= 0.66 and p["tile_elems"] <= 8192
+
+
+def test_headline_plans_unchanged(dyt):
+    """The measured plans of 32,768 x 4,096 and 4,194,304 x 32 bfloat16."""
+    b = dyt.dyt_get_plan(32768, 4096, "bf16", "f32")
+    f = dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")
+    assert (b["packed"], b["slots"], b["tile_elems"], b["col_blocks"], b["bwd_grid"]) == (0, 2, 4096, 1, 256)
+    assert (f["packed"], f["slots"], f["tile_elems"], f["col_blocks"], f["fwd_grid"]) == (0, 1, 2048, 2, 1024)
+    for p in (dyt.dyt_get_plan(4194304, 32, "bf16", "f32"), dyt.dyt_get_forward_plan(4194304, 32, "bf16", "f32")):
+        assert (p["packed"], p["slots"], p["rows_per_tile"], p["tile_elems"]) == (1, 2, 128, 4096)
 
 
 def test_tile_table_covers_every_dtype_width_and_size():

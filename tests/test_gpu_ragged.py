@@ -1,11 +1,14 @@
-"""Rows whose length is not a multiple of the 16-byte vector width (and rows
-wider than a tile): the vector kernels shift each row's last vector back to
-end at the row's end, so its first elements rewrite bytes a neighbouring slot
-owns (or, when the last column block is shorter than a vector, bytes of the
-previous block). Checked here: every output against the oracle, guard
+"""Awkward row widths. Rows whose length is not a multiple of the 16-byte
+vector width (and rows wider than a tile): the vector kernels shift each
+row's last vector back to end at the row's end, so its first elements
+rewrite bytes a neighbouring slot owns (or, when the last column block is
+shorter than a vector, bytes of the previous block). Widths that fill the
+default tiles poorly run re-tiled plans (K = 3 or 4 slots, packed tiles of
+up to 8,192 elements). Checked here: every output against the oracle, guard
 canaries around every output, unaligned bases equal to aligned ones bit for
-bit, row-strided launches equal to contiguous ones bit for bit, and the
-residual-fused layer."""
+bit, row-strided launches equal to contiguous ones bit for bit (with the
+element-wise kernels: y and dx, the gradients equal to a second strided
+launch), and the residual-fused layer."""
 import numpy as np
 import pytest
 import torch
@@ -86,26 +89,49 @@ def _check_shape(dyt, M, N, xdt, pdt):
     assert xu.data_ptr() % 16 != 0
     dyt.dyt_forward(xu, a, g, b, y=yu)
     _, dau, dgu, dbu = dyt.dyt_backward(xu, dyu, a, g, dx=dxu)
-    # row-strided: same kernels, same bits, gaps untouched
-    ld = N + 3
-    xs = torch.full((M, ld), CANARY, dtype=x.dtype, device="cuda")[:, :N]
-    xs.copy_(x)
-    dys = torch.full((M, ld + 1), CANARY, dtype=x.dtype, device="cuda")[:, :N]
-    dys.copy_(dy)
-    ysb = torch.full((M, ld + 5), CANARY, dtype=x.dtype, device="cuda")
-    dxsb = torch.full((M, ld + 2), CANARY, dtype=x.dtype, device="cuda")
-    ys, dxs = ysb[:, :N], dxsb[:, :N]
-    dyt.dyt_forward(xs, a, g, b, y=ys)
-    _, das, dgs, dbs = dyt.dyt_backward(xs, dys, a, g, dx=dxs)
+    # row-strided: same tiles, gaps untouched; packed rows whose length is
+    # not a multiple of the vector width take the element-wise kernels
+    def strided(ld):
+        xs = torch.full((M, ld), CANARY, dtype=x.dtype, device="cuda")[:, :N]
+        xs.copy_(x)
+        dys = torch.full((M, ld + 1), CANARY, dtype=x.dtype, device="cuda")[:, :N]
+        dys.copy_(dy)
+        ysb = torch.full((M, ld + 5), CANARY, dtype=x.dtype, device="cuda")
+        dxsb = torch.full((M, ld + 2), CANARY, dtype=x.dtype, device="cuda")
+        ys, dxs = ysb[:, :N], dxsb[:, :N]
+        dyt.dyt_forward(xs, a, g, b, y=ys)
+        _, das, dgs, dbs = dyt.dyt_backward(xs, dys, a, g, dx=dxs)
+        return ys, dxs, das, dgs, dbs, ysb, dxsb
+    ys, dxs, das, dgs, dbs, ysb, dxsb = strided(N + 3)
     torch.cuda.synchronize()
-    for u, v in ((yu, y), (dxu, dx), (dau, da), (dgu, dg), (dbu, db),
-                 (ys, y), (dxs, dx), (das, da), (dgs, dg), (dbs, db)):
-        assert np.array_equal(_bits(u), _bits(v))
+    v = 16 // x.element_size()
+    elementwise = bool(dyt.dyt_get_plan(M, N, xdt, pdt)["packed"]) and N % v != 0
+    if elementwise:
+        grads = strided(N + 9)[2:5]
+        torch.cuda.synchronize()
+    else:
+        grads = (da, dg, db)
+    for u, w in ((yu, y), (dxu, dx), (dau, da), (dgu, dg), (dbu, db), (ys, y), (dxs, dx),
+                 (das, grads[0]), (dgs, grads[1]), (dbs, grads[2])):
+        assert np.array_equal(_bits(u), _bits(w))
     assert bool((ysb[:, N:] == CANARY).all()) and bool((dxsb[:, N:] == CANARY).all())
+    if elementwise:
+        assert_reports(f"ragged strided {M}x{N}", full_reports(inp, ys, dxs, das, dgs, dbs))
 
 
 @pytest.mark.parametrize("M,N,xdt,pdt", SHAPES)
 def test_ragged_rows(dyt, M, N, xdt, pdt):
+    _check_shape(dyt, M, N, xdt, pdt)
+
+
+# re-tiled for slot occupancy (the CPU test test_occupancy_retiling checks
+# that these shapes get K = 3 / 4 and packed tiles beyond 4,096 elements)
+RETILED = [(301, 1500, "bf16", "f32"), (1100, 5120, "bf16", "f32"), (2000, 2560, "bf16", "bf16"),
+           (1700, 2560, "f32", "f32"), (2100, 4104, "f32", "f32"), (1400, 3072, "bf16", "f32")]
+
+
+@pytest.mark.parametrize("M,N,xdt,pdt", RETILED)
+def test_retiled_widths(dyt, M, N, xdt, pdt):
     _check_shape(dyt, M, N, xdt, pdt)
 
 
