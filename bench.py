@@ -558,6 +558,78 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         f.write("\n".join(rows + cold_rows) + "\n")
 
 
+WIDTH_CASES = ([("bf16", n, 0) for n in (1500, 2048, 2560, 3072, 4095, 4096, 4104, 5120, 6144, 7168,
+                                        8192, 10240)]
+               + [("f32", n, 0) for n in (2560, 4104, 5120)]
+               + [("bf16", 4096, 1), ("bf16", 32, 1), ("f32", 100, 1)])
+
+
+def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, rounds: int = 3) -> None:
+    """Row widths that do not fill 4,096-element tiles, ragged rows and bases
+    one element off 16-byte alignment, each at 2^27 elements (synthetic
+    normal data, fp32 parameters): median over `rounds` of the mean forward
+    and backward (pass 1 + pass 2) time of `steps` continuous calls (HIP
+    events), with the plan each direction ran."""
+    rows = ["Each case: 2^27 elements, x ~ N(0, 1), fp32 parameters; HIP events around "
+            f"{steps} continuous calls after {warmup} warm-up calls, median of {rounds} rounds; "
+            "backward = pass 1 + pass 2. Occupancy = share of the tile's vector slots that carry data.",
+            "", "| x | N | M | base | fwd us | fwd GB/s | bwd us | bwd GB/s | fwd plan | bwd plan |",
+            "|---|---:|---:|---|---:|---:|---:|---:|---|---|"]
+    for xdt, N, off in WIDTH_CASES:
+        M = (1 << 27) // N
+        dt = torch.bfloat16 if xdt == "bf16" else torch.float32
+        gen = torch.Generator(device="cuda").manual_seed(N)
+
+        def act():
+            buf = torch.empty(M * N + 8, dtype=dt, device="cuda")
+            v = buf[off:off + M * N].view(M, N)
+            v.copy_(torch.randn(M, N, generator=gen, device="cuda"))
+            return v
+        x, dy, y, dx = act(), act(), act(), act()
+        a = torch.tensor([0.5], device="cuda")
+        g = torch.randn(N, generator=gen, device="cuda")
+        b = torch.randn(N, generator=gen, device="cuda")
+        da, dg, db = torch.empty(1, device="cuda"), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+        ws = torch.empty(max(16, dyt.dyt_backward_workspace_size(M, N, xdt, "f32")), dtype=torch.uint8,
+                         device="cuda")
+
+        def fwd():
+            dyt.dyt_forward(x, a, g, b, y=y)
+
+        def bwd():
+            dyt.dyt_backward(x, dy, a, g, dx=dx, dalpha=da, dgamma=dg, dbeta=db, workspace=ws)
+        times = {}
+        for key, fn in (("fwd", fwd), ("bwd", bwd)):
+            med = []
+            for _ in range(rounds):
+                for _ in range(warmup):
+                    fn()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                e1.synchronize()
+                med.append(e0.elapsed_time(e1) * 1e3 / steps)
+            times[key] = statistics.median(med)
+
+        def desc(pl):
+            cap = pl["block"] * pl["vec"] * pl["slots"]
+            occ = pl["tile_elems"] / cap if pl["packed"] else N / (pl["col_blocks"] * cap)
+            lay = f"packed R={pl['rows_per_tile']}" if pl["packed"] else f"rows nb={pl['col_blocks']}"
+            return f"{lay}, K={pl['slots']}, occupancy {occ:.2f}"
+        sx = 2 if xdt == "bf16" else 4
+        byt = M * N * sx
+        rows.append(f"| {xdt} | {N} | {M} | {'+1 element' if off else 'aligned'} | {times['fwd']:.1f} | "
+                    f"{2 * byt / times['fwd'] / 1e3:.0f} | {times['bwd']:.1f} | {3 * byt / times['bwd'] / 1e3:.0f} | "
+                    f"{desc(dyt.dyt_get_forward_plan(M, N, xdt, 'f32'))} | {desc(dyt.dyt_get_plan(M, N, xdt, 'f32'))} |")
+        log(rows[-1])
+        del x, dy, y, dx, ws
+    with open(path, "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
 def load_traffic(kernel: str) -> dict | None:
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -586,6 +658,8 @@ def main() -> int:
                     help="skip the residual-fused vs unfused comparison")
     ap.add_argument("--all-configs", metavar="FILE", default=None,
                     help="also time every workload shape and write a Markdown table to FILE")
+    ap.add_argument("--widths", metavar="FILE", default=None,
+                    help="also time awkward row widths and unaligned bases and write a Markdown table to FILE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -617,6 +691,8 @@ def main() -> int:
         copy_calibration(torch, args.copy_calibration_mib)
     if args.all_configs:
         report_all(dyt, torch, args.all_configs)
+    if args.widths:
+        report_widths(dyt, torch, args.widths)
 
     tensor_bytes = main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] in ("bf16", "f16") else 4)
     ceiling = copy_ceiling(torch, tensor_bytes)
