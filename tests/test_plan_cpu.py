@@ -1,0 +1,116 @@
+"""Launch plans over random shapes (pure host functions, no GPU): the tiling
+invariants the kernels rely on, for the forward and backward plans and the
+element-wise variant, and the slot rule of the row-segment kernels (each
+slot's vector lies inside the row; every column of a segment is owned by
+exactly one slot's own elements), restated from the kernels' documentation:
+slot k of thread t starts at o = (k * 256 + t) * V; a slot is used if
+o < segment length L; a used slot that would run past L is shifted back to
+end at L (its first lo = o - (L - V) elements are another slot's); unused
+slots recompute the segment's first whole vector."""
+import numpy as np
+import pytest
+
+hyp = pytest.importorskip("hypothesis")
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+VEC = {"f32": 4, "bf16": 8, "f16": 8}
+
+
+@pytest.fixture(scope="module")
+def dyt():
+    import __graft_entry__ as ge
+    ge._ensure_built()
+    import bwd_dyt_forward_amd as m
+    return m
+
+
+def _check_tiling(p, M, N, v, vector):
+    cap = p["block"] * p["vec"] * p["slots"]
+    assert p["block"] == 256
+    if vector:
+        assert p["vec"] == v and p["slots"] in (1, 2, 3, 4)
+    else:
+        assert p["vec"] == 1 and p["slots"] in (16, 32)
+    assert 1 <= p["tile_elems"] <= cap <= 8192
+    grid = p["fwd_grid"] if p["bwd_grid"] == 0 else p["bwd_grid"]
+    if p["packed"]:
+        R = p["rows_per_tile"]
+        assert R >= 1 and p["tile_elems"] == R * N and (R * N) % v == 0
+        assert p["col_blocks"] == 1 and p["tiles"] == -(-M // R)
+        assert 1 <= grid <= p["tiles"]
+    else:
+        T, nb = p["tile_elems"], p["col_blocks"]
+        assert p["rows_per_tile"] == 1 and T % v == 0
+        last = N - (nb - 1) * T
+        assert 1 <= last <= T
+        assert p["tiles"] == M * nb and grid % nb == 0 and nb <= grid <= p["tiles"]
+
+
+def _slot_rule(L, V, K):
+    """(used, off, lo) arrays over all (k, t) for a segment of length L."""
+    o = (np.arange(K)[:, None] * 256 + np.arange(256)[None, :]).ravel() * V
+    last = min(max(L - V, 1 - V), 8192 - V)
+    used = o < L
+    full = o + V <= L
+    off = np.where(~used, min(last, 0), np.where(full, o, last))
+    lo = np.where(used & ~full, o - last, 0)
+    return used, off, lo
+
+
+def _check_segments(p, N):
+    V, K, T, nb = p["vec"], p["slots"], p["tile_elems"], p["col_blocks"]
+    for b in {0, nb - 1}:
+        col_base = b * T
+        L = T if b < nb - 1 else N - (nb - 1) * T
+        used, off, lo = _slot_rule(L, V, K)
+        cols = col_base + off[:, None] + np.arange(V)[None, :]
+        assert cols.min() >= 0 and cols.max() < N, "a slot's vector leaves the row"
+        own = np.zeros(L, dtype=np.int64)
+        for e in range(V):
+            sel = used & (e >= lo)
+            np.add.at(own, (off[sel] + e), 1)
+        assert (own == 1).all(), "a column is not owned exactly once"
+
+
+@settings(max_examples=300, deadline=None)
+@given(M=st.integers(1, 1 << 22), N=st.integers(1, 1 << 20), xdt=st.sampled_from(["f32", "bf16", "f16"]))
+def test_plans_hold_their_invariants(dyt, M, N, xdt):
+    if M * N > (1 << 36):
+        return
+    v = VEC[xdt]
+    b = dyt.dyt_get_plan(M, N, xdt, "f32")
+    f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
+    for p in (b, f):
+        _check_tiling(p, M, N, v, True)
+        if not p["packed"]:
+            _check_segments(p, N)
+    e = dyt.dyt_get_plan(M, N, xdt, "f32", False)
+    _check_tiling(e, M, N, v, False)
+    for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "bwd_grid", "ws_row", "ws_bytes"):
+        assert e[key] == b[key], key
+    assert b["ws_row"] >= 2 * (N if b["packed"] else b["tile_elems"]) + 1 and b["ws_row"] % 4 == 0
+    assert b["ws_bytes"] == b["bwd_grid"] * b["ws_row"] * 4
+    assert dyt.dyt_backward_workspace_size(M, N, xdt, "f32") == -(-b["ws_bytes"] // 16) * 16
+
+
+@pytest.mark.parametrize("N,xdt", [(261121, "f32"), (522241, "bf16"), (4095, "bf16"), (10001, "f32")])
+def test_slot_rule_on_short_and_ragged_segments(dyt, N, xdt):
+    """Segments shorter than a vector and ragged row ends keep the rule."""
+    for M in (1, 3, 1000):
+        for p in (dyt.dyt_get_plan(M, N, xdt, "f32"), dyt.dyt_get_forward_plan(M, N, xdt, "f32")):
+            assert not p["packed"]
+            _check_segments(p, N)
+
+
+def test_slot_rule_rejects_the_old_short_segment_offsets():
+    """The check above fails for the earlier rule (unused slots at offset 0
+    even in a segment shorter than a vector), which wrote past the row end."""
+    L, V, K, N, col_base = 1, 4, 1, 261121, 261120
+    o = np.arange(256) * V
+    used = o < L
+    last = L - V
+    off = np.where(~used, 0, np.where(o + V <= L, o, last))
+    cols = col_base + off[:, None] + np.arange(V)[None, :]
+    assert cols.max() >= N
+    used2, off2, _ = _slot_rule(L, V, K)
+    assert (col_base + off2[:, None] + np.arange(V)[None, :]).max() < N
