@@ -50,10 +50,13 @@ RANGES = [(1, 16, 8), (17, 48, 32), (49, 80, 64), (81, 160, 100), (161, 512, 255
           (513, 2048, 768), (2049, 6144, 4096), (6145, 1 << 30, 8192)]
 # problem-size ranges (elements M * N) and their representative sizes
 # (2^27: the 32768 x 4096 and 4194304 x 32 workloads at N = 4096, 32)
-# Each range is represented by the sizes at its two ends (the top range by
-# its lower edge and 2^27), shared with the neighbouring ranges.
+# Each range is represented by the sizes at its two ends, shared with the
+# neighbouring ranges; the top range (2^27 and up, where the 2-byte forward
+# prefers smaller tiles by 3-10% while at 2^26 the candidates are within 2%)
+# by its lower edge alone.
 SIZES = [(1, (1 << 22) - 1, (1 << 20, 1 << 22)), (1 << 22, (1 << 24) - 1, (1 << 22, 1 << 24)),
-         (1 << 24, (1 << 26) - 1, (1 << 24, 1 << 26)), (1 << 26, 1 << 62, (1 << 26, 1 << 27))]
+         (1 << 24, (1 << 26) - 1, (1 << 24, 1 << 26)), (1 << 26, (1 << 27) - 1, (1 << 26, 1 << 27)),
+         (1 << 27, 1 << 62, (1 << 27,))]
 REP_SIZES = sorted({e for _, _, reps in SIZES for e in reps})
 DEFAULT = "a_mt1024_k0_g256"
 # name -> (min_tiles, kcap, fwd_grid, bwd_grid); min_tiles acts on packed

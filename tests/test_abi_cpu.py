@@ -189,9 +189,11 @@ def test_headline_plans_unchanged(dyt):
     b = dyt.dyt_get_plan(32768, 4096, "bf16", "f32")
     f = dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")
     assert (b["packed"], b["slots"], b["tile_elems"], b["col_blocks"], b["bwd_grid"]) == (0, 2, 4096, 1, 256)
-    assert (f["packed"], f["slots"], f["tile_elems"], f["col_blocks"], f["fwd_grid"]) == (0, 1, 2048, 2, 1024)
-    for p in (dyt.dyt_get_plan(4194304, 32, "bf16", "f32"), dyt.dyt_get_forward_plan(4194304, 32, "bf16", "f32")):
-        assert (p["packed"], p["slots"], p["rows_per_tile"], p["tile_elems"]) == (1, 2, 128, 4096)
+    assert (f["packed"], f["slots"], f["tile_elems"], f["col_blocks"], f["fwd_grid"]) == (0, 1, 2048, 2, 512)
+    b = dyt.dyt_get_plan(4194304, 32, "bf16", "f32")
+    f = dyt.dyt_get_forward_plan(4194304, 32, "bf16", "f32")
+    assert (b["packed"], b["slots"], b["rows_per_tile"], b["tile_elems"], b["bwd_grid"]) == (1, 2, 128, 4096, 256)
+    assert (f["packed"], f["slots"], f["rows_per_tile"], f["tile_elems"], f["fwd_grid"]) == (1, 1, 64, 2048, 512)
 
 
 def test_tile_table_covers_every_dtype_width_and_size():
