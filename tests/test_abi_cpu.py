@@ -388,3 +388,23 @@ def test_module_constructs_on_cpu(dyt):
 def test_residual_module_constructs_on_cpu(dyt):
     layer = dyt.DyTResidual(8, alpha_init=0.5)
     assert layer.weight.shape == (8,) and isinstance(layer, dyt.DyT)
+
+
+def test_c_caller_builds_links_and_runs(tmp_path):
+    """The header is plain C99 and the library is callable from C without
+    Python (only calls that never reach the GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    pkg = os.path.join(ROOT, "bwd_dyt_forward_amd")
+    exe = str(tmp_path / "abi_check")
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+    cc = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                         f"-I{os.path.join(ROOT, 'include')}", src, "-o", exe, f"-L{pkg}", "-ldyt",
+                         f"-Wl,-rpath,{pkg}"], capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "FAIL" not in run.stdout and run.stdout.count("ok ") == 9
