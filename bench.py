@@ -526,7 +526,7 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
             "| workload | M x N | x/params | fwd us | fwd GB/s | fwd % | bwd us | bwd GB/s | bwd % | "
             "step GB/s | step % | graph step us | graph GB/s | graph % | plan |",
             "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
-    cold_rows = ["", "Cold cache (SURVEY timing protocol): a 1 GiB buffer is read before each timed "
+    cold_rows = ["", "Cold cache: a 1 GiB buffer is read before each timed "
                  "launch; HIP events around the forward and around pass 1 + pass 2; median [p10, p90] over "
                  "30 repetitions. CPU oracle: the fp64 oracle as it is, per direction, on a sample of whole "
                  "rows (at most 2^20 elements), median of 3 runs on one pinned core of the host: "
