@@ -547,10 +547,12 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         B = r["bytes"]
         step_us = r["fwd_us_median"] + r["bwd_us_median"]
         sgbps = (B["fwd"] + B["bwd"]) / (step_us * 1e-6) / 1e9
-        def desc(pl, grid):
+        def desc(pl, grid, fwd=False):
+            if fwd and pl["flat"]:
+                return f"flat, V={pl['vec']}, grid {pl['flat_grid']}"
             return (f"{'packed R=' + str(pl['rows_per_tile']) if pl['packed'] else 'rows nb=' + str(pl['col_blocks'])}"
                     f", V={pl['vec']} K={pl['slots']}, {pl['tiles']} tiles, grid {grid}")
-        plan = (f"fwd: {desc(r['fwd_plan'], r['fwd_plan']['fwd_grid'])}; "
+        plan = (f"fwd: {desc(r['fwd_plan'], r['fwd_plan']['fwd_grid'], True)}; "
                 f"bwd: {desc(r['plan'], r['plan']['bwd_grid'])}")
         rows.append(f"| {name} | {r['M']} x {r['N']} | {r['x_dtype']}/{r['param_dtype']} | "
                     f"{r['fwd_us_median']:.1f} | {r['fwd_gbps']:.0f} | {100 * r['fwd_frac']:.1f} | "
@@ -562,10 +564,10 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         f.write("\n".join(rows + cold_rows) + "\n")
 
 
-WIDTH_CASES = ([("bf16", n, 0) for n in (1500, 2048, 2560, 3072, 4095, 4096, 4104, 5120, 6144, 7168,
-                                        8192, 10240)]
+WIDTH_CASES = ([("bf16", n, 0) for n in (768, 1500, 1536, 2048, 2560, 3072, 4095, 4096, 4104, 5120, 6144,
+                                        7168, 8192, 10240)]
                + [("f32", n, 0) for n in (2560, 4104, 5120)]
-               + [("bf16", 4096, 1), ("bf16", 32, 1), ("f32", 100, 1)])
+               + [("bf16", 4096, 1), ("bf16", 2560, 1), ("bf16", 32, 1), ("f32", 100, 1)])
 
 
 def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, rounds: int = 3) -> None:
@@ -574,7 +576,8 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
     normal data, fp32 parameters): median over `rounds` of the mean forward
     and backward (pass 1 + pass 2) time of `steps` continuous calls (HIP
     events), with the plan each direction ran."""
-    rows = ["Each case: 2^27 elements, x ~ N(0, 1), fp32 parameters; HIP events around "
+    rows = ["Each case: 2^27 elements, x ~ N(0, 1), fp32 parameters; a settling run of "
+            f"{SETTLE_S} s of forward + backward calls, then HIP events around "
             f"{steps} continuous calls after {warmup} warm-up calls, median of {rounds} rounds; "
             "backward = pass 1 + pass 2. Occupancy = share of the tile's vector slots that carry data.",
             "", "| x | N | M | base | fwd us | fwd GB/s | bwd us | bwd GB/s | fwd plan | bwd plan |",
@@ -603,6 +606,12 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
         def bwd():
             dyt.dyt_backward(x, dy, a, g, dx=dx, dalpha=da, dgamma=dg, dbeta=db, workspace=ws)
         times = {}
+        # settle the clocks on this case's own work before any timing
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            fwd()
+            bwd()
+            torch.cuda.synchronize()
         for key, fn in (("fwd", fwd), ("bwd", bwd)):
             med = []
             for _ in range(rounds):
@@ -618,16 +627,18 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
                 med.append(e0.elapsed_time(e1) * 1e3 / steps)
             times[key] = statistics.median(med)
 
-        def desc(pl):
+        def desc(pl, fwd):
             cap = pl["block"] * pl["vec"] * pl["slots"]
             occ = pl["tile_elems"] / cap if pl["packed"] else N / (pl["col_blocks"] * cap)
             lay = f"packed R={pl['rows_per_tile']}" if pl["packed"] else f"rows nb={pl['col_blocks']}"
+            if fwd and pl["flat"]:
+                return f"flat walk, grid {pl['flat_grid']} (tiles: {lay}, K={pl['slots']}, occupancy {occ:.2f})"
             return f"{lay}, K={pl['slots']}, occupancy {occ:.2f}"
         sx = 2 if xdt == "bf16" else 4
         byt = M * N * sx
         rows.append(f"| {xdt} | {N} | {M} | {'+1 element' if off else 'aligned'} | {times['fwd']:.1f} | "
                     f"{2 * byt / times['fwd'] / 1e3:.0f} | {times['bwd']:.1f} | {3 * byt / times['bwd'] / 1e3:.0f} | "
-                    f"{desc(dyt.dyt_get_forward_plan(M, N, xdt, 'f32'))} | {desc(dyt.dyt_get_plan(M, N, xdt, 'f32'))} |")
+                    f"{desc(dyt.dyt_get_forward_plan(M, N, xdt, 'f32'), True)} | {desc(dyt.dyt_get_plan(M, N, xdt, 'f32'), False)} |")
         log(rows[-1])
         del x, dy, y, dx, ws
     with open(path, "w") as f:

@@ -20,6 +20,8 @@ DYT_F32 = 0
 DYT_BF16 = 1
 DYT_F16 = 2
 DYT_OK = 0
+# DYT_ABI_VERSION of include/dyt.h that the signatures and DytPlan below mirror
+ABI_VERSION = 4
 
 _TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16, torch.float16: DYT_F16}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
@@ -40,6 +42,7 @@ class DytPlan(ctypes.Structure):
         ("tile_elems", ctypes.c_int64), ("col_blocks", ctypes.c_int64), ("tiles", ctypes.c_int64),
         ("fwd_grid", ctypes.c_int64), ("bwd_grid", ctypes.c_int64), ("ws_row", ctypes.c_int64),
         ("fin_grid", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
+        ("flat", ctypes.c_int64), ("flat_grid", ctypes.c_int64),
     ]
 
 
@@ -80,6 +83,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    found = lib.dyt_abi_version()
+    if found != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {found}, this binding expects {ABI_VERSION}; "
+                          "rebuild the library")
     return lib
 
 

@@ -91,6 +91,7 @@ using dyt::host::BwdPtrs;
 using dyt::host::FwdPtrs;
 using dyt::host::Plan;
 using dyt::FinGeo;
+using dyt::FlatGeo;
 using dyt::bf16_t;
 using dyt::kBlock;
 
@@ -194,6 +195,32 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_OCC_KMIN
 #define DYT_OCC_KMIN 2
 #endif
+// The flat forward (dyt_fwd_flat_kernel) serves contiguous rows whose length
+// is a multiple of the vector width and at most kFlatMaxN (gamma and beta as
+// float32 in at most 64 KB of LDS) when the tiles fit the rows poorly: for
+// 2-byte x, tiles filled below DYT_FLAT_OCC_2B or packed tiles of K >= 2
+// slots (the 2-byte forward streams slower from those at any fill); for
+// float32 x, tiles filled below DYT_FLAT_OCC_4B. Measured on MI355X at 2^27
+// elements (interleaved medians of 20-launch means): the flat walk streams
+// bf16 at 6.0-6.15 TB/s whatever the width (rows of 768 / 1,536 / 2,560 /
+// 4,104: 87-89 us against 92-97 us tiled) and float32 at 5.8-5.9 TB/s
+// (2,560 / 4,104 / 5,120: 180-184 us against 199-236 us), while tiles that
+// fit stay ahead (bf16 4,096: 82.5 against 89 us; 3,072 in two 2,048-wide
+// segments, 0.75 filled: 86 against 88 us; 7,168 at 0.88: 86 against 90 us).
+// The forward has no reduction, so the choice changes no result bit.
+#ifndef DYT_FLAT_OCC_2B
+#define DYT_FLAT_OCC_2B 0.7
+#endif
+#ifndef DYT_FLAT_OCC_4B
+#define DYT_FLAT_OCC_4B 0.9
+#endif
+// Workgroups of the flat forward (one per CU measured fastest, 4 vectors
+// per thread and step).
+#ifndef DYT_FLAT_GRID
+#define DYT_FLAT_GRID 256
+#endif
+constexpr int64_t kFlatMaxN = 8192;
+
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
     if (M < 0 || N < 0 || N > kMaxN) return DYT_ERR_INVALID_ARG;
@@ -253,6 +280,13 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
             }
         }
         if (best_occ >= occ + DYT_OCC_GAIN) p = best;
+    }
+    const bool poor_fit = sx == 2 ? occupancy(p, N) < DYT_FLAT_OCC_2B || (p.packed && p.slots >= 2)
+                                  : occupancy(p, N) < DYT_FLAT_OCC_4B;
+    if (dir == Dir::Fwd && N % vmax == 0 && N <= kFlatMaxN && poor_fit) {
+        const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);
+        p.flat = true;
+        p.flat_grid = std::min<int64_t>(groups, DYT_FLAT_GRID);
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
@@ -448,6 +482,17 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
+    if (base.flat && !strided && !res) {
+        FlatGeo f;
+        f.nvec = M * N / (16 / sx);
+        f.N = (int32_t)N;
+        f.cstep = (int32_t)((base.flat_grid * DYT_FLAT_U * kBlock * (16 / sx)) % N);
+        const bool ok = with_dtype(x_dtype, [&](auto xt) {
+            return dyt::host::launch_forward_flat<decltype(xt)>(param_dtype, base, f, a, s);
+        });
+        if (!ok) return DYT_ERR_INVALID_ARG;   // not reachable: the plan checked N
+        return hip_status();
+    }
     const Plan p = variant_for(base, vector_ok(base, N, sx, strided));
     Geo g = make_geo(p, M, N);
     g.pitch[0] = ldx;
@@ -482,6 +527,8 @@ void fill_plan(const Plan& p, dyt_plan* out) {
     out->tile_elems = p.T;
     out->col_blocks = p.nb;
     out->tiles = p.tiles;
+    out->flat = 0;
+    out->flat_grid = 0;
 }
 
 }  // namespace
@@ -512,6 +559,8 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
     if (st != DYT_OK) return st;
     const Plan p = variant_for(base, vector_access != 0);
     fill_plan(p, out);
+    out->flat = fbase.flat && vector_access != 0;
+    out->flat_grid = out->flat ? fbase.flat_grid : 0;
     out->fwd_grid = fbase.grid;
     out->bwd_grid = p.grid;
     out->ws_row = p.ld;
@@ -528,6 +577,8 @@ int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int
     if (st != DYT_OK) return st;
     const Plan p = variant_for(base, vector_access != 0);
     fill_plan(p, out);
+    out->flat = base.flat && vector_access != 0;
+    out->flat_grid = out->flat ? base.flat_grid : 0;
     out->fwd_grid = p.grid;
     out->bwd_grid = 0;
     out->ws_row = 0;

@@ -620,6 +620,149 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     }
 }
 
+// ------------------------------------------------------------ flat forward
+// The forward over contiguous rows whose length N is a multiple of V but
+// fills the slot tiles poorly (e.g. 2,560 bfloat16 columns: 62% of the slots
+// of two 2,048-element row segments). The problem is walked as one run of
+// nvec = M*N/V vectors, so every access carries data; since no vector
+// straddles a row, vector q covers columns c .. c+V-1 with c = (q*V) mod N,
+// and gamma/beta come from a float32 copy of both in LDS (2*N floats)
+// instead of per-thread registers. The vectors are cut into groups of
+// B = U * kBlock (one contiguous run); workgroup w of G takes groups w,
+// w + G, ..., and thread tid vectors tid, tid + kBlock, ... of each, so
+// every wave access covers 64 adjacent vectors. A thread's U columns each
+// advance by cstep = (G*B*V) mod N from one of its groups to the next. The
+// last, partial group (nvec mod B vectors) goes to workgroup
+// (nvec / B) mod G, with a bounds check per vector. Loads, arithmetic,
+// rounding and stores per element are those of dyt_fwd_kernel: both give
+// the same bits.
+struct FlatGeo {
+    int64_t nvec;      // vectors in the problem (M * N / V)
+    int32_t N;         // row length, a multiple of V
+    int32_t cstep;     // (G * U * kBlock * V) mod N
+};
+
+template <typename XT, int U, bool RES>
+__device__ __forceinline__ void flat_load(const XT* __restrict__ x, const XT* __restrict__ r,
+                                          int64_t q, typename Raw<XT, 16 / sizeof(XT)>::T (&rx)[U],
+                                          typename Raw<XT, 16 / sizeof(XT)>::T (&rr)[U]) {
+    constexpr int V = 16 / sizeof(XT);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int64_t at = (q + j * kBlock) * V;
+        rx[j] = Raw<XT, V>::template load<DYT_FWD_NT>(x + at);
+        if constexpr (RES) rr[j] = Raw<XT, V>::template load<DYT_FWD_NT>(r + at);
+    }
+}
+
+// Computes and stores vector q + j*kBlock (column col[j]) of a loaded group.
+template <typename XT, bool ACC, bool RES>
+__device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>::T& rx,
+                                         const typename Raw<XT, 16 / sizeof(XT)>::T& rr,
+                                         XT* __restrict__ y, XT* __restrict__ h, int64_t at,
+                                         int col, const float* sg, const float* sb, float alpha) {
+    constexpr int V = 16 / sizeof(XT);
+    float v[V], gm[V], bt[V];
+    fwd_input<XT, V, RES>(rx, rr, h + at, v);
+    // col is a multiple of V (and so of 4): 16-byte LDS reads
+#pragma unroll
+    for (int e = 0; e < V; e += 4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(sg + col + e);
+        const float4 b4 = *reinterpret_cast<const float4*>(sb + col + e);
+        gm[e] = g4.x; gm[e + 1] = g4.y; gm[e + 2] = g4.z; gm[e + 3] = g4.w;
+        bt[e] = b4.x; bt[e + 1] = b4.y; bt[e + 2] = b4.z; bt[e + 3] = b4.w;
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = __builtin_fmaf(gm[e], dyt_tanh<ACC>(alpha * v[e]), bt[e]);
+    Raw<XT, V>::template store<DYT_FWD_NT>(y + at, v);
+}
+
+// Computes and stores a loaded group, then moves each column on to this
+// thread's next group.
+template <typename XT, int U, bool ACC, bool RES>
+__device__ __forceinline__ void flat_group(const typename Raw<XT, 16 / sizeof(XT)>::T (&rx)[U],
+                                           const typename Raw<XT, 16 / sizeof(XT)>::T (&rr)[U],
+                                           XT* __restrict__ y, XT* __restrict__ h, int64_t q,
+                                           int (&col)[U], const float* sg, const float* sb,
+                                           float alpha, int N, int cstep) {
+    constexpr int V = 16 / sizeof(XT);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        flat_vec<XT, ACC, RES>(rx[j], rr[j], y, h, (q + j * kBlock) * V, col[j], sg, sb, alpha);
+        const int c = col[j] + cstep;
+        col[j] = c >= N ? c - N : c;
+    }
+}
+
+// Dynamic LDS: 2 * N floats (gamma, then beta). r and h as in dyt_fwd_kernel
+// (null without RES).
+template <typename XT, typename PT, int U, bool RES>
+__global__ void __launch_bounds__(kBlock)
+dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
+                    const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
+                    const PT* __restrict__ beta, XT* __restrict__ y, XT* __restrict__ h,
+                    const FlatGeo f) {
+    constexpr int V = 16 / sizeof(XT);
+    constexpr int64_t B = (int64_t)U * kBlock;   // vectors per group
+    using R = Raw<XT, V>;
+    constexpr bool ACC = std::is_same<XT, float>::value;
+    extern __shared__ float4 flat_lds[];
+    float* const sg = reinterpret_cast<float*>(flat_lds);
+    float* const sb = sg + f.N;
+    const int N = f.N;
+    const int tid = threadIdx.x;
+    for (int c = tid; c < N; c += kBlock) {
+        sg[c] = to_f32(gamma[c]);
+        sb[c] = to_f32(beta[c]);
+    }
+    __syncthreads();
+    const float alpha = to_f32(alpha_p[0]);
+    const int64_t w = blockIdx.x;
+    const int64_t G = gridDim.x;
+    const int64_t ngroups = f.nvec / B;                 // whole groups
+    const int64_t iters = w < ngroups ? (ngroups - w + G - 1) / G : 0;
+    int col[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) col[j] = (int)(((w * B + j * kBlock + tid) * V) % N);
+
+    // Same two-buffer loop as dyt_fwd_kernel; a last A load past this
+    // workgroup's groups re-reads the previous group.
+    const int64_t gstep = G * B;
+    if (iters > 0) {
+        typename R::T xa[U], xb[U], ra[U], rb[U];
+        int64_t qa = w * B + tid;
+        flat_load<XT, U, RES>(x, r, qa, xa, ra);
+        const int64_t npairs = iters / 2;
+        for (int64_t pi = 0; pi < npairs; ++pi) {
+            const int64_t qb = qa + gstep;
+            flat_load<XT, U, RES>(x, r, qb, xb, rb);
+            __builtin_amdgcn_sched_barrier(0);
+            flat_group<XT, U, ACC, RES>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep);
+            __builtin_amdgcn_sched_barrier(0);
+            const int64_t qn = 2 * pi + 2 < iters ? qb + gstep : qb;
+            flat_load<XT, U, RES>(x, r, qn, xa, ra);
+            __builtin_amdgcn_sched_barrier(0);
+            flat_group<XT, U, ACC, RES>(xb, rb, y, h, qb, col, sg, sb, alpha, N, f.cstep);
+            __builtin_amdgcn_sched_barrier(0);
+            qa = qn;
+        }
+        if (iters & 1) flat_group<XT, U, ACC, RES>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep);
+    }
+    // The partial group: its owner's columns have advanced to group ngroups.
+    if (ngroups * B < f.nvec && w == ngroups % G) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t q = ngroups * B + j * kBlock + tid;
+            if (q < f.nvec) {
+                typename R::T x1, r1{};
+                x1 = R::template load<DYT_FWD_NT>(x + q * V);
+                if constexpr (RES) r1 = R::template load<DYT_FWD_NT>(r + q * V);
+                flat_vec<XT, ACC, RES>(x1, r1, y, h, q * V, col[j], sg, sb, alpha);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- backward
 // Pass 1: dx, plus one float32 partial row per workgroup.
 // RAG (row segments with N not a multiple of V): elements e < lo of a

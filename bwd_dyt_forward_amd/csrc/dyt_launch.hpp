@@ -11,6 +11,12 @@
 #include "dyt.h"
 #include "dyt_kernels.hpp"
 
+// Vectors per thread and step of the flat forward (U * kBlock vectors per
+// workgroup step); the host plan and the kernel instances share it.
+#ifndef DYT_FLAT_U
+#define DYT_FLAT_U 4
+#endif
+
 namespace dyt {
 namespace host {
 
@@ -30,6 +36,11 @@ struct Plan {
     int64_t wcols = 0;
     int64_t fin_grid = 1;
     int64_t ws_bytes = 0;
+    // Forward only: the contiguous launch walks the problem as one run of
+    // vectors (dyt_fwd_flat_kernel) on flat_grid workgroups; row-strided
+    // launches keep the tiles above.
+    bool flat = false;
+    int64_t flat_grid = 0;
 };
 
 // Device pointers of one launch; r/h (forward) and dres (backward) are null
@@ -67,6 +78,9 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
 template <typename XT>
 bool launch_backward(int pdt, bool res, bool strided, const Plan& p, const Geo& g,
                      const BwdPtrs& a, hipStream_t s);
+// The flat forward (contiguous, no residual) for a plan with p.flat set.
+template <typename XT>
+bool launch_forward_flat(int pdt, const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s);
 
 }  // namespace host
 }  // namespace dyt

@@ -134,6 +134,26 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
     }
 }
 
+template <typename XT, typename PT>
+bool launch_flat_pt(const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
+    const size_t lds = 2 * (size_t)f.N * sizeof(float);   // gamma and beta as float32
+    hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, false>), dim3((unsigned)p.flat_grid),
+                       dim3(kBlock), lds, s, (const XT*)a.x, (const XT*)nullptr, (const PT*)a.alpha,
+                       (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)nullptr, f);
+    return true;
+}
+
+template <typename XT>
+bool launch_forward_flat(int pdt, const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
+    if (!p.flat || f.N % (int)(16 / sizeof(XT)) != 0) return false;
+    switch (pdt) {
+        case DYT_F32: return launch_flat_pt<XT, float>(p, f, a, s);
+        case DYT_BF16: return launch_flat_pt<XT, bf16_t>(p, f, a, s);
+        case DYT_F16: return launch_flat_pt<XT, f16_t>(p, f, a, s);
+        default: return false;
+    }
+}
+
 template <typename XT>
 bool launch_backward(int pdt, bool res, bool strided, const Plan& p, const Geo& g,
                      const BwdPtrs& a, hipStream_t s) {

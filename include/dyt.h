@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 3
+#define DYT_ABI_VERSION 4
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -269,6 +269,13 @@ typedef struct dyt_plan {
     int64_t ws_row;        /* floats per partial row */
     int64_t fin_grid;      /* backward pass-2 workgroups */
     int64_t ws_bytes;      /* workspace bytes this plan uses */
+    int64_t flat;          /* forward: 1 if a contiguous launch walks the problem as one
+                              run of 16-byte vectors instead of the tiles above (rows whose
+                              length is a multiple of vec, at most 8192, that the tiles
+                              fit poorly); row-strided launches use the tiles. 0 for the
+                              element-wise variant (vector_access = 0). dyt_get_plan
+                              reports the forward's value; the backward always tiles */
+    int64_t flat_grid;     /* workgroups of that flat forward, 0 if flat = 0 */
 } dyt_plan;
 
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,

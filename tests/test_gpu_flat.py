@@ -1,0 +1,162 @@
+"""The flat forward: contiguous rows of a whole number of 16-byte vectors
+that the slot tiles fill poorly are walked as one run of vectors, with gamma
+and beta read from an LDS copy by computed column. Checked against the fp64
+oracle element by element, bit for bit against the tiled kernels (a
+row-strided launch of the same shape runs the tiles), on problems whose last
+vector group is partial, with guard canaries around y, at a base one element
+off 16-byte alignment, at the largest width the LDS copy allows, and on a
+problem above 2^31 elements."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import TORCH_DT, assert_reports, log, to_np
+from oracle import compare, dyt_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dyt():
+    import __graft_entry__ as ge
+    ge._ensure_built()
+    import bwd_dyt_forward_amd as m
+    return m
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).numpy().copy()
+
+
+CANARY = -12288.0
+
+# (M, N, x dtype, param dtype): every one takes the flat walk (asserted);
+# vector groups of 1,024 per workgroup step, the last one partial in most
+SHAPES = [
+    (1000, 2560, "bf16", "f32"),    # 312.5 groups; row segments 0.62 filled
+    (777, 4104, "f32", "f32"),      # 778.5 groups
+    (3, 1032, "bf16", "bf16"),      # less than one group; packed tiles of K = 2
+    (1, 5120, "f32", "f16"),        # 1.25 groups, one row
+    (2, 2560, "bf16", "f32"),
+    (20000, 1536, "bf16", "f32"),   # packed tiles of K = 2 at 0.75
+    (1001, 4104, "bf16", "f32"),
+    (129, 1040, "bf16", "f16"),
+    (4097, 1032, "f16", "f32"),
+    (1234, 4100, "f32", "bf16"),
+    (300, 7372, "f32", "f32"),      # widest flat row: 59 KB of LDS
+]
+
+
+def _inputs(dyt, M, N, xdt, pdt, seed):
+    inp = workloads.custom(M, N, xdt, pdt, alpha=0.7, seed=seed)
+    xt, pt = TORCH_DT[xdt], TORCH_DT[pdt]
+    x = torch.from_numpy(inp.x).cuda().to(xt)
+    a = torch.from_numpy(inp.alpha).cuda().to(pt)
+    g = torch.from_numpy(inp.gamma).cuda().to(pt)
+    b = torch.from_numpy(inp.beta).cuda().to(pt)
+    return inp, x, a, g, b
+
+
+@pytest.mark.parametrize("M,N,xdt,pdt", SHAPES)
+def test_flat_forward_matches_oracle_and_tiles(dyt, M, N, xdt, pdt):
+    plan = dyt.dyt_get_forward_plan(M, N, xdt, pdt)
+    log(f"[flat] M={M} N={N} x={xdt} p={pdt} plan={plan}")
+    assert plan["flat"] == 1 and plan["flat_grid"] >= 1
+    inp, x, a, g, b = _inputs(dyt, M, N, xdt, pdt, seed=M * 7 + N)
+    xt = TORCH_DT[xdt]
+
+    # contiguous: the flat kernel, y inside a buffer with canaries on both sides
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), CANARY, dtype=xt, device="cuda")
+    y = buf[pad:pad + M * N].view(M, N)
+    dyt.dyt_forward(x, a, g, b, y=y)
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == CANARY).all()) and bool((buf[pad + M * N:] == CANARY).all())
+    f = dyt_oracle.forward(inp.x, inp.alpha, inp.gamma, inp.beta)
+    assert_reports(f"flat M={M} N={N}", [compare.check_y(to_np(y), f.y, f.scale, xdt)])
+
+    # row-strided launch of the same shape: the tiled kernels, same bits
+    xs_buf = torch.full((M, N + 8), CANARY, dtype=xt, device="cuda")
+    xs = xs_buf[:, :N]
+    xs.copy_(x)
+    ys_buf = torch.full((M, N + 16), CANARY, dtype=xt, device="cuda")
+    ys = ys_buf[:, :N]
+    dyt.dyt_forward(xs, a, g, b, y=ys)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ys), _bits(y))
+    assert bool((ys_buf[:, N:] == CANARY).all())
+
+
+@pytest.mark.parametrize("M,N,xdt", [(1000, 2560, "bf16"), (777, 4104, "f32"), (4097, 1032, "f16")])
+def test_flat_forward_unaligned_base(dyt, M, N, xdt):
+    """x and y one element off 16-byte alignment: the same bits as aligned."""
+    inp, x, a, g, b = _inputs(dyt, M, N, xdt, "f32", seed=N)
+    xt = TORCH_DT[xdt]
+    assert dyt.dyt_get_forward_plan(M, N, xdt, "f32")["flat"] == 1
+    y = dyt.dyt_forward(x, a, g, b)
+    xb = torch.empty(M * N + 1, dtype=xt, device="cuda")
+    xu = xb[1:].view(M, N)
+    xu.copy_(x)
+    yb = torch.full((M * N + 2,), CANARY, dtype=xt, device="cuda")
+    yu = yb[1:M * N + 1].view(M, N)
+    assert xu.data_ptr() % 16 != 0 and yu.data_ptr() % 16 != 0
+    dyt.dyt_forward(xu, a, g, b, y=yu)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(yu), _bits(y))
+    assert float(yb[0]) == CANARY and float(yb[-1]) == CANARY
+
+
+def test_flat_forward_repeat_is_bitwise_stable(dyt):
+    M, N = 1001, 4104
+    _, x, a, g, b = _inputs(dyt, M, N, "bf16", "f32", seed=5)
+    y1 = dyt.dyt_forward(x, a, g, b)
+    y2 = dyt.dyt_forward(x, a, g, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y1), _bits(y2))
+
+
+def test_flat_forward_above_2_31_elements(dyt):
+    """838,865 x 2,560 bfloat16 (2.15e9 elements, 64-bit vector offsets):
+    y against the oracle on sampled elements around element 2^31 and at the
+    end, and equal to the tiled (row-strided) launch there."""
+    M, N = 838865, 2560
+    total = M * N
+    assert total > 2 ** 31
+    free, _ = torch.cuda.mem_get_info()
+    if free < 24 * 2 ** 30:
+        pytest.skip("needs ~24 GB of free device memory")
+    plan = dyt.dyt_get_forward_plan(M, N, "bf16", "f32")
+    log(f"[flat large] M={M} N={N} plan={plan}")
+    assert plan["flat"] == 1
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    x = torch.randn(M, N, generator=gen, device="cuda", dtype=torch.bfloat16)
+    gamma = torch.rand(N, generator=gen, device="cuda") + 0.5
+    beta = torch.randn(N, generator=gen, device="cuda") * 0.1
+    alpha = torch.full((1,), 0.8, device="cuda")
+    y = dyt.dyt_forward(x, alpha, gamma, beta)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    idx = np.unique(np.concatenate([rng.integers(0, total, 1 << 18),
+                                    np.arange(2 ** 31 - 4096, 2 ** 31 + 4096),
+                                    np.arange(total - 4096, total)]))
+    assert idx[0] >= 0 and idx[-1] < total
+    it = torch.from_numpy(idx).cuda()
+    xs = to_np(x.view(-1)[it])
+    cols = idx % N
+    ys, ss = dyt_oracle.forward_at(xs, cols, [0.8], to_np(gamma), to_np(beta))
+    got = y.view(-1)[it]
+    assert_reports("flat large y", [compare.check_y(to_np(got), ys, ss, "bf16")])
+    # the tiled kernels on the rows around element 2^31 and the last rows
+    for r0 in ((2 ** 31) // N - 2, M - 3):
+        xs_buf = torch.empty((3, N + 8), dtype=torch.bfloat16, device="cuda")
+        xv = xs_buf[:, :N]
+        xv.copy_(x[r0:r0 + 3])
+        ys_buf = torch.empty((3, N + 8), dtype=torch.bfloat16, device="cuda")
+        yv = ys_buf[:, :N]
+        dyt.dyt_forward(xv, alpha, gamma, beta, y=yv)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(yv), _bits(y[r0:r0 + 3]))
+    del x, y
+    torch.cuda.empty_cache()

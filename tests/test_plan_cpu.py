@@ -72,6 +72,27 @@ def _check_segments(p, N):
         assert (own == 1).all(), "a column is not owned exactly once"
 
 
+def _occupancy(p, N):
+    cap = p["block"] * p["vec"] * p["slots"]
+    return p["tile_elems"] / cap if p["packed"] else N / (p["col_blocks"] * cap)
+
+
+def _check_flat(f, M, N, xdt):
+    """The forward walks flat exactly for rows of a whole number of 16-byte
+    vectors, at most 8,192 long, that its tiles fit poorly: filled below
+    0.9 (float32 x) or 0.7 (2-byte x), or, for 2-byte x, packed tiles of two
+    or more slots; its grid is one workgroup per 1,024 vectors, at most 256."""
+    v = VEC[xdt]
+    occ = _occupancy(f, N)
+    poor = occ < 0.9 if xdt == "f32" else (occ < 0.7 or (f["packed"] and f["slots"] >= 2))
+    want = N % v == 0 and N <= 8192 and poor
+    assert f["flat"] == int(want)
+    if want:
+        assert f["flat_grid"] == min(256, -(-(M * N // v) // 1024))
+    else:
+        assert f["flat_grid"] == 0
+
+
 @settings(max_examples=300, deadline=None)
 @given(M=st.integers(1, 1 << 22), N=st.integers(1, 1 << 20), xdt=st.sampled_from(["f32", "bf16", "f16"]))
 def test_plans_hold_their_invariants(dyt, M, N, xdt):
@@ -84,8 +105,11 @@ def test_plans_hold_their_invariants(dyt, M, N, xdt):
         _check_tiling(p, M, N, v, True)
         if not p["packed"]:
             _check_segments(p, N)
+    _check_flat(f, M, N, xdt)
+    assert (b["flat"], b["flat_grid"]) == (f["flat"], f["flat_grid"])
     e = dyt.dyt_get_plan(M, N, xdt, "f32", False)
     _check_tiling(e, M, N, v, False)
+    assert e["flat"] == 0 and e["flat_grid"] == 0
     for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "bwd_grid", "ws_row", "ws_bytes"):
         assert e[key] == b[key], key
     assert b["ws_row"] >= 2 * (N if b["packed"] else b["tile_elems"]) + 1 and b["ws_row"] % 4 == 0
@@ -114,3 +138,20 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     assert cols.max() >= N
     used2, off2, _ = _slot_rule(L, V, K)
     assert (col_base + off2[:, None] + np.arange(V)[None, :]).max() < N
+
+
+@pytest.mark.parametrize("N,xdt,flat", [
+    (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
+    (3072, "bf16", 0), (4096, "bf16", 0), (32, "bf16", 0), (7168, "bf16", 0), (5120, "bf16", 0),
+    (4095, "bf16", 0),
+    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 0),
+    (2560, "f16", 1)])
+def test_flat_forward_choice(dyt, N, xdt, flat):
+    """At 2^27 elements the measured choice: the flat walk for widths the
+    tiles fill poorly, the tiles where they fill (or N is not a whole number
+    of vectors, or gamma/beta would not fit the LDS copy)."""
+    M = (1 << 27) // N
+    f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
+    assert f["flat"] == flat
+    _check_flat(f, M, N, xdt)
+    assert dyt.dyt_get_forward_plan(M, N, xdt, "f32", False)["flat"] == 0
