@@ -19,6 +19,8 @@
  *   - "Small widths": narrow rows are packed several to a workgroup tile
  *     (whenever two or more fit a 4096-element tile, so every width up to
  *     256 qualifies); wider rows are cut into row segments, one per tile.
+ *     The forward walks contiguous rows that these tiles fit poorly as one
+ *     run of 16-byte vectors instead (dyt_plan.flat).
  *   - "Padding": lanes past the end of the data are removed from the
  *     reductions after the arithmetic, so alpha = +inf cannot inject
  *     tanh(inf * 0) = NaN into dgamma, dbeta or dalpha.
