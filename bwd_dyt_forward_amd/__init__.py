@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     dyt_forward,
     dyt_forward_residual,
     dyt_get_forward_plan,
+    dyt_get_forward_residual_plan,
     dyt_get_plan,
     dyt_status_string,
     lib,
@@ -37,4 +38,5 @@ __all__ = [
     "dyt_backward_workspace_size", "dyt_forward_residual", "dyt_backward_residual",
     "dyt_backward_residual_partials",
     "dyt_status_string", "dyt_abi_version", "dyt_get_plan", "dyt_get_forward_plan",
+    "dyt_get_forward_residual_plan",
 ]

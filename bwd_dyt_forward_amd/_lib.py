@@ -70,6 +70,7 @@ SIGNATURES = {
     "dyt_abi_version": (_int, []),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
     "dyt_get_forward_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
+    "dyt_get_forward_residual_plan": (_int, [_i64, _i64, _int, _int, ctypes.POINTER(DytPlan)]),
 }
 
 
@@ -342,6 +343,15 @@ def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_access: bool = Tru
     st = lib.dyt_get_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
                           1 if vector_access else 0, ctypes.byref(p))
     _check("dyt_get_plan", st)
+    return {name: getattr(p, name) for name, _ in DytPlan._fields_}
+
+
+def dyt_get_forward_residual_plan(M: int, N: int, x_dtype, param_dtype) -> dict:
+    """The residual-fused forward's plan (its tiles or flat walk, and grid)."""
+    p = DytPlan()
+    st = lib.dyt_get_forward_residual_plan(int(M), int(N), _code(x_dtype), _code(param_dtype),
+                                           ctypes.byref(p))
+    _check("dyt_get_forward_residual_plan", st)
     return {name: getattr(p, name) for name, _ in DytPlan._fields_}
 
 

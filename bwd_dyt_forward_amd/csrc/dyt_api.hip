@@ -207,6 +207,12 @@ double occupancy(const Plan& p, int64_t N) {
 // (2,560 / 4,104 / 5,120: 180-184 us against 199-236 us), while tiles that
 // fit stay ahead (bf16 4,096: 82.5 against 89 us; 3,072 in two 2,048-wide
 // segments, 0.75 filled: 86 against 88 us; 7,168 at 0.88: 86 against 90 us).
+// The residual-fused forward (two inputs, two outputs) walks flat whenever
+// its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
+// the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:
+// 181.6 / 179.7 against 180.9 / 180.6 us) and faster everywhere else (bf16
+// 1,536 / 2,560 / 3,072 / 4,104: 181-182 us against 191-227 us; f32 2,560 /
+// 4,104 / 5,120: 370-380 us against 402-512 us).
 // The forward has no reduction, so the choice changes no result bit.
 #ifndef DYT_FLAT_OCC_2B
 #define DYT_FLAT_OCC_2B 0.7
@@ -281,9 +287,11 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         }
         if (best_occ >= occ + DYT_OCC_GAIN) p = best;
     }
-    const bool poor_fit = sx == 2 ? occupancy(p, N) < DYT_FLAT_OCC_2B || (p.packed && p.slots >= 2)
-                                  : occupancy(p, N) < DYT_FLAT_OCC_4B;
-    if (dir == Dir::Fwd && N % vmax == 0 && N <= kFlatMaxN && poor_fit) {
+    const double fill = occupancy(p, N);
+    const bool k2 = sx == 2 && p.packed && p.slots >= 2;
+    const bool poor_fit = dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || k2 : fill < DYT_FLAT_OCC_4B)
+                                          : fill < 1.0 - 1e-9 || k2;
+    if (dir != Dir::Bwd && N % vmax == 0 && N <= kFlatMaxN && poor_fit) {
         const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);
         p.flat = true;
         p.flat_grid = std::min<int64_t>(groups, DYT_FLAT_GRID);
@@ -482,13 +490,13 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
-    if (base.flat && !strided && !res) {
+    if (base.flat && !strided) {
         FlatGeo f;
         f.nvec = M * N / (16 / sx);
         f.N = (int32_t)N;
         f.cstep = (int32_t)((base.flat_grid * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {
-            return dyt::host::launch_forward_flat<decltype(xt)>(param_dtype, base, f, a, s);
+            return dyt::host::launch_forward_flat<decltype(xt)>(param_dtype, res, base, f, a, s);
         });
         if (!ok) return DYT_ERR_INVALID_ARG;   // not reachable: the plan checked N
         return hip_status();
@@ -579,6 +587,23 @@ int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int
     fill_plan(p, out);
     out->flat = base.flat && vector_access != 0;
     out->flat_grid = out->flat ? base.flat_grid : 0;
+    out->fwd_grid = p.grid;
+    out->bwd_grid = 0;
+    out->ws_row = 0;
+    out->fin_grid = 0;
+    out->ws_bytes = 0;
+    return DYT_OK;
+}
+
+int dyt_get_forward_residual_plan(int64_t M, int64_t N, int x_dtype, int param_dtype,
+                                  dyt_plan* out) {
+    if (!out) return DYT_ERR_INVALID_ARG;
+    Plan p;
+    const int st = make_plan(M, N, x_dtype, param_dtype, Dir::ResFwd, p);
+    if (st != DYT_OK) return st;
+    fill_plan(p, out);
+    out->flat = p.flat;
+    out->flat_grid = p.flat_grid;
     out->fwd_grid = p.grid;
     out->bwd_grid = 0;
     out->ws_row = 0;

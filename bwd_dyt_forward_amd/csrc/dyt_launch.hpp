@@ -78,9 +78,11 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
 template <typename XT>
 bool launch_backward(int pdt, bool res, bool strided, const Plan& p, const Geo& g,
                      const BwdPtrs& a, hipStream_t s);
-// The flat forward (contiguous, no residual) for a plan with p.flat set.
+// The flat forward (contiguous; res: the residual add fused) for a plan with
+// p.flat set.
 template <typename XT>
-bool launch_forward_flat(int pdt, const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s);
+bool launch_forward_flat(int pdt, bool res, const Plan& p, const FlatGeo& f, const FwdPtrs& a,
+                         hipStream_t s);
 
 }  // namespace host
 }  // namespace dyt

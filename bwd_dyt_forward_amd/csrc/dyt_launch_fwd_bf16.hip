@@ -4,6 +4,6 @@
 namespace dyt {
 namespace host {
 template bool launch_forward<bf16_t>(int, bool, bool, const Plan&, const Geo&, const FwdPtrs&, hipStream_t);
-template bool launch_forward_flat<bf16_t>(int, const Plan&, const FlatGeo&, const FwdPtrs&, hipStream_t);
+template bool launch_forward_flat<bf16_t>(int, bool, const Plan&, const FlatGeo&, const FwdPtrs&, hipStream_t);
 }  // namespace host
 }  // namespace dyt

@@ -134,22 +134,28 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
     }
 }
 
-template <typename XT, typename PT>
+template <typename XT, typename PT, bool RES>
 bool launch_flat_pt(const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
     const size_t lds = 2 * (size_t)f.N * sizeof(float);   // gamma and beta as float32
-    hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, false>), dim3((unsigned)p.flat_grid),
-                       dim3(kBlock), lds, s, (const XT*)a.x, (const XT*)nullptr, (const PT*)a.alpha,
-                       (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)nullptr, f);
+    hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, RES>), dim3((unsigned)p.flat_grid),
+                       dim3(kBlock), lds, s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
+                       (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
     return true;
 }
 
+template <typename XT, typename PT>
+bool launch_flat_res(bool res, const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
+    return res ? launch_flat_pt<XT, PT, true>(p, f, a, s) : launch_flat_pt<XT, PT, false>(p, f, a, s);
+}
+
 template <typename XT>
-bool launch_forward_flat(int pdt, const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
+bool launch_forward_flat(int pdt, bool res, const Plan& p, const FlatGeo& f, const FwdPtrs& a,
+                         hipStream_t s) {
     if (!p.flat || f.N % (int)(16 / sizeof(XT)) != 0) return false;
     switch (pdt) {
-        case DYT_F32: return launch_flat_pt<XT, float>(p, f, a, s);
-        case DYT_BF16: return launch_flat_pt<XT, bf16_t>(p, f, a, s);
-        case DYT_F16: return launch_flat_pt<XT, f16_t>(p, f, a, s);
+        case DYT_F32: return launch_flat_res<XT, float>(res, p, f, a, s);
+        case DYT_BF16: return launch_flat_res<XT, bf16_t>(res, p, f, a, s);
+        case DYT_F16: return launch_flat_res<XT, f16_t>(res, p, f, a, s);
         default: return false;
     }
 }

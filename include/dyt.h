@@ -292,6 +292,15 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
 int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype,
                          int vector_access, dyt_plan* out);
 
+/*
+ * The residual-fused forward's geometry (dyt_forward_residual), which has a
+ * row of its own in the tile table and its own flat-walk rule (flat
+ * whenever the tiles leave a slot empty). Same struct and conventions as
+ * dyt_get_forward_plan, for the contiguous layout that entry point takes.
+ */
+int dyt_get_forward_residual_plan(int64_t M, int64_t N, int x_dtype, int param_dtype,
+                                  dyt_plan* out);
+
 #ifdef __cplusplus
 }
 #endif

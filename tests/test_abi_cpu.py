@@ -31,7 +31,8 @@ def test_header_declares_expected_entry_points():
         "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
         "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
-        "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided"])
+        "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided",
+        "dyt_get_forward_residual_plan"])
 
 
 def test_library_exports_every_declared_symbol(dyt):

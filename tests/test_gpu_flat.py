@@ -5,7 +5,8 @@ oracle element by element, bit for bit against the tiled kernels (a
 row-strided launch of the same shape runs the tiles), on problems whose last
 vector group is partial, with guard canaries around y, at a base one element
 off 16-byte alignment, at the largest width the LDS copy allows, and on a
-problem above 2^31 elements."""
+problem above 2^31 elements; the residual-fused forward walks flat in the
+same way (h exact, y equal to the tiled forward of h)."""
 import numpy as np
 import pytest
 import torch
@@ -160,3 +161,52 @@ def test_flat_forward_above_2_31_elements(dyt):
         assert np.array_equal(_bits(yv), _bits(y[r0:r0 + 3]))
     del x, y
     torch.cuda.empty_cache()
+
+
+RES_SHAPES = [  # residual-fused forward: every one walks flat (asserted)
+    (1000, 2560, "bf16", "f32"),
+    (4099, 3072, "bf16", "bf16"),   # tiles 0.75 filled: the plain forward keeps them, this one not
+    (777, 4104, "f32", "f32"),
+    (129, 1040, "bf16", "f16"),
+    (3, 1032, "f16", "f32"),
+    (300, 7372, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("M,N,xdt,pdt", RES_SHAPES)
+def test_flat_residual_forward(dyt, M, N, xdt, pdt):
+    """h = x + r exactly the oracle's rounded sum, y within tolerance of the
+    oracle on h and bit for bit the tiled forward of h (row-strided launch);
+    canaries around h and y untouched."""
+    plan = dyt.dyt_get_forward_residual_plan(M, N, xdt, pdt)
+    log(f"[flat residual] M={M} N={N} x={xdt} p={pdt} plan={plan}")
+    assert plan["flat"] == 1
+    inp = workloads.custom(M, N, xdt, pdt, alpha=0.6, seed=N + 3 * M)
+    r, _ = workloads.residual_pair(M, N, xdt, N)
+    xt, pt = TORCH_DT[xdt], TORCH_DT[pdt]
+    x = torch.from_numpy(inp.x).cuda().to(xt)
+    rt = torch.from_numpy(np.ascontiguousarray(r)).cuda().to(xt)
+    a = torch.from_numpy(inp.alpha).cuda().to(pt)
+    g = torch.from_numpy(inp.gamma).cuda().to(pt)
+    b = torch.from_numpy(inp.beta).cuda().to(pt)
+    pad = 2048
+    hb = torch.full((M * N + 2 * pad,), CANARY, dtype=xt, device="cuda")
+    yb = torch.full((M * N + 2 * pad,), CANARY, dtype=xt, device="cuda")
+    h = hb[pad:pad + M * N].view(M, N)
+    y = yb[pad:pad + M * N].view(M, N)
+    dyt.dyt_forward_residual(x, rt, a, g, b, h=h, y=y)
+    torch.cuda.synchronize()
+    for buf in (hb, yb):
+        assert bool((buf[:pad] == CANARY).all()) and bool((buf[pad + M * N:] == CANARY).all())
+    h_ref, f = dyt_oracle.forward_residual(inp.x, r, inp.alpha, inp.gamma, inp.beta, xdt)
+    assert_reports(f"flat residual M={M} N={N}",
+                   [compare.check_exact(to_np(h), h_ref, "h"),
+                    compare.check_y(to_np(y), f.y, f.scale, xdt)])
+    hs_buf = torch.empty((M, N + 8), dtype=xt, device="cuda")
+    hs = hs_buf[:, :N]
+    hs.copy_(h)
+    ys_buf = torch.empty((M, N + 8), dtype=xt, device="cuda")
+    ys = ys_buf[:, :N]
+    dyt.dyt_forward(hs, a, g, b, y=ys)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ys), _bits(y))

@@ -77,14 +77,20 @@ def _occupancy(p, N):
     return p["tile_elems"] / cap if p["packed"] else N / (p["col_blocks"] * cap)
 
 
-def _check_flat(f, M, N, xdt):
+def _check_flat(f, M, N, xdt, residual=False):
     """The forward walks flat exactly for rows of a whole number of 16-byte
     vectors, at most 8,192 long, that its tiles fit poorly: filled below
     0.9 (float32 x) or 0.7 (2-byte x), or, for 2-byte x, packed tiles of two
-    or more slots; its grid is one workgroup per 1,024 vectors, at most 256."""
+    or more slots; the residual-fused forward whenever its tiles leave a slot
+    empty or are such packed tiles. The grid is one workgroup per 1,024
+    vectors, at most 256."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
-    poor = occ < 0.9 if xdt == "f32" else (occ < 0.7 or (f["packed"] and f["slots"] >= 2))
+    k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
+    if residual:
+        poor = occ < 1 - 1e-9 or k2
+    else:
+        poor = occ < 0.9 if xdt == "f32" else (occ < 0.7 or k2)
     want = N % v == 0 and N <= 8192 and poor
     assert f["flat"] == int(want)
     if want:
@@ -107,6 +113,9 @@ def test_plans_hold_their_invariants(dyt, M, N, xdt):
             _check_segments(p, N)
     _check_flat(f, M, N, xdt)
     assert (b["flat"], b["flat_grid"]) == (f["flat"], f["flat_grid"])
+    r = dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")
+    _check_tiling(r, M, N, v, True)
+    _check_flat(r, M, N, xdt, residual=True)
     e = dyt.dyt_get_plan(M, N, xdt, "f32", False)
     _check_tiling(e, M, N, v, False)
     assert e["flat"] == 0 and e["flat_grid"] == 0
@@ -155,3 +164,15 @@ def test_flat_forward_choice(dyt, N, xdt, flat):
     assert f["flat"] == flat
     _check_flat(f, M, N, xdt)
     assert dyt.dyt_get_forward_plan(M, N, xdt, "f32", False)["flat"] == 0
+
+
+@pytest.mark.parametrize("N,xdt,flat", [
+    (2560, "bf16", 1), (3072, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1),
+    (4096, "bf16", 0), (32, "bf16", 1), (4095, "bf16", 0), (2560, "f32", 1), (4104, "f32", 1)])
+def test_flat_residual_forward_choice(dyt, N, xdt, flat):
+    """The residual-fused forward at 2^27 elements: flat unless its tiles are
+    full (and then not 2-byte packed tiles of two or more slots)."""
+    M = (1 << 27) // N
+    r = dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")
+    assert r["flat"] == flat
+    _check_flat(r, M, N, xdt, residual=True)
