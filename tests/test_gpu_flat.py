@@ -210,3 +210,39 @@ def test_flat_residual_forward(dyt, M, N, xdt, pdt):
     dyt.dyt_forward(hs, a, g, b, y=ys)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(ys), _bits(y))
+
+
+@pytest.mark.parametrize("M,N,xdt", [(1000, 2560, "bf16"), (777, 4104, "f32")])
+def test_flat_forward_ieee_special_values(dyt, M, N, xdt):
+    """alpha = +inf on a flat shape: real elements with x = 0 give NaN
+    (tanh(inf * 0)), float32 subnormal x gives +-gamma + beta (no flush),
+    every other element +-gamma + beta; matches the oracle element by element
+    and the tiled kernels bit for bit."""
+    inp = workloads.custom(M, N, xdt, "f32", alpha=float("inf"), seed=N + 1)
+    x = inp.x.copy()
+    rng = np.random.default_rng(5)
+    zi = rng.integers(0, M * N, 64)
+    x.reshape(-1)[zi] = 0.0
+    if xdt == "f32":
+        si = rng.integers(0, M * N, 64)
+        si = si[~np.isin(si, zi)]
+        x.reshape(-1)[si] = np.float32(1e-41) * np.where(rng.random(si.size) < 0.5, -1, 1).astype(np.float32)
+    assert dyt.dyt_get_forward_plan(M, N, xdt, "f32")["flat"] == 1
+    xt = TORCH_DT[xdt]
+    xg = torch.from_numpy(x).cuda().to(xt)
+    a = torch.full((1,), float("inf"), device="cuda")
+    g = torch.from_numpy(inp.gamma).cuda()
+    b = torch.from_numpy(inp.beta).cuda()
+    y = dyt.dyt_forward(xg, a, g, b)
+    xs_buf = torch.empty((M, N + 8), dtype=xt, device="cuda")
+    xs = xs_buf[:, :N]
+    xs.copy_(xg)
+    ys_buf = torch.empty((M, N + 8), dtype=xt, device="cuda")
+    ys = ys_buf[:, :N]
+    dyt.dyt_forward(xs, a, g, b, y=ys)
+    torch.cuda.synchronize()
+    f = dyt_oracle.forward(x, [np.inf], inp.gamma, inp.beta)
+    assert_reports(f"flat alpha=inf M={M} N={N}", [compare.check_y(to_np(y), f.y, f.scale, xdt)])
+    yn = to_np(y)
+    assert np.isnan(yn.reshape(-1)[zi]).all() and np.isnan(yn).sum() == np.unique(zi).size
+    assert np.array_equal(_bits(ys), _bits(y))
