@@ -570,7 +570,23 @@ WIDTH_CASES = ([("bf16", n, 0) for n in (768, 1500, 1536, 2048, 2560, 3072, 4095
                + [("bf16", 4096, 1), ("bf16", 2560, 1), ("bf16", 32, 1), ("f32", 100, 1)])
 
 
-def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, rounds: int = 3) -> None:
+def parse_width_cases(spec: str | None) -> list:
+    """'bf16:2560,f32:4104+1' -> [("bf16", 2560, 0), ("f32", 4104, 1)] (a '+1'
+    suffix: bases one element off alignment); None -> every default case."""
+    if not spec:
+        return list(WIDTH_CASES)
+    out = []
+    for item in spec.split(","):
+        xdt, n = item.strip().split(":")
+        off = 1 if n.endswith("+1") else 0
+        if xdt not in ("bf16", "f32"):
+            raise ValueError(f"--width-cases: x dtype must be bf16 or f32, got {xdt!r}")
+        out.append((xdt, int(n[:-2] if off else n), off))
+    return out
+
+
+def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, rounds: int = 3,
+                  cases=None) -> None:
     """Row widths that do not fill 4,096-element tiles, ragged rows and bases
     one element off 16-byte alignment, each at 2^27 elements (synthetic
     normal data, fp32 parameters): median over `rounds` of the mean forward
@@ -582,7 +598,7 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
             "backward = pass 1 + pass 2. Occupancy = share of the tile's vector slots that carry data.",
             "", "| x | N | M | base | fwd us | fwd GB/s | bwd us | bwd GB/s | fwd plan | bwd plan |",
             "|---|---:|---:|---|---:|---:|---:|---:|---|---|"]
-    for xdt, N, off in WIDTH_CASES:
+    for xdt, N, off in (WIDTH_CASES if cases is None else cases):
         M = (1 << 27) // N
         dt = torch.bfloat16 if xdt == "bf16" else torch.float32
         gen = torch.Generator(device="cuda").manual_seed(N)
@@ -675,6 +691,8 @@ def main() -> int:
                     help="also time every workload shape and write a Markdown table to FILE")
     ap.add_argument("--widths", metavar="FILE", default=None,
                     help="also time awkward row widths and unaligned bases and write a Markdown table to FILE")
+    ap.add_argument("--width-cases", default=None,
+                    help="with --widths: only these cases, e.g. 'bf16:2560,f32:4104,bf16:4096+1'")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -707,7 +725,7 @@ def main() -> int:
     if args.all_configs:
         report_all(dyt, torch, args.all_configs)
     if args.widths:
-        report_widths(dyt, torch, args.widths)
+        report_widths(dyt, torch, args.widths, cases=parse_width_cases(args.width_cases))
 
     tensor_bytes = main_res["M"] * main_res["N"] * (2 if main_res["x_dtype"] in ("bf16", "f16") else 4)
     ceiling = copy_ceiling(torch, tensor_bytes)

@@ -52,3 +52,11 @@ def test_stream_reference_library_exports_and_rejects_bad_arguments():
     assert lib.stream_ref_copy(a, a + 0x1000, 63, None) == 1          # not a multiple of 16
     assert lib.stream_ref_copy(a + 4, a + 0x1000, 64, None) == 1      # misaligned
     assert lib.stream_ref_2in1out(a, None, a + 0x1000, 64, None) == 1
+
+
+def test_width_case_filter():
+    assert bench.parse_width_cases("bf16:2560,f32:4104+1") == [("bf16", 2560, 0), ("f32", 4104, 1)]
+    assert bench.parse_width_cases(None) == list(bench.WIDTH_CASES)
+    import pytest
+    with pytest.raises(ValueError):
+        bench.parse_width_cases("f16:2560")
