@@ -202,11 +202,14 @@ double occupancy(const Plan& p, int64_t N) {
 // slots (the 2-byte forward streams slower from those at any fill); for
 // float32 x, tiles filled below DYT_FLAT_OCC_4B. Measured on MI355X at 2^27
 // elements (interleaved medians of 20-launch means): the flat walk streams
-// bf16 at 6.0-6.15 TB/s whatever the width (rows of 768 / 1,536 / 2,560 /
-// 4,104: 87-89 us against 92-97 us tiled) and float32 at 5.8-5.9 TB/s
-// (2,560 / 4,104 / 5,120: 180-184 us against 199-236 us), while tiles that
-// fit stay ahead (bf16 4,096: 82.5 against 89 us; 3,072 in two 2,048-wide
-// segments, 0.75 filled: 86 against 88 us; 7,168 at 0.88: 86 against 90 us).
+// bf16 at 6.3-6.55 TB/s whatever the width (rows of 768 / 1,536 / 2,048 /
+// 2,560 / 4,104: 82-86 us against 90-97 us tiled) and float32 at 5.9 TB/s
+// (2,560 / 4,104 / 5,120: 181-183 us against 199-236 us). The thresholds
+// were set when the flat walk still stored nontemporally and ran 87-89 us,
+// so tiles that fit kept the lead then (bf16 4,096: 82.5 against 89 us;
+// 3,072 in two 2,048-wide segments, 0.75 filled: 86 against 88 us; 7,168 at
+// 0.88: 86 against 90 us); with its present store rule (dyt_kernels.hpp,
+// fwd_flat_store_nt) it matches full tiles, and 3,072 measured 86.7 us tiled.
 // The residual-fused forward (two inputs, two outputs) walks flat whenever
 // its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
 // the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:

@@ -101,9 +101,11 @@ struct FinGeo {
 // Raw<XT, V>: the V elements of one access as loaded from memory (one
 // 16-byte vector, or one element). Loads return raw registers so that every
 // load of a tile is issued before any value is needed. x, dy, y and dx are
-// each touched exactly once, so every access carries the nontemporal hint
-// (streaming through the caches instead of displacing other data); on
-// MI355X this lifts a plain 16-byte copy from ~5.7 to ~6.4 TB/s.
+// each touched exactly once, so the loads and the backward's stores carry
+// the nontemporal hint (streaming through the caches instead of displacing
+// other data; on MI355X this lifts a plain 16-byte copy from ~5.7 to ~6.4
+// TB/s); the forward's stores take the hint only where it measured faster
+// (fwd_tile_store_nt, fwd_flat_store_nt).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // The same vectors as seen in memory: only element alignment is assumed.
@@ -467,8 +469,24 @@ __device__ __forceinline__ void fwd_load(const XT* __restrict__ x, const XT* __r
         }
 }
 
-// v = x (+ r, rounded to XT and stored to h when RES)
-template <typename XT, int V, bool RES>
+// Store hint of the forward's outputs (y, and h with the residual add).
+// Loads always stream nontemporally. Stores: plain write-back stores where
+// each thread stores one vector per tile (K = 1) and in the flat walk over
+// 2-byte data, nontemporal otherwise. Measured on MI355X, alone and in
+// back-to-back forward + backward steps, bit-identical outputs: float16
+// 32768 x 4096 (K = 1 tiles) 93.9 -> 82.0 us alone, step 236.6 -> 225.8 us;
+// the flat walk over bfloat16 / float16 rows of 2,560 89.1 / 86.4 -> 83.6 /
+// 83.5 us alone, step -2.7% / -2.2%; but float32 flat rows of 5,120 182.0 ->
+// 189.2 us and the residual-fused forward at K = 2 178.4 -> 185.5 us with
+// plain stores, so those keep the hint. (For the bfloat16 and float32 K = 1
+// tiles the compiler had already emitted plain stores.)
+template <typename XT, int K>
+constexpr bool fwd_tile_store_nt() { return DYT_FWD_NT && K >= 2; }
+template <typename XT, bool RES>
+constexpr bool fwd_flat_store_nt() { return DYT_FWD_NT && (RES || sizeof(XT) == 4); }
+
+// v = x (+ r, rounded to XT and stored to h when RES; store hint ST_NT)
+template <typename XT, int V, bool RES, bool ST_NT>
 __device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
                                           const typename Raw<XT, V>::T& rr, XT* __restrict__ h,
                                           float (&v)[V]) {
@@ -480,7 +498,7 @@ __device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
 #pragma unroll
         for (int e = 0; e < V; ++e) v[e] += rv[e];
         const typename R::T hr = R::pack(v);
-        R::template store_raw<DYT_FWD_NT>(h, hr);
+        R::template store_raw<ST_NT>(h, hr);
         R::unpack(hr, v);
     }
 }
@@ -496,12 +514,13 @@ __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t at = bo + j * ao.upitch + ao.off[k];
+            constexpr bool kStNt = fwd_tile_store_nt<XT, K>();
             float v[V];
-            fwd_input<XT, V, RES>(rx[j][k], rr[j][k], h + at, v);
+            fwd_input<XT, V, RES, kStNt>(rx[j][k], rr[j][k], h + at, v);
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-            Raw<XT, V>::template store<DYT_FWD_NT>(y + at, v);
+            Raw<XT, V>::template store<kStNt>(y + at, v);
         }
 }
 
@@ -599,7 +618,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
                 if (n >= V) {
                     typename R::T rr{};
                     if constexpr (RES) rr = R::load(r + oi);
-                    fwd_input<XT, V, RES>(R::load(x + oi), rr, h + oo, v);
+                    fwd_input<XT, V, RES, fwd_tile_store_nt<XT, K>()>(R::load(x + oi), rr, h + oo, v);
                 } else {
                     load_partial<XT, V>(x + oi, n, v);
                     if constexpr (RES) {
@@ -613,7 +632,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-                if (n >= V) R::store(y + oo, v);
+                if (n >= V) R::template store<fwd_tile_store_nt<XT, K>()>(y + oo, v);
                 else store_partial<XT, V>(y + oo, n, v);
             }
         }
@@ -663,7 +682,8 @@ __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>
                                          int col, const float* sg, const float* sb, float alpha) {
     constexpr int V = 16 / sizeof(XT);
     float v[V], gm[V], bt[V];
-    fwd_input<XT, V, RES>(rx, rr, h + at, v);
+    constexpr bool kStNt = fwd_flat_store_nt<XT, RES>();
+    fwd_input<XT, V, RES, kStNt>(rx, rr, h + at, v);
     // col is a multiple of V (and so of 4): 16-byte LDS reads
 #pragma unroll
     for (int e = 0; e < V; e += 4) {
@@ -674,7 +694,7 @@ __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) v[e] = __builtin_fmaf(gm[e], dyt_tanh<ACC>(alpha * v[e]), bt[e]);
-    Raw<XT, V>::template store<DYT_FWD_NT>(y + at, v);
+    Raw<XT, V>::template store<kStNt>(y + at, v);
 }
 
 // Computes and stores a loaded group, then moves each column on to this
