@@ -21,7 +21,7 @@ DYT_BF16 = 1
 DYT_F16 = 2
 DYT_OK = 0
 # DYT_ABI_VERSION of include/dyt.h that the signatures and DytPlan below mirror
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16, torch.float16: DYT_F16}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
@@ -43,6 +43,7 @@ class DytPlan(ctypes.Structure):
         ("fwd_grid", ctypes.c_int64), ("bwd_grid", ctypes.c_int64), ("ws_row", ctypes.c_int64),
         ("fin_grid", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
         ("flat", ctypes.c_int64), ("flat_grid", ctypes.c_int64),
+        ("flat_aligned_only", ctypes.c_int64),
     ]
 
 

@@ -198,18 +198,23 @@ double occupancy(const Plan& p, int64_t N) {
 // The flat forward (dyt_fwd_flat_kernel) serves contiguous rows whose length
 // is a multiple of the vector width and at most kFlatMaxN (gamma and beta as
 // float32 in at most 64 KB of LDS) when the tiles fit the rows poorly: for
-// 2-byte x, tiles filled below DYT_FLAT_OCC_2B or packed tiles of K >= 2
-// slots (the 2-byte forward streams slower from those at any fill); for
-// float32 x, tiles filled below DYT_FLAT_OCC_4B. Measured on MI355X at 2^27
-// elements (interleaved medians of 20-launch means): the flat walk streams
-// bf16 at 6.3-6.55 TB/s whatever the width (rows of 768 / 1,536 / 2,048 /
-// 2,560 / 4,104: 82-86 us against 90-97 us tiled) and float32 at 5.9 TB/s
-// (2,560 / 4,104 / 5,120: 181-183 us against 199-236 us). The thresholds
-// were set when the flat walk still stored nontemporally and ran 87-89 us,
-// so tiles that fit kept the lead then (bf16 4,096: 82.5 against 89 us;
-// 3,072 in two 2,048-wide segments, 0.75 filled: 86 against 88 us; 7,168 at
-// 0.88: 86 against 90 us); with its present store rule (dyt_kernels.hpp,
-// fwd_flat_store_nt) it matches full tiles, and 3,072 measured 86.7 us tiled.
+// 2-byte x, packed tiles (several rows each) at any fill and row segments
+// filled below DYT_FLAT_OCC_2B; for float32 x, tiles filled below
+// DYT_FLAT_OCC_4B. Measured on MI355X at 2^27 elements (interleaved medians
+// of 20-launch means, outputs bit-identical): the 2-byte flat walk (plain
+// stores, dyt_kernels.hpp fwd_flat_store_nt) against the tiles it replaces,
+// bf16 rows of 32 / 64 (packed, full): 81.4 / 81.4 against 83.7 / 85.4 us;
+// 768 / 1,536 / 2,048 (packed): 82.0 / 82.8 / 82.9 against 90-95 us; row
+// segments 3,072 / 5,120 filled 0.75 / 0.83: 84.5 / 87.1 against 85.8 /
+// 89.9 us; 2,560 / 4,104 (0.62 / 0.67): 84.0 / 85.6 against 97 / 95 us;
+// while row segments filled 0.88 or fully keep the lead (7,168: 85.6
+// against 89.0; 4,096 / 6,144 / 8,192: 82.0 / 82.4 / 85.3 against 84.9 /
+// 87.8 / 90.6 us). float32 flat rows of 2,560 / 4,104 / 5,120: 181-183 us
+// against 199-236 us tiled. At bases one element off 16-byte alignment the
+// packed one-slot tiles of full rows keep the lead (bf16 32 / 64 wide: 89.5 /
+// 90.9 against 92.3 / 92.6 us flat), while the flat walk keeps its own
+// (768 / 2,048 / 3,072 wide: 94.0-96.4 against 105.9-106.6 us), so the
+// former walk flat only from aligned bases (Plan::flat_aligned_only).
 // The residual-fused forward (two inputs, two outputs) walks flat whenever
 // its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
 // the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:
@@ -218,7 +223,7 @@ double occupancy(const Plan& p, int64_t N) {
 // 4,104 / 5,120: 370-380 us against 402-512 us).
 // The forward has no reduction, so the choice changes no result bit.
 #ifndef DYT_FLAT_OCC_2B
-#define DYT_FLAT_OCC_2B 0.7
+#define DYT_FLAT_OCC_2B 0.85
 #endif
 #ifndef DYT_FLAT_OCC_4B
 #define DYT_FLAT_OCC_4B 0.9
@@ -228,7 +233,13 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_GRID
 #define DYT_FLAT_GRID 256
 #endif
-constexpr int64_t kFlatMaxN = 8192;
+// Widest rows of the flat forward (gamma and beta as float32 in 64 KB of LDS;
+// 0 turns the flat walk off).
+#ifndef DYT_FLAT_MAX_N
+#define DYT_FLAT_MAX_N 8192
+#endif
+static_assert(DYT_FLAT_MAX_N <= 8192, "the flat forward stages 2 N floats in at most 64 KB of LDS");
+constexpr int64_t kFlatMaxN = DYT_FLAT_MAX_N;
 
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
@@ -292,12 +303,15 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     }
     const double fill = occupancy(p, N);
     const bool k2 = sx == 2 && p.packed && p.slots >= 2;
-    const bool poor_fit = dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || k2 : fill < DYT_FLAT_OCC_4B)
-                                          : fill < 1.0 - 1e-9 || k2;
+    const bool poor_fit =
+        dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B)
+                        : fill < 1.0 - 1e-9 || k2;
     if (dir != Dir::Bwd && N % vmax == 0 && N <= kFlatMaxN && poor_fit) {
         const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);
         p.flat = true;
         p.flat_grid = std::min<int64_t>(groups, DYT_FLAT_GRID);
+        p.flat_aligned_only = dir == Dir::Fwd && sx == 2 && p.packed && p.slots == 1 &&
+                              fill >= DYT_FLAT_OCC_2B;
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
@@ -493,7 +507,8 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
-    if (base.flat && !strided) {
+    const bool bases16 = aligned(a.x, 16) && aligned(a.y, 16);
+    if (base.flat && !strided && (bases16 || !base.flat_aligned_only)) {
         FlatGeo f;
         f.nvec = M * N / (16 / sx);
         f.N = (int32_t)N;
@@ -540,6 +555,7 @@ void fill_plan(const Plan& p, dyt_plan* out) {
     out->tiles = p.tiles;
     out->flat = 0;
     out->flat_grid = 0;
+    out->flat_aligned_only = 0;
 }
 
 }  // namespace
@@ -572,6 +588,7 @@ int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_
     fill_plan(p, out);
     out->flat = fbase.flat && vector_access != 0;
     out->flat_grid = out->flat ? fbase.flat_grid : 0;
+    out->flat_aligned_only = out->flat && fbase.flat_aligned_only;
     out->fwd_grid = fbase.grid;
     out->bwd_grid = p.grid;
     out->ws_row = p.ld;
@@ -590,6 +607,7 @@ int dyt_get_forward_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int
     fill_plan(p, out);
     out->flat = base.flat && vector_access != 0;
     out->flat_grid = out->flat ? base.flat_grid : 0;
+    out->flat_aligned_only = out->flat && base.flat_aligned_only;
     out->fwd_grid = p.grid;
     out->bwd_grid = 0;
     out->ws_row = 0;
@@ -607,6 +625,7 @@ int dyt_get_forward_residual_plan(int64_t M, int64_t N, int x_dtype, int param_d
     fill_plan(p, out);
     out->flat = p.flat;
     out->flat_grid = p.flat_grid;
+    out->flat_aligned_only = p.flat_aligned_only;
     out->fwd_grid = p.grid;
     out->bwd_grid = 0;
     out->ws_row = 0;

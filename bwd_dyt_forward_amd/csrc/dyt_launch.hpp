@@ -41,6 +41,9 @@ struct Plan {
     // launches keep the tiles above.
     bool flat = false;
     int64_t flat_grid = 0;
+    // The flat walk only where x and y start 16-byte aligned (2-byte packed
+    // tiles of one full slot, which stay ahead at other bases).
+    bool flat_aligned_only = false;
 };
 
 // Device pointers of one launch; r/h (forward) and dres (backward) are null

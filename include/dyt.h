@@ -19,8 +19,8 @@
  *   - "Small widths": narrow rows are packed several to a workgroup tile
  *     (whenever two or more fit a 4096-element tile, so every width up to
  *     256 qualifies); wider rows are cut into row segments, one per tile.
- *     The forward walks contiguous rows that these tiles fit poorly as one
- *     run of 16-byte vectors instead (dyt_plan.flat).
+ *     The forward walks contiguous rows as one run of 16-byte vectors
+ *     instead where that measured faster than these tiles (dyt_plan.flat).
  *   - "Padding": lanes past the end of the data are removed from the
  *     reductions after the arithmetic, so alpha = +inf cannot inject
  *     tanh(inf * 0) = NaN into dgamma, dbeta or dalpha.
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 4
+#define DYT_ABI_VERSION 5
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -274,10 +274,14 @@ typedef struct dyt_plan {
     int64_t flat;          /* forward: 1 if a contiguous launch walks the problem as one
                               run of 16-byte vectors instead of the tiles above (rows whose
                               length is a multiple of vec, at most 8192, that the tiles
-                              fit poorly); row-strided launches use the tiles. 0 for the
+                              fit poorly, and 2-byte x in packed tiles); row-strided
+                              launches use the tiles. 0 for the
                               element-wise variant (vector_access = 0). dyt_get_plan
                               reports the forward's value; the backward always tiles */
     int64_t flat_grid;     /* workgroups of that flat forward, 0 if flat = 0 */
+    int64_t flat_aligned_only; /* 1 if that flat walk is taken only when x and y start
+                              16-byte aligned (2-byte x in packed tiles of one full slot,
+                              which the tiles serve faster at other bases); 0 otherwise */
 } dyt_plan;
 
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,

@@ -55,7 +55,7 @@ def test_no_cpu_fallback_in_product_path():
 
 
 def test_version_and_status_strings(dyt):
-    assert dyt.dyt_abi_version() == 4
+    assert dyt.dyt_abi_version() == 5
     names = [dyt.dyt_status_string(i) for i in range(6)]
     assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
                      "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]
@@ -195,7 +195,10 @@ def test_headline_plans_unchanged(dyt):
     f = dyt.dyt_get_forward_plan(4194304, 32, "bf16", "f32")
     assert (b["packed"], b["slots"], b["rows_per_tile"], b["tile_elems"], b["bwd_grid"]) == (1, 2, 128, 4096, 256)
     assert (f["packed"], f["slots"], f["rows_per_tile"], f["tile_elems"], f["fwd_grid"]) == (1, 1, 64, 2048, 512)
-    assert f["flat"] == 0 and dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")["flat"] == 0
+    # the 4,194,304 x 32 forward walks flat (packed 2-byte tiles) from 16-byte
+    # aligned bases; its tiles stay what row-strided and unaligned launches run
+    assert f["flat"] == 1 and f["flat_grid"] == 256 and f["flat_aligned_only"] == 1
+    assert dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")["flat"] == 0
 
 
 def test_tile_table_covers_every_dtype_width_and_size():

@@ -47,6 +47,9 @@ SHAPES = [
     (4097, 1032, "f16", "f32"),
     (1234, 4100, "f32", "bf16"),
     (300, 7372, "f32", "f32"),      # widest flat row: 59 KB of LDS
+    (5001, 32, "bf16", "f32"),      # packed tiles of one full slot (aligned bases only)
+    (3001, 64, "f16", "bf16"),
+    (999, 256, "bf16", "f32"),
 ]
 
 
@@ -90,12 +93,17 @@ def test_flat_forward_matches_oracle_and_tiles(dyt, M, N, xdt, pdt):
     assert bool((ys_buf[:, N:] == CANARY).all())
 
 
-@pytest.mark.parametrize("M,N,xdt", [(1000, 2560, "bf16"), (777, 4104, "f32"), (4097, 1032, "f16")])
-def test_flat_forward_unaligned_base(dyt, M, N, xdt):
-    """x and y one element off 16-byte alignment: the same bits as aligned."""
+@pytest.mark.parametrize("M,N,xdt,aligned_only", [
+    (1000, 2560, "bf16", 0), (777, 4104, "f32", 0), (4097, 1032, "f16", 0),
+    (5001, 32, "bf16", 1), (3001, 64, "f16", 1)])
+def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
+    """x and y one element off 16-byte alignment: the same bits as aligned
+    (full one-slot packed tiles then run the tiles instead of the walk)."""
     inp, x, a, g, b = _inputs(dyt, M, N, xdt, "f32", seed=N)
     xt = TORCH_DT[xdt]
-    assert dyt.dyt_get_forward_plan(M, N, xdt, "f32")["flat"] == 1
+    plan = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
+    log(f"[flat-unaligned] M={M} N={N} x={xdt} plan={plan}")
+    assert plan["flat"] == 1 and plan["flat_aligned_only"] == aligned_only
     y = dyt.dyt_forward(x, a, g, b)
     xb = torch.empty(M * N + 1, dtype=xt, device="cuda")
     xu = xb[1:].view(M, N)
@@ -107,6 +115,8 @@ def test_flat_forward_unaligned_base(dyt, M, N, xdt):
     torch.cuda.synchronize()
     assert np.array_equal(_bits(yu), _bits(y))
     assert float(yb[0]) == CANARY and float(yb[-1]) == CANARY
+    f = dyt_oracle.forward(inp.x, inp.alpha, inp.gamma, inp.beta)
+    assert_reports(f"flat unaligned M={M} N={N}", [compare.check_y(to_np(yu), f.y, f.scale, xdt)])
 
 
 def test_flat_forward_repeat_is_bitwise_stable(dyt):

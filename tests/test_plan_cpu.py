@@ -80,23 +80,26 @@ def _occupancy(p, N):
 def _check_flat(f, M, N, xdt, residual=False):
     """The forward walks flat exactly for rows of a whole number of 16-byte
     vectors, at most 8,192 long, that its tiles fit poorly: filled below
-    0.9 (float32 x) or 0.7 (2-byte x), or, for 2-byte x, packed tiles of two
-    or more slots; the residual-fused forward whenever its tiles leave a slot
-    empty or are such packed tiles. The grid is one workgroup per 1,024
-    vectors, at most 256."""
+    0.9 (float32 x); for 2-byte x, packed tiles or row segments filled below
+    0.85; the residual-fused forward whenever its tiles leave a slot empty or
+    are 2-byte packed tiles of two or more slots. The grid is one workgroup
+    per 1,024 vectors, at most 256. Only the plain forward's 2-byte packed
+    tiles of one slot filled at least 0.85 walk flat at aligned bases alone."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
     if residual:
         poor = occ < 1 - 1e-9 or k2
     else:
-        poor = occ < 0.9 if xdt == "f32" else (occ < 0.7 or k2)
+        poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
     want = N % v == 0 and N <= 8192 and poor
     assert f["flat"] == int(want)
     if want:
         assert f["flat_grid"] == min(256, -(-(M * N // v) // 1024))
     else:
         assert f["flat_grid"] == 0
+    aligned_only = want and not residual and xdt != "f32" and f["packed"] and f["slots"] == 1 and occ >= 0.85
+    assert f["flat_aligned_only"] == int(aligned_only)
 
 
 @settings(max_examples=300, deadline=None)
@@ -112,13 +115,13 @@ def test_plans_hold_their_invariants(dyt, M, N, xdt):
         if not p["packed"]:
             _check_segments(p, N)
     _check_flat(f, M, N, xdt)
-    assert (b["flat"], b["flat_grid"]) == (f["flat"], f["flat_grid"])
+    assert (b["flat"], b["flat_grid"], b["flat_aligned_only"]) == (f["flat"], f["flat_grid"], f["flat_aligned_only"])
     r = dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")
     _check_tiling(r, M, N, v, True)
     _check_flat(r, M, N, xdt, residual=True)
     e = dyt.dyt_get_plan(M, N, xdt, "f32", False)
     _check_tiling(e, M, N, v, False)
-    assert e["flat"] == 0 and e["flat_grid"] == 0
+    assert e["flat"] == 0 and e["flat_grid"] == 0 and e["flat_aligned_only"] == 0
     for key in ("packed", "rows_per_tile", "tile_elems", "col_blocks", "tiles", "bwd_grid", "ws_row", "ws_bytes"):
         assert e[key] == b[key], key
     assert b["ws_row"] >= 2 * (N if b["packed"] else b["tile_elems"]) + 1 and b["ws_row"] % 4 == 0
@@ -151,8 +154,8 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
 
 @pytest.mark.parametrize("N,xdt,flat", [
     (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
-    (3072, "bf16", 0), (4096, "bf16", 0), (32, "bf16", 0), (7168, "bf16", 0), (5120, "bf16", 0),
-    (4095, "bf16", 0),
+    (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
+    (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0), (4095, "bf16", 0),
     (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 0),
     (2560, "f16", 1)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
