@@ -215,6 +215,14 @@ double occupancy(const Plan& p, int64_t N) {
 // 90.9 against 92.3 / 92.6 us flat), while the flat walk keeps its own
 // (768 / 2,048 / 3,072 wide: 94.0-96.4 against 105.9-106.6 us), so the
 // former walk flat only from aligned bases (Plan::flat_aligned_only).
+// Rows that are not a whole number of vectors walk flat in the plain
+// forward (the LDS copy then holds 4 shifted copies per parameter, so
+// N + V <= 2,048) for 2-byte x at any fill and for float32 x below
+// DYT_FLAT_OCC_4B: bf16 rows of 3 / 17 / 100 / 255 / 511 / 1,001 / 1,500 /
+// 2,039: 81.9-88.4 us against 89.2-113.2 us for the shifted-slot tiles
+// (1,500 at a base one element off: 99.3 against 118.2); float32 1,501 (0.73
+// filled): 192.9 against 236.0 us, while full float32 tiles tie at 2^27
+// elements and win at 100,003 x 255 (37.3 against 41.2 us).
 // The residual-fused forward (two inputs, two outputs) walks flat whenever
 // its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
 // the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:
@@ -227,6 +235,11 @@ double occupancy(const Plan& p, int64_t N) {
 #endif
 #ifndef DYT_FLAT_OCC_4B
 #define DYT_FLAT_OCC_4B 0.9
+#endif
+// Rows that are not a whole number of vectors (plain forward only; 0 keeps
+// the shifted-slot tiles there).
+#ifndef DYT_FLAT_RAG
+#define DYT_FLAT_RAG 1
 #endif
 // Workgroups of the flat forward (one per CU measured fastest, 4 vectors
 // per thread and step).
@@ -306,11 +319,17 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     const bool poor_fit =
         dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B)
                         : fill < 1.0 - 1e-9 || k2;
-    if (dir != Dir::Bwd && N % vmax == 0 && N <= kFlatMaxN && poor_fit) {
+    const bool rag = N % vmax != 0;
+    const bool rag_fits =
+        4 * dyt::flat_rag_len((int)std::min<int64_t>(N, kFlatMaxN), (int)vmax) <= kFlatMaxN;
+    const bool flat_ok = rag ? dir == Dir::Fwd && DYT_FLAT_RAG && rag_fits &&
+                                   (sx == 2 || fill < DYT_FLAT_OCC_4B)
+                             : dir != Dir::Bwd && N <= kFlatMaxN && poor_fit;
+    if (flat_ok) {
         const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);
         p.flat = true;
-        p.flat_grid = std::min<int64_t>(groups, DYT_FLAT_GRID);
-        p.flat_aligned_only = dir == Dir::Fwd && sx == 2 && p.packed && p.slots == 1 &&
+        p.flat_grid = std::max<int64_t>(1, std::min<int64_t>(groups, DYT_FLAT_GRID));
+        p.flat_aligned_only = !rag && dir == Dir::Fwd && sx == 2 && p.packed && p.slots == 1 &&
                               fill >= DYT_FLAT_OCC_2B;
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
@@ -511,6 +530,7 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     if (base.flat && !strided && (bases16 || !base.flat_aligned_only)) {
         FlatGeo f;
         f.nvec = M * N / (16 / sx);
+        f.total = M * N;
         f.N = (int32_t)N;
         f.cstep = (int32_t)((base.flat_grid * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {

@@ -640,13 +640,20 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 }
 
 // ------------------------------------------------------------ flat forward
-// The forward over contiguous rows whose length N is a multiple of V but
-// fills the slot tiles poorly (e.g. 2,560 bfloat16 columns: 62% of the slots
-// of two 2,048-element row segments). The problem is walked as one run of
-// nvec = M*N/V vectors, so every access carries data; since no vector
-// straddles a row, vector q covers columns c .. c+V-1 with c = (q*V) mod N,
-// and gamma/beta come from a float32 copy of both in LDS (2*N floats)
-// instead of per-thread registers. The vectors are cut into groups of
+// The forward over contiguous rows that the slot tiles fit poorly (e.g.
+// 2,560 bfloat16 columns: 62% of the slots of two 2,048-element row
+// segments) or whose length N is not a multiple of V (RAG: the tiles then
+// shift their slots row by row). The problem is walked as one run of
+// nvec = floor(M*N/V) vectors, so every access carries data; vector q
+// covers elements q*V .. q*V+V-1, whose columns are c .. c+V-1 taken mod N
+// with c = (q*V) mod N, and gamma/beta come from a float32 copy of both in
+// LDS instead of per-thread registers: 2*N floats. With RAG, c is any
+// column and the entries c .. c+V-1 may run past column N - 1 (no vector
+// straddles a row when N is a multiple of V), so each parameter is kept as
+// 4 copies of N+V entries running on with columns 0, 1, ... again, copy s
+// shifted left by s words: entry c then sits at the multiple of 4 c - s of
+// copy s = c mod 4, and every read is a 16-byte LDS read as without RAG. The last M*N mod V elements (RAG only)
+// are done by one thread of workgroup 0. The vectors are cut into groups of
 // B = U * kBlock (one contiguous run); workgroup w of G takes groups w,
 // w + G, ..., and thread tid vectors tid, tid + kBlock, ... of each, so
 // every wave access covers 64 adjacent vectors. A thread's U columns each
@@ -655,9 +662,16 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 // (nvec / B) mod G, with a bounds check per vector. Loads, arithmetic,
 // rounding and stores per element are those of dyt_fwd_kernel: both give
 // the same bits.
+// Words per copy of the RAG layout: entries 0 .. N+V-1, rounded up to a
+// multiple of 4 (every copy starts 16-byte aligned). 4 copies per parameter.
+__host__ __device__ constexpr int flat_rag_len(int N, int V) {
+    return (N + V + 3) / 4 * 4;
+}
+
 struct FlatGeo {
-    int64_t nvec;      // vectors in the problem (M * N / V)
-    int32_t N;         // row length, a multiple of V
+    int64_t nvec;      // whole vectors in the problem (floor(M * N / V))
+    int64_t total;     // elements (M * N)
+    int32_t N;         // row length
     int32_t cstep;     // (G * U * kBlock * V) mod N
 };
 
@@ -675,20 +689,28 @@ __device__ __forceinline__ void flat_load(const XT* __restrict__ x, const XT* __
 }
 
 // Computes and stores vector q + j*kBlock (column col[j]) of a loaded group.
-template <typename XT, bool ACC, bool RES>
+template <typename XT, bool ACC, bool RES, bool RAG>
 __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>::T& rx,
                                          const typename Raw<XT, 16 / sizeof(XT)>::T& rr,
                                          XT* __restrict__ y, XT* __restrict__ h, int64_t at,
-                                         int col, const float* sg, const float* sb, float alpha) {
+                                         int col, const float* sg, const float* sb, float alpha,
+                                         int L) {
     constexpr int V = 16 / sizeof(XT);
     float v[V], gm[V], bt[V];
     constexpr bool kStNt = fwd_flat_store_nt<XT, RES>();
     fwd_input<XT, V, RES, kStNt>(rx, rr, h + at, v);
-    // col is a multiple of V (and so of 4): 16-byte LDS reads
+    // Without RAG col is a multiple of V (and so of 4); with RAG copy s =
+    // col mod 4 holds entry col at the multiple of 4 col - s. Either way the
+    // V entries from col on are 16-byte LDS reads.
+    int base = col;
+    if constexpr (RAG) {
+        const int s = col & 3;
+        base = (col - s) + s * L;
+    }
 #pragma unroll
     for (int e = 0; e < V; e += 4) {
-        const float4 g4 = *reinterpret_cast<const float4*>(sg + col + e);
-        const float4 b4 = *reinterpret_cast<const float4*>(sb + col + e);
+        const float4 g4 = *reinterpret_cast<const float4*>(sg + base + e);
+        const float4 b4 = *reinterpret_cast<const float4*>(sb + base + e);
         gm[e] = g4.x; gm[e + 1] = g4.y; gm[e + 2] = g4.z; gm[e + 3] = g4.w;
         bt[e] = b4.x; bt[e + 1] = b4.y; bt[e + 2] = b4.z; bt[e + 3] = b4.w;
     }
@@ -699,24 +721,24 @@ __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>
 
 // Computes and stores a loaded group, then moves each column on to this
 // thread's next group.
-template <typename XT, int U, bool ACC, bool RES>
+template <typename XT, int U, bool ACC, bool RES, bool RAG>
 __device__ __forceinline__ void flat_group(const typename Raw<XT, 16 / sizeof(XT)>::T (&rx)[U],
                                            const typename Raw<XT, 16 / sizeof(XT)>::T (&rr)[U],
                                            XT* __restrict__ y, XT* __restrict__ h, int64_t q,
                                            int (&col)[U], const float* sg, const float* sb,
-                                           float alpha, int N, int cstep) {
+                                           float alpha, int N, int cstep, int L) {
     constexpr int V = 16 / sizeof(XT);
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-        flat_vec<XT, ACC, RES>(rx[j], rr[j], y, h, (q + j * kBlock) * V, col[j], sg, sb, alpha);
+        flat_vec<XT, ACC, RES, RAG>(rx[j], rr[j], y, h, (q + j * kBlock) * V, col[j], sg, sb, alpha, L);
         const int c = col[j] + cstep;
         col[j] = c >= N ? c - N : c;
     }
 }
 
-// Dynamic LDS: 2 * N floats (gamma, then beta). r and h as in dyt_fwd_kernel
-// (null without RES).
-template <typename XT, typename PT, int U, bool RES>
+// Dynamic LDS: 2 * N floats (gamma, then beta), with RAG 8 * flat_rag_len.
+// r and h as in dyt_fwd_kernel (null without RES).
+template <typename XT, typename PT, int U, bool RES, bool RAG>
 __global__ void __launch_bounds__(kBlock)
 dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
                     const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
@@ -727,13 +749,17 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     extern __shared__ float4 flat_lds[];
-    float* const sg = reinterpret_cast<float*>(flat_lds);
-    float* const sb = sg + f.N;
     const int N = f.N;
+    const int L = RAG ? flat_rag_len(N, V) : N;         // words per copy
+    const int NW = RAG ? 4 * L : N;                     // LDS words per parameter
+    float* const sg = reinterpret_cast<float*>(flat_lds);
+    float* const sb = sg + NW;
     const int tid = threadIdx.x;
-    for (int c = tid; c < N; c += kBlock) {
-        sg[c] = to_f32(gamma[c]);
-        sb[c] = to_f32(beta[c]);
+    for (int i = tid; i < NW; i += kBlock) {
+        // RAG: word k of copy s = i / L is column (k + s) mod N
+        const int src = RAG ? (i % L + i / L) % N : i;
+        sg[i] = to_f32(gamma[src]);
+        sb[i] = to_f32(beta[src]);
     }
     __syncthreads();
     const float alpha = to_f32(alpha_p[0]);
@@ -757,16 +783,16 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             const int64_t qb = qa + gstep;
             flat_load<XT, U, RES>(x, r, qb, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
-            flat_group<XT, U, ACC, RES>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep);
+            flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t qn = 2 * pi + 2 < iters ? qb + gstep : qb;
             flat_load<XT, U, RES>(x, r, qn, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
-            flat_group<XT, U, ACC, RES>(xb, rb, y, h, qb, col, sg, sb, alpha, N, f.cstep);
+            flat_group<XT, U, ACC, RES, RAG>(xb, rb, y, h, qb, col, sg, sb, alpha, N, f.cstep, L);
             __builtin_amdgcn_sched_barrier(0);
             qa = qn;
         }
-        if (iters & 1) flat_group<XT, U, ACC, RES>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep);
+        if (iters & 1) flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
     }
     // The partial group: its owner's columns have advanced to group ngroups.
     if (ngroups * B < f.nvec && w == ngroups % G) {
@@ -777,8 +803,29 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
                 typename R::T x1, r1{};
                 x1 = R::template load<DYT_FWD_NT>(x + q * V);
                 if constexpr (RES) r1 = R::template load<DYT_FWD_NT>(r + q * V);
-                flat_vec<XT, ACC, RES>(x1, r1, y, h, q * V, col[j], sg, sb, alpha);
+                flat_vec<XT, ACC, RES, RAG>(x1, r1, y, h, q * V, col[j], sg, sb, alpha, L);
             }
+        }
+    }
+    // RAG: the last total - nvec*V (< V) elements, columns c0 .. c0+n-1 mod N.
+    if constexpr (RAG) {
+        const int64_t t0 = f.nvec * V;
+        if (t0 < f.total && w == 0 && tid == 0) {
+            const int n = (int)(f.total - t0);
+            const int c0 = (int)(t0 % N);
+            float v[V];
+            load_partial<XT, V>(x + t0, n, v);
+            if constexpr (RES) {
+                float rv[V];
+                load_partial<XT, V>(r + t0, n, rv);
+#pragma unroll
+                for (int e = 0; e < V; ++e) v[e] = to_f32(from_f32<XT>(v[e] + rv[e]));
+                store_partial<XT, V>(h + t0, n, v);
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e)   // copy 0: word c is column c mod N
+                v[e] = __builtin_fmaf(sg[c0 + e], dyt_tanh<ACC>(alpha * v[e]), sb[c0 + e]);
+            store_partial<XT, V>(y + t0, n, v);
         }
     }
 }

@@ -136,10 +136,23 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
 
 template <typename XT, typename PT, bool RES>
 bool launch_flat_pt(const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
-    const size_t lds = 2 * (size_t)f.N * sizeof(float);   // gamma and beta as float32
-    hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, RES>), dim3((unsigned)p.flat_grid),
-                       dim3(kBlock), lds, s, (const XT*)a.x, (const XT*)a.r, (const PT*)a.alpha,
-                       (const PT*)a.gamma, (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
+    constexpr int V = 16 / sizeof(XT);
+    const bool rag = f.N % V != 0;
+    // gamma and beta as float32; rows that are not whole vectors carry V more of each
+    const size_t lds = 2 * (size_t)(rag ? 4 * dyt::flat_rag_len(f.N, V) : f.N) * sizeof(float);
+    if (rag) {
+        if constexpr (RES) return false;   // the residual forward keeps its tiles there
+        else
+            hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, false, true>),
+                               dim3((unsigned)p.flat_grid), dim3(kBlock), lds, s, (const XT*)a.x,
+                               (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
+                               (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
+    } else {
+        hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, RES, false>),
+                           dim3((unsigned)p.flat_grid), dim3(kBlock), lds, s, (const XT*)a.x,
+                           (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
+                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
+    }
     return true;
 }
 
@@ -151,7 +164,7 @@ bool launch_flat_res(bool res, const Plan& p, const FlatGeo& f, const FwdPtrs& a
 template <typename XT>
 bool launch_forward_flat(int pdt, bool res, const Plan& p, const FlatGeo& f, const FwdPtrs& a,
                          hipStream_t s) {
-    if (!p.flat || f.N % (int)(16 / sizeof(XT)) != 0) return false;
+    if (!p.flat || p.flat_grid < 1) return false;
     switch (pdt) {
         case DYT_F32: return launch_flat_res<XT, float>(res, p, f, a, s);
         case DYT_BF16: return launch_flat_res<XT, bf16_t>(res, p, f, a, s);

@@ -274,8 +274,10 @@ typedef struct dyt_plan {
     int64_t flat;          /* forward: 1 if a contiguous launch walks the problem as one
                               run of 16-byte vectors instead of the tiles above (rows whose
                               length is a multiple of vec, at most 8192, that the tiles
-                              fit poorly, and 2-byte x in packed tiles); row-strided
-                              launches use the tiles. 0 for the
+                              fit poorly, and 2-byte x in packed tiles; rows that are
+                              not, up to N + vec <= 2048, in the plain forward: 2-byte
+                              x always, float32 x when the tiles fit poorly);
+                              row-strided launches use the tiles. 0 for the
                               element-wise variant (vector_access = 0). dyt_get_plan
                               reports the forward's value; the backward always tiles */
     int64_t flat_grid;     /* workgroups of that flat forward, 0 if flat = 0 */

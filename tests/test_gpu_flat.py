@@ -4,9 +4,10 @@ and beta read from an LDS copy by computed column. Checked against the fp64
 oracle element by element, bit for bit against the tiled kernels (a
 row-strided launch of the same shape runs the tiles), on problems whose last
 vector group is partial, with guard canaries around y, at a base one element
-off 16-byte alignment, at the largest width the LDS copy allows, and on a
-problem above 2^31 elements; the residual-fused forward walks flat in the
-same way (h exact, y equal to the tiled forward of h)."""
+off 16-byte alignment, at the largest width the LDS copy allows, on rows
+that are not a whole number of vectors (down to fewer elements than one
+vector), and on a problem above 2^31 elements; the residual-fused forward
+walks flat in the same way (h exact, y equal to the tiled forward of h)."""
 import numpy as np
 import pytest
 import torch
@@ -50,6 +51,15 @@ SHAPES = [
     (5001, 32, "bf16", "f32"),      # packed tiles of one full slot (aligned bases only)
     (3001, 64, "f16", "bf16"),
     (999, 256, "bf16", "f32"),
+    # rows that are not a whole number of vectors: gamma/beta as 4 shifted
+    # copies, the last M*N mod V elements done one by one
+    (3001, 1500, "bf16", "f32"),    # 562.7 groups, 4 tail elements
+    (777, 17, "bf16", "bf16"),      # 13,209 elements: 1,651 vectors + 1
+    (5, 3, "bf16", "f32"),          # N < V: one vector + 7 tail elements
+    (1, 7, "f16", "f32"),           # less than one vector: tail only
+    (1000, 1501, "f32", "f32"),     # float32 tiles 0.73 filled
+    (999, 2039, "f16", "f32"),      # widest: 4 copies of 2,048 words
+    (4097, 255, "bf16", "f16"),
 ]
 
 
@@ -95,7 +105,7 @@ def test_flat_forward_matches_oracle_and_tiles(dyt, M, N, xdt, pdt):
 
 @pytest.mark.parametrize("M,N,xdt,aligned_only", [
     (1000, 2560, "bf16", 0), (777, 4104, "f32", 0), (4097, 1032, "f16", 0),
-    (5001, 32, "bf16", 1), (3001, 64, "f16", 1)])
+    (5001, 32, "bf16", 1), (3001, 64, "f16", 1), (3001, 1500, "bf16", 0), (777, 17, "bf16", 0)])
 def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
     """x and y one element off 16-byte alignment: the same bits as aligned
     (full one-slot packed tiles then run the tiles instead of the walk)."""

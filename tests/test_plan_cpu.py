@@ -83,8 +83,11 @@ def _check_flat(f, M, N, xdt, residual=False):
     0.9 (float32 x); for 2-byte x, packed tiles or row segments filled below
     0.85; the residual-fused forward whenever its tiles leave a slot empty or
     are 2-byte packed tiles of two or more slots. The grid is one workgroup
-    per 1,024 vectors, at most 256. Only the plain forward's 2-byte packed
-    tiles of one slot filled at least 0.85 walk flat at aligned bases alone."""
+    per 1,024 vectors (at least one), at most 256. Only the plain forward's
+    2-byte packed tiles of one slot filled at least 0.85 walk flat at
+    aligned bases alone. Rows that are not a whole number of vectors walk
+    flat in the plain forward when four copies of N + V entries (rounded up
+    to 4) fit in 8,192 words: 2-byte x always, float32 x below 0.9."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
@@ -92,13 +95,18 @@ def _check_flat(f, M, N, xdt, residual=False):
         poor = occ < 1 - 1e-9 or k2
     else:
         poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
-    want = N % v == 0 and N <= 8192 and poor
+    if N % v:
+        fits = 4 * (-(-(N + v) // 4) * 4) <= 8192
+        want = not residual and fits and (xdt != "f32" or occ < 0.9)
+    else:
+        want = N <= 8192 and poor
     assert f["flat"] == int(want)
     if want:
-        assert f["flat_grid"] == min(256, -(-(M * N // v) // 1024))
+        assert f["flat_grid"] == max(1, min(256, -(-(M * N // v) // 1024)))
     else:
         assert f["flat_grid"] == 0
-    aligned_only = want and not residual and xdt != "f32" and f["packed"] and f["slots"] == 1 and occ >= 0.85
+    aligned_only = (want and not residual and N % v == 0 and xdt != "f32" and f["packed"] and f["slots"] == 1
+                    and occ >= 0.85)
     assert f["flat_aligned_only"] == int(aligned_only)
 
 
@@ -157,11 +165,16 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
     (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0), (4095, "bf16", 0),
     (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 0),
-    (2560, "f16", 1)])
+    (2560, "f16", 1),
+    # rows that are not a whole number of vectors
+    (1500, "bf16", 1), (1001, "bf16", 1), (255, "bf16", 1), (17, "bf16", 1), (3, "bf16", 1),
+    (2039, "bf16", 1), (2041, "bf16", 0), (8183, "bf16", 0), (1500, "f16", 1),
+    (1501, "f32", 1), (255, "f32", 0), (17, "f32", 0), (2043, "f32", 0)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
     """At 2^27 elements the measured choice: the flat walk for widths the
-    tiles fill poorly, the tiles where they fill (or N is not a whole number
-    of vectors, or gamma/beta would not fit the LDS copy)."""
+    tiles fill poorly and for rows that are not a whole number of vectors
+    (float32: only when the tiles fill poorly), the tiles where they fill
+    or gamma/beta would not fit the LDS copy."""
     M = (1 << 27) // N
     f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
     assert f["flat"] == flat
@@ -171,7 +184,8 @@ def test_flat_forward_choice(dyt, N, xdt, flat):
 
 @pytest.mark.parametrize("N,xdt,flat", [
     (2560, "bf16", 1), (3072, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1),
-    (4096, "bf16", 0), (32, "bf16", 1), (4095, "bf16", 0), (2560, "f32", 1), (4104, "f32", 1)])
+    (4096, "bf16", 0), (32, "bf16", 1), (4095, "bf16", 0), (1500, "bf16", 0), (2560, "f32", 1),
+    (4104, "f32", 1)])
 def test_flat_residual_forward_choice(dyt, N, xdt, flat):
     """The residual-fused forward at 2^27 elements: flat unless its tiles are
     full (and then not 2-byte packed tiles of two or more slots)."""
