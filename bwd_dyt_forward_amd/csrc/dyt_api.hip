@@ -216,8 +216,8 @@ double occupancy(const Plan& p, int64_t N) {
 // (768 / 2,048 / 3,072 wide: 94.0-96.4 against 105.9-106.6 us), so the
 // former walk flat only from aligned bases (Plan::flat_aligned_only).
 // Rows that are not a whole number of vectors walk flat in the plain
-// forward (the LDS copy then holds 4 shifted copies per parameter, so
-// N + V <= 2,048) for 2-byte x at any fill and for float32 x below
+// forward (the LDS copy then holds 4 shifted copies per parameter, N + V up
+// to DYT_FLAT_RAG_MAX_LEN) for 2-byte x at any fill and for float32 x below
 // DYT_FLAT_OCC_4B: bf16 rows of 3 / 17 / 100 / 255 / 511 / 1,001 / 1,500 /
 // 2,039: 81.9-88.4 us against 89.2-113.2 us for the shifted-slot tiles
 // (1,500 at a base one element off: 99.3 against 118.2); float32 1,501 (0.73
@@ -253,6 +253,16 @@ double occupancy(const Plan& p, int64_t N) {
 #endif
 static_assert(DYT_FLAT_MAX_N <= 8192, "the flat forward stages 2 N floats in at most 64 KB of LDS");
 constexpr int64_t kFlatMaxN = DYT_FLAT_MAX_N;
+// Rows that are not whole vectors: longest copy (flat_rag_len words; 8 of
+// them, the four shifted copies of gamma and beta, up to 112 KB of the
+// 160 KB of LDS a gfx950 workgroup may hold). Measured at 2^27 bf16
+// elements, flat against tiles: 2,047 / 3,071 wide 85.8 / 89.1 against
+// 98.0 / 94.2 us, but 4,095 / 5,111 wide 92.4 / 94.4 against 89.9 / 92.1
+// (filling the copies grows with N).
+#ifndef DYT_FLAT_RAG_MAX_LEN
+#define DYT_FLAT_RAG_MAX_LEN 3584
+#endif
+static_assert(8 * DYT_FLAT_RAG_MAX_LEN * 4 <= 160 * 1024, "four copies of gamma and beta exceed 160 KB of LDS");
 
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
@@ -320,8 +330,8 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B)
                         : fill < 1.0 - 1e-9 || k2;
     const bool rag = N % vmax != 0;
-    const bool rag_fits =
-        4 * dyt::flat_rag_len((int)std::min<int64_t>(N, kFlatMaxN), (int)vmax) <= kFlatMaxN;
+    const bool rag_fits = kFlatMaxN > 0 && N <= kFlatMaxN &&
+                          dyt::flat_rag_len((int)N, (int)vmax) <= DYT_FLAT_RAG_MAX_LEN;
     const bool flat_ok = rag ? dir == Dir::Fwd && DYT_FLAT_RAG && rag_fits &&
                                    (sx == 2 || fill < DYT_FLAT_OCC_4B)
                              : dir != Dir::Bwd && N <= kFlatMaxN && poor_fit;

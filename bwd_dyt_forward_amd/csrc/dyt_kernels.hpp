@@ -755,11 +755,21 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     float* const sg = reinterpret_cast<float*>(flat_lds);
     float* const sb = sg + NW;
     const int tid = threadIdx.x;
-    for (int i = tid; i < NW; i += kBlock) {
-        // RAG: word k of copy s = i / L is column (k + s) mod N
-        const int src = RAG ? (i % L + i / L) % N : i;
-        sg[i] = to_f32(gamma[src]);
-        sb[i] = to_f32(beta[src]);
+    if constexpr (RAG) {
+        // word k of copy s is column (k + s) mod N (no division: k + s < N + V + 6)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            for (int k = tid; k < L; k += kBlock) {
+                int src = k + s;
+                while (src >= N) src -= N;
+                sg[s * L + k] = to_f32(gamma[src]);
+                sb[s * L + k] = to_f32(beta[src]);
+            }
+    } else {
+        for (int c = tid; c < N; c += kBlock) {
+            sg[c] = to_f32(gamma[c]);
+            sb[c] = to_f32(beta[c]);
+        }
     }
     __syncthreads();
     const float alpha = to_f32(alpha_p[0]);

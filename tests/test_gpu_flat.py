@@ -58,7 +58,9 @@ SHAPES = [
     (5, 3, "bf16", "f32"),          # N < V: one vector + 7 tail elements
     (1, 7, "f16", "f32"),           # less than one vector: tail only
     (1000, 1501, "f32", "f32"),     # float32 tiles 0.73 filled
-    (999, 2039, "f16", "f32"),      # widest: 4 copies of 2,048 words
+    (999, 2039, "f16", "f32"),      # 4 copies of 2,048 words (64 KB of LDS)
+    (301, 3575, "bf16", "f32"),     # widest: 4 copies of 3,584 words (112 KB)
+    (257, 3071, "bf16", "bf16"),
     (4097, 255, "bf16", "f16"),
 ]
 

@@ -86,8 +86,9 @@ def _check_flat(f, M, N, xdt, residual=False):
     per 1,024 vectors (at least one), at most 256. Only the plain forward's
     2-byte packed tiles of one slot filled at least 0.85 walk flat at
     aligned bases alone. Rows that are not a whole number of vectors walk
-    flat in the plain forward when four copies of N + V entries (rounded up
-    to 4) fit in 8,192 words: 2-byte x always, float32 x below 0.9."""
+    flat in the plain forward when N + V rounded up to 4 is at most 3,584
+    (four copies of both parameters in 112 KB of LDS): 2-byte x always,
+    float32 x below 0.9."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
@@ -96,7 +97,7 @@ def _check_flat(f, M, N, xdt, residual=False):
     else:
         poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
     if N % v:
-        fits = 4 * (-(-(N + v) // 4) * 4) <= 8192
+        fits = -(-(N + v) // 4) * 4 <= 3584
         want = not residual and fits and (xdt != "f32" or occ < 0.9)
     else:
         want = N <= 8192 and poor
@@ -163,12 +164,14 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
 @pytest.mark.parametrize("N,xdt,flat", [
     (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
     (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
-    (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0), (4095, "bf16", 0),
+    (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0),
     (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 0),
     (2560, "f16", 1),
     # rows that are not a whole number of vectors
     (1500, "bf16", 1), (1001, "bf16", 1), (255, "bf16", 1), (17, "bf16", 1), (3, "bf16", 1),
-    (2039, "bf16", 1), (2041, "bf16", 0), (8183, "bf16", 0), (1500, "f16", 1),
+    (2039, "bf16", 1), (2047, "bf16", 1), (3071, "bf16", 1), (3575, "bf16", 1), (3577, "bf16", 0),
+    (4095, "bf16", 0), (5111, "bf16", 0),
+    (8183, "bf16", 0), (1500, "f16", 1),
     (1501, "f32", 1), (255, "f32", 0), (17, "f32", 0), (2043, "f32", 0)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
     """At 2^27 elements the measured choice: the flat walk for widths the
