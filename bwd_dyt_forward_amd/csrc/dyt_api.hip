@@ -254,15 +254,20 @@ double occupancy(const Plan& p, int64_t N) {
 static_assert(DYT_FLAT_MAX_N <= 8192, "the flat forward stages 2 N floats in at most 64 KB of LDS");
 constexpr int64_t kFlatMaxN = DYT_FLAT_MAX_N;
 // Rows that are not whole vectors: longest copy (flat_rag_len words; 8 of
-// them, the four shifted copies of gamma and beta, up to 112 KB of the
-// 160 KB of LDS a gfx950 workgroup may hold). Measured at 2^27 bf16
-// elements, flat against tiles: 2,047 / 3,071 wide 85.8 / 89.1 against
-// 98.0 / 94.2 us, but 4,095 / 5,111 wide 92.4 / 94.4 against 89.9 / 92.1
-// (filling the copies grows with N).
+// them, the four shifted copies of gamma and beta, in the 160 KB of LDS a
+// gfx950 workgroup may hold), for 2-byte and for float32 x. Measured at
+// 2^27 elements, flat against tiles: bf16 2,047 / 3,071 wide 85.8-86.8 /
+// 89.1 against 97.6-98.0 / 93.8-94.2 us, but 4,095 / 5,111 wide 91.2-92.4 /
+// 94.2-94.4 against 89.9 / 92.0-92.1; float32 3,001 / 5,113 wide (tiles 0.73
+// / 0.83 filled) 188.4 / 192.6 against 214.7 / 233.2.
 #ifndef DYT_FLAT_RAG_MAX_LEN
 #define DYT_FLAT_RAG_MAX_LEN 3584
 #endif
-static_assert(8 * DYT_FLAT_RAG_MAX_LEN * 4 <= 160 * 1024, "four copies of gamma and beta exceed 160 KB of LDS");
+#ifndef DYT_FLAT_RAG_MAX_LEN_4B
+#define DYT_FLAT_RAG_MAX_LEN_4B 5120
+#endif
+static_assert(8 * DYT_FLAT_RAG_MAX_LEN * 4 <= 160 * 1024 && 8 * DYT_FLAT_RAG_MAX_LEN_4B * 4 <= 160 * 1024,
+              "four copies of gamma and beta exceed 160 KB of LDS");
 
 int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     if (!dtype_ok(xdt) || !dtype_ok(pdt)) return DYT_ERR_UNSUPPORTED_DTYPE;
@@ -331,7 +336,8 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
                         : fill < 1.0 - 1e-9 || k2;
     const bool rag = N % vmax != 0;
     const bool rag_fits = kFlatMaxN > 0 && N <= kFlatMaxN &&
-                          dyt::flat_rag_len((int)N, (int)vmax) <= DYT_FLAT_RAG_MAX_LEN;
+                          dyt::flat_rag_len((int)N, (int)vmax) <=
+                              (sx == 2 ? DYT_FLAT_RAG_MAX_LEN : DYT_FLAT_RAG_MAX_LEN_4B);
     const bool flat_ok = rag ? dir == Dir::Fwd && DYT_FLAT_RAG && rag_fits &&
                                    (sx == 2 || fill < DYT_FLAT_OCC_4B)
                              : dir != Dir::Bwd && N <= kFlatMaxN && poor_fit;

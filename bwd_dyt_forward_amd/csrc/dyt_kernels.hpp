@@ -756,15 +756,19 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     float* const sb = sg + NW;
     const int tid = threadIdx.x;
     if constexpr (RAG) {
-        // word k of copy s is column (k + s) mod N (no division: k + s < N + V + 6)
+        // word k of copy s is column (k + s) mod N: column c, read once,
+        // goes to words c - s + m*N (m >= 0) of copy s that lie in [0, L)
+        for (int c = tid; c < N; c += kBlock) {
+            const float gv = to_f32(gamma[c]);
+            const float bv = to_f32(beta[c]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            for (int k = tid; k < L; k += kBlock) {
-                int src = k + s;
-                while (src >= N) src -= N;
-                sg[s * L + k] = to_f32(gamma[src]);
-                sb[s * L + k] = to_f32(beta[src]);
-            }
+            for (int s = 0; s < 4; ++s)
+                for (int k = c - s; k < L; k += N)
+                    if (k >= 0) {
+                        sg[s * L + k] = gv;
+                        sb[s * L + k] = bv;
+                    }
+        }
     } else {
         for (int c = tid; c < N; c += kBlock) {
             sg[c] = to_f32(gamma[c]);

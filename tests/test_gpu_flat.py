@@ -61,6 +61,7 @@ SHAPES = [
     (999, 2039, "f16", "f32"),      # 4 copies of 2,048 words (64 KB of LDS)
     (301, 3575, "bf16", "f32"),     # widest: 4 copies of 3,584 words (112 KB)
     (257, 3071, "bf16", "bf16"),
+    (263, 5113, "f32", "f32"),      # widest float32: 4 copies of 5,120 words (160 KB)
     (4097, 255, "bf16", "f16"),
 ]
 

@@ -87,8 +87,8 @@ def _check_flat(f, M, N, xdt, residual=False):
     2-byte packed tiles of one slot filled at least 0.85 walk flat at
     aligned bases alone. Rows that are not a whole number of vectors walk
     flat in the plain forward when N + V rounded up to 4 is at most 3,584
-    (four copies of both parameters in 112 KB of LDS): 2-byte x always,
-    float32 x below 0.9."""
+    (2-byte x, always) or 5,120 (float32 x, below 0.9): four copies of both
+    parameters in at most 160 KB of LDS."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
@@ -97,7 +97,7 @@ def _check_flat(f, M, N, xdt, residual=False):
     else:
         poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
     if N % v:
-        fits = -(-(N + v) // 4) * 4 <= 3584
+        fits = -(-(N + v) // 4) * 4 <= (5120 if xdt == "f32" else 3584)
         want = not residual and fits and (xdt != "f32" or occ < 0.9)
     else:
         want = N <= 8192 and poor
@@ -172,7 +172,8 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2039, "bf16", 1), (2047, "bf16", 1), (3071, "bf16", 1), (3575, "bf16", 1), (3577, "bf16", 0),
     (4095, "bf16", 0), (5111, "bf16", 0),
     (8183, "bf16", 0), (1500, "f16", 1),
-    (1501, "f32", 1), (255, "f32", 0), (17, "f32", 0), (2043, "f32", 0)])
+    (1501, "f32", 1), (3001, "f32", 1), (5113, "f32", 1), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
+    (2043, "f32", 0)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
     """At 2^27 elements the measured choice: the flat walk for widths the
     tiles fill poorly and for rows that are not a whole number of vectors
