@@ -215,9 +215,10 @@ double occupancy(const Plan& p, int64_t N) {
 // 90.9 against 92.3 / 92.6 us flat), while the flat walk keeps its own
 // (768 / 2,048 / 3,072 wide: 94.0-96.4 against 105.9-106.6 us), so the
 // former walk flat only from aligned bases (Plan::flat_aligned_only).
-// Rows that are not a whole number of vectors walk flat in the plain
-// forward (the LDS copy then holds 4 shifted copies per parameter, N + V up
-// to DYT_FLAT_RAG_MAX_LEN) for 2-byte x at any fill and for float32 x below
+// Rows that are not a whole number of vectors walk flat in the plain and
+// the residual forward (the LDS copy then holds 4 shifted copies per
+// parameter, N + V up to DYT_FLAT_RAG_MAX_LEN / _4B) for 2-byte x at any fill
+// and for float32 x below
 // DYT_FLAT_OCC_4B: bf16 rows of 3 / 17 / 100 / 255 / 511 / 1,001 / 1,500 /
 // 2,039: 81.9-88.4 us against 89.2-113.2 us for the shifted-slot tiles
 // (1,500 at a base one element off: 99.3 against 118.2); float32 1,501 (0.73
@@ -236,10 +237,17 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_OCC_4B
 #define DYT_FLAT_OCC_4B 0.9
 #endif
-// Rows that are not a whole number of vectors (plain forward only; 0 keeps
-// the shifted-slot tiles there).
+// Rows that are not a whole number of vectors (0 keeps the shifted-slot
+// tiles there).
 #ifndef DYT_FLAT_RAG
 #define DYT_FLAT_RAG 1
+#endif
+// The residual-fused forward as well, with the same rule: bf16 rows of 17 /
+// 255 / 1,001 / 1,500 / 3,071 181-186 us against 214-234 us tiled, float32
+// 1,501 / 3,001 (0.73 filled) 384 / 387 against 516 / 502, float32 255
+// (full tiles) 429 against 428.
+#ifndef DYT_FLAT_RAG_RES
+#define DYT_FLAT_RAG_RES 1
 #endif
 // Workgroups of the flat forward (one per CU measured fastest, 4 vectors
 // per thread and step).
@@ -338,7 +346,8 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     const bool rag_fits = kFlatMaxN > 0 && N <= kFlatMaxN &&
                           dyt::flat_rag_len((int)N, (int)vmax) <=
                               (sx == 2 ? DYT_FLAT_RAG_MAX_LEN : DYT_FLAT_RAG_MAX_LEN_4B);
-    const bool flat_ok = rag ? dir == Dir::Fwd && DYT_FLAT_RAG && rag_fits &&
+    const bool rag_dir = dir == Dir::Fwd || (dir == Dir::ResFwd && DYT_FLAT_RAG_RES);
+    const bool flat_ok = rag ? rag_dir && DYT_FLAT_RAG && rag_fits &&
                                    (sx == 2 || fill < DYT_FLAT_OCC_4B)
                              : dir != Dir::Bwd && N <= kFlatMaxN && poor_fit;
     if (flat_ok) {

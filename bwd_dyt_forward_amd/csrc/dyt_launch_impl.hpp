@@ -141,12 +141,10 @@ bool launch_flat_pt(const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream
     // gamma and beta as float32; rows that are not whole vectors carry V more of each
     const size_t lds = 2 * (size_t)(rag ? 4 * dyt::flat_rag_len(f.N, V) : f.N) * sizeof(float);
     if (rag) {
-        if constexpr (RES) return false;   // the residual forward keeps its tiles there
-        else
-            hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, false, true>),
-                               dim3((unsigned)p.flat_grid), dim3(kBlock), lds, s, (const XT*)a.x,
-                               (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
-                               (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
+        hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, RES, true>),
+                           dim3((unsigned)p.flat_grid), dim3(kBlock), lds, s, (const XT*)a.x,
+                           (const XT*)a.r, (const PT*)a.alpha, (const PT*)a.gamma,
+                           (const PT*)a.beta, (XT*)a.y, (XT*)a.h, f);
     } else {
         hipLaunchKernelGGL((dyt::dyt_fwd_flat_kernel<XT, PT, DYT_FLAT_U, RES, false>),
                            dim3((unsigned)p.flat_grid), dim3(kBlock), lds, s, (const XT*)a.x,

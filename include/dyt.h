@@ -275,7 +275,7 @@ typedef struct dyt_plan {
                               run of 16-byte vectors instead of the tiles above (rows whose
                               length is a multiple of vec, at most 8192, that the tiles
                               fit poorly, and 2-byte x in packed tiles; rows that are
-                              not, in the plain forward: 2-byte x up to N + vec <= 3584,
+                              not: 2-byte x up to N + vec <= 3584,
                               float32 x up to N + vec <= 5120 when the tiles fit poorly);
                               row-strided launches use the tiles. 0 for the
                               element-wise variant (vector_access = 0). dyt_get_plan

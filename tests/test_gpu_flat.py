@@ -193,6 +193,11 @@ RES_SHAPES = [  # residual-fused forward: every one walks flat (asserted)
     (129, 1040, "bf16", "f16"),
     (3, 1032, "f16", "f32"),
     (300, 7372, "f32", "f32"),
+    # rows that are not a whole number of vectors
+    (3001, 1500, "bf16", "f32"),
+    (777, 17, "bf16", "bf16"),
+    (5, 3, "f16", "f32"),           # one vector + 7 tail elements
+    (1000, 1501, "f32", "f32"),
 ]
 
 

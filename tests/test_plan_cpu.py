@@ -86,7 +86,7 @@ def _check_flat(f, M, N, xdt, residual=False):
     per 1,024 vectors (at least one), at most 256. Only the plain forward's
     2-byte packed tiles of one slot filled at least 0.85 walk flat at
     aligned bases alone. Rows that are not a whole number of vectors walk
-    flat in the plain forward when N + V rounded up to 4 is at most 3,584
+    flat (plain and residual forward) when N + V rounded up to 4 is at most 3,584
     (2-byte x, always) or 5,120 (float32 x, below 0.9): four copies of both
     parameters in at most 160 KB of LDS."""
     v = VEC[xdt]
@@ -98,7 +98,7 @@ def _check_flat(f, M, N, xdt, residual=False):
         poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
     if N % v:
         fits = -(-(N + v) // 4) * 4 <= (5120 if xdt == "f32" else 3584)
-        want = not residual and fits and (xdt != "f32" or occ < 0.9)
+        want = fits and (xdt != "f32" or occ < 0.9)
     else:
         want = N <= 8192 and poor
     assert f["flat"] == int(want)
@@ -188,11 +188,12 @@ def test_flat_forward_choice(dyt, N, xdt, flat):
 
 @pytest.mark.parametrize("N,xdt,flat", [
     (2560, "bf16", 1), (3072, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1),
-    (4096, "bf16", 0), (32, "bf16", 1), (4095, "bf16", 0), (1500, "bf16", 0), (2560, "f32", 1),
-    (4104, "f32", 1)])
+    (4096, "bf16", 0), (32, "bf16", 1), (4095, "bf16", 0), (1500, "bf16", 1), (17, "bf16", 1),
+    (2560, "f32", 1), (4104, "f32", 1), (1501, "f32", 1), (255, "f32", 0)])
 def test_flat_residual_forward_choice(dyt, N, xdt, flat):
     """The residual-fused forward at 2^27 elements: flat unless its tiles are
-    full (and then not 2-byte packed tiles of two or more slots)."""
+    full (and then not 2-byte packed tiles of two or more slots); rows that
+    are not a whole number of vectors as in the plain forward."""
     M = (1 << 27) // N
     r = dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")
     assert r["flat"] == flat
