@@ -249,6 +249,11 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_RAG_RES
 #define DYT_FLAT_RAG_RES 1
 #endif
+// Tensors that start off the 16-byte grid (all by the same amount): the flat
+// walk starts at the first aligned element, with the ragged layout.
+#ifndef DYT_FLAT_SHIFT
+#define DYT_FLAT_SHIFT 1
+#endif
 // Workgroups of the flat forward (one per CU measured fastest, 4 vectors
 // per thread and step).
 #ifndef DYT_FLAT_GRID
@@ -356,6 +361,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         p.flat_grid = std::max<int64_t>(1, std::min<int64_t>(groups, DYT_FLAT_GRID));
         p.flat_aligned_only = !rag && dir == Dir::Fwd && sx == 2 && p.packed && p.slots == 1 &&
                               fill >= DYT_FLAT_OCC_2B;
+        p.flat_shift = rag_fits && DYT_FLAT_SHIFT;
     }
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
@@ -553,9 +559,18 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
     const bool bases16 = aligned(a.x, 16) && aligned(a.y, 16);
     if (base.flat && !strided && (bases16 || !base.flat_aligned_only)) {
+        // off the 16-byte grid: start the walk at the first aligned element
+        // when every operand is off by the same amount
+        const uintptr_t mis = (uintptr_t)a.x % 16;
+        const bool same = (uintptr_t)a.y % 16 == mis &&
+                          (!res || ((uintptr_t)a.r % 16 == mis && (uintptr_t)a.h % 16 == mis));
+        const int64_t head =
+            (mis != 0 && same && base.flat_shift) ? std::min<int64_t>((16 - (int64_t)mis) / sx, M * N) : 0;
         FlatGeo f;
-        f.nvec = M * N / (16 / sx);
-        f.total = M * N;
+        f.head = (int32_t)head;
+        f.pad_ = 0;
+        f.total = M * N - head;
+        f.nvec = f.total / (16 / sx);
         f.N = (int32_t)N;
         f.cstep = (int32_t)((base.flat_grid * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {

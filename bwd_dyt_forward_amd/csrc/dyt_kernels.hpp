@@ -652,8 +652,14 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 // straddles a row when N is a multiple of V), so each parameter is kept as
 // 4 copies of N+V entries running on with columns 0, 1, ... again, copy s
 // shifted left by s words: entry c then sits at the multiple of 4 c - s of
-// copy s = c mod 4, and every read is a 16-byte LDS read as without RAG. The last M*N mod V elements (RAG only)
-// are done by one thread of workgroup 0. The vectors are cut into groups of
+// copy s = c mod 4, and every read is a 16-byte LDS read as without RAG.
+// The last M*N mod V elements (RAG only) are done by one thread of
+// workgroup 0. With RAG the walk may also start head < V elements in, at
+// the first element whose address is a multiple of 16 bytes when the
+// tensors start off that grid: every vector access is then aligned, the
+// head elements are done by one thread of the last workgroup, and vector q
+// covers elements head + q*V ... with columns from (q*V + head) mod N.
+// The vectors are cut into groups of
 // B = U * kBlock (one contiguous run); workgroup w of G takes groups w,
 // w + G, ..., and thread tid vectors tid, tid + kBlock, ... of each, so
 // every wave access covers 64 adjacent vectors. A thread's U columns each
@@ -669,10 +675,12 @@ __host__ __device__ constexpr int flat_rag_len(int N, int V) {
 }
 
 struct FlatGeo {
-    int64_t nvec;      // whole vectors in the problem (floor(M * N / V))
-    int64_t total;     // elements (M * N)
+    int64_t nvec;      // whole vectors of the walk (floor(total / V))
+    int64_t total;     // elements of the walk (M * N - head)
     int32_t N;         // row length
     int32_t cstep;     // (G * U * kBlock * V) mod N
+    int32_t head;      // RAG only: elements before the walk (< V), done one by one
+    int32_t pad_;
 };
 
 template <typename XT, int U, bool RES>
@@ -779,11 +787,34 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const float alpha = to_f32(alpha_p[0]);
     const int64_t w = blockIdx.x;
     const int64_t G = gridDim.x;
+    const int hd = RAG ? f.head : 0;
+    if (RAG && hd > 0 && w == G - 1 && tid == 0) {
+        // the head: columns 0 .. hd-1 (copy 0: word c is column c mod N)
+        float v[V];
+        load_partial<XT, V>(x, hd, v);
+        if constexpr (RES) {
+            float rv[V];
+            load_partial<XT, V>(r, hd, rv);
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[e] = to_f32(from_f32<XT>(v[e] + rv[e]));
+            store_partial<XT, V>(h, hd, v);
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = __builtin_fmaf(sg[e], dyt_tanh<ACC>(alpha * v[e]), sb[e]);
+        store_partial<XT, V>(y, hd, v);
+    }
+    // the walk, from element hd on
+    x += hd;
+    y += hd;
+    if constexpr (RES) {
+        r += hd;
+        h += hd;
+    }
     const int64_t ngroups = f.nvec / B;                 // whole groups
     const int64_t iters = w < ngroups ? (ngroups - w + G - 1) / G : 0;
     int col[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) col[j] = (int)(((w * B + j * kBlock + tid) * V) % N);
+    for (int j = 0; j < U; ++j) col[j] = (int)(((w * B + j * kBlock + tid) * V + hd) % N);
 
     // Same two-buffer loop as dyt_fwd_kernel; a last A load past this
     // workgroup's groups re-reads the previous group.
@@ -826,7 +857,7 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         const int64_t t0 = f.nvec * V;
         if (t0 < f.total && w == 0 && tid == 0) {
             const int n = (int)(f.total - t0);
-            const int c0 = (int)(t0 % N);
+            const int c0 = (int)((t0 + hd) % N);
             float v[V];
             load_partial<XT, V>(x + t0, n, v);
             if constexpr (RES) {

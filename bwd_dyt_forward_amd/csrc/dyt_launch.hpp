@@ -44,6 +44,9 @@ struct Plan {
     // The flat walk only where x and y start 16-byte aligned (2-byte packed
     // tiles of one full slot, which stay ahead at other bases).
     bool flat_aligned_only = false;
+    // The four shifted gamma/beta copies fit in LDS: the flat walk can start
+    // at the first 16-byte-aligned element when the tensors do not.
+    bool flat_shift = false;
 };
 
 // Device pointers of one launch; r/h (forward) and dres (backward) are null

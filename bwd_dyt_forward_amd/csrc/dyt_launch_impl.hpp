@@ -137,7 +137,7 @@ bool launch_forward(int pdt, bool res, bool strided, const Plan& p, const Geo& g
 template <typename XT, typename PT, bool RES>
 bool launch_flat_pt(const Plan& p, const FlatGeo& f, const FwdPtrs& a, hipStream_t s) {
     constexpr int V = 16 / sizeof(XT);
-    const bool rag = f.N % V != 0;
+    const bool rag = f.N % V != 0 || f.head > 0;
     // gamma and beta as float32; rows that are not whole vectors carry V more of each
     const size_t lds = 2 * (size_t)(rag ? 4 * dyt::flat_rag_len(f.N, V) : f.N) * sizeof(float);
     if (rag) {

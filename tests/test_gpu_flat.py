@@ -132,6 +132,28 @@ def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
     assert_reports(f"flat unaligned M={M} N={N}", [compare.check_y(to_np(yu), f.y, f.scale, xdt)])
 
 
+@pytest.mark.parametrize("M,N,xdt,xo,yo", [
+    (1000, 2560, "bf16", 1, 3), (3001, 1500, "bf16", 2, 0), (777, 4104, "f32", 0, 1), (5, 3, "bf16", 3, 3),
+    (1, 5, "bf16", 5, 5)])
+def test_flat_forward_other_misalignments(dyt, M, N, xdt, xo, yo):
+    """x and y off the 16-byte grid by xo and yo elements (equal: the walk
+    starts at the first aligned element; different: it runs unaligned):
+    the same bits as the aligned call, canaries around y untouched."""
+    inp, x, a, g, b = _inputs(dyt, M, N, xdt, "f32", seed=N + xo)
+    xt = TORCH_DT[xdt]
+    log(f"[flat-misaligned] M={M} N={N} x={xdt} xo={xo} yo={yo}")
+    y = dyt.dyt_forward(x, a, g, b)
+    xb = torch.empty(M * N + 8, dtype=xt, device="cuda")
+    xu = xb[xo:xo + M * N].view(M, N)
+    xu.copy_(x)
+    yb = torch.full((M * N + 16,), CANARY, dtype=xt, device="cuda")
+    yu = yb[yo:yo + M * N].view(M, N)
+    dyt.dyt_forward(xu, a, g, b, y=yu)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(yu), _bits(y))
+    assert bool((yb[:yo] == CANARY).all()) and bool((yb[yo + M * N:] == CANARY).all())
+
+
 def test_flat_forward_repeat_is_bitwise_stable(dyt):
     M, N = 1001, 4104
     _, x, a, g, b = _inputs(dyt, M, N, "bf16", "f32", seed=5)
