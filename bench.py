@@ -647,7 +647,8 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
             cap = pl["block"] * pl["vec"] * pl["slots"]
             occ = pl["tile_elems"] / cap if pl["packed"] else N / (pl["col_blocks"] * cap)
             lay = f"packed R={pl['rows_per_tile']}" if pl["packed"] else f"rows nb={pl['col_blocks']}"
-            if fwd and pl["flat"] and not (off and pl["flat_aligned_only"]):
+            # (every operand here is off by the same amount: the walk then starts aligned)
+            if fwd and pl["flat"]:
                 return f"flat walk, grid {pl['flat_grid']} (tiles: {lay}, K={pl['slots']}, occupancy {occ:.2f})"
             return f"{lay}, K={pl['slots']}, occupancy {occ:.2f}"
         sx = 2 if xdt == "bf16" else 4

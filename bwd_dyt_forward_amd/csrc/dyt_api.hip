@@ -557,15 +557,24 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
             if (i.lo != i.hi && overlap(o, i)) return DYT_ERR_INVALID_ARG;
     }
     if (res && overlap(outs[0], outs[1])) return DYT_ERR_INVALID_ARG;
+    // Off the 16-byte grid, the flat walk starts at the first element on the
+    // 128-byte (cache line) grid when every operand is off it by the same
+    // amount, else at the first element on the 16-byte grid when they agree
+    // on that (head: the elements before it).
+    auto off = [&](uintptr_t m) {
+        const uintptr_t o = (uintptr_t)a.x % m;
+        const bool same = (uintptr_t)a.y % m == o &&
+                          (!res || ((uintptr_t)a.r % m == o && (uintptr_t)a.h % m == o));
+        return same ? (int64_t)((m - o) % m) : (int64_t)-1;
+    };
+    int64_t head = 0;
+    if (base.flat && !strided && (uintptr_t)a.x % 16 != 0 && base.flat_shift) {
+        const int64_t line = off(128), vec = off(16);
+        head = line >= 0 ? line / sx : vec > 0 ? vec / sx : 0;
+        head = std::min<int64_t>(head, M * N);
+    }
     const bool bases16 = aligned(a.x, 16) && aligned(a.y, 16);
-    if (base.flat && !strided && (bases16 || !base.flat_aligned_only)) {
-        // off the 16-byte grid: start the walk at the first aligned element
-        // when every operand is off by the same amount
-        const uintptr_t mis = (uintptr_t)a.x % 16;
-        const bool same = (uintptr_t)a.y % 16 == mis &&
-                          (!res || ((uintptr_t)a.r % 16 == mis && (uintptr_t)a.h % 16 == mis));
-        const int64_t head =
-            (mis != 0 && same && base.flat_shift) ? std::min<int64_t>((16 - (int64_t)mis) / sx, M * N) : 0;
+    if (base.flat && !strided && (bases16 || head > 0 || !base.flat_aligned_only)) {
         FlatGeo f;
         f.head = (int32_t)head;
         f.pad_ = 0;

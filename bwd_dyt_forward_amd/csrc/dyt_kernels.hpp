@@ -654,11 +654,13 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 // shifted left by s words: entry c then sits at the multiple of 4 c - s of
 // copy s = c mod 4, and every read is a 16-byte LDS read as without RAG.
 // The last M*N mod V elements (RAG only) are done by one thread of
-// workgroup 0. With RAG the walk may also start head < V elements in, at
-// the first element whose address is a multiple of 16 bytes when the
-// tensors start off that grid: every vector access is then aligned, the
-// head elements are done by one thread of the last workgroup, and vector q
-// covers elements head + q*V ... with columns from (q*V + head) mod N.
+// workgroup 0. With RAG the walk may also start head elements in, at the
+// first element whose address is a multiple of 128 bytes (a cache line; 16
+// bytes if the tensors are not all off the line grid by the same amount)
+// when the tensors start off that grid: every wave access then covers whole
+// lines, the head elements are done one per thread of the last workgroup,
+// and vector q covers elements head + q*V ... with columns from
+// (q*V + head) mod N.
 // The vectors are cut into groups of
 // B = U * kBlock (one contiguous run); workgroup w of G takes groups w,
 // w + G, ..., and thread tid vectors tid, tid + kBlock, ... of each, so
@@ -679,7 +681,7 @@ struct FlatGeo {
     int64_t total;     // elements of the walk (M * N - head)
     int32_t N;         // row length
     int32_t cstep;     // (G * U * kBlock * V) mod N
-    int32_t head;      // RAG only: elements before the walk (< V), done one by one
+    int32_t head;      // RAG only: elements before the walk (< 128 bytes), one per thread
     int32_t pad_;
 };
 
@@ -788,20 +790,16 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t w = blockIdx.x;
     const int64_t G = gridDim.x;
     const int hd = RAG ? f.head : 0;
-    if (RAG && hd > 0 && w == G - 1 && tid == 0) {
-        // the head: columns 0 .. hd-1 (copy 0: word c is column c mod N)
-        float v[V];
-        load_partial<XT, V>(x, hd, v);
+    if (RAG && hd > 0 && w == G - 1 && tid < hd) {
+        // the head, one element per thread: column tid mod N (copy 0: word c
+        // is column c mod N)
+        const int c = tid % N;
+        float v = to_f32(x[tid]);
         if constexpr (RES) {
-            float rv[V];
-            load_partial<XT, V>(r, hd, rv);
-#pragma unroll
-            for (int e = 0; e < V; ++e) v[e] = to_f32(from_f32<XT>(v[e] + rv[e]));
-            store_partial<XT, V>(h, hd, v);
+            v = to_f32(from_f32<XT>(v + to_f32(r[tid])));
+            h[tid] = from_f32<XT>(v);
         }
-#pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = __builtin_fmaf(sg[e], dyt_tanh<ACC>(alpha * v[e]), sb[e]);
-        store_partial<XT, V>(y, hd, v);
+        y[tid] = from_f32<XT>(__builtin_fmaf(sg[c], dyt_tanh<ACC>(alpha * v), sb[c]));
     }
     // the walk, from element hd on
     x += hd;

@@ -41,8 +41,9 @@ struct Plan {
     // launches keep the tiles above.
     bool flat = false;
     int64_t flat_grid = 0;
-    // The flat walk only where x and y start 16-byte aligned (2-byte packed
-    // tiles of one full slot, which stay ahead at other bases).
+    // The flat walk only where x and y start 16-byte aligned or can start it
+    // at an aligned element (2-byte packed tiles of one full slot, which stay
+    // ahead of an unaligned walk).
     bool flat_aligned_only = false;
     // The four shifted gamma/beta copies fit in LDS: the flat walk can start
     // at the first 16-byte-aligned element when the tensors do not.

@@ -282,8 +282,10 @@ typedef struct dyt_plan {
                               reports the forward's value; the backward always tiles */
     int64_t flat_grid;     /* workgroups of that flat forward, 0 if flat = 0 */
     int64_t flat_aligned_only; /* 1 if that flat walk is taken only when x and y start
-                              16-byte aligned (2-byte x in packed tiles of one full slot,
-                              which the tiles serve faster at other bases); 0 otherwise */
+                              16-byte aligned or off that grid by the same amount (the
+                              walk then starts at their first aligned element); 2-byte x
+                              in packed tiles of one full slot, which the tiles serve
+                              faster than an unaligned walk; 0 otherwise */
 } dyt_plan;
 
 int dyt_get_plan(int64_t M, int64_t N, int x_dtype, int param_dtype, int vector_access,

@@ -110,8 +110,9 @@ def test_flat_forward_matches_oracle_and_tiles(dyt, M, N, xdt, pdt):
     (1000, 2560, "bf16", 0), (777, 4104, "f32", 0), (4097, 1032, "f16", 0),
     (5001, 32, "bf16", 1), (3001, 64, "f16", 1), (3001, 1500, "bf16", 0), (777, 17, "bf16", 0)])
 def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
-    """x and y one element off 16-byte alignment: the same bits as aligned
-    (full one-slot packed tiles then run the tiles instead of the walk)."""
+    """x and y one element off 16-byte alignment (both by the same amount:
+    the walk starts at their first element on the 128-byte grid, also for
+    full one-slot packed tiles): the same bits as aligned."""
     inp, x, a, g, b = _inputs(dyt, M, N, xdt, "f32", seed=N)
     xt = TORCH_DT[xdt]
     plan = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
@@ -134,11 +135,13 @@ def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
 
 @pytest.mark.parametrize("M,N,xdt,xo,yo", [
     (1000, 2560, "bf16", 1, 3), (3001, 1500, "bf16", 2, 0), (777, 4104, "f32", 0, 1), (5, 3, "bf16", 3, 3),
-    (1, 5, "bf16", 5, 5)])
+    (1, 5, "bf16", 5, 5), (1000, 2560, "bf16", 1, 9), (777, 4104, "f32", 1, 5), (999, 1500, "bf16", 7, 7),
+    (5001, 32, "bf16", 1, 3), (5001, 32, "bf16", 3, 3)])   # one-slot packed: tiles, then the shifted walk
 def test_flat_forward_other_misalignments(dyt, M, N, xdt, xo, yo):
-    """x and y off the 16-byte grid by xo and yo elements (equal: the walk
-    starts at the first aligned element; different: it runs unaligned):
-    the same bits as the aligned call, canaries around y untouched."""
+    """x and y off the 16-byte grid by xo and yo elements (equal offsets
+    within a 128-byte line: the walk starts on the line grid; equal only
+    within 16 bytes: on the 16-byte grid; else it runs unaligned): the same
+    bits as the aligned call, canaries around y untouched."""
     inp, x, a, g, b = _inputs(dyt, M, N, xdt, "f32", seed=N + xo)
     xt = TORCH_DT[xdt]
     log(f"[flat-misaligned] M={M} N={N} x={xdt} xo={xo} yo={yo}")
