@@ -214,16 +214,17 @@ double occupancy(const Plan& p, int64_t N) {
 // packed one-slot tiles of full rows keep the lead (bf16 32 / 64 wide: 89.5 /
 // 90.9 against 92.3 / 92.6 us flat), while the flat walk keeps its own
 // (768 / 2,048 / 3,072 wide: 94.0-96.4 against 105.9-106.6 us), so the
-// former walk flat only from aligned bases (Plan::flat_aligned_only).
+// former walk flat only from aligned bases or from bases where the walk can
+// start aligned (DYT_FLAT_SHIFT; Plan::flat_aligned_only).
 // Rows that are not a whole number of vectors walk flat in the plain and
 // the residual forward (the LDS copy then holds 4 shifted copies per
-// parameter, N + V up to DYT_FLAT_RAG_MAX_LEN / _4B) for 2-byte x at any fill
-// and for float32 x below
-// DYT_FLAT_OCC_4B: bf16 rows of 3 / 17 / 100 / 255 / 511 / 1,001 / 1,500 /
-// 2,039: 81.9-88.4 us against 89.2-113.2 us for the shifted-slot tiles
-// (1,500 at a base one element off: 99.3 against 118.2); float32 1,501 (0.73
-// filled): 192.9 against 236.0 us, while full float32 tiles tie at 2^27
-// elements and win at 100,003 x 255 (37.3 against 41.2 us).
+// parameter, N + V up to DYT_FLAT_RAG_MAX_LEN / _4B) for 2-byte x at any
+// fill and for float32 x below DYT_FLAT_OCC_4B: bf16 rows of 3 / 17 / 100 /
+// 255 / 511 / 1,001 / 1,500 / 2,039: 81.9-88.4 us against 89.2-113.2 us for
+// the shifted-slot tiles (1,500 at a base one element off: 99.3 against
+// 118.2); float32 1,501 (0.73 filled): 192.9 against 236.0 us, while full
+// float32 tiles tie at 2^27 elements and win at 100,003 x 255 (37.3 against
+// 41.2 us).
 // The residual-fused forward (two inputs, two outputs) walks flat whenever
 // its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
 // the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:
@@ -250,7 +251,11 @@ double occupancy(const Plan& p, int64_t N) {
 #define DYT_FLAT_RAG_RES 1
 #endif
 // Tensors that start off the 16-byte grid (all by the same amount): the flat
-// walk starts at the first aligned element, with the ragged layout.
+// walk starts, with the ragged layout, at their first element on the
+// 128-byte line grid (else on the 16-byte grid). bf16 at +1 element: 2,560 /
+// 1,500 / 32 wide 87.6-87.9 / 85.4-85.5 / 81.7 us, against 95.5-96.0 / 99.1
+// for the unaligned walk and 89.9 for the 32-wide tiles (89.7 / 88.3 when
+// starting on the 16-byte grid).
 #ifndef DYT_FLAT_SHIFT
 #define DYT_FLAT_SHIFT 1
 #endif
@@ -260,7 +265,7 @@ double occupancy(const Plan& p, int64_t N) {
 #define DYT_FLAT_GRID 256
 #endif
 // Widest rows of the flat forward (gamma and beta as float32 in 64 KB of LDS;
-// 0 turns the flat walk off).
+// the measured range; 0 turns the flat walk off).
 #ifndef DYT_FLAT_MAX_N
 #define DYT_FLAT_MAX_N 8192
 #endif
