@@ -197,7 +197,7 @@ double occupancy(const Plan& p, int64_t N) {
 #endif
 // The flat forward (dyt_fwd_flat_kernel) serves contiguous rows whose length
 // is a multiple of the vector width and at most kFlatMaxN (gamma and beta as
-// float32 in at most 64 KB of LDS) when the tiles fit the rows poorly: for
+// float32 in at most 160 KB of LDS) when the tiles fit the rows poorly: for
 // 2-byte x, packed tiles (several rows each) at any fill and row segments
 // filled below DYT_FLAT_OCC_2B; for float32 x, tiles filled below
 // DYT_FLAT_OCC_4B. Measured on MI355X at 2^27 elements (interleaved medians
@@ -264,12 +264,15 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_GRID
 #define DYT_FLAT_GRID 256
 #endif
-// Widest rows of the flat forward (gamma and beta as float32 in 64 KB of LDS;
-// the measured range; 0 turns the flat walk off).
+// Widest rows of the flat forward (gamma and beta as float32 in the 160 KB
+// of LDS a gfx950 workgroup may hold; 0 turns the flat walk off). Above
+// 8,192 columns, measured at 2^27 elements: float32 9,216 / 10,240 / 13,312
+// / 14,336 wide (tiles 0.75 / 0.83 / 0.81 / 0.88 filled) 187.5-189.7 us
+// against 191.5-207.8 tiled; bf16 8,200 (0.80) 89.3 against 92.5.
 #ifndef DYT_FLAT_MAX_N
-#define DYT_FLAT_MAX_N 8192
+#define DYT_FLAT_MAX_N 20480
 #endif
-static_assert(DYT_FLAT_MAX_N <= 8192, "the flat forward stages 2 N floats in at most 64 KB of LDS");
+static_assert(DYT_FLAT_MAX_N <= 20480, "the flat forward stages 2 N floats in at most 160 KB of LDS");
 constexpr int64_t kFlatMaxN = DYT_FLAT_MAX_N;
 // Rows that are not whole vectors: longest copy (flat_rag_len words; 8 of
 // them, the four shifted copies of gamma and beta, in the 160 KB of LDS a

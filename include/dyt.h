@@ -273,7 +273,7 @@ typedef struct dyt_plan {
     int64_t ws_bytes;      /* workspace bytes this plan uses */
     int64_t flat;          /* forward: 1 if a contiguous launch walks the problem as one
                               run of 16-byte vectors instead of the tiles above (rows whose
-                              length is a multiple of vec, at most 8192, that the tiles
+                              length is a multiple of vec, at most 20480, that the tiles
                               fit poorly, and 2-byte x in packed tiles; rows that are
                               not: 2-byte x up to N + vec <= 3584,
                               float32 x up to N + vec <= 5120 when the tiles fit poorly);

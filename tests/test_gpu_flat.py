@@ -47,7 +47,10 @@ SHAPES = [
     (129, 1040, "bf16", "f16"),
     (4097, 1032, "f16", "f32"),
     (1234, 4100, "f32", "bf16"),
-    (300, 7372, "f32", "f32"),      # widest flat row: 59 KB of LDS
+    (300, 7372, "f32", "f32"),      # 59 KB of LDS
+    (1001, 13312, "f32", "f32"),    # above 8,192 columns: 104 KB of LDS
+    (601, 17408, "f32", "bf16"),    # 136 KB of LDS
+    (33, 8200, "bf16", "f32"),
     (5001, 32, "bf16", "f32"),      # packed tiles of one full slot (aligned bases only)
     (3001, 64, "f16", "bf16"),
     (999, 256, "bf16", "f32"),

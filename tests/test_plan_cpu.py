@@ -79,7 +79,7 @@ def _occupancy(p, N):
 
 def _check_flat(f, M, N, xdt, residual=False):
     """The forward walks flat exactly for rows of a whole number of 16-byte
-    vectors, at most 8,192 long, that its tiles fit poorly: filled below
+    vectors, at most 20,480 long, that its tiles fit poorly: filled below
     0.9 (float32 x); for 2-byte x, packed tiles or row segments filled below
     0.85; the residual-fused forward whenever its tiles leave a slot empty or
     are 2-byte packed tiles of two or more slots. The grid is one workgroup
@@ -100,7 +100,7 @@ def _check_flat(f, M, N, xdt, residual=False):
         fits = -(-(N + v) // 4) * 4 <= (5120 if xdt == "f32" else 3584)
         want = fits and (xdt != "f32" or occ < 0.9)
     else:
-        want = N <= 8192 and poor
+        want = N <= 20480 and poor
     assert f["flat"] == int(want)
     if want:
         assert f["flat_grid"] == max(1, min(256, -(-(M * N // v) // 1024)))
@@ -165,7 +165,9 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
     (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
     (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0),
-    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 0),
+    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 1),
+    (9216, "f32", 1), (13312, "f32", 1), (17408, "f32", 1), (18432, "f32", 0), (20480, "f32", 0),
+    (8200, "bf16", 1), (11264, "bf16", 0), (24576, "f32", 0),
     (2560, "f16", 1),
     # rows that are not a whole number of vectors
     (1500, "bf16", 1), (1001, "bf16", 1), (255, "bf16", 1), (17, "bf16", 1), (3, "bf16", 1),
