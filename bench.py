@@ -564,9 +564,9 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         f.write("\n".join(rows + cold_rows) + "\n")
 
 
-WIDTH_CASES = ([("bf16", n, 0) for n in (17, 255, 768, 1001, 1500, 1536, 2048, 2560, 3072, 4095, 4096, 4104,
-                                        5120, 6144, 7168, 8192, 10240)]
-               + [("f32", n, 0) for n in (1501, 2560, 4104, 5120)]
+WIDTH_CASES = ([("bf16", n, 0) for n in (17, 255, 768, 1001, 1500, 1536, 2048, 2560, 3071, 3072, 4095, 4096,
+                                        4104, 5120, 6144, 7168, 8192, 8200, 10240)]
+               + [("f32", n, 0) for n in (1501, 2560, 4104, 5120, 9216, 13312)]
                + [("bf16", 4096, 1), ("bf16", 2560, 1), ("bf16", 1500, 1), ("bf16", 32, 1), ("f32", 100, 1)])
 
 
