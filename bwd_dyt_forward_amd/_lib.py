@@ -120,6 +120,27 @@ def _stream(stream) -> int | None:
     return int(stream)
 
 
+def _keep_alive_on(stream, *made: torch.Tensor) -> None:
+    """Tensors this module allocated for a launch on an explicit stream other
+    than torch's current one: tell the caching allocator that `stream` uses
+    them, so that their memory is not handed out again (to work on the
+    current stream) before the kernels on `stream` are done with it."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        if int(stream) == cur.cuda_stream:
+            return
+        s = torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == cur.cuda_stream:
+        return
+    for t in made:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -141,7 +162,13 @@ def _pitch(t: torch.Tensor) -> int:
     return t.stride(0) if t.size(0) > 1 else t.size(1)
 
 
-def _check_params(N: int, alpha, *vecs) -> None:
+def _check_params(N: int, device, alpha, *vecs) -> None:
+    """alpha (one element) and gamma/beta (N elements each): contiguous device
+    tensors of one dtype on the activations' device. The kernels dereference
+    these pointers, so a host tensor must never reach the ABI."""
+    for name, t in (("alpha", alpha), *(("gamma/beta", v) for v in vecs)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a tensor on {device}, like the activations")
     if alpha.numel() != 1:
         raise ValueError("alpha must hold one element")
     for v in vecs:
@@ -158,7 +185,8 @@ def dyt_forward(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta:
     may be row-strided 2-D views (unit column stride); a new y is contiguous."""
     _check_act("x", x, strided=True)
     M, N = x.shape
-    _check_params(N, alpha, gamma, beta)
+    _check_params(N, x.device, alpha, gamma, beta)
+    made_y = y is None
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
@@ -174,6 +202,8 @@ def dyt_forward(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta:
         st = lib.dyt_forward_strided(_ptr(x), ldx, _ptr(alpha), _ptr(gamma), _ptr(beta), _ptr(y),
                                      ldy, M, N, _code(x.dtype), _code(alpha.dtype), _stream(stream))
         _check("dyt_forward_strided", st)
+    if made_y:
+        _keep_alive_on(stream, y)
     return y
 
 
@@ -193,9 +223,10 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
     M, N = x.shape
-    _check_params(N, alpha, gamma)
+    _check_params(N, x.device, alpha, gamma)
     pdt = alpha.dtype
     dev = x.device
+    made = [t is None for t in (dx, dalpha, dgamma, dbeta, workspace)]
     if dx is None:
         dx = torch.empty((M, N), dtype=x.dtype, device=dev)
     else:
@@ -224,6 +255,7 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
                                       _ptr(workspace), wbytes, M, N, _code(x.dtype), _code(pdt),
                                       _stream(stream))
         _check("dyt_backward_strided", st)
+    _keep_alive_on(stream, *(t for t, m in zip((dx, dalpha, dgamma, dbeta, workspace), made) if m))
     return dx, dalpha, dgamma, dbeta
 
 
@@ -234,7 +266,7 @@ def dyt_backward_partials(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor
     _check_act("x", x)
     _check_act("dy", dy)
     M, N = x.shape
-    _check_params(N, alpha, gamma)
+    _check_params(N, x.device, alpha, gamma)
     wbytes = workspace.numel() * workspace.element_size()
     st = lib.dyt_backward_partials(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx),
                                    _ptr(workspace), wbytes, M, N, _code(x.dtype),
@@ -268,7 +300,8 @@ def dyt_forward_residual(x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor,
     _check_act("x", x)
     _same("r", r, x)
     M, N = x.shape
-    _check_params(N, alpha, gamma, beta)
+    _check_params(N, x.device, alpha, gamma, beta)
+    made = [h is None, y is None]
     if h is None:
         h = torch.empty_like(x)
     if y is None:
@@ -277,6 +310,7 @@ def dyt_forward_residual(x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor,
                                   _ptr(y), M, N, _code(x.dtype), _code(alpha.dtype),
                                   _stream(stream))
     _check("dyt_forward_residual", st)
+    _keep_alive_on(stream, *(t for t, m in zip((h, y), made) if m))
     return h, y
 
 
@@ -290,9 +324,10 @@ def dyt_backward_residual(h: torch.Tensor, dy: torch.Tensor, dres: torch.Tensor,
     _same("dy", dy, h)
     _same("dres", dres, h)
     M, N = h.shape
-    _check_params(N, alpha, gamma)
+    _check_params(N, h.device, alpha, gamma)
     pdt = alpha.dtype
     dev = h.device
+    made = [t is None for t in (dh, dalpha, dgamma, dbeta, workspace)]
     if dh is None:
         dh = torch.empty_like(h)
     if dalpha is None:
@@ -310,6 +345,7 @@ def dyt_backward_residual(h: torch.Tensor, dy: torch.Tensor, dres: torch.Tensor,
                                    _ptr(workspace), wbytes, M, N, _code(h.dtype), _code(pdt),
                                    _stream(stream))
     _check("dyt_backward_residual", st)
+    _keep_alive_on(stream, *(t for t, m in zip((dh, dalpha, dgamma, dbeta, workspace), made) if m))
     return dh, dalpha, dgamma, dbeta
 
 
@@ -321,7 +357,7 @@ def dyt_backward_residual_partials(h: torch.Tensor, dy: torch.Tensor, dres: torc
     _same("dy", dy, h)
     _same("dres", dres, h)
     M, N = h.shape
-    _check_params(N, alpha, gamma)
+    _check_params(N, h.device, alpha, gamma)
     wbytes = workspace.numel() * workspace.element_size()
     st = lib.dyt_backward_residual_partials(_ptr(h), _ptr(dy), _ptr(dres), _ptr(alpha),
                                             _ptr(gamma), _ptr(dh), _ptr(workspace), wbytes, M, N,

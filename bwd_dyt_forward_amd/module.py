@@ -112,15 +112,20 @@ class DyTResidualFunction(torch.autograd.Function):
         h, alpha, gamma = ctx.saved_tensors
         shape = ctx.x_shape
         if grad_y is None:
-            dh = _dense_rows(grad_h.to(h.dtype))
-            return dh.view(shape), dh.view(shape), None, None, None
+            dh = _dense_rows(grad_h.to(h.dtype)).view(shape)
+            return dh, dh, None, None, None
         dy2 = _dense_rows(grad_y.to(h.dtype))
         if grad_h is None:
             dh, dalpha, dgamma, dbeta = _lib.dyt_backward(h, dy2, alpha, gamma)
         else:
             dres = _dense_rows(grad_h.to(h.dtype))
             dh, dalpha, dgamma, dbeta = _lib.dyt_backward_residual(h, dy2, dres, alpha, gamma)
-        return dh.view(shape), dh.view(shape), dalpha, dgamma, dbeta
+        # One tensor object for both inputs (as torch's own add backward does):
+        # two views would be two tensors on one storage, which gradient
+        # accumulation into leaf x and r would then both adopt, aliasing
+        # x.grad with r.grad. With one object it copies before it keeps one.
+        dh = dh.view(shape)
+        return dh, dh, dalpha, dgamma, dbeta
 
 
 def dyt_residual(x: torch.Tensor, r: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,

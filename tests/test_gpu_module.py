@@ -67,3 +67,55 @@ def test_module_rejects_wrong_width(dyt):
     layer = dyt.DyT(8, device="cuda")
     with pytest.raises(ValueError):
         layer(torch.randn(2, 9, device="cuda"))
+
+
+def test_residual_module_leaf_grads_accumulate_separately(dyt):
+    """x and r both leaves: each gets dh, in its own storage, and a second
+    backward pass doubles both (no aliasing between x.grad and r.grad)."""
+    layer = dyt.DyTResidual(64, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn(32, 64, device="cuda", generator=g).requires_grad_(True)
+    r = torch.randn(32, 64, device="cuda", generator=g).requires_grad_(True)
+
+    def loss():
+        h, y = layer(x, r)
+        return (y * y).sum() + 3 * h.sum()
+
+    loss().backward()
+    gx, gr = x.grad.clone(), r.grad.clone()
+    assert torch.equal(gx, gr) and x.grad.data_ptr() != r.grad.data_ptr()
+    loss().backward()
+    assert torch.equal(x.grad, 2 * gx) and torch.equal(r.grad, 2 * gr)
+    assert x.grad.data_ptr() != r.grad.data_ptr()
+
+
+def test_host_parameters_are_rejected_before_launch(dyt):
+    x = torch.randn(8, 16, device="cuda")
+    a, gm, bt = torch.tensor([0.5]), torch.ones(16), torch.zeros(16)
+    with pytest.raises(ValueError):
+        dyt.dyt_forward(x, a, gm.cuda(), bt.cuda())
+    with pytest.raises(ValueError):
+        dyt.dyt_forward(x, a.cuda(), gm, bt.cuda())
+    with pytest.raises(ValueError):
+        dyt.dyt_backward(x, x, a, gm.cuda())
+    with pytest.raises(ValueError):
+        dyt.dyt_forward_residual(x, x, a.cuda(), gm.cuda(), bt)
+
+
+def test_explicit_side_stream_matches_current_stream(dyt):
+    x = torch.randn(1000, 96, device="cuda")
+    dy = torch.randn(1000, 96, device="cuda")
+    a = torch.tensor([0.7], device="cuda")
+    gm, bt = torch.randn(96, device="cuda"), torch.randn(96, device="cuda")
+    y0 = dyt.dyt_forward(x, a, gm, bt)
+    b0 = dyt.dyt_backward(x, dy, a, gm)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for stream in (s, s.cuda_stream):
+        y1 = dyt.dyt_forward(x, a, gm, bt, stream=stream)
+        b1 = dyt.dyt_backward(x, dy, a, gm, stream=stream)
+        s.synchronize()
+        assert torch.equal(y0, y1)
+        for u, v in zip(b0, b1):
+            assert torch.equal(u, v)
