@@ -34,7 +34,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -49,27 +48,25 @@ SECONDARY = "c5_4194304x32_bf16_outliers"  # the narrow-row bulk shape the 60% t
 HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, vendor figure
 SETTLE_S = 0.3                         # minimum untimed warm-up wall time
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "bwd_dyt_forward_amd", "csrc", f)
-                  for f in ("dyt_api.hip", "dyt_kernels.hpp", "dyt_math.hpp", "dyt_tune_table.inc",
-                            "dyt_launch.hpp", "dyt_launch_impl.hpp")]
-
-
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _build_module():
+    """bwd_dyt_forward_amd/build.py, loaded by path (no torch, no library)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_dyt_build", os.path.join(ROOT, "bwd_dyt_forward_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel and launch sources with comments and blank space
-    removed, so that counter figures stay attached to the code they measured."""
-    import re
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p) as f:
-            src = f.read()
-        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        src = re.sub(r"//[^\n]*", "", src)
-        h.update(" ".join(src.split()).encode())
-    return h.hexdigest()[:16]
+    """Build id of the current sources (hash of the kernel, launch and host
+    sources without comments, and of the compiler flags), so that counter
+    figures stay attached to the code they measured."""
+    return _build_module().source_hash()
 
 
 def algorithmic_bytes(M: int, N: int, sx: int, sp: int) -> dict:

@@ -14,7 +14,7 @@ import os
 # (same SONAME), so torch's streams and allocations are valid across the ABI.
 import torch
 
-from .build import LIB_PATH
+from .build import LIB_PATH, source_hash
 
 DYT_F32 = 0
 DYT_BF16 = 1
@@ -69,6 +69,7 @@ SIGNATURES = {
                                               _i64, _i64, _int, _int, _vp]),
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
+    "dyt_build_id": (ctypes.c_char_p, []),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
     "dyt_get_forward_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
     "dyt_get_forward_residual_plan": (_int, [_i64, _i64, _int, _int, ctypes.POINTER(DytPlan)]),
@@ -89,6 +90,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if found != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {found}, this binding expects {ABI_VERSION}; "
                           "rebuild the library")
+    built, want = lib.dyt_build_id().decode(), source_hash()
+    if built != want:
+        raise ImportError(f"{path} was built from other sources (build id {built}, sources "
+                          f"{want}); rebuild it (python bwd_dyt_forward_amd/build.py)")
     return lib
 
 

@@ -5,7 +5,9 @@ and writes ``bwd_dyt_forward_amd/libdyt.so``. Cross-compiling needs no GPU.
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -43,6 +45,44 @@ HIPCC_FLAGS = [
 JOBS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
 
 
+# The library embeds BUILD_ID_MARK followed by the 16 hex digits of
+# source_hash() as it was at build time (and returns them from
+# dyt_build_id()), so a library can be matched to the sources it came from.
+BUILD_ID_MARK = b"DYT_BUILD_ID="
+
+
+def source_hash() -> str:
+    """Hash of every source the library is built from (kernels, launch and
+    host code, the tile table, the header) with comments and blank space
+    removed, and of the compiler flags: two trees with the same hash build
+    the same code."""
+    h = hashlib.sha256()
+    for p in DEPENDS:
+        with open(p) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(os.path.basename(p).encode() + b"\0")
+        h.update(" ".join(src.split()).encode() + b"\0")
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def built_id(path: str = LIB_PATH) -> str | None:
+    """The build id embedded in a built library (read from the file, without
+    loading it), or None if the file or the id is missing."""
+    try:
+        with open(path, "rb") as f:
+            data = f.read()
+    except OSError:
+        return None
+    at = data.find(BUILD_ID_MARK)
+    if at < 0:
+        return None
+    hexid = data[at + len(BUILD_ID_MARK): at + len(BUILD_ID_MARK) + 16]
+    return hexid.decode("ascii", "replace")
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -55,7 +95,7 @@ def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bo
     """Compile the library (and, by default, the reference streaming kernels
     next to the default library path); returns the library's path. Always
     recompiles."""
-    _compile(out, SOURCES, extra_flags, verbose)
+    _compile(out, SOURCES, [*(extra_flags or []), f'-DDYT_BUILD_ID="{source_hash()}"'], verbose)
     if with_stream_ref and out == LIB_PATH:
         _compile(STREAM_REF_PATH, [STREAM_REF_SOURCE], None, verbose)
     return out
@@ -87,10 +127,9 @@ def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbos
 
 
 def is_stale(path: str = LIB_PATH) -> bool:
-    if not os.path.exists(path):
-        return True
-    t = os.path.getmtime(path)
-    return any(os.path.getmtime(d) > t for d in DEPENDS)
+    """True if the library is missing or was built from other sources or
+    flags than the current ones (by content, not by file times)."""
+    return built_id(path) != source_hash()
 
 
 if __name__ == "__main__":

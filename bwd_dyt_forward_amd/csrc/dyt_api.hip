@@ -635,11 +635,21 @@ void fill_plan(const Plan& p, dyt_plan* out) {
     out->flat_aligned_only = 0;
 }
 
+// The build id, after a marker that lets a build step find it in the file
+// without loading the library.
+#ifndef DYT_BUILD_ID
+#define DYT_BUILD_ID "unknown"
+#endif
+__attribute__((used)) const char kBuildId[] = "DYT_BUILD_ID=" DYT_BUILD_ID;
+constexpr int kBuildIdSkip = sizeof("DYT_BUILD_ID=") - 1;
+
 }  // namespace
 
 extern "C" {
 
 int dyt_abi_version(void) { return DYT_ABI_VERSION; }
+
+const char* dyt_build_id(void) { return kBuildId + kBuildIdSkip; }
 
 const char* dyt_status_string(int status) {
     switch (status) {

@@ -245,6 +245,14 @@ const char* dyt_status_string(int status);
 int dyt_abi_version(void);
 
 /*
+ * Build id of the loaded library: 16 hex digits identifying the sources and
+ * compiler flags it was built from (static storage; never NULL). The Python
+ * binding refuses a library whose id differs from that of the sources next
+ * to it.
+ */
+const char* dyt_build_id(void);
+
+/*
  * Launch geometry the library would use (for tests and reports; pure host
  * function, no HIP calls). dyt_get_plan describes the backward (pass 1 tiles,
  * grid and workspace layout; fwd_grid is the forward's grid), which depends

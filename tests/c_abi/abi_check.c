@@ -19,6 +19,7 @@ int main(void) {
     dyt_plan p;
     expect(dyt_abi_version() == DYT_ABI_VERSION, "abi version matches the header");
     expect(strcmp(dyt_status_string(DYT_OK), "DYT_OK") == 0, "status string of DYT_OK");
+    expect(strlen(dyt_build_id()) == 16, "build id of 16 hex digits");
     expect(dyt_get_plan(32768, 4096, DYT_BF16, DYT_F32, 1, &p) == DYT_OK, "backward plan");
     expect(p.vec == 8 && p.block == 256 && p.ws_bytes > 0, "plan fields");
     expect(dyt_backward_workspace_size(32768, 4096, DYT_BF16, DYT_F32) >= (size_t)p.ws_bytes,

@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
         "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
         "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided",
-        "dyt_get_forward_residual_plan"])
+        "dyt_get_forward_residual_plan", "dyt_build_id"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -412,4 +412,36 @@ def test_c_caller_builds_links_and_runs(tmp_path):
     assert cc.returncode == 0, cc.stderr
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
-    assert "FAIL" not in run.stdout and run.stdout.count("ok ") == 9
+    assert "FAIL" not in run.stdout and run.stdout.count("ok ") == 10
+
+
+def test_library_build_id_matches_current_sources(dyt):
+    """The library under test was built from exactly these sources: the id
+    it returns, the id embedded in the file and the hash of the sources next
+    to it agree (the binding refuses to load otherwise)."""
+    from bwd_dyt_forward_amd import build
+    want = build.source_hash()
+    assert dyt.lib.dyt_build_id().decode() == want
+    assert build.built_id() == want
+    assert not build.is_stale()
+
+
+def test_source_hash_follows_code_and_flags_not_comments(tmp_path, monkeypatch):
+    from bwd_dyt_forward_amd import build
+    src = tmp_path / "k.hpp"
+    src.write_text("int a = 1;  // one\n")
+    monkeypatch.setattr(build, "DEPENDS", [str(src)])
+    h0 = build.source_hash()
+    src.write_text("/* one */ int a =\n 1;\n\n")
+    assert build.source_hash() == h0
+    src.write_text("int a = 2;\n")
+    h1 = build.source_hash()
+    assert h1 != h0
+    monkeypatch.setattr(build, "HIPCC_FLAGS", [*build.HIPCC_FLAGS, "-ffast-math"])
+    assert build.source_hash() != h1
+    # a library file carrying another id is stale
+    lib = tmp_path / "libx.so"
+    lib.write_bytes(b"\x7fELF..." + build.BUILD_ID_MARK + b"0123456789abcdef" + b"\0")
+    assert build.built_id(str(lib)) == "0123456789abcdef"
+    assert build.is_stale(str(lib))
+    assert build.built_id(str(tmp_path / "missing.so")) is None
