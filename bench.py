@@ -659,6 +659,294 @@ def report_widths(dyt, torch, path: str, steps: int = 20, warmup: int = 5, round
         f.write("\n".join(rows) + "\n")
 
 
+TIMELINE_FLAGS = ["-DDYT_WG_TIMELINE=1"]
+
+
+def timeline_library():
+    """The library built with the workgroup timeline compiled in
+    (bwd_dyt_forward_amd/libdyt_timeline.so; built here if missing or
+    stale), loaded beside the default one with the same C signatures plus
+    dyt_timeline_set."""
+    import ctypes
+    b = _build_module()
+    path = os.path.join(ROOT, "bwd_dyt_forward_amd", "libdyt_timeline.so")
+    if b.is_stale(path, TIMELINE_FLAGS):
+        log("[bench] building the workgroup-timeline variant of the library")
+        b.build(out=path, extra_flags=TIMELINE_FLAGS, with_stream_ref=False)
+    from bwd_dyt_forward_amd import _lib
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    for name, (res, argtypes) in _lib.SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = argtypes
+    lib.dyt_timeline_set.restype = ctypes.c_int
+    lib.dyt_timeline_set.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _timeline_stats(st, tick_us: float) -> dict:
+    """Summary of one launch's workgroup records st (G x 4 int64: entry,
+    loop end, exit, ids), times in us from the earliest entry."""
+    import numpy as np
+    t = st[:, :3].astype(np.float64)
+    t0 = t[:, 0].min()
+    t = (t - t0) * tick_us
+    xcc = (st[:, 3] >> 32) & 0xF
+    ex = t[:, 2]
+    per_xcd = {}
+    for k in range(8):
+        m = xcc == k
+        if m.any():
+            per_xcd[k] = (float(np.median(ex[m])), float(ex[m].max()), int(m.sum()),
+                          float(np.median(t[m, 1] - t[m, 0])))
+    return {
+        "span": float(ex.max()),
+        "entry_spread": float(t[:, 0].max()),
+        "exit_min": float(ex.min()), "exit_median": float(np.median(ex)), "exit_max": float(ex.max()),
+        "end_phase": float(np.median(t[:, 2] - t[:, 1])),
+        "tail": float(ex.max() - np.median(ex)),
+        "per_xcd": per_xcd,
+        "late": [(int(i), int(xcc[i]), float(ex[i])) for i in np.argsort(-ex)[:6]],
+    }
+
+
+def report_wg_timeline(torch, path: str, reps: int = 30,
+                       names=(HEADLINE, SECONDARY)) -> None:
+    """Per-workgroup timeline of the forward and backward pass 1 in steady
+    back-to-back steps (forward, pass 1, pass 2), from the timeline build of
+    the library: when each workgroup starts, ends its streaming loop and
+    exits, and on which XCD it ran. Writes a Markdown summary to path."""
+    import numpy as np
+    import workloads
+    from bwd_dyt_forward_amd import _lib
+    lib = timeline_library()
+    tick_us = 0.01          # the real-time counter runs at 100 MHz
+    rows = [f"# Workgroup timeline: forward and backward pass 1", "",
+            f"Command: `python bench.py --wg-timeline {path}` "
+            f"(library built with {' '.join(TIMELINE_FLAGS)}; {reps} recorded steps after "
+            f"{SETTLE_S} s of untimed steps; medians over the recorded steps). "
+            f"Device: {torch.cuda.get_device_name(0)}.", "",
+            "Times in us from the launch's earliest workgroup entry (real-time counter, "
+            "100 MHz). span = last exit; tail = last exit - median exit; end phase = "
+            "exit - end of the streaming loop (reduction and partial-row write in pass 1).", ""]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    for name in names:
+        inp = workloads.generate(name)
+        xdt, pdt = tdt[inp.x_dtype], tdt[inp.p_dtype]
+        dev = torch.device("cuda:0")
+        x = torch.from_numpy(inp.x).to(dev).to(xdt)
+        dy = torch.from_numpy(inp.dy).to(dev).to(xdt)
+        a = torch.from_numpy(inp.alpha).to(dev).to(pdt)
+        g = torch.from_numpy(inp.gamma).to(dev).to(pdt)
+        b = torch.from_numpy(inp.beta).to(dev).to(pdt)
+        M, N = inp.M, inp.N
+        del inp
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        da = torch.empty(1, dtype=pdt, device=dev)
+        dg = torch.empty(N, dtype=pdt, device=dev)
+        db = torch.empty(N, dtype=pdt, device=dev)
+        xc, pc = _lib._code(xdt), _lib._code(pdt)
+        need = lib.dyt_backward_workspace_size(M, N, xc, pc)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        s = torch.cuda.current_stream()
+        sp = s.cuda_stream
+        pl = _lib.DytPlan()
+        assert lib.dyt_get_plan(M, N, xc, pc, 1, ctypes_byref(pl)) == 0
+        fpl = _lib.DytPlan()
+        assert lib.dyt_get_forward_plan(M, N, xc, pc, 1, ctypes_byref(fpl)) == 0
+        gf = fpl.flat_grid if fpl.flat else fpl.fwd_grid
+        gb = pl.bwd_grid
+        fst = torch.zeros((reps, gf, 4), dtype=torch.int64, device=dev)
+        pst = torch.zeros((reps, gb, 4), dtype=torch.int64, device=dev)
+
+        def step(r=None):
+            lib.dyt_timeline_set(None if r is None else fst[r].data_ptr())
+            assert lib.dyt_forward(x.data_ptr(), a.data_ptr(), g.data_ptr(), b.data_ptr(),
+                                   y.data_ptr(), M, N, xc, pc, sp) == 0
+            lib.dyt_timeline_set(None if r is None else pst[r].data_ptr())
+            assert lib.dyt_backward_partials(x.data_ptr(), dy.data_ptr(), a.data_ptr(), g.data_ptr(),
+                                             dx.data_ptr(), ws.data_ptr(), ws.numel(), M, N, xc, pc,
+                                             sp) == 0
+            lib.dyt_timeline_set(None)
+            assert lib.dyt_backward_finish(ws.data_ptr(), ws.numel(), da.data_ptr(), dg.data_ptr(),
+                                           db.data_ptr(), M, N, xc, pc, sp) == 0
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            step()
+        e1.record(s)
+        e1.synchronize()
+        plain_us = e0.elapsed_time(e1) * 1e3 / reps
+        e0.record(s)
+        for r in range(reps):
+            step(r)
+        e1.record(s)
+        e1.synchronize()
+        rec_us = e0.elapsed_time(e1) * 1e3 / reps
+        fa, pa = fst.cpu().numpy(), pst.cpu().numpy()
+        del x, dy, y, dx, ws, fst, pst
+        torch.cuda.empty_cache()
+        rows += [f"## {name} ({M} x {N})", "",
+                 f"Step time (forward + pass 1 + pass 2): {plain_us:.1f} us without recording, "
+                 f"{rec_us:.1f} us while recording.", ""]
+        for kname, arr, grid in (("forward" + (" (flat walk)" if fpl.flat else ""), fa, gf),
+                                 ("backward pass 1", pa, gb)):
+            sts = [_timeline_stats(arr[r], tick_us) for r in range(reps)]
+            med = lambda k: statistics.median(st[k] for st in sts)
+            rows += [f"### {kname}: {grid} workgroups", "",
+                     "| span | entry spread | first exit | median exit | last exit | tail | end phase |",
+                     "|---:|---:|---:|---:|---:|---:|---:|",
+                     f"| {med('span'):.2f} | {med('entry_spread'):.2f} | {med('exit_min'):.2f} | "
+                     f"{med('exit_median'):.2f} | {med('exit_max'):.2f} | {med('tail'):.2f} | "
+                     f"{med('end_phase'):.2f} |", "",
+                     "| XCD | workgroups | median exit | last exit | median loop time |",
+                     "|---:|---:|---:|---:|---:|"]
+            for k in range(8):
+                vals = [st["per_xcd"][k] for st in sts if k in st["per_xcd"]]
+                if not vals:
+                    continue
+                rows.append(f"| {k} | {vals[0][2]} | {statistics.median(v[0] for v in vals):.2f} | "
+                            f"{statistics.median(v[1] for v in vals):.2f} | "
+                            f"{statistics.median(v[3] for v in vals):.2f} |")
+            late = {}
+            for st in sts:
+                for i, k, _t in st["late"]:
+                    late[(i, k)] = late.get((i, k), 0) + 1
+            top = sorted(late.items(), key=lambda kv: -kv[1])[:8]
+            rows += ["", "Workgroups most often among the six last to exit (index, XCD: times): " +
+                     ", ".join(f"{i} (XCD {k}): {n}" for (i, k), n in top), ""]
+        log(f"[bench] timeline {name}: step {plain_us:.1f} us plain, {rec_us:.1f} us recording")
+    with open(path, "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
+# Library variants that --variants times against the default build: a
+# compile-time option each, measured, not adopted (the reasons are in the
+# written report).
+VARIANTS = {
+    # pass 1's last workgroup (by an arrival counter in the workspace) sums
+    # the partial rows itself instead of a second launch
+    "fused_finish": ["-DDYT_FUSED_FIN=1"],
+}
+
+
+def variant_library(name: str):
+    import ctypes
+    flags = VARIANTS[name]
+    b = _build_module()
+    path = os.path.join(ROOT, "bwd_dyt_forward_amd", f"libdyt_variant_{name}.so")
+    if b.is_stale(path, flags):
+        log(f"[bench] building library variant {name} ({' '.join(flags)})")
+        b.build(out=path, extra_flags=flags, with_stream_ref=False)
+    from bwd_dyt_forward_amd import _lib
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    for fn_name, (res, argtypes) in _lib.SIGNATURES.items():
+        fn = getattr(lib, fn_name)
+        fn.restype = res
+        fn.argtypes = argtypes
+    return lib
+
+
+def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
+    """Each named library variant against the default build on every
+    workload: the backward's outputs compared bit for bit, then whole steps
+    (forward, then the backward of the library under test) timed in
+    interleaved rounds of back-to-back steps; medians. Writes Markdown."""
+    import workloads
+    from bwd_dyt_forward_amd import _lib
+    libs = {"default": dyt.lib}
+    for n in names:
+        libs[n] = variant_library(n)
+    rows = ["# Library variants against the default build", "",
+            f"Command: `python bench.py --variants {','.join(names)} --variants-report {path}`. "
+            f"Device: {torch.cuda.get_device_name(0)}. " +
+            "; ".join(f"{n}: {' '.join(VARIANTS[n])}" for n in names) + ".", "",
+            f"Step = forward (default library) + backward (`dyt_backward` of the library under test), "
+            f"back to back; us per step, median of {rounds} interleaved rounds. 'bitwise' compares "
+            "dx, dgamma, dbeta and dalpha with the default build's.", "",
+            "| workload | " + " | ".join(libs) + " | bitwise |",
+            "|---|" + "---:|" * len(libs) + "---|"]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream()
+    sp = s.cuda_stream
+    for name in workloads.config_names():
+        inp = workloads.generate(name)
+        xdt, pdt = tdt[inp.x_dtype], tdt[inp.p_dtype]
+        x = torch.from_numpy(inp.x).to(dev).to(xdt)
+        dy = torch.from_numpy(inp.dy).to(dev).to(xdt)
+        a = torch.from_numpy(inp.alpha).to(dev).to(pdt)
+        g = torch.from_numpy(inp.gamma).to(dev).to(pdt)
+        b = torch.from_numpy(inp.beta).to(dev).to(pdt)
+        M, N = inp.M, inp.N
+        del inp
+        xc, pc = _lib._code(xdt), _lib._code(pdt)
+        y = torch.empty_like(x)
+        bufs = {}
+        for v, L in libs.items():
+            need = L.dyt_backward_workspace_size(M, N, xc, pc)
+            # zero-filled: a variant may keep counters in the workspace
+            bufs[v] = (torch.zeros(max(need, 16), dtype=torch.uint8, device=dev), torch.empty_like(x),
+                       torch.empty(1, dtype=pdt, device=dev), torch.empty(N, dtype=pdt, device=dev),
+                       torch.empty(N, dtype=pdt, device=dev))
+
+        def bwd(v):
+            ws, dx, da, dg, db = bufs[v]
+            rc = libs[v].dyt_backward(x.data_ptr(), dy.data_ptr(), a.data_ptr(), g.data_ptr(), dx.data_ptr(),
+                                      da.data_ptr(), dg.data_ptr(), db.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      M, N, xc, pc, sp)
+            if rc != 0:
+                raise RuntimeError(f"variant {v}: dyt_backward returned {rc}")
+
+        def step(v):
+            dyt.dyt_forward(x, a, g, b, y=y, stream=s)
+            bwd(v)
+
+        same = []
+        for v in libs:
+            for _ in range(2):
+                bwd(v)
+            torch.cuda.synchronize()
+            same.append(all(torch.equal(p.view(torch.uint8), q.view(torch.uint8))
+                            for p, q in zip(bufs[v][1:], bufs["default"][1:])))
+        reps = 10 if M * N >= (1 << 26) else 20
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            for v in libs:
+                step(v)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        us = {v: [] for v in libs}
+        order = list(libs)
+        for r in range(rounds):
+            for k in range(len(order)):
+                v = order[(r + k) % len(order)]
+                e0.record(s)
+                for _ in range(reps):
+                    step(v)
+                e1.record(s)
+                e1.synchronize()
+                us[v].append(e0.elapsed_time(e1) * 1e3 / reps)
+        rows.append(f"| {name} | " + " | ".join(f"{statistics.median(us[v]):.2f}" for v in libs) +
+                    f" | {'equal' if all(same) else 'DIFFERENT'} |")
+        log(f"[bench] variants {name}: " + ", ".join(f"{v} {statistics.median(us[v]):.2f}" for v in libs))
+        del x, dy, y, bufs
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        f.write("\n".join(rows) + "\n")
+
+
+def ctypes_byref(obj):
+    import ctypes
+    return ctypes.byref(obj)
+
+
 def load_traffic(kernel: str) -> dict | None:
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -691,6 +979,13 @@ def main() -> int:
                     help="also time awkward row widths and unaligned bases and write a Markdown table to FILE")
     ap.add_argument("--width-cases", default=None,
                     help="with --widths: only these cases, e.g. 'bf16:2560,f32:4104,bf16:4096+1'")
+    ap.add_argument("--wg-timeline", metavar="FILE", default=None,
+                    help="only record the per-workgroup timeline of the forward and backward pass 1 "
+                         "(timeline build of the library) and write a Markdown summary to FILE")
+    ap.add_argument("--variants", default=None,
+                    help="only time these library variants (comma-separated names of VARIANTS) "
+                         "against the default build on every workload")
+    ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -707,6 +1002,15 @@ def main() -> int:
     import __graft_entry__ as ge
     ge._ensure_built()
     import bwd_dyt_forward_amd as dyt
+
+    if args.variants:
+        report_variants(dyt, torch, args.variants_report, args.variants.split(","))
+        log(f"[bench] variant report written to {args.variants_report}")
+        return 0
+    if args.wg_timeline:
+        report_wg_timeline(torch, args.wg_timeline)
+        log(f"[bench] workgroup timeline written to {args.wg_timeline}")
+        return 0
 
     main_res = measure(dyt, torch, args.workload, args.steps, args.warmup)
     log(f"[bench] {json.dumps(main_res)}")

@@ -51,11 +51,11 @@ JOBS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffi
 BUILD_ID_MARK = b"DYT_BUILD_ID="
 
 
-def source_hash() -> str:
+def source_hash(extra_flags=()) -> str:
     """Hash of every source the library is built from (kernels, launch and
     host code, the tile table, the header) with comments and blank space
-    removed, and of the compiler flags: two trees with the same hash build
-    the same code."""
+    removed, and of the compiler flags (plus the extra flags of a variant
+    build): two trees with the same hash build the same code."""
     h = hashlib.sha256()
     for p in DEPENDS:
         with open(p) as f:
@@ -64,7 +64,7 @@ def source_hash() -> str:
         src = re.sub(r"//[^\n]*", "", src)
         h.update(os.path.basename(p).encode() + b"\0")
         h.update(" ".join(src.split()).encode() + b"\0")
-    h.update(" ".join(HIPCC_FLAGS).encode())
+    h.update(" ".join([*HIPCC_FLAGS, *extra_flags]).encode())
     return h.hexdigest()[:16]
 
 
@@ -95,7 +95,8 @@ def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bo
     """Compile the library (and, by default, the reference streaming kernels
     next to the default library path); returns the library's path. Always
     recompiles."""
-    _compile(out, SOURCES, [*(extra_flags or []), f'-DDYT_BUILD_ID="{source_hash()}"'], verbose)
+    extra = list(extra_flags or [])
+    _compile(out, SOURCES, [*extra, f'-DDYT_BUILD_ID="{source_hash(extra)}"'], verbose)
     if with_stream_ref and out == LIB_PATH:
         _compile(STREAM_REF_PATH, [STREAM_REF_SOURCE], None, verbose)
     return out
@@ -126,10 +127,10 @@ def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbos
         os.replace(tmp, out)
 
 
-def is_stale(path: str = LIB_PATH) -> bool:
+def is_stale(path: str = LIB_PATH, extra_flags=()) -> bool:
     """True if the library is missing or was built from other sources or
     flags than the current ones (by content, not by file times)."""
-    return built_id(path) != source_hash()
+    return built_id(path) != source_hash(extra_flags)
 
 
 if __name__ == "__main__":

@@ -374,6 +374,16 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     p.ld = round_up(2 * p.wcols + 1, 4);
     p.fin_grid = ceil_div(2 * N + 1, 64);
     p.ws_bytes = p.grid * p.ld * (int64_t)sizeof(float);
+#if DYT_FUSED_FIN
+#ifndef DYT_FUSED_FIN_MAX
+#define DYT_FUSED_FIN_MAX (1 << 20)
+#endif
+    if (dir == Dir::Bwd && p.nb == 1 && p.ws_bytes <= DYT_FUSED_FIN_MAX) {
+        p.fused = true;
+        p.ctr_off = round_up(p.ws_bytes, 128);
+        p.ws_bytes = p.ctr_off + 128;
+    }
+#endif
     return DYT_OK;
 }
 
@@ -388,8 +398,21 @@ Plan variant_for(const Plan& p, bool vector) {
     return q;
 }
 
+#if DYT_WG_TIMELINE
+// Workgroup timeline buffer of the next launches (measurement builds only;
+// set by dyt_timeline_set).
+uint64_t* g_stamps = nullptr;
+#endif
+
 Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     Geo g;
+#if DYT_WG_TIMELINE
+    g.stamps = g_stamps;
+#endif
+#if DYT_FUSED_FIN
+    g.fin_out[0] = g.fin_out[1] = g.fin_out[2] = nullptr;
+    g.ctr = nullptr;
+#endif
     g.total = M * N;
     g.ntiles = p.tiles;
     g.N = N;
@@ -508,7 +531,7 @@ int validate_backward(const void* x, const void* dy, const void* dres, bool use_
 }
 
 int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int x_dtype,
-                  int param_dtype, hipStream_t s) {
+                  int param_dtype, hipStream_t s, void* const* fin_out = nullptr) {
     if (M == 0 || N == 0) return DYT_OK;
     const bool res = a.dres != nullptr;
     const int64_t ldx = pitch_or(a.ldx, N), lddy = pitch_or(a.lddy, N), lddx = pitch_or(a.lddx, N);
@@ -519,6 +542,16 @@ int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int 
     g.pitch[0] = ldx;
     g.pitch[1] = lddy;
     g.pitch[2] = lddx;
+#if DYT_FUSED_FIN
+    g.fin_out[0] = g.fin_out[1] = g.fin_out[2] = nullptr;
+    g.ctr = nullptr;
+    if (fin_out && base.fused) {
+        for (int k = 0; k < 3; ++k) g.fin_out[k] = fin_out[k];
+        g.ctr = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(a.ws) + base.ctr_off);
+    }
+#else
+    (void)fin_out;
+#endif
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return dyt::host::launch_backward<decltype(xt)>(param_dtype, res, strided, p, g, a, s);
     });
@@ -584,6 +617,9 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     const bool bases16 = aligned(a.x, 16) && aligned(a.y, 16);
     if (base.flat && !strided && (bases16 || head > 0 || !base.flat_aligned_only)) {
         FlatGeo f;
+#if DYT_WG_TIMELINE
+        f.stamps = g_stamps;
+#endif
         f.head = (int32_t)head;
         f.pad_ = 0;
         f.total = M * N - head;
@@ -616,6 +652,12 @@ int backward_impl(const BwdPtrs& a, bool res, void* dalpha, void* dgamma, void* 
                                dbeta, a.ws, workspace_bytes, M, N, x_dtype, param_dtype, true,
                                true, base, a.ldx, a.lddy, a.lddx);
     if (st != DYT_OK) return st;
+#if DYT_FUSED_FIN
+    if (base.fused && M > 0 && N > 0) {
+        void* outs[3] = {dgamma, dbeta, dalpha};
+        return enqueue_pass1(base, a, M, N, x_dtype, param_dtype, s, outs);
+    }
+#endif
     st = enqueue_pass1(base, a, M, N, x_dtype, param_dtype, s);
     if (st != DYT_OK) return st;
     return enqueue_pass2(base, a.ws, dalpha, dgamma, dbeta, N, param_dtype, s);
@@ -650,6 +692,17 @@ extern "C" {
 int dyt_abi_version(void) { return DYT_ABI_VERSION; }
 
 const char* dyt_build_id(void) { return kBuildId + kBuildIdSkip; }
+
+#if DYT_WG_TIMELINE
+// Measurement builds only (not part of the ABI in dyt.h): the device buffer
+// (4 words per workgroup, large enough for the grid) that the forward and
+// backward pass-1 launches enqueued after this call record their workgroup
+// timeline into; NULL stops recording.
+int dyt_timeline_set(void* device_buffer) {
+    g_stamps = static_cast<uint64_t*>(device_buffer);
+    return DYT_OK;
+}
+#endif
 
 const char* dyt_status_string(int status) {
     switch (status) {

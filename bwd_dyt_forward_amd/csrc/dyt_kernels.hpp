@@ -72,6 +72,41 @@ constexpr int kSlotsMax = 4;            // largest K of the vector kernels
 constexpr int kFinBlock = 1024;   // pass-2 threads: 64 outputs x 16 segments
 constexpr int kFinSegs = kFinBlock / 64;
 
+// Workgroup timeline, compiled in only for measurement builds
+// (-DDYT_WG_TIMELINE=1): thread 0 of each workgroup of the forward kernels
+// and of backward pass 1 records the constant-rate real-time counter at
+// entry (word 0), at the end of its streaming loop (word 1) and at exit
+// (word 2), and the XCD and hardware ids it ran on (word 3: XCC_ID << 32 |
+// HW_ID), at 4 words per workgroup of a buffer the host supplies (null: no
+// record). Default builds carry none of it.
+#ifndef DYT_WG_TIMELINE
+#define DYT_WG_TIMELINE 0
+#endif
+#ifndef DYT_FUSED_FIN
+#define DYT_FUSED_FIN 0
+#endif
+#if DYT_WG_TIMELINE
+#define DYT_STAMPS_FIELD uint64_t* stamps;
+__device__ __forceinline__ void wg_stamp(uint64_t* s, int k) {
+    if (s && threadIdx.x == 0) s[blockIdx.x * 4 + k] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void wg_stamp_exit(uint64_t* s) {
+    if (s && threadIdx.x == 0) {
+        uint32_t xcc, hw;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        s[blockIdx.x * 4 + 2] = __builtin_amdgcn_s_memrealtime();
+        s[blockIdx.x * 4 + 3] = ((uint64_t)xcc << 32) | hw;
+    }
+}
+#define DYT_STAMP(G, k) wg_stamp((G).stamps, (k))
+#define DYT_STAMP_EXIT(G) wg_stamp_exit((G).stamps)
+#else
+#define DYT_STAMPS_FIELD
+#define DYT_STAMP(G, k) ((void)0)
+#define DYT_STAMP_EXIT(G) ((void)0)
+#endif
+
 struct Geo {
     int64_t total;     // M * N
     int64_t ntiles;
@@ -85,6 +120,15 @@ struct Geo {
     // Row pitches (elements) of the activations of a strided launch: forward
     // x (and r), y (and h); backward x (and dres), dy, dx. N when contiguous.
     int64_t pitch[3];
+    DYT_STAMPS_FIELD
+#if DYT_FUSED_FIN
+    // Fused finish (backward pass 1 only): when fin_out[0] is set, the
+    // workgroup that finishes last sums the partial rows and writes dgamma,
+    // dbeta, dalpha (fin_out[0..2], parameter dtype); ctr is the workspace's
+    // arrival counter (zero on entry, left zero).
+    void* fin_out[3];
+    unsigned* ctr;
+#endif
 };
 
 struct FinGeo {
@@ -550,6 +594,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
+    DYT_STAMP(g, 0);
 
     float gm[K][V], bt[K][V];
 #pragma unroll
@@ -602,6 +647,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         fwd_load<XT, V, K, 1, RES>(x, r, w.col_base + u * ai.upitch, ai, x1, r1);
         fwd_tile<XT, V, K, 1, ACC, RES>(x1, r1, y, h, w.col_base + u * ao.upitch, ao, gm, bt, alpha);
     }
+    DYT_STAMP(g, 1);
 
     if (PACKED && w.tail) {
         const int64_t ti = w.units * ai.upitch;   // the partial tile, input side
@@ -637,6 +683,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             }
         }
     }
+    DYT_STAMP_EXIT(g);
 }
 
 // ------------------------------------------------------------ flat forward
@@ -683,6 +730,7 @@ struct FlatGeo {
     int32_t cstep;     // (G * U * kBlock * V) mod N
     int32_t head;      // RAG only: elements before the walk (< 128 bytes), one per thread
     int32_t pad_;
+    DYT_STAMPS_FIELD
 };
 
 template <typename XT, int U, bool RES>
@@ -759,6 +807,7 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     using R = Raw<XT, V>;
     constexpr bool ACC = std::is_same<XT, float>::value;
     extern __shared__ float4 flat_lds[];
+    DYT_STAMP(f, 0);
     const int N = f.N;
     const int L = RAG ? flat_rag_len(N, V) : N;         // words per copy
     const int NW = RAG ? 4 * L : N;                     // LDS words per parameter
@@ -837,6 +886,7 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         }
         if (iters & 1) flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
     }
+    DYT_STAMP(f, 1);
     // The partial group: its owner's columns have advanced to group ngroups.
     if (ngroups * B < f.nvec && w == ngroups % G) {
 #pragma unroll
@@ -871,7 +921,68 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             store_partial<XT, V>(y + t0, n, v);
         }
     }
+    DYT_STAMP_EXIT(f);
 }
+
+#if DYT_FUSED_FIN
+// The finish of pass 2 done by one workgroup of kBlock threads, in pass 2's
+// summation order (16 contiguous row segments, each summed in row order from
+// 0, then the 16 segment sums in order), so the results equal pass 2's bit
+// for bit. Output j < N sits at column j of the partial rows (dgamma),
+// N <= j < 2N at wcols + j - N (dbeta), j = 2N at 2 wcols (dalpha). Threads
+// take 16 outputs x 16 segments per round, several rounds in flight.
+template <typename PT>
+__device__ void finish_in_workgroup(const float* __restrict__ ws, int64_t P, int ld, int64_t N,
+                                    int wcols, PT* __restrict__ dg, PT* __restrict__ db,
+                                    PT* __restrict__ da) {
+    constexpr int kR = 4;                       // rounds in flight
+    __shared__ float seg_sum[kR][16][16];
+    const int tid = threadIdx.x;
+    const int seg = tid >> 4, c = tid & 15;
+    const int64_t nout = 2 * N + 1;
+    const int64_t i0 = seg * P / 16, i1 = (seg + 1) * P / 16;
+    for (int64_t base = 0; base < nout; base += 16 * kR) {
+        float acc[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int64_t j = base + r * 16 + c;
+            int64_t off = 0;
+            if (j < N) off = j;
+            else if (j < 2 * N) off = wcols + (j - N);
+            else off = 2 * (int64_t)wcols;
+            acc[r] = 0.0f;
+            const bool ok = j < nout;
+            const float* __restrict__ p = ws + i0 * ld + off;
+            int64_t i = i0;
+            for (; i + 16 <= i1; i += 16, p += 16 * (int64_t)ld) {
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) v[q] = ok ? p[q * (int64_t)ld] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[r] += v[q];
+            }
+            for (; i < i1; ++i, p += ld) acc[r] += ok ? *p : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) seg_sum[r][seg][c] = acc[r];
+        __syncthreads();
+        if (tid < 16 * kR) {
+            const int r = tid >> 4, cc = tid & 15;
+            const int64_t j = base + r * 16 + cc;
+            if (j < nout) {
+                float t = seg_sum[r][0][cc];
+#pragma unroll
+                for (int q = 1; q < 16; ++q) t += seg_sum[r][q][cc];
+                const PT out = from_f32<PT>(t);
+                if (j < N) dg[j] = out;
+                else if (j < 2 * N) db[j - N] = out;
+                else da[0] = out;
+            }
+        }
+        __syncthreads();
+    }
+}
+#endif
 
 // ---------------------------------------------------------------- backward
 // Pass 1: dx, plus one float32 partial row per workgroup.
@@ -966,6 +1077,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[2]) : ax;
+    DYT_STAMP(g, 0);
 
     float gm[K][V], ag[K][V], ab[K][V];
     float aa[K];     // dalpha partial per slot: unused slots are dropped at the end
@@ -1067,6 +1179,8 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             }
         }
     }
+
+    DYT_STAMP(g, 1);
 
     // ---- workgroup reduction into one partial row
     float* __restrict__ wrow = ws + wg * (int64_t)g.ld;
@@ -1211,7 +1325,26 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
         for (int q = 1; q < kBlock / 64; ++q) s += red[q];
         wrow[2 * g.wcols] = s;
     }
+#if DYT_FUSED_FIN
+    if (g.fin_out[0] != nullptr) {
+        // publish this workgroup's partial row at device scope, then count it
+        __threadfence();
+        __syncthreads();
+        __shared__ unsigned ticket;
+        if (tid == 0)
+            ticket = __hip_atomic_fetch_add(g.ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket == (unsigned)(G - 1)) {
+            __threadfence();   // every workgroup's row is visible to every thread here
+            finish_in_workgroup<PT>(ws, G, g.ld, g.N, g.wcols, (PT*)g.fin_out[0],
+                                    (PT*)g.fin_out[1], (PT*)g.fin_out[2]);
+            if (tid == 0) __hip_atomic_store(g.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+#endif
+    DYT_STAMP_EXIT(g);
 }
+
 
 // Pass 2: out[j] = fixed-order sum of the partial rows' column j, rounded to
 // the parameter dtype. Outputs j < N are dgamma, N <= j < 2N dbeta, j = 2N

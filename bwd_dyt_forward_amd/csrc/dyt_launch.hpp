@@ -48,6 +48,12 @@ struct Plan {
     // The four shifted gamma/beta copies fit in LDS: the flat walk can start
     // at the first 16-byte-aligned element when the tensors do not.
     bool flat_shift = false;
+#if DYT_FUSED_FIN
+    // Backward: pass 1's last workgroup does the finish (no pass-2 launch);
+    // the arrival counter sits at byte ctr_off of the workspace.
+    bool fused = false;
+    int64_t ctr_off = 0;
+#endif
 };
 
 // Device pointers of one launch; r/h (forward) and dres (backward) are null

@@ -86,3 +86,55 @@ def assert_reports(tag, reps):
         log(f"  {tag}: {rep}")
     bad = [str(rep) for rep in reps if not rep.ok]
     assert not bad, f"{tag}: " + "; ".join(bad)
+
+
+def merge_reports(name, parts):
+    """One report over the concatenation of chunk reports: parts is a list of
+    (element offset of the chunk, Report)."""
+    out = compare.Report(name, 0)
+    for off, rep in parts:
+        out.n += rep.n
+        out.n_fail += rep.n_fail
+        out.nan_mismatch += rep.nan_mismatch
+        out.inf_mismatch += rep.inf_mismatch
+        out.worst_ratio = max(out.worst_ratio, rep.worst_ratio)
+        if len(out.first_fail) < 5:
+            out.first_fail += [off + i for i in rep.first_fail][:5 - len(out.first_fail)]
+    return out
+
+
+def every_element_reports(inp, y, dx, da, dg, db, rows_per_chunk=None, threads=16):
+    """Every element of y and dx against the oracle, in row chunks on host
+    threads (NumPy releases the interpreter lock inside its array loops);
+    the gradients against the sums of the same chunks' oracle results."""
+    from concurrent.futures import ThreadPoolExecutor
+    M, N = inp.x.shape
+    rows = rows_per_chunk or max(1, (1 << 21) // N)
+    y_h = y.float().cpu().numpy()
+    dx_h = dx.float().cpu().numpy()
+    cols = np.arange(N)
+    dga_col = np.abs(inp.gamma.astype(np.float64) * float(inp.alpha[0]))
+
+    def work(r0):
+        r1 = min(M, r0 + rows)
+        xc, dyc = inp.x[r0:r1], inp.dy[r0:r1]
+        yo, so = dyt_oracle.forward_at(xc, cols, inp.alpha, inp.gamma, inp.beta)
+        b = dyt_oracle.backward(xc, dyc, inp.alpha, inp.gamma)
+        ry = compare.check_y(y_h[r0:r1], yo, so, inp.x_dtype, "y")
+        rdx = compare.check_dx(dx_h[r0:r1], b.dx, inp.x_dtype, np.abs(dyc.astype(np.float64)) * dga_col, "dx")
+        sums = (b.dgamma, b.dbeta, b.dalpha, b.rss_dgamma ** 2, b.rss_dbeta ** 2, b.rss_dalpha ** 2)
+        return r0 * N, ry, rdx, sums
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(work, range(0, M, rows)))
+    dgo = sum(r[3][0] for r in res)
+    dbo = sum(r[3][1] for r in res)
+    dao = sum(r[3][2] for r in res)
+    rss = [np.sqrt(sum(r[3][k] for r in res)) for k in (3, 4, 5)]
+    return [
+        merge_reports("y[every element]", [(r[0], r[1]) for r in res]),
+        merge_reports("dx[every element]", [(r[0], r[2]) for r in res]),
+        compare.check_grad(to_np(dg), dgo, rss[0], inp.p_dtype, "dgamma"),
+        compare.check_grad(to_np(db), dbo, rss[1], inp.p_dtype, "dbeta"),
+        compare.check_grad(to_np(da), dao, rss[2], inp.p_dtype, "dalpha"),
+    ]

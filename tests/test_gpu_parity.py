@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import assert_reports, full_reports, log, run_both, sampled_reports, upload
+from gpu_util import (assert_reports, every_element_reports, full_reports, log, run_both,
+                      sampled_reports, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,3 +79,27 @@ def test_parity_shape_sweep(dyt, M, N, xdt, pdt, alpha):
     inp = workloads.custom(M, N, xdt, pdt, alpha=alpha, x_sigma=2.0, seed=M + N)
     outs = run_both(dyt, upload(inp))
     assert_reports(inp.name, full_reports(inp, *outs))
+
+
+@pytest.mark.parametrize("name", ["c4_32768x4096_bf16", "c5_4194304x32_bf16_outliers"])
+def test_parity_full_size_every_element(dyt, name, capsys):
+    """All 134,217,728 elements of y and dx at the full size and launch plan
+    the benchmark times, each against the oracle, plus the gradients. The
+    reports go to the terminal even when pytest captures output."""
+    import time
+    t0 = time.perf_counter()
+    log(f"[parity full every element] {name}")
+    inp = workloads.generate(name)
+    d = upload(inp)
+    outs = run_both(dyt, d)
+    del d
+    log(f"  inputs and GPU run {time.perf_counter() - t0:.1f} s")
+    reps = every_element_reports(inp, *outs)
+    log(f"  oracle comparison done at {time.perf_counter() - t0:.1f} s")
+    assert reps[0].n == inp.M * inp.N and reps[1].n == inp.M * inp.N
+    del outs
+    torch.cuda.empty_cache()
+    with capsys.disabled():
+        for rep in reps:
+            print(f"\n  [every element] {name}: {rep}", flush=True)
+    assert_reports(name, reps)
