@@ -672,7 +672,7 @@ def timeline_library():
     path = os.path.join(ROOT, "bwd_dyt_forward_amd", "libdyt_timeline.so")
     if b.is_stale(path, TIMELINE_FLAGS):
         log("[bench] building the workgroup-timeline variant of the library")
-        b.build(out=path, extra_flags=TIMELINE_FLAGS, with_stream_ref=False)
+        b.build(out=path, extra_flags=TIMELINE_FLAGS, with_stream_ref=False, cache=True)
     from bwd_dyt_forward_amd import _lib
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
     for name, (res, argtypes) in _lib.SIGNATURES.items():
@@ -843,7 +843,7 @@ def variant_library(name: str):
     path = os.path.join(ROOT, "bwd_dyt_forward_amd", f"libdyt_variant_{name}.so")
     if b.is_stale(path, flags):
         log(f"[bench] building library variant {name} ({' '.join(flags)})")
-        b.build(out=path, extra_flags=flags, with_stream_ref=False)
+        b.build(out=path, extra_flags=flags, with_stream_ref=False, cache=True)
     from bwd_dyt_forward_amd import _lib
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
     for fn_name, (res, argtypes) in _lib.SIGNATURES.items():

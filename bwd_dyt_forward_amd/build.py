@@ -90,13 +90,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the DyT library needs ROCm's hipcc to build")
 
 
+# Object files of cached builds (build(cache=True)), keyed by the content of
+# the source, of every header and of the flags.
+OBJ_CACHE = os.path.join(PKG_DIR, "_build")
+
+
 def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False,
-          with_stream_ref: bool = True) -> str:
+          with_stream_ref: bool = True, cache: bool = False) -> str:
     """Compile the library (and, by default, the reference streaming kernels
     next to the default library path); returns the library's path. Always
-    recompiles."""
+    recompiles every source, unless cache=True, which reuses the object of
+    a translation unit whose source, headers and flags are unchanged. Only
+    the host translation unit carries the build id."""
     extra = list(extra_flags or [])
-    _compile(out, SOURCES, [*extra, f'-DDYT_BUILD_ID="{source_hash(extra)}"'], verbose)
+    per_source = {SOURCES[0]: [f'-DDYT_BUILD_ID="{source_hash(extra)}"']}
+    _compile(out, SOURCES, extra, verbose, per_source, OBJ_CACHE if cache else None)
     if with_stream_ref and out == LIB_PATH:
         _compile(STREAM_REF_PATH, [STREAM_REF_SOURCE], None, verbose)
     return out
@@ -114,14 +122,46 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print(msgs, flush=True)
 
 
-def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbose: bool) -> None:
+def _object_key(src: str, flags: list[str]) -> str:
+    h = hashlib.sha256()
+    for p in [src] + [d for d in DEPENDS if not d.endswith(".hip")]:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(flags).encode())
+    return h.hexdigest()[:20]
+
+
+def _compile(out: str, sources: list[str], extra_flags: list[str] | None, verbose: bool,
+             per_source: dict | None = None, cache_dir: str | None = None) -> None:
     """Each source to an object (in parallel), then one shared library."""
     flags = [*HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra_flags or [])]
+    per_source = per_source or {}
     with tempfile.TemporaryDirectory(prefix="dyt_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources]
-        with ThreadPoolExecutor(max_workers=min(JOBS, len(sources))) as ex:
-            list(ex.map(lambda so: _run([hipcc(), *flags, "-c", "-o", so[1], so[0]], verbose),
-                        zip(sources, objs)))
+        jobs = []
+        objs = []
+        for src in sources:
+            f = [*flags, *per_source.get(src, [])]
+            name = os.path.basename(src)
+            if cache_dir:
+                os.makedirs(cache_dir, exist_ok=True)
+                obj = os.path.join(cache_dir, f"{name}-{_object_key(src, f)}.o")
+                if not os.path.exists(obj):
+                    jobs.append((f, src, obj))
+            else:
+                obj = os.path.join(tmpdir, name + ".o")
+                jobs.append((f, src, obj))
+            objs.append(obj)
+
+        def one(job):
+            f, src, obj = job
+            tmp_obj = obj + ".tmp" if cache_dir else obj
+            _run([hipcc(), *f, "-c", "-o", tmp_obj, src], verbose)
+            if cache_dir:
+                os.replace(tmp_obj, obj)
+
+        if jobs:
+            with ThreadPoolExecutor(max_workers=min(JOBS, len(jobs))) as ex:
+                list(ex.map(one, jobs))
         tmp = out + ".tmp"
         _run([hipcc(), *flags, "-shared", "-o", tmp, *objs], verbose)
         os.replace(tmp, out)
