@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     dyt_abi_version,
     dyt_backward,
     dyt_backward_finish,
+    dyt_backward_noalloc,
     dyt_backward_partials,
     dyt_backward_residual,
     dyt_backward_residual_partials,
@@ -35,7 +36,7 @@ __all__ = [
     "DyT", "DyTFunction", "dyt", "DyTResidual", "DyTResidualFunction", "dyt_residual",
     "DYT_F32", "DYT_BF16", "DYT_F16", "DYT_OK", "DytError", "LIB_FILE", "lib",
     "dyt_forward", "dyt_backward", "dyt_backward_partials", "dyt_backward_finish",
-    "dyt_backward_workspace_size", "dyt_forward_residual", "dyt_backward_residual",
+    "dyt_backward_workspace_size", "dyt_backward_noalloc", "dyt_forward_residual", "dyt_backward_residual",
     "dyt_backward_residual_partials",
     "dyt_status_string", "dyt_abi_version", "dyt_get_plan", "dyt_get_forward_plan",
     "dyt_get_forward_residual_plan",

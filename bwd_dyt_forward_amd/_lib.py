@@ -21,7 +21,7 @@ DYT_BF16 = 1
 DYT_F16 = 2
 DYT_OK = 0
 # DYT_ABI_VERSION of include/dyt.h that the signatures and DytPlan below mirror
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16, torch.float16: DYT_F16}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
@@ -67,6 +67,8 @@ SIGNATURES = {
                                      ctypes.c_size_t, _i64, _i64, _int, _int, _vp]),
     "dyt_backward_residual_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                               _i64, _i64, _int, _int, _vp]),
+    "dyt_backward_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int,
+                                    _vp]),
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
     "dyt_build_id": (ctypes.c_char_p, []),
@@ -261,6 +263,32 @@ def dyt_backward(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: 
                                       _stream(stream))
         _check("dyt_backward_strided", st)
     _keep_alive_on(stream, *(t for t, m in zip((dx, dalpha, dgamma, dbeta, workspace), made) if m))
+    return dx, dalpha, dgamma, dbeta
+
+
+# Bytes of the static device array dyt_backward_noalloc keeps its partial
+# rows in (DYT_NOALLOC_SCRATCH_BYTES of include/dyt.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def dyt_backward_noalloc(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor,
+                         gamma: torch.Tensor, dx: torch.Tensor, dalpha: torch.Tensor,
+                         dgamma: torch.Tensor, dbeta: torch.Tensor, stream=None):
+    """dyt_backward with the library's static scratch instead of a workspace:
+    the caller passes every output, the call allocates nothing. Calls that
+    overlap on one GPU share the scratch and race."""
+    _check_act("x", x)
+    _same("dy", dy, x)
+    _same("dx", dx, x)
+    M, N = x.shape
+    _check_params(N, x.device, alpha, gamma)
+    _check_params(N, x.device, dalpha, dgamma, dbeta)
+    if dalpha.dtype != alpha.dtype:
+        raise ValueError("dalpha, dgamma and dbeta must have the parameters' dtype")
+    st = lib.dyt_backward_noalloc(_ptr(x), _ptr(dy), _ptr(alpha), _ptr(gamma), _ptr(dx),
+                                  _ptr(dalpha), _ptr(dgamma), _ptr(dbeta), M, N, _code(x.dtype),
+                                  _code(alpha.dtype), _stream(stream))
+    _check("dyt_backward_noalloc", st)
     return dx, dalpha, dgamma, dbeta
 
 

@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "dyt.h"
@@ -677,6 +678,42 @@ void fill_plan(const Plan& p, dyt_plan* out) {
     out->flat_aligned_only = 0;
 }
 
+// ------------------------------------------------ allocation-free backward
+// dyt_backward_noalloc keeps its partial rows in `scratch`, a file-scope
+// device array of DYT_NOALLOC_SCRATCH_BYTES that every GPU the library runs
+// on holds until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (with that device current) and only that address is handed to
+// kernels. Nothing in it has to start at zero: pass 1 writes every entry
+// pass 2 reads. Calls that overlap on one GPU share the array and race.
+}  // namespace
+
+static __device__ __align__(256) float scratch[DYT_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DYT_ERR_HIP;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    });
+    if (slot.err != hipSuccess || slot.ptr == nullptr) return DYT_ERR_HIP;
+    *out = slot.ptr;
+    return DYT_OK;
+}
+
 // The build id, after a marker that lets a build step find it in the file
 // without loading the library.
 #ifndef DYT_BUILD_ID
@@ -857,6 +894,23 @@ int dyt_backward(const void* x, const void* dy, const void* alpha, const void* g
     return backward_impl(BwdPtrs{x, dy, nullptr, alpha, gamma, dx, static_cast<float*>(workspace)},
                          false, dalpha, dgamma, dbeta, workspace_bytes, M, N, x_dtype, param_dtype,
                          static_cast<hipStream_t>(stream));
+}
+
+int dyt_backward_noalloc(const void* x, const void* dy, const void* alpha, const void* gamma,
+                         void* dx, void* dalpha, void* dgamma, void* dbeta, int64_t M, int64_t N,
+                         int x_dtype, int param_dtype, void* stream) {
+    // sizes first (pure host): a problem whose partial rows exceed the
+    // static scratch is refused before any HIP call
+    Plan p;
+    const int st = make_plan(M, N, x_dtype, param_dtype, Dir::Bwd, p);
+    if (st != DYT_OK) return st;
+    if (round_up(p.ws_bytes, 16) > (int64_t)DYT_NOALLOC_SCRATCH_BYTES) return DYT_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const int sa = scratch_address(&ws);
+    if (sa != DYT_OK) return sa;
+    return backward_impl(BwdPtrs{x, dy, nullptr, alpha, gamma, dx, static_cast<float*>(ws)}, false,
+                         dalpha, dgamma, dbeta, DYT_NOALLOC_SCRATCH_BYTES, M, N, x_dtype,
+                         param_dtype, static_cast<hipStream_t>(stream));
 }
 
 int dyt_backward_residual(const void* h, const void* dy, const void* dres, const void* alpha,

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 5
+#define DYT_ABI_VERSION 6
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -237,6 +237,28 @@ int dyt_backward_residual_partials(const void* h, const void* dy, const void* dr
                                    void* workspace, size_t workspace_bytes,
                                    int64_t M, int64_t N, int x_dtype, int param_dtype,
                                    void* stream);
+
+/*
+ * dyt_backward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The entry point allocates
+ * nothing; the partial rows live in a static device array of
+ * DYT_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up once per device,
+ * on the first call with that device current). Arguments, results, dtypes,
+ * layout and the fixed summation order are those of dyt_backward (the same
+ * kernels run, so the results equal dyt_backward's bit for bit).
+ * Returns DYT_ERR_WORKSPACE_TOO_SMALL, before any HIP call, when
+ * dyt_backward_workspace_size(M, N, ...) exceeds DYT_NOALLOC_SCRATCH_BYTES
+ * (rows of up to 20,480 columns stay below 13 MiB; a single row of 2^22
+ * float32 columns needs 32 MiB), and DYT_ERR_HIP if the array cannot be
+ * located on the current device. Calls that overlap on one GPU (other
+ * streams or host threads) share the array and race: serialise them.
+ */
+#define DYT_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int dyt_backward_noalloc(const void* x, const void* dy, const void* alpha, const void* gamma,
+                         void* dx, void* dalpha, void* dgamma, void* dbeta,
+                         int64_t M, int64_t N, int x_dtype, int param_dtype, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* dyt_status_string(int status);

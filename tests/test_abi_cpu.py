@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
         "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
         "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided",
-        "dyt_get_forward_residual_plan", "dyt_build_id"])
+        "dyt_get_forward_residual_plan", "dyt_build_id", "dyt_backward_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -55,7 +55,7 @@ def test_no_cpu_fallback_in_product_path():
 
 
 def test_version_and_status_strings(dyt):
-    assert dyt.dyt_abi_version() == 5
+    assert dyt.dyt_abi_version() == 6
     names = [dyt.dyt_status_string(i) for i in range(6)]
     assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
                      "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]
@@ -445,3 +445,20 @@ def test_source_hash_follows_code_and_flags_not_comments(tmp_path, monkeypatch):
     assert build.built_id(str(lib)) == "0123456789abcdef"
     assert build.is_stale(str(lib))
     assert build.built_id(str(tmp_path / "missing.so")) is None
+
+
+def test_noalloc_size_limit_is_checked_before_any_hip_call(dyt):
+    """dyt_backward_noalloc refuses a problem whose partial rows exceed its
+    static scratch with DYT_ERR_WORKSPACE_TOO_SMALL, before touching the GPU
+    (so this runs without one); rows of up to 20,480 columns fit."""
+    limit = dyt._lib.NOALLOC_SCRATCH_BYTES
+    assert dyt.dyt_backward_workspace_size(1, 1 << 22, "f32", "f32") > limit
+    st = dyt.lib.dyt_backward_noalloc(None, None, None, None, None, None, None, None, 1, 1 << 22,
+                                      dyt.DYT_F32, dyt.DYT_F32, None)
+    assert st == 3
+    assert dyt.lib.dyt_backward_noalloc(None, None, None, None, None, None, None, None, 4, 4, 99,
+                                        dyt.DYT_F32, None) == 2
+    for xdt in ("f32", "bf16", "f16"):
+        for N in list(range(1, 20481, 7)) + [4096, 8192, 16384, 20480]:
+            for M in (1000, 100003, 1 << 22):
+                assert dyt.dyt_backward_workspace_size(M, N, xdt, "f32") <= 13 << 20, (M, N, xdt)
