@@ -722,7 +722,7 @@ def report_wg_timeline(torch, path: str, reps: int = 30,
     lib = timeline_library()
     tick_us = 0.01          # the real-time counter runs at 100 MHz
     rows = [f"# Workgroup timeline: forward and backward pass 1", "",
-            f"Command: `python bench.py --wg-timeline {path}` "
+            f"Command: `python bench.py --wg-timeline {path} --timeline-workloads {','.join(names)}` "
             f"(library built with {' '.join(TIMELINE_FLAGS)}; {reps} recorded steps after "
             f"{SETTLE_S} s of untimed steps; medians over the recorded steps). "
             f"Device: {torch.cuda.get_device_name(0)}.", "",
@@ -942,9 +942,256 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
         f.write("\n".join(rows) + "\n")
 
 
+def graph_vs_eager(dyt, torch, name: str, steps: int = 50) -> dict:
+    """The same step (forward, pass 1, pass 2) run eagerly and as a captured
+    HIP graph, each for `steps` back-to-back steps after a settling run,
+    with a 50 ms idle gap between the two phases (so that a kernel trace of
+    this run splits into them). Returns us per step for each."""
+    import workloads
+    inp = workloads.generate(name)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    xdt, pdt = tdt[inp.x_dtype], tdt[inp.p_dtype]
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp.x).to(dev).to(xdt)
+    dy = torch.from_numpy(inp.dy).to(dev).to(xdt)
+    a = torch.from_numpy(inp.alpha).to(dev).to(pdt)
+    g = torch.from_numpy(inp.gamma).to(dev).to(pdt)
+    b = torch.from_numpy(inp.beta).to(dev).to(pdt)
+    M, N = inp.M, inp.N
+    del inp
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    da = torch.empty(1, dtype=pdt, device=dev)
+    dg = torch.empty(N, dtype=pdt, device=dev)
+    db = torch.empty(N, dtype=pdt, device=dev)
+    ws = torch.empty(max(16, dyt.dyt_backward_workspace_size(M, N, xdt, pdt)), dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream()
+
+    def step():
+        dyt.dyt_forward(x, a, g, b, y=y, stream=s)
+        dyt.dyt_backward_partials(x, dy, a, g, dx, ws, stream=s)
+        dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db, stream=s)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            for _ in range(20):
+                step()
+            s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+        for _ in range(5):
+            graph.replay()
+        s.synchronize()
+        time.sleep(0.05)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = {}
+        for phase in ("eager", "graph"):
+            e0.record(s)
+            for _ in range(steps):
+                if phase == "eager":
+                    step()
+                else:
+                    graph.replay()
+            e1.record(s)
+            e1.synchronize()
+            out[phase] = e0.elapsed_time(e1) * 1e3 / steps
+            time.sleep(0.05)
+    return out
+
+
+def graph_trace_summary(d: str) -> str:
+    """From a rocprofv3 kernel trace of `bench.py --graph-vs-eager W`: the
+    dispatches of the two timed phases (the last two runs of back-to-back
+    DyT kernels separated by an idle gap), with each kernel family's mean
+    duration and the mean gap from one kernel's end to the next one's
+    start, per phase."""
+    import csv
+    import glob
+    recs = []
+    for fn in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                fam = _family(r["Kernel_Name"])
+                if fam and fam != "calibration":
+                    recs.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), fam))
+    recs.sort()
+    runs, cur = [], [recs[0]]
+    for r in recs[1:]:
+        if r[0] - cur[-1][1] > 10_000_000:      # an idle gap of more than 10 ms
+            runs.append(cur)
+            cur = []
+        cur.append(r)
+    runs.append(cur)
+    lines = ["| phase | dispatches | " + " | ".join(f"{f} us" for f, _ in KERNEL_FAMILIES if f != "dyt_fwd_flat_kernel")
+             + " | forward (flat) us | mean gap us | us per step |", "|---|---:|" + "---:|" * 6]
+    for phase, run in zip(("eager", "graph"), runs[-2:]):
+        dur = {}
+        for st, en, fam in run:
+            dur.setdefault(fam, []).append((en - st) / 1e3)
+        gaps = [(run[i + 1][0] - run[i][1]) / 1e3 for i in range(len(run) - 1)]
+        nsteps = max(1, len(dur.get("dyt_bwd_finish_kernel", [])))
+        span = (run[-1][1] - run[0][0]) / 1e3
+        m = lambda f: f"{statistics.mean(dur[f]):.2f}" if f in dur else "-"
+        lines.append(f"| {phase} | {len(run)} | {m('dyt_fwd_kernel')} | {m('dyt_bwd_partial_kernel')} | "
+                     f"{m('dyt_bwd_finish_kernel')} | {m('dyt_fwd_flat_kernel')} | "
+                     f"{statistics.mean(gaps):.2f} | {span / nsteps:.2f} |")
+    return "\n".join(lines)
+
+
 def ctypes_byref(obj):
     import ctypes
     return ctypes.byref(obj)
+
+
+# Kernel families, matched in the names the profiler records.
+KERNEL_FAMILIES = (("dyt_fwd_flat_kernel", "dyt_fwd_flat_kernel<"), ("dyt_fwd_kernel", "dyt_fwd_kernel<"),
+                   ("dyt_bwd_partial_kernel", "dyt_bwd_partial_kernel<"),
+                   ("dyt_bwd_finish_kernel", "dyt_bwd_finish_kernel<"))
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "sq": ["VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES", "SQ_INSTS_VMEM_RD",
+           "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS"],
+}
+
+
+def _family(name: str):
+    for fam, pat in KERNEL_FAMILIES:
+        if pat in name:
+            return fam
+    return "calibration" if "neg_kernel" in name else None
+
+
+def _read_counters(d: str) -> dict:
+    """Mean value per dispatch of each counter, per kernel family, from the
+    rocprofv3 CSV files under d (a counter spread over several rows of one
+    dispatch is summed)."""
+    import csv
+    import glob
+    per = {}
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                fam = _family(r["Kernel_Name"])
+                if fam is None:
+                    continue
+                key = (fam, r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    acc = {}
+    for (fam, cn, _d), v in per.items():
+        acc.setdefault(fam, {}).setdefault(cn, []).append(v)
+    return {fam: {cn: sum(v) / len(v) for cn, v in cs.items()} for fam, cs in acc.items()}
+
+
+def _read_trace_stats(d: str) -> dict:
+    """Calls and mean duration (us) per kernel family from a rocprofv3
+    --kernel-trace --stats run under d."""
+    import csv
+    import glob
+    out = {}
+    for fn in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                fam = _family(r["Name"])
+                if fam is None or fam == "calibration":
+                    continue
+                calls, total = int(r["Calls"]), float(r["TotalDurationNs"])
+                c0, t0 = out.get(fam, (0, 0.0))
+                out[fam] = (c0 + calls, t0 + total)
+    return {fam: {"calls": c, "mean_us": t / c / 1e3} for fam, (c, t) in out.items()}
+
+
+def ingest_counters(root: str, calib_mib: int, md_path: str) -> None:
+    """Reads the profiler output of `root/<workload>/{trace,fetch,write,sq}`
+    (one directory per rocprofv3 pass over `bench.py --workload <workload>`;
+    the counter passes with --copy-calibration-mib), scales the byte
+    counters by what they read for the calibration copy of calib_mib MiB,
+    and writes profiles/traffic_counters.json (per kernel and workload,
+    tagged with the build id) and a Markdown summary."""
+    import workloads
+    h = kernel_source_hash()
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            table = {k: v for k, v in json.load(f).items() if v.get("source_hash") == h}
+    cal_bytes = calib_mib * (1 << 20)
+    rows = ["# HBM bytes, VALU activity and kernel durations per workload", "",
+            "Commands, per workload W (from the repository root; one profiler pass each):", "", "```",
+            "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/W/trace -o W -- "
+            "python3 bench.py --workload W --secondary none --no-residual --no-cpu-baseline --steps 20 --warmup 5"]
+    for pname, cnts in COUNTER_PASSES.items():
+        rows.append(f"rocprofv3 --pmc {' '.join(cnts)} --output-format csv -d gpurun_out/pmc/W/{pname} -o W -- "
+                    f"python3 bench.py --workload W --secondary none --no-residual --no-cpu-baseline "
+                    f"--steps 3 --warmup 1 --copy-calibration-mib {calib_mib}")
+    rows += [f"python3 bench.py --ingest-counters gpurun_out/pmc --ingest-md {md_path}", "```", "",
+             f"Byte counters are scaled by what they read for a plain elementwise copy of {calib_mib} MiB "
+             "(torch.neg, reading and writing it once) in the same run. Counter values are means over "
+             "every dispatch of the run; durations are the kernel trace's means. Algorithmic bytes: "
+             "forward 2MN sx + (2N+1) sp, backward pass 1 3MN sx + (N+1) sp; pass 2 reads the "
+             "workspace only. VALUBusy is the profiler's own derived metric; VALU and 2^x/1/x "
+             "(transcendental) instructions are per element, counted per lane.", "",
+             "| workload | kernel | trace us | GB/s | % of 8 TB/s | fetch MB | write MB | traffic / algorithmic "
+             "| VALUBusy % | VALU inst / elem | transcendental / elem | LDS inst / elem |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for w in sorted(os.listdir(root)):
+        wd = os.path.join(root, w)
+        if w not in workloads.CONFIGS or not os.path.isdir(wd):
+            continue
+        cfg = workloads.CONFIGS[w]
+        sx = 4 if cfg.x_dtype == "f32" else 2
+        sp = 4 if cfg.p_dtype == "f32" else 2
+        B = algorithmic_bytes(cfg.M, cfg.N, sx, sp)
+        elems = cfg.M * cfg.N
+        trace = _read_trace_stats(os.path.join(wd, "trace"))
+        F = _read_counters(os.path.join(wd, "fetch"))
+        W = _read_counters(os.path.join(wd, "write"))
+        Q = _read_counters(os.path.join(wd, "sq"))
+        ff = F.get("calibration", {}).get("FETCH_SIZE", 0) * 1024 / cal_bytes or None
+        fw = W.get("calibration", {}).get("WRITE_SIZE", 0) * 1024 / cal_bytes or None
+        for fam, _pat in KERNEL_FAMILIES:
+            if fam not in trace and fam not in F:
+                continue
+            alg = {"dyt_fwd_flat_kernel": B["fwd"], "dyt_fwd_kernel": B["fwd"],
+                   "dyt_bwd_partial_kernel": B["pass1"], "dyt_bwd_finish_kernel": None}[fam]
+            ent = {"source_hash": h}
+            fb = F.get(fam, {}).get("FETCH_SIZE")
+            wb = W.get(fam, {}).get("WRITE_SIZE")
+            if fb is not None and wb is not None and ff and fw:
+                ent["fetch_bytes"] = round(fb * 1024 / ff)
+                ent["write_bytes"] = round(wb * 1024 / fw)
+                ent["bytes_per_launch"] = ent["fetch_bytes"] + ent["write_bytes"]
+            q = Q.get(fam, {})
+            if q:
+                ent["valu_busy_pct"] = round(q.get("VALUBusy", float("nan")), 2)
+                ent["valu_insts_per_elem"] = round(q.get("SQ_INSTS_VALU", 0) * 64 / elems, 3)
+                ent["trans_insts_per_elem"] = round(q.get("SQ_INSTS_VALU_TRANS_F32", 0) * 64 / elems, 3)
+                ent["lds_insts_per_elem"] = round(q.get("SQ_INSTS_LDS", 0) * 64 / elems, 3)
+            if fam in trace:
+                ent["trace_mean_us"] = round(trace[fam]["mean_us"], 2)
+                ent["trace_calls"] = trace[fam]["calls"]
+            if alg:
+                ent["algorithmic_bytes"] = alg
+            table[f"{fam}:{w}"] = ent
+            t_us = ent.get("trace_mean_us")
+            gbps = alg / (t_us * 1e-6) / 1e9 if (alg and t_us) else None
+            f2 = lambda v, fmt: "-" if v is None else format(v, fmt)
+            rows.append(
+                f"| {w} | {fam} | {f2(t_us, '.2f')} | {f2(gbps, '.0f')} | "
+                f"{f2(None if gbps is None else 100 * gbps / HBM_PEAK_GBPS, '.1f')} | "
+                f"{f2(ent.get('fetch_bytes', None) and ent['fetch_bytes'] / 1e6, '.1f')} | "
+                f"{f2(ent.get('write_bytes', None) and ent['write_bytes'] / 1e6, '.1f')} | "
+                f"{f2(alg and ent.get('bytes_per_launch') and ent['bytes_per_launch'] / alg, '.3f')} | "
+                f"{f2(ent.get('valu_busy_pct'), '.1f')} | {f2(ent.get('valu_insts_per_elem'), '.2f')} | "
+                f"{f2(ent.get('trans_insts_per_elem'), '.2f')} | {f2(ent.get('lds_insts_per_elem'), '.3f')} |")
+    rows += ["", f"Build id of the measured library: `{h}`; bench.py reports these figures only while "
+             "the sources still have this id."]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    with open(md_path, "w") as f:
+        f.write("\n".join(rows) + "\n")
 
 
 def load_traffic(kernel: str) -> dict | None:
@@ -982,11 +1229,29 @@ def main() -> int:
     ap.add_argument("--wg-timeline", metavar="FILE", default=None,
                     help="only record the per-workgroup timeline of the forward and backward pass 1 "
                          "(timeline build of the library) and write a Markdown summary to FILE")
+    ap.add_argument("--timeline-workloads", default=f"{HEADLINE},{SECONDARY}",
+                    help="with --wg-timeline: comma-separated workload names")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="only read the profiler output under DIR/<workload>/{trace,fetch,write,sq} and "
+                         "write profiles/traffic_counters.json and the Markdown summary --ingest-md")
+    ap.add_argument("--ingest-md", default=os.path.join("profiles", "dyt_kernels_counters.md"))
+    ap.add_argument("--graph-vs-eager", metavar="WORKLOAD", default=None,
+                    help="only time WORKLOAD's step eagerly and as a replayed HIP graph (for a kernel trace)")
+    ap.add_argument("--graph-trace", metavar="DIR", default=None,
+                    help="only summarise a kernel trace of --graph-vs-eager found under DIR (no GPU)")
     ap.add_argument("--variants", default=None,
                     help="only time these library variants (comma-separated names of VARIANTS) "
                          "against the default build on every workload")
     ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
     args = ap.parse_args()
+
+    if args.graph_trace:
+        print(graph_trace_summary(args.graph_trace))
+        return 0
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters, args.copy_calibration_mib or 1024, args.ingest_md)
+        log(f"[bench] counters written to {TRAFFIC_FILE} and {args.ingest_md}")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1003,12 +1268,16 @@ def main() -> int:
     ge._ensure_built()
     import bwd_dyt_forward_amd as dyt
 
+    if args.graph_vs_eager:
+        r = graph_vs_eager(dyt, torch, args.graph_vs_eager)
+        log(f"[bench] {args.graph_vs_eager}: eager {r['eager']:.2f} us per step, graph {r['graph']:.2f} us per step")
+        return 0
     if args.variants:
         report_variants(dyt, torch, args.variants_report, args.variants.split(","))
         log(f"[bench] variant report written to {args.variants_report}")
         return 0
     if args.wg_timeline:
-        report_wg_timeline(torch, args.wg_timeline)
+        report_wg_timeline(torch, args.wg_timeline, names=args.timeline_workloads.split(","))
         log(f"[bench] workgroup timeline written to {args.wg_timeline}")
         return 0
 
@@ -1047,6 +1316,16 @@ def main() -> int:
         "kernel": kernel, "algorithmic_bytes_per_launch": rl_bytes,
         "mean_launch_us": round(main_res["pass1_us_mean"], 2),
     }
+    # The same kernel's mean duration in the committed kernel trace of this
+    # workload (profiles/dyt_kernels_counters.md), while the sources are
+    # those it measured: HIP events around one launch include its dispatch,
+    # the trace does not.
+    if traffic is not None and traffic.get("trace_mean_us"):
+        t_us = traffic["trace_mean_us"]
+        roofline["trace_mean_us"] = t_us
+        roofline["trace_achieved"] = round(rl_bytes / (t_us * 1e-6) / 1e9, 1)
+        roofline["trace_frac"] = round(rl_bytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        roofline["counters"] = "profiles/dyt_kernels_counters.md"
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_seconds)
