@@ -826,13 +826,23 @@ def report_wg_timeline(torch, path: str, reps: int = 30,
         f.write("\n".join(rows) + "\n")
 
 
-# Library variants that --variants times against the default build: a
-# compile-time option each, measured, not adopted (the reasons are in the
-# written report).
+# Library variants that --variants times against the default build: each a
+# compile-time option of the sources, measured and not adopted (or, for
+# default_constants, the tile table's own baseline).
 VARIANTS = {
     # pass 1's last workgroup (by an arrival counter in the workspace) sums
     # the partial rows itself instead of a second launch
     "fused_finish": ["-DDYT_FUSED_FIN=1"],
+    # plain loads and stores instead of nontemporal ones in both directions
+    "no_nt_hints": ["-DDYT_FWD_NT=0", "-DDYT_BWD_NT=0"],
+    # two tiles per pipeline buffer in pass 1 / one in the forward
+    "bwd_two_units": ["-DDYT_BWD_U=2"],
+    "fwd_one_unit": ["-DDYT_FWD_U=1"],
+    # the default constants (one 256-thread workgroup per CU, largest tiles)
+    # instead of the measured tile table
+    "default_constants": ["-DDYT_TUNE_TABLE=0"],
+    # the tiled forward everywhere (no flat walk)
+    "no_flat_forward": ["-DDYT_FLAT_MAX_N=0"],
 }
 
 
@@ -853,11 +863,13 @@ def variant_library(name: str):
     return lib
 
 
-def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
+def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
     """Each named library variant against the default build on every
-    workload: the backward's outputs compared bit for bit, then whole steps
-    (forward, then the backward of the library under test) timed in
-    interleaved rounds of back-to-back steps; medians. Writes Markdown."""
+    workload, with its own forward and backward: the outputs compared bit
+    for bit with the default build's, then back-to-back forwards, back-to-
+    back backwards (both passes) and back-to-back steps (forward then
+    backward), every library's run of each kind interleaved over rounds;
+    medians. Writes Markdown."""
     import workloads
     from bwd_dyt_forward_amd import _lib
     libs = {"default": dyt.lib}
@@ -865,13 +877,15 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
         libs[n] = variant_library(n)
     rows = ["# Library variants against the default build", "",
             f"Command: `python bench.py --variants {','.join(names)} --variants-report {path}`. "
-            f"Device: {torch.cuda.get_device_name(0)}. " +
-            "; ".join(f"{n}: {' '.join(VARIANTS[n])}" for n in names) + ".", "",
-            f"Step = forward (default library) + backward (`dyt_backward` of the library under test), "
-            f"back to back; us per step, median of {rounds} interleaved rounds. 'bitwise' compares "
-            "dx, dgamma, dbeta and dalpha with the default build's.", "",
-            "| workload | " + " | ".join(libs) + " | bitwise |",
-            "|---|" + "---:|" * len(libs) + "---|"]
+            f"Device: {torch.cuda.get_device_name(0)}.", "",
+            "Variants (compile-time options of the same sources): " +
+            "; ".join(f"`{n}`: {' '.join(VARIANTS[n])}" for n in names) + ".", "",
+            f"us per call: forward alone, backward (pass 1 + pass 2) alone and the step (forward then "
+            f"backward), each a run of back-to-back calls between two HIP events; median of {rounds} "
+            "rounds in which every library's run of each kind is interleaved. 'bits' compares y, dx, "
+            "dgamma, dbeta and dalpha with the default build's.", "",
+            "| workload | library | forward us | backward us | step us | step vs default | bits |",
+            "|---|---|---:|---:|---:|---:|---|"]
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     dev = torch.device("cuda:0")
     s = torch.cuda.current_stream()
@@ -887,17 +901,23 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
         M, N = inp.M, inp.N
         del inp
         xc, pc = _lib._code(xdt), _lib._code(pdt)
-        y = torch.empty_like(x)
         bufs = {}
         for v, L in libs.items():
             need = L.dyt_backward_workspace_size(M, N, xc, pc)
             # zero-filled: a variant may keep counters in the workspace
             bufs[v] = (torch.zeros(max(need, 16), dtype=torch.uint8, device=dev), torch.empty_like(x),
                        torch.empty(1, dtype=pdt, device=dev), torch.empty(N, dtype=pdt, device=dev),
-                       torch.empty(N, dtype=pdt, device=dev))
+                       torch.empty(N, dtype=pdt, device=dev), torch.empty_like(x))
+
+        def fwd(v):
+            y = bufs[v][5]
+            rc = libs[v].dyt_forward(x.data_ptr(), a.data_ptr(), g.data_ptr(), b.data_ptr(), y.data_ptr(),
+                                     M, N, xc, pc, sp)
+            if rc != 0:
+                raise RuntimeError(f"variant {v}: dyt_forward returned {rc}")
 
         def bwd(v):
-            ws, dx, da, dg, db = bufs[v]
+            ws, dx, da, dg, db, _y = bufs[v]
             rc = libs[v].dyt_backward(x.data_ptr(), dy.data_ptr(), a.data_ptr(), g.data_ptr(), dx.data_ptr(),
                                       da.data_ptr(), dg.data_ptr(), db.data_ptr(), ws.data_ptr(), ws.numel(),
                                       M, N, xc, pc, sp)
@@ -905,16 +925,16 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
                 raise RuntimeError(f"variant {v}: dyt_backward returned {rc}")
 
         def step(v):
-            dyt.dyt_forward(x, a, g, b, y=y, stream=s)
+            fwd(v)
             bwd(v)
 
-        same = []
+        same = {}
         for v in libs:
             for _ in range(2):
-                bwd(v)
+                step(v)
             torch.cuda.synchronize()
-            same.append(all(torch.equal(p.view(torch.uint8), q.view(torch.uint8))
-                            for p, q in zip(bufs[v][1:], bufs["default"][1:])))
+            same[v] = all(torch.equal(p.view(torch.uint8), q.view(torch.uint8))
+                          for p, q in zip(bufs[v][1:], bufs["default"][1:]))
         reps = 10 if M * N >= (1 << 26) else 20
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < SETTLE_S:
@@ -922,21 +942,26 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 12) -> None:
                 step(v)
             torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        us = {v: [] for v in libs}
+        kinds = {"fwd": fwd, "bwd": bwd, "step": step}
+        us = {(v, k): [] for v in libs for k in kinds}
         order = list(libs)
         for r in range(rounds):
-            for k in range(len(order)):
-                v = order[(r + k) % len(order)]
-                e0.record(s)
-                for _ in range(reps):
-                    step(v)
-                e1.record(s)
-                e1.synchronize()
-                us[v].append(e0.elapsed_time(e1) * 1e3 / reps)
-        rows.append(f"| {name} | " + " | ".join(f"{statistics.median(us[v]):.2f}" for v in libs) +
-                    f" | {'equal' if all(same) else 'DIFFERENT'} |")
-        log(f"[bench] variants {name}: " + ", ".join(f"{v} {statistics.median(us[v]):.2f}" for v in libs))
-        del x, dy, y, bufs
+            for kname, fn in kinds.items():
+                for j in range(len(order)):
+                    v = order[(r + j) % len(order)]
+                    e0.record(s)
+                    for _ in range(reps):
+                        fn(v)
+                    e1.record(s)
+                    e1.synchronize()
+                    us[(v, kname)].append(e0.elapsed_time(e1) * 1e3 / reps)
+        med = {key: statistics.median(val) for key, val in us.items()}
+        for v in libs:
+            rows.append(f"| {name} | {v} | {med[(v, 'fwd')]:.2f} | {med[(v, 'bwd')]:.2f} | "
+                        f"{med[(v, 'step')]:.2f} | {med[(v, 'step')] / med[('default', 'step')]:.3f} | "
+                        f"{'equal' if same[v] else 'differ'} |")
+        log(f"[bench] variants {name}: " + ", ".join(f"{v} {med[(v, 'step')]:.2f}" for v in libs))
+        del x, dy, bufs
         torch.cuda.empty_cache()
     with open(path, "w") as f:
         f.write("\n".join(rows) + "\n")

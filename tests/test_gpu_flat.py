@@ -139,7 +139,11 @@ def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
 @pytest.mark.parametrize("M,N,xdt,xo,yo", [
     (1000, 2560, "bf16", 1, 3), (3001, 1500, "bf16", 2, 0), (777, 4104, "f32", 0, 1), (5, 3, "bf16", 3, 3),
     (1, 5, "bf16", 5, 5), (1000, 2560, "bf16", 1, 9), (777, 4104, "f32", 1, 5), (999, 1500, "bf16", 7, 7),
-    (5001, 32, "bf16", 1, 3), (5001, 32, "bf16", 3, 3)])   # one-slot packed: tiles, then the shifted walk
+    (5001, 32, "bf16", 1, 3), (5001, 32, "bf16", 3, 3),   # one-slot packed: tiles, then the shifted walk
+    # rows over 8,192 columns (gamma/beta in 104-160 KB of LDS; no shifted copies fit, so
+    # these walk unaligned from element 0)
+    (1001, 13312, "f32", 1, 1), (1001, 13312, "f32", 1, 2), (33, 8200, "bf16", 1, 3),
+    (33, 8200, "bf16", 5, 5), (7, 20480, "f32", 3, 0)])
 def test_flat_forward_other_misalignments(dyt, M, N, xdt, xo, yo):
     """x and y off the 16-byte grid by xo and yo elements (equal offsets
     within a 128-byte line: the walk starts on the line grid; equal only
