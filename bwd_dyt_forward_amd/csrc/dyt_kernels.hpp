@@ -484,7 +484,7 @@ __device__ __forceinline__ int64_t tile_off(int o, const Geo& g, int64_t ld) {
 
 template <bool ACC>
 __device__ __forceinline__ float dyt_tanh(float u) {
-    if constexpr (ACC) return tanh_accurate(u);
+    if constexpr (ACC) return tanh_fwd_f32(u);
     else return tanh_fast(u);
 }
 template <bool ACC>

@@ -12,12 +12,15 @@
 // which is then >= 0.87 and exact enough).
 //
 // Two variants, chosen by the storage dtype of x:
-//   * accurate (float32 outputs): e via Cody & Waite's additive range
-//     reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
-//     Functions", 1980) with the hardware 2^x on the reduced argument, a
-//     Newton-refined reciprocal, and the Taylor series of tanh up to u^13
-//     for |u| < 0.35 (coefficients 2^2n (2^2n - 1) B_2n / (2n)!, B the
-//     Bernoulli numbers). About 3-5 float32 ulp on t and on sech^2.
+//   * accurate (float32 outputs): in the backward, e via Cody & Waite's
+//     additive range reduction (W. J. Cody, W. Waite, "Software Manual for
+//     the Elementary Functions", 1980) with the hardware 2^x on the reduced
+//     argument, a Newton-refined reciprocal, and the Taylor series of tanh
+//     up to u^13 for |u| < 0.35 (coefficients 2^2n (2^2n - 1) B_2n / (2n)!,
+//     B the Bernoulli numbers): about 3-5 float32 ulp on t and on sech^2.
+//     The forward needs t only, which is well conditioned in e, so it takes
+//     e from the hardware 2^x directly and the series through u^9
+//     (tanh_fwd_f32).
 //   * fast (bfloat16 outputs): e straight from the hardware 2^x and 1/x
 //     (about 1e-5 relative at |u| = 50, far below half a bfloat16 ulp);
 //     in the forward tanh u ~= u below 2^-6 (relative error < 1e-4), in the
@@ -48,20 +51,6 @@ __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(
 // copysign as one bitfield insert: magnitude bits of m, sign bit of s.
 __device__ __forceinline__ float copy_sign(float m, float s) {
     return __builtin_copysignf(m, s);
-}
-
-// e^z for z <= 0, z possibly -inf or NaN. Cody-Waite: z = k ln2 + r with
-// |r| <= ln2/2; e^z = 2^k * 2^(r log2 e). The fused multiply-adds carry
-// k*ln2 beyond float32 precision. Below -104, e^z rounds to 0 in float32,
-// so z is replaced by -104 there (a select, so NaN stays NaN and -inf maps
-// to an exact 0).
-__device__ __forceinline__ float exp_nonpos_accurate(float z) {
-    z = (z < -104.0f) ? -104.0f : z;
-    const float k = __builtin_rintf(z * kLog2e);
-    float r = __builtin_fmaf(-k, kLn2Hi, z);
-    r = __builtin_fmaf(-k, kLn2Lo, r);
-    const float er = hw_exp2(r * kLog2e);
-    return __builtin_amdgcn_ldexpf(er, (int)k);
 }
 
 // Taylor series of tanh(u)/u - 1 in s = u^2 (terms through s^6, u^13).
@@ -112,15 +101,26 @@ __device__ __forceinline__ void tanh_sech2_accurate(float x, float alpha, float&
     d = small ? ds : dl;
 }
 
-__device__ __forceinline__ float tanh_accurate(float u) {
+// Forward tanh for float32 outputs. y is checked at 1e-6 of |gamma t| +
+// |beta|, and an error in e moves t = (1 - e)/(1 + e) by only
+// sech^2(u)/2 times e's relative error, so the hardware 2^x of the rounded
+// argument -2|u| log2(e) and one hardware reciprocal (each within one
+// float32 ulp) suffice above |u| = 0.35; below, where 1 - e cancels, the odd
+// series through u^9 (its truncation is under 3e-7 relative at 0.35).
+// Modelled with 2^x and 1/x each off by one ulp either way, the worst
+// relative error over |u| <= 12 is 4.1e-7. u = +-inf gives +-1; NaN
+// propagates; subnormal u returns u.
+__device__ __forceinline__ float tanh_fwd_f32(float u) {
     const float a = __builtin_fabsf(u);
-    const float e = exp_nonpos_accurate(-2.0f * a);
-    const float p = 1.0f + e;
-    float r = hw_rcp(p);
-    r = __builtin_fmaf(r, __builtin_fmaf(-p, r, 1.0f), r);
+    const float e = hw_exp2(a * kMinus2Log2e);
+    const float r = hw_rcp(1.0f + e);
     const float tl = (1.0f - e) * r;
     const float s = u * u;
-    const float ts = __builtin_fmaf(u * s, tanh_series_tail(s), u);
+    float p = 0x1.664f48p-6f;                  //  62/2835
+    p = __builtin_fmaf(p, s, -0x1.ba1ba2p-5f); // -17/315
+    p = __builtin_fmaf(p, s, 0x1.111112p-3f);  //  2/15
+    p = __builtin_fmaf(p, s, -0x1.555556p-2f); // -1/3
+    const float ts = __builtin_fmaf(u * s, p, u);
     return (a < kAccurateSmall) ? ts : copy_sign(tl, u);
 }
 
