@@ -843,6 +843,12 @@ VARIANTS = {
     "default_constants": ["-DDYT_TUNE_TABLE=0"],
     # the tiled forward everywhere (no flat walk)
     "no_flat_forward": ["-DDYT_FLAT_MAX_N=0"],
+    # the forward's groups dealt round-robin to every workgroup instead of
+    # the XCD-weighted deal
+    "xcd_even_share_off": ["-DDYT_XCD_EVEN_SHARE_Q=0"],
+    "xcd_even_share_56": ["-DDYT_XCD_EVEN_SHARE_Q=573"],
+    # the 2-byte flat walk with the tiles' 53% share
+    "xcd_even_share_flat_53": ["-DDYT_XCD_EVEN_SHARE_FLAT_Q=543"],
 }
 
 

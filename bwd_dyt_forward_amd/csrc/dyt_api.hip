@@ -265,6 +265,23 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_GRID
 #define DYT_FLAT_GRID 256
 #endif
+// Share (x 1024) of the groups that the forward's workgroups on even XCDs
+// take where the forward streams with write-back stores; 512 would be an
+// even deal, 0 deals round-robin. With round-robin tiles of one slot the
+// odd XCDs' workgroups end 12-14% after the even ones on MI355X (32,768 x
+// 4,096 bf16: median exits 61 against 70 us). 543 (53%) measured best there:
+// forward 82.6 -> 79.9 us, step 218.7 -> 213.5 us; 100,003 x 255 float32
+// forward 37.6 -> 36.8 us; 573 (56%) over-corrects (81.1 us).
+#ifndef DYT_XCD_EVEN_SHARE_Q
+#define DYT_XCD_EVEN_SHARE_Q 543
+#endif
+// The same for the 2-byte flat walk, whose odd/even gap is about half the
+// tiles' (69.8 against 74.3 us median exits at 4,194,304 x 32): 53% over-
+// corrected it (forward 81.2 -> 82.0 us, even XCDs now last), so the flat
+// walk keeps the round-robin deal.
+#ifndef DYT_XCD_EVEN_SHARE_FLAT_Q
+#define DYT_XCD_EVEN_SHARE_FLAT_Q 0
+#endif
 // Widest rows of the flat forward (gamma and beta as float32 in the 160 KB
 // of LDS a gfx950 workgroup may hold; 0 turns the flat walk off). Above
 // 8,192 columns, measured at 2^27 elements: float32 9,216 / 10,240 / 13,312
@@ -424,6 +441,7 @@ Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     g.ld = (int32_t)p.ld;
     g.wcols = (int32_t)p.wcols;
     g.pitch[0] = g.pitch[1] = g.pitch[2] = N;
+    g.even_share_q = 0;
     return g;
 }
 
@@ -622,11 +640,17 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
         f.stamps = g_stamps;
 #endif
         f.head = (int32_t)head;
-        f.pad_ = 0;
         f.total = M * N - head;
         f.nvec = f.total / (16 / sx);
         f.N = (int32_t)N;
-        f.cstep = (int32_t)((base.flat_grid * DYT_FLAT_U * kBlock * (16 / sx)) % N);
+        // the XCD-weighted deal where the walk stores with write-back stores
+        // (2-byte x, no residual add) and each class gets several groups
+        const int64_t fgroups = f.nvec / (DYT_FLAT_U * kBlock);
+        const bool weigh = DYT_XCD_EVEN_SHARE_FLAT_Q != 0 && sx == 2 && !res && base.flat_grid % 2 == 0 &&
+                           fgroups >= 4 * base.flat_grid;
+        f.even_share_q = weigh ? DYT_XCD_EVEN_SHARE_FLAT_Q : 0;
+        const int64_t fstride = weigh ? base.flat_grid / 2 : base.flat_grid;
+        f.cstep = (int32_t)((fstride * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {
             return dyt::host::launch_forward_flat<decltype(xt)>(param_dtype, res, base, f, a, s);
         });
@@ -637,6 +661,9 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     Geo g = make_geo(p, M, N);
     g.pitch[0] = ldx;
     g.pitch[1] = ldy;
+    // the XCD-weighted deal for tiles of one vector slot (write-back stores),
+    // plain forward, enough groups per workgroup
+    if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid) g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return dyt::host::launch_forward<decltype(xt)>(param_dtype, res, strided, p, g, a, s);
     });

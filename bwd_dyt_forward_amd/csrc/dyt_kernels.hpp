@@ -120,6 +120,9 @@ struct Geo {
     // Row pitches (elements) of the activations of a strided launch: forward
     // x (and r), y (and h); backward x (and dres), dy, dx. N when contiguous.
     int64_t pitch[3];
+    // Forward only: the share (x 1024) of each column block's groups that
+    // the workgroups on even XCDs take (make_walk); 0: round-robin.
+    int32_t even_share_q;
     DYT_STAMPS_FIELD
 #if DYT_FUSED_FIN
     // Fused finish (backward pass 1 only): when fin_out[0] is set, the
@@ -417,27 +420,61 @@ struct TileWalk {
     int64_t col_base;  // first column of this workgroup's block (0 when packed)
     int seg_len;       // elements (packed) or columns (row segments) per tile
     bool tail;         // this workgroup also owns the partial packed tile
+    // The groups of U units of the main loop: g_first, g_first + g_stride,
+    // ... below g_end.
+    int64_t g_first, g_stride, g_end;
 };
 
-__device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G) {
+// Groups of ng that the even-XCD class takes at share share_q / 1024.
+__host__ __device__ __forceinline__ int64_t even_groups(int64_t ng, int share_q) {
+    return (ng * share_q + 512) >> 10;
+}
+
+//
+// XCD-weighted deal (share_q != 0, the forward's write-back-store kernels).
+// The hardware hands workgroup w to XCD w mod 8, and on MI355X workgroups
+// on the odd XCDs stream with write-back (plain) stores 12-14% slower than
+// those on the even XCDs, which end early and idle (bench.py --wg-timeline).
+// With share_q the workgroups form two classes by the parity of w, each pair
+// 2i, 2i + 1 sharing column block i mod nb; in every block the even class
+// takes the first share_q / 1024 of the groups and the odd class the rest,
+// each round-robin among its members. Needs G a multiple of 2 nb, else
+// (and with share_q = 0) every group is dealt round-robin to all of the
+// block's workgroups. The forward has no reduction: the deal changes which
+// workgroup computes an element, never its bits.
+template <int U>
+__device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G,
+                                              int share_q) {
     TileWalk w;
+    const int64_t nb = packed ? 1 : g.nb;
+    const bool weighted = share_q != 0 && G % (2 * nb) == 0;
+    const int64_t pair = wg >> 1, odd = wg & 1;
+    const int64_t b = weighted ? pair % nb : wg % nb;
+    w.gw = weighted ? 2 * (pair / nb) + odd : wg / nb;
+    w.gcount = G / nb;
     if (packed) {
         w.units = g.total / g.T;
         w.unit = g.T;
-        w.gw = wg;
-        w.gcount = G;
         w.col_base = 0;
         w.seg_len = g.T;
         w.tail = (w.units * (int64_t)g.T < g.total) && (wg == w.units % G);
     } else {
-        const int b = (int)(wg % g.nb);
         w.units = g.ntiles / g.nb;   // rows
         w.unit = g.N;
-        w.gw = wg / g.nb;
-        w.gcount = G / g.nb;
-        w.col_base = (int64_t)b * g.T;
+        w.col_base = b * g.T;
         w.seg_len = (b == g.nb - 1) ? g.last_len : g.T;
         w.tail = false;
+    }
+    const int64_t ng = w.units / U;
+    if (weighted) {
+        const int64_t ne = even_groups(ng, share_q);
+        w.g_first = (odd ? ne : 0) + pair / nb;
+        w.g_stride = w.gcount / 2;
+        w.g_end = odd ? ng : ne;
+    } else {
+        w.g_first = w.gw;
+        w.g_stride = w.gcount;
+        w.g_end = ng;
     }
     return w;
 }
@@ -590,7 +627,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t wg = blockIdx.x;
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    const TileWalk w = make_walk(g, PACKED, wg, G);
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
@@ -614,13 +651,13 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     // barrier. A last A load past this workgroup's groups re-reads the
     // previous group (valid memory, never computed).
     const int64_t ng = w.units / U;
-    const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
-    const int64_t ustep = w.gcount * U;          // units between this workgroup's groups
+    const int64_t iters = w.g_first < w.g_end ? (w.g_end - w.g_first + w.g_stride - 1) / w.g_stride : 0;
+    const int64_t ustep = w.g_stride * U;        // units between this workgroup's groups
     const int64_t gsi = ustep * ai.upitch, gso = ustep * ao.upitch;
     if (iters > 0) {
         typename R::T xa[U][K], xb[U][K], ra[U][K], rb[U][K];
-        int64_t bia = w.col_base + w.gw * U * ai.upitch;   // input / output bases of group A
-        int64_t boa = STRIDED ? w.col_base + w.gw * U * ao.upitch : bia;
+        int64_t bia = w.col_base + w.g_first * U * ai.upitch;   // input / output bases of group A
+        int64_t boa = STRIDED ? w.col_base + w.g_first * U * ao.upitch : bia;
         fwd_load<XT, V, K, U, RES>(x, r, bia, ai, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
@@ -729,7 +766,7 @@ struct FlatGeo {
     int32_t N;         // row length
     int32_t cstep;     // (G * U * kBlock * V) mod N
     int32_t head;      // RAG only: elements before the walk (< 128 bytes), one per thread
-    int32_t pad_;
+    int32_t even_share_q;  // share (x 1024) of the groups the even-XCD workgroups take; 0: round-robin
     DYT_STAMPS_FIELD
 };
 
@@ -858,17 +895,27 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         h += hd;
     }
     const int64_t ngroups = f.nvec / B;                 // whole groups
-    const int64_t iters = w < ngroups ? (ngroups - w + G - 1) / G : 0;
+    // The groups of this workgroup: round-robin over all workgroups, or with
+    // even_share_q (G even) the XCD-weighted deal of make_walk: the even
+    // workgroups take the first even_groups(ngroups) groups, the odd ones the
+    // rest, each round-robin among the G / 2 of its class.
+    const bool weighted = f.even_share_q != 0;
+    const int64_t ne = weighted ? even_groups(ngroups, f.even_share_q) : ngroups;
+    const int64_t g_stride = weighted ? G / 2 : G;
+    const int64_t g_first = weighted ? ((w & 1) ? ne : 0) + (w >> 1) : w;
+    const int64_t g_end = weighted && (w & 1) ? ngroups : ne;
+    const int64_t iters = g_first < g_end ? (g_end - g_first + g_stride - 1) / g_stride : 0;
     int col[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) col[j] = (int)(((w * B + j * kBlock + tid) * V + hd) % N);
+    for (int j = 0; j < U; ++j) col[j] = (int)(((g_first * B + j * kBlock + tid) * V + hd) % N);
 
     // Same two-buffer loop as dyt_fwd_kernel; a last A load past this
-    // workgroup's groups re-reads the previous group.
-    const int64_t gstep = G * B;
+    // workgroup's groups re-reads the previous group. f.cstep advances the
+    // columns by g_stride groups.
+    const int64_t gstep = g_stride * B;
     if (iters > 0) {
         typename R::T xa[U], xb[U], ra[U], rb[U];
-        int64_t qa = w * B + tid;
+        int64_t qa = g_first * B + tid;
         flat_load<XT, U, RES>(x, r, qa, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
@@ -887,8 +934,11 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         if (iters & 1) flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
     }
     DYT_STAMP(f, 1);
-    // The partial group: its owner's columns have advanced to group ngroups.
-    if (ngroups * B < f.nvec && w == ngroups % G) {
+    // The partial group (index ngroups) goes to the workgroup whose sequence
+    // reaches it; its columns have advanced to that group.
+    const bool owns_partial = weighted ? ((w & 1) && (w >> 1) == (ngroups - ne) % g_stride)
+                                       : w == ngroups % G;
+    if (ngroups * B < f.nvec && owns_partial) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int64_t q = ngroups * B + j * kBlock + tid;
@@ -1072,7 +1122,9 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const int64_t wg = blockIdx.x;
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    const TileWalk w = make_walk(g, PACKED, wg, G);
+    // round-robin deal: the rows summed into each partial row depend on the
+    // shape only
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, 0);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;
@@ -1097,13 +1149,13 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     // Same two-buffer persistent loop over groups of U adjacent units as the
     // forward.
     const int64_t ng = w.units / U;
-    const int64_t iters = w.gw < ng ? (ng - w.gw + w.gcount - 1) / w.gcount : 0;
-    const int64_t ustep = w.gcount * U;
+    const int64_t iters = w.g_first < w.g_end ? (w.g_end - w.g_first + w.g_stride - 1) / w.g_stride : 0;
+    const int64_t ustep = w.g_stride * U;
     const int64_t cb = w.col_base;
     const int64_t gsx = ustep * ax.upitch, gsd = ustep * ad.upitch, gso = ustep * ao.upitch;
     if (iters > 0) {
         typename R::T xa[U][K], da[U][K], ra[U][K], xb[U][K], db[U][K], rb[U][K];
-        const int64_t u0 = w.gw * U;
+        const int64_t u0 = w.g_first * U;
         // without row pitches all three operands share one offset
         int64_t bxa = cb + u0 * ax.upitch;
         int64_t bda = STRIDED ? cb + u0 * ad.upitch : bxa, boa = STRIDED ? cb + u0 * ao.upitch : bxa;

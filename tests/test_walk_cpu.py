@@ -1,0 +1,90 @@
+"""The workgroup deals of the forward kernels, restated from their
+documentation as a model on the CPU (no GPU): every group of a column block,
+and every flat-walk group including the partial one, goes to exactly one
+workgroup, with the XCD-weighted deal as with the round-robin one.
+
+Tiled walk (make_walk): G workgroups, nb column blocks, ng groups per block.
+Round-robin: workgroup w serves block w mod nb and takes groups
+w div nb, + G/nb, ... With share q (G a multiple of 2 nb): pair p = w div 2
+serves block p mod nb; the even workgroup of the pair takes groups
+i, i + G/(2 nb), ... below e = round(ng q / 1024), the odd one groups
+e + i, e + i + G/(2 nb), ... below ng (i = p div nb).
+
+Flat walk: ngroups whole groups and possibly a partial one (index ngroups).
+Round-robin: w takes w, w + G, ...; the partial group goes to ngroups mod G.
+Weighted (G even): even w takes w/2, w/2 + G/2, ... below e; odd w takes
+e + (w-1)/2, ... below ngroups; the partial group goes to the odd workgroup
+with (w-1)/2 = (ngroups - e) mod G/2. Its column offset advances by
+(G' B V) mod N per group, G' = G/2 weighted, G otherwise.
+"""
+import pytest
+
+hyp = pytest.importorskip("hypothesis")
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+def even_groups(ng, q):
+    return (ng * q + 512) >> 10
+
+
+def tiled_deal(G, nb, ng, q):
+    """{(block, group): workgroup} of the main loop."""
+    weighted = q != 0 and G % (2 * nb) == 0
+    out = {}
+    for w in range(G):
+        pair, odd = w >> 1, w & 1
+        b = pair % nb if weighted else w % nb
+        gcount = G // nb
+        if weighted:
+            ne = even_groups(ng, q)
+            first, stride, end = (ne if odd else 0) + pair // nb, gcount // 2, ng if odd else ne
+        else:
+            first, stride, end = w // nb, gcount, ng
+        for gi in range(first, end, stride):
+            assert (b, gi) not in out, (G, nb, ng, q, w, gi)
+            out[(b, gi)] = w
+    return out
+
+
+def flat_deal(G, ngroups, partial, q):
+    weighted = q != 0 and G % 2 == 0
+    ne = even_groups(ngroups, q) if weighted else ngroups
+    stride = G // 2 if weighted else G
+    out = {}
+    for w in range(G):
+        first = ((ne if w & 1 else 0) + (w >> 1)) if weighted else w
+        end = ngroups if (weighted and w & 1) or not weighted else ne
+        last_next = None
+        for gi in range(first, end, stride):
+            assert gi not in out
+            out[gi] = w
+            last_next = gi + stride
+        owns = ((w & 1) and (w >> 1) == (ngroups - ne) % stride) if weighted else w == ngroups % G
+        if partial and owns:
+            assert ngroups not in out
+            out[ngroups] = w
+            # the owner's sequence reaches the partial group exactly
+            nxt = first if last_next is None else last_next
+            assert nxt == ngroups, (G, ngroups, q, w, first, nxt)
+    return out
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.sampled_from([2, 4, 8, 64, 128, 256, 512, 1024, 6, 254, 510]),
+       st.sampled_from([1, 2, 3, 4]), st.integers(0, 5000), st.sampled_from([0, 512, 543, 560, 600]))
+def test_tiled_deal_covers_every_group_once(G, nb, ng, q):
+    if G % nb:
+        return
+    d = tiled_deal(G, nb, ng, q)
+    assert set(d) == {(b, gi) for b in range(nb) for gi in range(ng)}
+    if q and G % (2 * nb) == 0 and ng >= 4 * G:
+        even = sum(1 for w in d.values() if w % 2 == 0)
+        assert abs(even - nb * even_groups(ng, q)) == 0
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.sampled_from([2, 4, 8, 128, 129, 256]), st.integers(0, 20000), st.booleans(),
+       st.sampled_from([0, 512, 543, 600]))
+def test_flat_deal_covers_every_group_once(G, ngroups, partial, q):
+    d = flat_deal(G, ngroups, partial, q)
+    assert set(d) == set(range(ngroups + (1 if partial else 0)))
