@@ -849,6 +849,9 @@ VARIANTS = {
     "xcd_even_share_56": ["-DDYT_XCD_EVEN_SHARE_Q=573"],
     # the 2-byte flat walk with the tiles' 53% share
     "xcd_even_share_flat_53": ["-DDYT_XCD_EVEN_SHARE_FLAT_Q=543"],
+    # backward pass 1 weighted too
+    "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
+    "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],
 }
 
 

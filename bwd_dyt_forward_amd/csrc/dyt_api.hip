@@ -282,6 +282,12 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_XCD_EVEN_SHARE_FLAT_Q
 #define DYT_XCD_EVEN_SHARE_FLAT_Q 0
 #endif
+// The same for backward pass 1 (nontemporal stores; its XCDs end within
+// about 1 us of each other at 32,768 x 4,096). A constant of the build, so
+// the rows summed into each partial row still depend on the shape only.
+#ifndef DYT_XCD_EVEN_SHARE_BWD_Q
+#define DYT_XCD_EVEN_SHARE_BWD_Q 0
+#endif
 // Widest rows of the flat forward (gamma and beta as float32 in the 160 KB
 // of LDS a gfx950 workgroup may hold; 0 turns the flat walk off). Above
 // 8,192 columns, measured at 2^27 elements: float32 9,216 / 10,240 / 13,312
@@ -292,6 +298,11 @@ double occupancy(const Plan& p, int64_t N) {
 #endif
 static_assert(DYT_FLAT_MAX_N <= 20480, "the flat forward stages 2 N floats in at most 160 KB of LDS");
 constexpr int64_t kFlatMaxN = DYT_FLAT_MAX_N;
+// The residual-fused forward walks flat only up to 8,192 columns, the range
+// its flat-against-tiles measurements cover; wider rows keep its tiles.
+#ifndef DYT_FLAT_MAX_N_RES
+#define DYT_FLAT_MAX_N_RES 8192
+#endif
 // Rows that are not whole vectors: longest copy (flat_rag_len words; 8 of
 // them, the four shifted copies of gamma and beta, in the 160 KB of LDS a
 // gfx950 workgroup may hold), for 2-byte and for float32 x. Measured at
@@ -378,9 +389,10 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
                           dyt::flat_rag_len((int)N, (int)vmax) <=
                               (sx == 2 ? DYT_FLAT_RAG_MAX_LEN : DYT_FLAT_RAG_MAX_LEN_4B);
     const bool rag_dir = dir == Dir::Fwd || (dir == Dir::ResFwd && DYT_FLAT_RAG_RES);
-    const bool flat_ok = rag ? rag_dir && DYT_FLAT_RAG && rag_fits &&
+    const int64_t max_n = dir == Dir::ResFwd ? std::min<int64_t>(kFlatMaxN, DYT_FLAT_MAX_N_RES) : kFlatMaxN;
+    const bool flat_ok = rag ? rag_dir && DYT_FLAT_RAG && rag_fits && N <= max_n &&
                                    (sx == 2 || fill < DYT_FLAT_OCC_4B)
-                             : dir != Dir::Bwd && N <= kFlatMaxN && poor_fit;
+                             : dir != Dir::Bwd && N <= max_n && poor_fit;
     if (flat_ok) {
         const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);
         p.flat = true;
@@ -561,6 +573,7 @@ int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int 
     g.pitch[0] = ldx;
     g.pitch[1] = lddy;
     g.pitch[2] = lddx;
+    if (p.vec > 1 && p.tiles >= 8 * p.grid) g.even_share_q = DYT_XCD_EVEN_SHARE_BWD_Q;
 #if DYT_FUSED_FIN
     g.fin_out[0] = g.fin_out[1] = g.fin_out[2] = nullptr;
     g.ctr = nullptr;

@@ -1122,9 +1122,9 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const int64_t wg = blockIdx.x;
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    // round-robin deal: the rows summed into each partial row depend on the
-    // shape only
-    const TileWalk w = make_walk<U>(g, PACKED, wg, G, 0);
+    // the deal (round-robin, or XCD-weighted with g.even_share_q) depends
+    // on the shape only, so do the rows summed into each partial row
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;

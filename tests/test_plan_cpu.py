@@ -81,8 +81,9 @@ def _check_flat(f, M, N, xdt, residual=False):
     """The forward walks flat exactly for rows of a whole number of 16-byte
     vectors, at most 20,480 long, that its tiles fit poorly: filled below
     0.9 (float32 x); for 2-byte x, packed tiles or row segments filled below
-    0.85; the residual-fused forward whenever its tiles leave a slot empty or
-    are 2-byte packed tiles of two or more slots. The grid is one workgroup
+    0.85; the residual-fused forward, for rows of at most 8,192, whenever its
+    tiles leave a slot empty or are 2-byte packed tiles of two or more
+    slots. The grid is one workgroup
     per 1,024 vectors (at least one), at most 256. Only the plain forward's
     2-byte packed tiles of one slot filled at least 0.85 walk flat at
     aligned bases alone. Rows that are not a whole number of vectors walk
@@ -100,7 +101,7 @@ def _check_flat(f, M, N, xdt, residual=False):
         fits = -(-(N + v) // 4) * 4 <= (5120 if xdt == "f32" else 3584)
         want = fits and (xdt != "f32" or occ < 0.9)
     else:
-        want = N <= 20480 and poor
+        want = N <= (8192 if residual else 20480) and poor
     assert f["flat"] == int(want)
     if want:
         assert f["flat_grid"] == max(1, min(256, -(-(M * N // v) // 1024)))
@@ -200,3 +201,13 @@ def test_flat_residual_forward_choice(dyt, N, xdt, flat):
     r = dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")
     assert r["flat"] == flat
     _check_flat(r, M, N, xdt, residual=True)
+
+
+@pytest.mark.parametrize("M,N,xdt", [(33, 20000, "f32"), (100, 19456, "f32"), (33, 8200, "bf16"),
+                                     (41, 13312, "f32")])
+def test_wide_residual_forward_keeps_its_tiles(dyt, M, N, xdt):
+    """Rows over 8,192 columns: the plain forward may walk flat (gamma/beta in
+    up to 160 KB of LDS), the residual-fused one keeps its tiles, the range
+    its flat walk was measured on ending at 8,192."""
+    assert dyt.dyt_get_forward_residual_plan(M, N, xdt, "f32")["flat"] == 0
+    assert dyt.dyt_get_forward_residual_plan(M, 8192, xdt, "f32")["flat"] in (0, 1)
