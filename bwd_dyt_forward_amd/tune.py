@@ -222,9 +222,9 @@ def cmd_emit(path: str) -> None:
         data = json.load(f)
     cands = {k: tuple(v) for k, v in data["candidates"].items()}
     dflt = data["default"]
-    lines = HEADER + [f"// measured: {os.path.basename(path)}; note = representative shapes, chosen "
-                      "candidate (a-k, see tune.py) and its times relative to the default a "
-                      "(forward; backward; residual forward)"]
+    lines = HEADER + ["// measured with tune.py measure on one MI355X (interleaved rounds, medians); "
+                      "note = representative shapes, chosen candidate (a-k, see tune.py) and its times "
+                      "relative to the default a (forward; backward; residual forward)"]
     groups = {}
     for d in DTYPES:
         for lo, hi, _ in RANGES:
