@@ -7,11 +7,12 @@ Prints ONE JSON line on stdout:
                of forward + backward / measured step time
   roofline     the dominant kernel (backward pass 1) against the 8 TB/s HBM
                peak: algorithmic bytes per launch / mean launch duration from
-               HIP events recorded on the launch stream inside the timed loop
+               HIP events recorded on the launch stream around a timed run of
+               back-to-back launches
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
                workload, on one pinned host core
   stream_ceiling  measured ceilings on the same tensor size: a plain 16-byte
-               nontemporal copy and a 2-in/1-out stream (reference kernels in
+               copy and a 2-in/1-out stream (reference kernels in
                libdyt_streamref.so), with the forward's and pass 1's fraction
                of them
 Algorithmic bytes (sx = x dtype size, sp = parameter dtype size):
@@ -24,10 +25,16 @@ dh = dres + dx), the line also carries "residual": fused and unfused
 (torch.add beside the plain layer) times on the same shape.
 
 Timing: W warm-up steps (extended by untimed steps until 0.3 s have passed,
-because the GPU clocks ramp for the first ~100 steps after idle), then three
-timed regions of K steps each: A without events inside (the reported value
-and ms_per_step), B with events around backward pass 1 (the roofline
-figure), C with events around every kernel (forward/backward breakdown).
+because the GPU clocks ramp for the first ~100 steps after idle), then timed
+regions, each bracketed by one pair of HIP events on the launch stream and
+entered with one untimed call already queued: A, K whole steps (the reported
+value and ms_per_step); B, K back-to-back launches of backward pass 1 (the
+roofline figure); C, K back-to-back forwards; D, K back-to-back backwards
+(pass 1 + pass 2; pass 2's share is D - B). B, C and D are medians of three
+runs. No event is recorded between two kernels of a timed run: on some
+MI355X boxes each such record adds several microseconds to the kernel it
+brackets (events around every kernel of a step have read the 32,768 x 4,096
+forward at 91-93 us whose kernel trace shows 79.5 us).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -174,25 +181,37 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def fwd():
         dyt.dyt_forward(x, a, g, b, y=y, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        dyt.dyt_backward_partials(x, dy, a, g, dx, ws, stream=stream)
-        if ev:
-            ev[2].record(stream)
-        dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db, stream=stream)
-        if ev:
-            ev[3].record(stream)
 
-    def step_p1_events(ev):
-        dyt.dyt_forward(x, a, g, b, y=y, stream=stream)
-        ev[0].record(stream)
+    def pass1():
         dyt.dyt_backward_partials(x, dy, a, g, dx, ws, stream=stream)
-        ev[1].record(stream)
+
+    def bwd():
+        pass1()
         dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db, stream=stream)
+
+    def step():
+        fwd()
+        bwd()
+
+    def run_us(fn, n, rounds=3):
+        """Microseconds per call of n back-to-back calls of fn between one
+        pair of HIP events on the launch stream, entered with one untimed
+        call queued (the GPU is busy while the host records the first
+        event); median over rounds."""
+        out = []
+        for _ in range(rounds):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            fn()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / n)
+        return statistics.median(out)
 
     # Warm-up: `warmup` steps, extended by untimed steps until SETTLE_S of
     # wall time has passed. On MI355X the first ~100 steps after idle run up
@@ -207,9 +226,10 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
     torch.cuda.synchronize()
 
     # Timed region A (the reported value): `steps` whole steps, no events
-    # inside (each event record costs ~3 us of step time on this GPU).
+    # inside.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    step()
     h0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
@@ -219,22 +239,11 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
     host_s = time.perf_counter() - h0
     total_ms = start.elapsed_time(end)
 
-    # Timed region B (roofline): the same steps with events around the
-    # dominant kernel (backward pass 1) on its launch stream.
-    p1ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        step_p1_events(p1ev[i])
-    torch.cuda.synchronize()
-    p1 = [e[0].elapsed_time(e[1]) for e in p1ev]
-
-    # Timed region C (breakdown): events around every kernel.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    fwd = [e[0].elapsed_time(e[1]) for e in evs]
-    p2 = [e[2].elapsed_time(e[3]) for e in evs]
-    bwd = [e[1].elapsed_time(e[3]) for e in evs]
+    # Timed regions B, C, D: backward pass 1 (the dominant kernel: the
+    # roofline figure), the forward and the backward, each run back to back.
+    p1_us = run_us(pass1, steps)
+    fwd_us = run_us(fwd, steps)
+    bwd_us = run_us(bwd, steps)
     sx = x.element_size()
     sp = a.element_size()
     B = algorithmic_bytes(M, N, sx, sp)
@@ -243,13 +252,13 @@ def measure(dyt, torch, name: str, steps: int, warmup: int, graph: bool = False,
         "workload": name, "M": M, "N": N, "x_dtype": cfg.x_dtype, "param_dtype": cfg.p_dtype,
         "ms_per_step": ms_step, "host_s": host_s, "warmup_steps_run": n_warm,
         "gbps_step": (B["fwd"] + B["bwd"]) / (ms_step * 1e-3) / 1e9,
-        "fwd_us_median": statistics.median(fwd) * 1e3,
-        "bwd_us_median": statistics.median(bwd) * 1e3,
-        "pass1_us_mean": statistics.fmean(p1) * 1e3,
-        "pass2_us_mean": statistics.fmean(p2) * 1e3,
-        "fwd_gbps": B["fwd"] / (statistics.median(fwd) * 1e-3) / 1e9,
-        "bwd_gbps": B["bwd"] / (statistics.median(bwd) * 1e-3) / 1e9,
-        "pass1_gbps": B["pass1"] / (statistics.fmean(p1) * 1e-3) / 1e9,
+        "fwd_us": fwd_us,
+        "bwd_us": bwd_us,
+        "pass1_us": p1_us,
+        "pass2_us": bwd_us - p1_us,
+        "fwd_gbps": B["fwd"] / (fwd_us * 1e-6) / 1e9,
+        "bwd_gbps": B["bwd"] / (bwd_us * 1e-6) / 1e9,
+        "pass1_gbps": B["pass1"] / (p1_us * 1e-6) / 1e9,
         "bytes": B,
         "workspace_bytes": need,
         "plan": dyt.dyt_get_plan(M, N, xdt, pdt, True),
@@ -338,9 +347,9 @@ def measure_residual(dyt, torch, name: str, reps: int = 40, rounds: int = 3) -> 
 
 def stream_ceilings(torch, nbytes: int, reps: int = 40, rounds: int = 3) -> dict:
     """Measured streaming ceilings on tensors of nbytes each, from the
-    reference kernels in libdyt_streamref.so (16-byte nontemporal streams at
-    their best measured launch shapes): a copy (the forward's 1 read + 1
-    write) and a 2-in/1-out stream (backward pass 1's traffic). GB/s count
+    reference kernels in libdyt_streamref.so (16-byte streams with their
+    best measured launch shapes and store kinds): a copy (the forward's 1
+    read + 1 write) and a 2-in/1-out stream (backward pass 1's traffic). GB/s count
     every byte read and written; medians of `rounds` samples of `reps`
     back-to-back launches after a settling warm-up."""
     import ctypes
@@ -516,13 +525,18 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         e1.synchronize()
         fl.append(e0.elapsed_time(e1) * 1e3 / 100)
     floor_us = statistics.median(fl)
-    rows = [f"Launch floor (1 x 8 forward, 100 back-to-back launches): {floor_us:.2f} us per launch", "",
-            "Per-kernel columns: HIP events around each launch of a continuous eager loop "
-            "(small shapes include host launch cost). Graph columns: one captured step "
-            "(forward, pass 1, pass 2) replayed back to back.", "",
+    rows = [f"Launch floor (1 x 8 forward, 100 back-to-back launches from the host): {floor_us:.2f} us "
+            "per launch.", "",
+            "Per-kernel columns: HIP events around a run of back-to-back forwards, backwards (pass 1 + "
+            "pass 2) or pass-1 launches (small shapes: host launch cost included). Graph columns: one "
+            "captured step (forward, pass 1, pass 2) replayed back to back. Stream columns: the "
+            "forward against a copy of the same tensor bytes, backward pass 1 against a two-input, "
+            "one-output stream of the same tensor bytes (libdyt_streamref.so, measured alongside at "
+            "that size): stream time / kernel time.", "",
             "| workload | M x N | x/params | fwd us | fwd GB/s | fwd % | bwd us | bwd GB/s | bwd % | "
-            "step GB/s | step % | graph step us | graph GB/s | graph % | plan |",
-            "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
+            "step GB/s | step % | graph step us | graph GB/s | graph % | "
+            "fwd / copy | pass 1 us | pass 1 / 2-in-1-out | plan |",
+            "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
     cold_rows = ["", "Cold cache: a 1 GiB buffer is read before each timed "
                  "launch; HIP events around the forward and around pass 1 + pass 2; median [p10, p90] over "
                  "30 repetitions. CPU oracle: the fp64 oracle as it is, per direction, on a sample of whole "
@@ -542,8 +556,12 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
             f"{o['bwd_gbps']:.3f} |")
         log(cold_rows[-1])
         B = r["bytes"]
-        step_us = r["fwd_us_median"] + r["bwd_us_median"]
+        step_us = r["fwd_us"] + r["bwd_us"]
         sgbps = (B["fwd"] + B["bwd"]) / (step_us * 1e-6) / 1e9
+        tensor = r["M"] * r["N"] * (4 if r["x_dtype"] == "f32" else 2)
+        sc = stream_ceilings(torch, max(tensor, 16))
+        copy_us = 2 * sc["tensor_bytes"] / (sc["copy_GBps"] * 1e3)
+        s21_us = 3 * sc["tensor_bytes"] / (sc["two_in_one_out_GBps"] * 1e3)
         def desc(pl, grid, fwd=False):
             if fwd and pl["flat"]:
                 return f"flat, V={pl['vec']}, grid {pl['flat_grid']}"
@@ -552,10 +570,12 @@ def report_all(dyt, torch, path: str, steps: int = 20, warmup: int = 5) -> None:
         plan = (f"fwd: {desc(r['fwd_plan'], r['fwd_plan']['fwd_grid'], True)}; "
                 f"bwd: {desc(r['plan'], r['plan']['bwd_grid'])}")
         rows.append(f"| {name} | {r['M']} x {r['N']} | {r['x_dtype']}/{r['param_dtype']} | "
-                    f"{r['fwd_us_median']:.1f} | {r['fwd_gbps']:.0f} | {100 * r['fwd_frac']:.1f} | "
-                    f"{r['bwd_us_median']:.1f} | {r['bwd_gbps']:.0f} | {100 * r['bwd_frac']:.1f} | "
+                    f"{r['fwd_us']:.1f} | {r['fwd_gbps']:.0f} | {100 * r['fwd_frac']:.1f} | "
+                    f"{r['bwd_us']:.1f} | {r['bwd_gbps']:.0f} | {100 * r['bwd_frac']:.1f} | "
                     f"{sgbps:.0f} | {100 * sgbps / HBM_PEAK_GBPS:.1f} | {r['graph_step_us']:.1f} | "
-                    f"{r['graph_step_gbps']:.0f} | {100 * r['graph_step_gbps'] / HBM_PEAK_GBPS:.1f} | {plan} |")
+                    f"{r['graph_step_gbps']:.0f} | {100 * r['graph_step_gbps'] / HBM_PEAK_GBPS:.1f} | "
+                    f"{copy_us / r['fwd_us']:.2f} | {r['pass1_us']:.1f} | "
+                    f"{s21_us / r['pass1_us']:.2f} | {plan} |")
         log(rows[-1])
     with open(path, "w") as f:
         f.write("\n".join(rows + cold_rows) + "\n")
@@ -852,6 +872,11 @@ VARIANTS = {
     # backward pass 1 weighted too
     "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
     "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],
+    # the forward's write-back stores: ordinary stores for float32 x too
+    # (default: sc1, device-scope write-through buffer stores), or sc1 for
+    # 2-byte x too (default: ordinary)
+    "fwd_store_f32_plain": ["-DDYT_FWD_STORE_POL_F32=0"],
+    "fwd_store_sc1_all": ["-DDYT_FWD_STORE_POL_2B=16"],
 }
 
 
@@ -1348,12 +1373,12 @@ def main() -> int:
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
         "kernel": kernel, "algorithmic_bytes_per_launch": rl_bytes,
-        "mean_launch_us": round(main_res["pass1_us_mean"], 2),
+        "mean_launch_us": round(main_res["pass1_us"], 2),
     }
     # The same kernel's mean duration in the committed kernel trace of this
     # workload (profiles/dyt_kernels_counters.md), while the sources are
-    # those it measured: HIP events around one launch include its dispatch,
-    # the trace does not.
+    # those it measured: the events' run of back-to-back launches includes
+    # the dispatch gaps between launches, the trace does not.
     if traffic is not None and traffic.get("trace_mean_us"):
         t_us = traffic["trace_mean_us"]
         roofline["trace_mean_us"] = t_us
@@ -1384,10 +1409,10 @@ def main() -> int:
         "copy_ceiling_GBps": round(ceiling, 1),
         "stream_ceiling": streams,
         "fwd": {"GBps": round(main_res["fwd_gbps"], 1), "frac": round(main_res["fwd_frac"], 4),
-                "us": round(main_res["fwd_us_median"], 2)},
+                "us": round(main_res["fwd_us"], 2)},
         "bwd": {"GBps": round(main_res["bwd_gbps"], 1), "frac": round(main_res["bwd_frac"], 4),
-                "us": round(main_res["bwd_us_median"], 2),
-                "pass2_us": round(main_res["pass2_us_mean"], 2)},
+                "us": round(main_res["bwd_us"], 2),
+                "pass2_us": round(main_res["pass2_us"], 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -1396,9 +1421,9 @@ def main() -> int:
             "workload": sec["workload"], "GBps": round(sec["gbps_step"], 1),
             "frac": round(sec["gbps_step"] / HBM_PEAK_GBPS, 4),
             "fwd": {"GBps": round(sec["fwd_gbps"], 1), "frac": round(sec["fwd_frac"], 4),
-                    "us": round(sec["fwd_us_median"], 2)},
+                    "us": round(sec["fwd_us"], 2)},
             "bwd": {"GBps": round(sec["bwd_gbps"], 1), "frac": round(sec["bwd_frac"], 4),
-                    "us": round(sec["bwd_us_median"], 2)},
+                    "us": round(sec["bwd_us"], 2)},
         }
     if resid:
         out["residual"] = resid

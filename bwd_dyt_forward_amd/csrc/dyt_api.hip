@@ -454,6 +454,7 @@ Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     g.wcols = (int32_t)p.wcols;
     g.pitch[0] = g.pitch[1] = g.pitch[2] = N;
     g.even_share_q = 0;
+    g.buf_store = 0;
     return g;
 }
 
@@ -662,6 +663,7 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
         const bool weigh = DYT_XCD_EVEN_SHARE_FLAT_Q != 0 && sx == 2 && !res && base.flat_grid % 2 == 0 &&
                            fgroups >= 4 * base.flat_grid;
         f.even_share_q = weigh ? DYT_XCD_EVEN_SHARE_FLAT_Q : 0;
+        f.buf_store = aligned(static_cast<const char*>(a.y) + head * sx, 16);
         const int64_t fstride = weigh ? base.flat_grid / 2 : base.flat_grid;
         f.cstep = (int32_t)((fstride * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {
@@ -677,6 +679,10 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     // the XCD-weighted deal for tiles of one vector slot (write-back stores),
     // plain forward, enough groups per workgroup
     if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid) g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
+    // every vector of y on the 16-byte grid: y aligned, tiles (and, for row
+    // segments, rows) a whole number of vectors
+    g.buf_store = !strided && p.vec > 1 && aligned(a.y, 16) && p.T % p.vec == 0 &&
+                  (p.packed || N % p.vec == 0);
     const bool ok = with_dtype(x_dtype, [&](auto xt) {
         return dyt::host::launch_forward<decltype(xt)>(param_dtype, res, strided, p, g, a, s);
     });

@@ -123,6 +123,10 @@ struct Geo {
     // Forward only: the share (x 1024) of each column block's groups that
     // the workgroups on even XCDs take (make_walk); 0: round-robin.
     int32_t even_share_q;
+    // Forward only: 1 when every 16-byte vector of y lies on the 16-byte grid
+    // (y aligned, rows a whole number of vectors), so its write-back stores
+    // may go through store_with_policy.
+    int32_t buf_store;
     DYT_STAMPS_FIELD
 #if DYT_FUSED_FIN
     // Fused finish (backward pass 1 only): when fin_out[0] is set, the
@@ -566,6 +570,37 @@ constexpr bool fwd_tile_store_nt() { return DYT_FWD_NT && K >= 2; }
 template <typename XT, bool RES>
 constexpr bool fwd_flat_store_nt() { return DYT_FWD_NT && (RES || sizeof(XT) == 4); }
 
+// Cache policy of the plain forward's write-back stores above (contiguous
+// launches with 16-byte vectors), per x dtype size: 0 keeps ordinary
+// stores; a nonzero value sends each such store through a buffer descriptor
+// based at the workgroup-uniform start of its tile with those cache-policy
+// bits (16: sc1, written through to device scope instead of staying dirty
+// in its XCD's L2). Measured on MI355X (bench.py --variants
+// fwd_store_f32_plain,fwd_store_sc1_all): sc1 made the float32 100,003 x
+// 100 and x 255 forwards 4-10% faster and the bfloat16 32,768 x 4,096 and
+// 4,194,304 x 32 forwards 9-13% slower.
+#ifndef DYT_FWD_STORE_POL_F32
+#define DYT_FWD_STORE_POL_F32 16
+#endif
+#ifndef DYT_FWD_STORE_POL_2B
+#define DYT_FWD_STORE_POL_2B 0
+#endif
+template <typename XT>
+constexpr int fwd_store_pol() { return sizeof(XT) == 4 ? DYT_FWD_STORE_POL_F32 : DYT_FWD_STORE_POL_2B; }
+
+// 16-byte store of raw (one vector) at byte_off from a workgroup-uniform
+// base, through a raw buffer descriptor of span_bytes (stores past the span
+// are dropped by the hardware's range check; callers stay inside it), with
+// cache-policy bits POL.
+template <int POL, typename T>
+__device__ __forceinline__ void store_with_policy(void* uniform_base, uint32_t span_bytes,
+                                                  uint32_t byte_off, const T& raw) {
+    static_assert(sizeof(T) == 16, "one 16-byte vector");
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(uniform_base, (short)0, (int)span_bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, raw), rs, (int)byte_off, 0, POL);
+}
+
 // v = x (+ r, rounded to XT and stored to h when RES; store hint ST_NT)
 template <typename XT, int V, bool RES, bool ST_NT>
 __device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
@@ -584,12 +619,16 @@ __device__ __forceinline__ void fwd_input(const typename Raw<XT, V>::T& rx,
     }
 }
 
-template <typename XT, int V, int K, int U, bool ACC, bool RES, typename AD>
+// BUF: y's stores go through store_with_policy when span_bytes, the tile's
+// bytes, is nonzero (bo, the tile's start, is workgroup-uniform); else, and
+// without BUF, plain stores.
+template <typename XT, int V, int K, int U, bool ACC, bool RES, bool BUF, typename AD>
 __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K],
                                          const typename Raw<XT, V>::T (&rr)[U][K],
                                          XT* __restrict__ y, XT* __restrict__ h, int64_t bo,
                                          const AD& ao, const float (&gm)[K][V],
-                                         const float (&bt)[K][V], float alpha) {
+                                         const float (&bt)[K][V], float alpha,
+                                         uint32_t span_bytes) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -601,7 +640,16 @@ __device__ __forceinline__ void fwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 v[e] = __builtin_fmaf(gm[k][e], dyt_tanh<ACC>(alpha * v[e]), bt[k][e]);
-            Raw<XT, V>::template store<kStNt>(y + at, v);
+            bool done = false;
+            if constexpr (BUF) {
+                if (span_bytes != 0) {
+                    store_with_policy<fwd_store_pol<XT>()>(y + bo + j * ao.upitch, span_bytes,
+                                                         (uint32_t)(ao.off[k] * (int)sizeof(XT)),
+                                                         Raw<XT, V>::pack(v));
+                    done = true;
+                }
+            }
+            if (!done) Raw<XT, V>::template store<kStNt>(y + at, v);
         }
 }
 
@@ -643,6 +691,10 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             gm[k][e] = to_f32(gamma[c]);
             bt[k][e] = to_f32(beta[c]);
         }
+    // write-back stores of y with a cache policy (see fwd_store_pol)
+    constexpr bool BUF = fwd_store_pol<XT>() != 0 && !STRIDED && !RES && V > 1 &&
+                         !fwd_tile_store_nt<XT, K>();
+    const uint32_t span = g.buf_store ? (uint32_t)w.seg_len * (uint32_t)sizeof(XT) : 0u;
 
     // Persistent loop over this workgroup's groups of U adjacent units,
     // alternating between two register buffers (A and B): the loads of one
@@ -664,25 +716,26 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             const int64_t bib = bia + gsi, bob = STRIDED ? boa + gso : bib;
             fwd_load<XT, V, K, U, RES>(x, r, bib, ai, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, boa, ao, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES, BUF>(xa, ra, y, h, boa, ao, gm, bt, alpha, span);
             __builtin_amdgcn_sched_barrier(0);
             const bool more = 2 * pi + 2 < iters;
             const int64_t bin = more ? bib + gsi : bib;
             const int64_t bon = STRIDED ? (more ? bob + gso : bob) : bin;
             fwd_load<XT, V, K, U, RES>(x, r, bin, ai, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
-            fwd_tile<XT, V, K, U, ACC, RES>(xb, rb, y, h, bob, ao, gm, bt, alpha);
+            fwd_tile<XT, V, K, U, ACC, RES, BUF>(xb, rb, y, h, bob, ao, gm, bt, alpha, span);
             __builtin_amdgcn_sched_barrier(0);
             bia = bin;
             boa = bon;
         }
-        if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES>(xa, ra, y, h, boa, ao, gm, bt, alpha);
+        if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES, BUF>(xa, ra, y, h, boa, ao, gm, bt, alpha, span);
     }
     // units after the last whole group (fewer than U in total)
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
         typename R::T x1[1][K], r1[1][K];
         fwd_load<XT, V, K, 1, RES>(x, r, w.col_base + u * ai.upitch, ai, x1, r1);
-        fwd_tile<XT, V, K, 1, ACC, RES>(x1, r1, y, h, w.col_base + u * ao.upitch, ao, gm, bt, alpha);
+        fwd_tile<XT, V, K, 1, ACC, RES, BUF>(x1, r1, y, h, w.col_base + u * ao.upitch, ao, gm, bt, alpha,
+                                             span);
     }
     DYT_STAMP(g, 1);
 
@@ -767,6 +820,7 @@ struct FlatGeo {
     int32_t cstep;     // (G * U * kBlock * V) mod N
     int32_t head;      // RAG only: elements before the walk (< 128 bytes), one per thread
     int32_t even_share_q;  // share (x 1024) of the groups the even-XCD workgroups take; 0: round-robin
+    int32_t buf_store;     // 1: y + head on the 16-byte grid (store_with_policy allowed)
     DYT_STAMPS_FIELD
 };
 
@@ -784,12 +838,16 @@ __device__ __forceinline__ void flat_load(const XT* __restrict__ x, const XT* __
 }
 
 // Computes and stores vector q + j*kBlock (column col[j]) of a loaded group.
-template <typename XT, bool ACC, bool RES, bool RAG>
+// BUF: y's store goes through store_with_policy at byte bo_bytes from yb,
+// the workgroup-uniform start of the group, when span_bytes (one group) is
+// nonzero.
+template <typename XT, bool ACC, bool RES, bool RAG, bool BUF = false>
 __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>::T& rx,
                                          const typename Raw<XT, 16 / sizeof(XT)>::T& rr,
                                          XT* __restrict__ y, XT* __restrict__ h, int64_t at,
                                          int col, const float* sg, const float* sb, float alpha,
-                                         int L) {
+                                         int L, XT* yb = nullptr, uint32_t bo_bytes = 0,
+                                         uint32_t span_bytes = 0) {
     constexpr int V = 16 / sizeof(XT);
     float v[V], gm[V], bt[V];
     constexpr bool kStNt = fwd_flat_store_nt<XT, RES>();
@@ -811,21 +869,36 @@ __device__ __forceinline__ void flat_vec(const typename Raw<XT, 16 / sizeof(XT)>
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) v[e] = __builtin_fmaf(gm[e], dyt_tanh<ACC>(alpha * v[e]), bt[e]);
-    Raw<XT, V>::template store<kStNt>(y + at, v);
+    bool done = false;
+    if constexpr (BUF) {
+        if (span_bytes != 0) {
+            store_with_policy<fwd_store_pol<XT>()>(yb, span_bytes, bo_bytes, Raw<XT, V>::pack(v));
+            done = true;
+        }
+    }
+    if (!done) Raw<XT, V>::template store<kStNt>(y + at, v);
 }
 
 // Computes and stores a loaded group, then moves each column on to this
 // thread's next group.
+// q: this thread's first vector of the group, q0: the group's first vector
+// (workgroup-uniform).
 template <typename XT, int U, bool ACC, bool RES, bool RAG>
 __device__ __forceinline__ void flat_group(const typename Raw<XT, 16 / sizeof(XT)>::T (&rx)[U],
                                            const typename Raw<XT, 16 / sizeof(XT)>::T (&rr)[U],
                                            XT* __restrict__ y, XT* __restrict__ h, int64_t q,
-                                           int (&col)[U], const float* sg, const float* sb,
-                                           float alpha, int N, int cstep, int L) {
+                                           int64_t q0, int (&col)[U], const float* sg,
+                                           const float* sb, float alpha, int N, int cstep, int L,
+                                           bool buf) {
     constexpr int V = 16 / sizeof(XT);
+    // write-back stores of y with a cache policy (see fwd_store_pol)
+    constexpr bool BUF = fwd_store_pol<XT>() != 0 && !fwd_flat_store_nt<XT, RES>();
+    XT* const yb = y + q0 * V;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-        flat_vec<XT, ACC, RES, RAG>(rx[j], rr[j], y, h, (q + j * kBlock) * V, col[j], sg, sb, alpha, L);
+        flat_vec<XT, ACC, RES, RAG, BUF>(rx[j], rr[j], y, h, (q + j * kBlock) * V, col[j], sg, sb, alpha,
+                                         L, yb, (uint32_t)((q - q0 + j * kBlock) * 16),
+                                         buf ? (uint32_t)(U * kBlock * 16) : 0u);
         const int c = col[j] + cstep;
         col[j] = c >= N ? c - N : c;
     }
@@ -915,23 +988,30 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t gstep = g_stride * B;
     if (iters > 0) {
         typename R::T xa[U], xb[U], ra[U], rb[U];
-        int64_t qa = g_first * B + tid;
+        int64_t qa0 = g_first * B;                       // group starts (uniform)
+        int64_t qa = qa0 + tid;
         flat_load<XT, U, RES>(x, r, qa, xa, ra);
         const int64_t npairs = iters / 2;
         for (int64_t pi = 0; pi < npairs; ++pi) {
-            const int64_t qb = qa + gstep;
+            const int64_t qb0 = qa0 + gstep, qb = qa + gstep;
             flat_load<XT, U, RES>(x, r, qb, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
-            flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
+            flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, qa0, col, sg, sb, alpha, N, f.cstep, L,
+                                             f.buf_store != 0);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t qn = 2 * pi + 2 < iters ? qb + gstep : qb;
+            const bool more = 2 * pi + 2 < iters;
+            const int64_t qn0 = more ? qb0 + gstep : qb0, qn = more ? qb + gstep : qb;
             flat_load<XT, U, RES>(x, r, qn, xa, ra);
             __builtin_amdgcn_sched_barrier(0);
-            flat_group<XT, U, ACC, RES, RAG>(xb, rb, y, h, qb, col, sg, sb, alpha, N, f.cstep, L);
+            flat_group<XT, U, ACC, RES, RAG>(xb, rb, y, h, qb, qb0, col, sg, sb, alpha, N, f.cstep, L,
+                                             f.buf_store != 0);
             __builtin_amdgcn_sched_barrier(0);
+            qa0 = qn0;
             qa = qn;
         }
-        if (iters & 1) flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, col, sg, sb, alpha, N, f.cstep, L);
+        if (iters & 1)
+            flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, qa0, col, sg, sb, alpha, N, f.cstep, L,
+                                             f.buf_store != 0);
     }
     DYT_STAMP(f, 1);
     // The partial group (index ngroups) goes to the workgroup whose sequence
