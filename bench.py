@@ -877,6 +877,9 @@ VARIANTS = {
     # 2-byte x too (default: ordinary)
     "fwd_store_f32_plain": ["-DDYT_FWD_STORE_POL_F32=0"],
     "fwd_store_sc1_all": ["-DDYT_FWD_STORE_POL_2B=16"],
+    # the float32 backward's longer small-|u| branch (tanh series through
+    # u^13 and sech^2 = 1 - t^2 below |u| = 0.35)
+    "bwd_f32_long_series": ["-DDYT_ACC_BWD_SERIES=1"],
 }
 
 

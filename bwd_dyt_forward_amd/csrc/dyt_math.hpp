@@ -15,12 +15,15 @@
 //   * accurate (float32 outputs): in the backward, e via Cody & Waite's
 //     additive range reduction (W. J. Cody, W. Waite, "Software Manual for
 //     the Elementary Functions", 1980) with the hardware 2^x on the reduced
-//     argument, a Newton-refined reciprocal, and the Taylor series of tanh
-//     up to u^13 for |u| < 0.35 (coefficients 2^2n (2^2n - 1) B_2n / (2n)!,
-//     B the Bernoulli numbers): about 3-5 float32 ulp on t and on sech^2.
-//     The forward needs t only, which is well conditioned in e, so it takes
-//     e from the hardware 2^x directly and the series through u^9
-//     (tanh_fwd_f32).
+//     argument and a Newton-refined reciprocal: about 3-5 float32 ulp on
+//     sech^2 at every |u| (4e/(1+e)^2 does not cancel near 0 either). The
+//     backward's t only feeds the float32 dgamma sums, judged at 1e-5, so
+//     below |u| = 2^-5 it takes u - u^3/3 and above (1 - e)/(1 + e), whose
+//     cancellation costs at most ~1e-6 relative just above 2^-5. The forward
+//     needs t to 1e-6, well conditioned in e, so it takes e from the
+//     hardware 2^x directly and the Taylor series of tanh through u^9 below
+//     |u| = 0.35 (tanh_fwd_f32; coefficients 2^2n (2^2n - 1) B_2n / (2n)!,
+//     B the Bernoulli numbers).
 //   * fast (bfloat16 outputs): e straight from the hardware 2^x and 1/x
 //     (about 1e-5 relative at |u| = 50, far below half a bfloat16 ulp);
 //     in the forward tanh u ~= u below 2^-6 (relative error < 1e-4), in the
@@ -53,6 +56,16 @@ __device__ __forceinline__ float copy_sign(float m, float s) {
     return __builtin_copysignf(m, s);
 }
 
+constexpr float kAccurateSmall = 0.35f;
+constexpr float kFastSmallBwd = 0x1p-5f;
+
+// DYT_ACC_BWD_SERIES = 1 restores the longer small-|u| branch of the
+// accurate backward (Taylor series of tanh through u^13 and sech^2 = 1 - t^2
+// below |u| = 0.35) for comparison.
+#ifndef DYT_ACC_BWD_SERIES
+#define DYT_ACC_BWD_SERIES 0
+#endif
+
 // Taylor series of tanh(u)/u - 1 in s = u^2 (terms through s^6, u^13).
 __device__ __forceinline__ float tanh_series_tail(float s) {
     float p = 0x1.d6d3d0p-9f;                  //  21844/6081075
@@ -63,8 +76,6 @@ __device__ __forceinline__ float tanh_series_tail(float s) {
     p = __builtin_fmaf(p, s, -0x1.555556p-2f); // -1/3
     return p;
 }
-
-constexpr float kAccurateSmall = 0.35f;
 
 // Accurate tanh(u) and sech^2(u) (float32 outputs) for u = alpha * x.
 // sech^2 has relative condition number 2|u tanh u| in u, so rounding u to
@@ -94,11 +105,17 @@ __device__ __forceinline__ void tanh_sech2_accurate(float x, float alpha, float&
     const float dl = ((4.0f * e) * rc) * rc;
     // small |u|
     const float s = u * u;
+#if DYT_ACC_BWD_SERIES
     const float ts = __builtin_fmaf(u * s, tanh_series_tail(s), u);
     const float ds = __builtin_fmaf(-ts, ts, 1.0f);
     const bool small = a < kAccurateSmall;
     t = small ? ts : copy_sign(tl, u);
     d = small ? ds : dl;
+#else
+    const float ts = __builtin_fmaf(u * s, -0x1.555556p-2f, u);
+    t = (a < kFastSmallBwd) ? ts : copy_sign(tl, u);
+    d = dl;
+#endif
 }
 
 // Forward tanh for float32 outputs. y is checked at 1e-6 of |gamma t| +
@@ -139,7 +156,6 @@ __device__ __forceinline__ float tanh_fast(float u) {
 // Fast tanh and sech^2 for the backward. t feeds the float32 dgamma sums,
 // which are compared at 1e-5 relative, so small |u| keeps two series terms
 // (u - u^3/3, relative error < 2e-7 below 2^-5) where 1 - e cancels.
-constexpr float kFastSmallBwd = 0x1p-5f;
 
 __device__ __forceinline__ void tanh_sech2_fast(float u, float& t, float& d) {
     const float a = __builtin_fabsf(u);
