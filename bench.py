@@ -719,7 +719,11 @@ def _timeline_stats(st, tick_us: float) -> dict:
         if m.any():
             per_xcd[k] = (float(np.median(ex[m])), float(ex[m].max()), int(m.sum()),
                           float(np.median(t[m, 1] - t[m, 0])))
+    # which XCD workgroup w ran on, as an offset k in XCD = (w + k) mod 8
+    vals, counts = np.unique((xcc - np.arange(st.shape[0])) % 8, return_counts=True)
     return {
+        "xcd_offset": int(vals[np.argmax(counts)]),
+        "xcd_offset_all": bool(counts.max() == st.shape[0]),
         "span": float(ex.max()),
         "entry_spread": float(t[:, 0].max()),
         "exit_min": float(ex.min()), "exit_median": float(np.median(ex)), "exit_max": float(ex.max()),
@@ -731,18 +735,22 @@ def _timeline_stats(st, tick_us: float) -> dict:
 
 
 def report_wg_timeline(torch, path: str, reps: int = 30,
-                       names=(HEADLINE, SECONDARY)) -> None:
+                       names=(HEADLINE, SECONDARY), side_streams: int = 0) -> None:
     """Per-workgroup timeline of the forward and backward pass 1 in steady
     back-to-back steps (forward, pass 1, pass 2), from the timeline build of
     the library: when each workgroup starts, ends its streaming loop and
-    exits, and on which XCD it ran. Writes a Markdown summary to path."""
+    exits, and on which XCD it ran. With side_streams, that many steps are
+    first captured in HIP graphs on new streams and replayed (the state of
+    a process that has used several streams). Writes a Markdown summary to
+    path."""
     import numpy as np
     import workloads
     from bwd_dyt_forward_amd import _lib
     lib = timeline_library()
     tick_us = 0.01          # the real-time counter runs at 100 MHz
     rows = [f"# Workgroup timeline: forward and backward pass 1", "",
-            f"Command: `python bench.py --wg-timeline {path} --timeline-workloads {','.join(names)}` "
+            f"Command: `python bench.py --wg-timeline {path} --timeline-workloads {','.join(names)}"
+            + (f" --timeline-side-streams {side_streams}" if side_streams else "") + "` "
             f"(library built with {' '.join(TIMELINE_FLAGS)}; {reps} recorded steps after "
             f"{SETTLE_S} s of untimed steps; medians over the recorded steps). "
             f"Device: {torch.cuda.get_device_name(0)}.", "",
@@ -791,6 +799,10 @@ def report_wg_timeline(torch, path: str, reps: int = 30,
             assert lib.dyt_backward_finish(ws.data_ptr(), ws.numel(), da.data_ptr(), dg.data_ptr(),
                                            db.data_ptr(), M, N, xc, pc, sp) == 0
 
+        if side_streams:
+            import bwd_dyt_forward_amd as dyt
+            for _ in range(side_streams):
+                graph_step_us(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt, reps=5)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < SETTLE_S:
             for _ in range(20):
@@ -834,6 +846,12 @@ def report_wg_timeline(torch, path: str, reps: int = 30,
                 rows.append(f"| {k} | {vals[0][2]} | {statistics.median(v[0] for v in vals):.2f} | "
                             f"{statistics.median(v[1] for v in vals):.2f} | "
                             f"{statistics.median(v[3] for v in vals):.2f} |")
+            offs = {}
+            for st in sts:
+                key = st["xcd_offset"] if st["xcd_offset_all"] else "mixed"
+                offs[key] = offs.get(key, 0) + 1
+            rows += ["", "XCD of workgroup w as (w + k) mod 8, launches per k (mixed: no single k): " +
+                     ", ".join(f"k = {k}: {n}" for k, n in sorted(offs.items(), key=lambda kv: str(kv[0])))]
             late = {}
             for st in sts:
                 for i, k, _t in st["late"]:
@@ -1002,6 +1020,135 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
         torch.cuda.empty_cache()
     with open(path, "w") as f:
         f.write("\n".join(rows) + "\n")
+
+
+def report_placement(dyt, torch, path: str, name: str, variants=(), reps: int = 50) -> None:
+    """The forward and backward pass 1 of one workload timed on tensors
+    allocated at process start, after 8 s of steps on them, on the same
+    shapes freed and allocated again, and again after an allocation churn
+    (buffers of 1-600 MiB allocated, freed and returned to the driver), each
+    after a 0.3 s settling run; HIP events around `reps` back-to-back
+    launches, median of 3 runs; the default library and each named variant
+    on the same tensors. Writes Markdown."""
+    import workloads
+    from bwd_dyt_forward_amd import _lib
+    libs = {"default": dyt.lib}
+    for v in variants:
+        libs[v] = variant_library(v)
+    cfg = workloads.CONFIGS[name]
+    M, N = cfg.M, cfg.N
+    xdt = {"f32": torch.float32, "bf16": torch.bfloat16}[cfg.x_dtype]
+    pdt = {"f32": torch.float32, "bf16": torch.bfloat16}[cfg.p_dtype]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    a = torch.full((1,), 0.5, dtype=pdt, device="cuda")
+    g = (1 + 0.02 * torch.randn(N, generator=gen, device="cuda")).to(pdt)
+    b = torch.zeros(N, dtype=pdt, device="cuda")
+    B = algorithmic_bytes(M, N, torch.empty((), dtype=xdt).element_size(), a.element_size())
+
+    def alloc():
+        x = torch.randn(M, N, generator=gen, device="cuda").to(xdt)
+        dy = torch.randn(M, N, generator=gen, device="cuda").to(xdt)
+        ws = torch.empty(max(dyt.dyt_backward_workspace_size(M, N, xdt, pdt), 16), dtype=torch.uint8,
+                         device="cuda")
+        return {"x": x, "dy": dy, "y": torch.empty_like(x), "dx": torch.empty_like(x), "ws": ws}
+
+    def run(t, fn):
+        out = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            fn(t)
+            e0.record()
+            for _ in range(reps):
+                fn(t)
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return statistics.median(out)
+
+    xc, pc = _lib._code(xdt), _lib._code(pdt)
+    s = torch.cuda.current_stream().cuda_stream
+
+    def fwd_of(L):
+        def f(t):
+            if L.dyt_forward(t["x"].data_ptr(), a.data_ptr(), g.data_ptr(), b.data_ptr(), t["y"].data_ptr(),
+                             M, N, xc, pc, s) != 0:
+                raise RuntimeError("dyt_forward failed")
+        return f
+
+    def p1_of(L):
+        def f(t):
+            if L.dyt_backward_partials(t["x"].data_ptr(), t["dy"].data_ptr(), a.data_ptr(), g.data_ptr(),
+                                       t["dx"].data_ptr(), t["ws"].data_ptr(), t["ws"].numel(), M, N, xc,
+                                       pc, s) != 0:
+                raise RuntimeError("dyt_backward_partials failed")
+        return f
+
+    fwd, p1 = fwd_of(dyt.lib), p1_of(dyt.lib)
+
+    def settle(t, seconds=SETTLE_S):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                fwd(t)
+                p1(t)
+            torch.cuda.synchronize()
+
+    rows = []
+
+    def phase(label, t):
+        settle(t)
+        for v, L in libs.items():
+            f, p = run(t, fwd_of(L)), run(t, p1_of(L))
+            rows.append(f"| {label} | {v} | {f:.2f} | {B['fwd'] / (f * 1e-6) / 1e9:.0f} | {p:.2f} | "
+                        f"{B['pass1'] / (p * 1e-6) / 1e9:.0f} |")
+            log("[bench] placement: " + rows[-1])
+
+    t = alloc()
+    phase("tensors allocated at process start", t)
+    settle(t, 8.0)
+    phase("the same tensors after 8 s of forward + pass 1", t)
+    t = None
+    torch.cuda.empty_cache()
+    t = alloc()
+    phase("freed, returned to the driver and allocated again", t)
+    for i in range(3):
+        t = None
+        torch.cuda.empty_cache()
+        for mib in (1, 8, 40, 100, 300, 600, 300, 100, 8):
+            z = [torch.empty(mib << 20, dtype=torch.uint8, device="cuda") for _ in range(3)]
+            del z
+            torch.cuda.empty_cache()
+        t = alloc()
+        phase(f"allocated again after an allocation churn ({i + 1})", t)
+    # the other measurements of a workload in --all-configs, then eager again
+    # on the same tensors
+    da = torch.empty(1, dtype=pdt, device="cuda")
+    dg = torch.empty(N, dtype=pdt, device="cuda")
+    db = torch.empty(N, dtype=pdt, device="cuda")
+    cold_times(dyt, torch, t["x"], t["dy"], a, g, b, t["y"], t["dx"], t["ws"], da, dg, db, M, N, xdt, 30, B)
+    torch.cuda.empty_cache()
+    phase("the same tensors after the cold-cache timing (1 GiB read before each launch)", t)
+    graph_step_us(dyt, torch, t["x"], t["dy"], a, g, b, t["y"], t["dx"], t["ws"], da, dg, db, M, N, xdt)
+    phase("the same tensors after a step captured in a HIP graph and replayed", t)
+    stream_ceilings(torch, M * N * torch.empty((), dtype=xdt).element_size())
+    phase("the same tensors after the reference streams", t)
+    for _ in range(6):
+        graph_step_us(dyt, torch, t["x"], t["dy"], a, g, b, t["y"], t["dx"], t["ws"], da, dg, db, M, N, xdt)
+    phase("the same tensors after six more graph steps, each captured on a new stream", t)
+    hdr = ["# Placement sensitivity: " + name, "",
+           f"Command: `python bench.py --placement {path} --workload {name}"
+           + (f" --placement-variants {','.join(variants)}" if variants else "") + "`. Device: "
+           f"{torch.cuda.get_device_name(0)}.", "",
+           "Each row: a 0.3 s settling run of forward + pass 1 calls on the tensors of that row, then "
+           f"HIP events around {reps} back-to-back launches, median of 3 runs. The allocation churn "
+           "allocates three buffers each of 1, 8, 40, 100, 300, 600, 300, 100 and 8 MiB in turn, "
+           "freeing them and returning the memory to the driver after each size.", "",
+           "| tensors | library | forward us | forward GB/s | pass 1 us | pass 1 GB/s |",
+           "|---|---|---:|---:|---:|---:|"]
+    with open(path, "w") as fh:
+        fh.write("\n".join(hdr + rows) + "\n")
 
 
 def graph_vs_eager(dyt, torch, name: str, steps: int = 50) -> dict:
@@ -1293,6 +1440,9 @@ def main() -> int:
                          "(timeline build of the library) and write a Markdown summary to FILE")
     ap.add_argument("--timeline-workloads", default=f"{HEADLINE},{SECONDARY}",
                     help="with --wg-timeline: comma-separated workload names")
+    ap.add_argument("--timeline-side-streams", type=int, default=0,
+                    help="with --wg-timeline: first capture and replay this many steps in HIP graphs "
+                         "on new streams")
     ap.add_argument("--ingest-counters", metavar="DIR", default=None,
                     help="only read the profiler output under DIR/<workload>/{trace,fetch,write,sq} and "
                          "write profiles/traffic_counters.json and the Markdown summary --ingest-md")
@@ -1305,6 +1455,11 @@ def main() -> int:
                     help="only time these library variants (comma-separated names of VARIANTS) "
                          "against the default build on every workload")
     ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
+    ap.add_argument("--placement", metavar="FILE", default=None,
+                    help="only time the --workload's forward and pass 1 on tensors allocated at "
+                         "process start, after sustained steps and after reallocation (Markdown to FILE)")
+    ap.add_argument("--placement-variants", default="",
+                    help="with --placement: also time these library variants (comma-separated)")
     args = ap.parse_args()
 
     if args.graph_trace:
@@ -1338,8 +1493,14 @@ def main() -> int:
         report_variants(dyt, torch, args.variants_report, args.variants.split(","))
         log(f"[bench] variant report written to {args.variants_report}")
         return 0
+    if args.placement:
+        report_placement(dyt, torch, args.placement, args.workload,
+                         [v for v in args.placement_variants.split(",") if v])
+        log(f"[bench] placement report written to {args.placement}")
+        return 0
     if args.wg_timeline:
-        report_wg_timeline(torch, args.wg_timeline, names=args.timeline_workloads.split(","))
+        report_wg_timeline(torch, args.wg_timeline, names=args.timeline_workloads.split(","),
+                           side_streams=args.timeline_side_streams)
         log(f"[bench] workgroup timeline written to {args.wg_timeline}")
         return 0
 

@@ -26,7 +26,9 @@ from ._lib import (  # noqa: F401
     dyt_get_forward_plan,
     dyt_get_forward_residual_plan,
     dyt_get_plan,
+    dyt_set_xcd_flip_override,
     dyt_status_string,
+    dyt_xcd_hint,
     lib,
 )
 
@@ -39,5 +41,5 @@ __all__ = [
     "dyt_backward_workspace_size", "dyt_backward_noalloc", "dyt_forward_residual", "dyt_backward_residual",
     "dyt_backward_residual_partials",
     "dyt_status_string", "dyt_abi_version", "dyt_get_plan", "dyt_get_forward_plan",
-    "dyt_get_forward_residual_plan",
+    "dyt_get_forward_residual_plan", "dyt_xcd_hint", "dyt_set_xcd_flip_override",
 ]

@@ -21,7 +21,7 @@ DYT_BF16 = 1
 DYT_F16 = 2
 DYT_OK = 0
 # DYT_ABI_VERSION of include/dyt.h that the signatures and DytPlan below mirror
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _TORCH_TO_CODE = {torch.float32: DYT_F32, torch.bfloat16: DYT_BF16, torch.float16: DYT_F16}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
@@ -72,6 +72,8 @@ SIGNATURES = {
     "dyt_status_string": (ctypes.c_char_p, [_int]),
     "dyt_abi_version": (_int, []),
     "dyt_build_id": (ctypes.c_char_p, []),
+    "dyt_xcd_hint": (_int, [ctypes.c_void_p]),
+    "dyt_set_xcd_flip_override": (_int, [_int]),
     "dyt_get_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
     "dyt_get_forward_plan": (_int, [_i64, _i64, _int, _int, _int, ctypes.POINTER(DytPlan)]),
     "dyt_get_forward_residual_plan": (_int, [_i64, _i64, _int, _int, ctypes.POINTER(DytPlan)]),
@@ -405,6 +407,16 @@ def dyt_status_string(status: int) -> str:
 
 def dyt_abi_version() -> int:
     return int(lib.dyt_abi_version())
+
+
+def dyt_xcd_hint(stream=None) -> int:
+    """The XCD (0-7) the last XCD-weighted forward on `stream` started on, -1 if none."""
+    return int(lib.dyt_xcd_hint(_stream(stream)))
+
+
+def dyt_set_xcd_flip_override(flip: int) -> None:
+    """Force the forward's XCD parity (0 or 1) for later launches; -1 follows the hint."""
+    _check("dyt_set_xcd_flip_override", lib.dyt_set_xcd_flip_override(int(flip)))
 
 
 def dyt_get_plan(M: int, N: int, x_dtype, param_dtype, vector_access: bool = True) -> dict:

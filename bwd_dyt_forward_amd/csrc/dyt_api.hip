@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
@@ -271,7 +272,12 @@ double occupancy(const Plan& p, int64_t N) {
 // odd XCDs' workgroups end 12-14% after the even ones on MI355X (32,768 x
 // 4,096 bf16: median exits 61 against 70 us). 543 (53%) measured best there:
 // forward 82.6 -> 79.9 us, step 218.7 -> 213.5 us; 100,003 x 255 float32
-// forward 37.6 -> 36.8 us; 573 (56%) over-corrects (81.1 us).
+// forward 37.6 -> 36.8 us; 573 (56%) over-corrects (81.1 us). Which
+// workgroups run on the even XCDs depends on the hardware queue (XCD of
+// workgroup w = (w + k) mod 8, k 0 in a one-stream process and 5 in one
+// that had captured graphs on six more streams), so the launch follows the
+// XCD parity hint below; with k odd and no hint the weighted deal measured
+// 84.0 against 82.2 us round-robin.
 #ifndef DYT_XCD_EVEN_SHARE_Q
 #define DYT_XCD_EVEN_SHARE_Q 543
 #endif
@@ -454,6 +460,8 @@ Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     g.wcols = (int32_t)p.wcols;
     g.pitch[0] = g.pitch[1] = g.pitch[2] = N;
     g.even_share_q = 0;
+    g.xcd_flip = 0;
+    g.xcd_seen = nullptr;
     g.buf_store = 0;
     return g;
 }
@@ -602,6 +610,76 @@ int enqueue_pass2(const Plan& base, const void* workspace, void* dalpha, void* d
     return hip_status();
 }
 
+// ------------------------------------------------------- XCD parity hint
+// The forward's XCD-weighted deal gives the larger share to the class of
+// workgroups expected on the even XCDs; which class that is depends on the
+// hardware queue the stream runs on (the XCD of its workgroup 0). Each
+// weighted launch records the XCD its workgroup 0 ran on in a slot of
+// coherent pinned host memory, and the next launch on that stream reads the
+// slot to choose its flip. The value is only a hint: flip is a kernel
+// argument, the same for the whole launch, and every flip covers every
+// group exactly once; a stale or raced slot costs time, never results. The
+// slots (64 per device, chosen by the stream's address) are allocated by
+// the device's first weighted forward outside stream capture and kept
+// until the process ends; without them flip is 0.
+constexpr int kHintDevices = 64;
+constexpr int kHintSlots = 64;
+struct XcdHint {
+    std::mutex mu;
+    std::atomic<int32_t*> host{nullptr};
+    int32_t* dev = nullptr;   // device address of host[0]
+    int xccs = 0;             // XCDs of the device, 0 if unknown
+    bool tried = false;
+};
+XcdHint g_xcd_hint[kHintDevices];
+std::atomic<int> g_flip_override{-1};   // dyt_set_xcd_flip_override
+
+// The hint slot of stream s on the current device (host and device
+// addresses) and the device's XCD count; false when there are no slots.
+bool xcd_hint_slot(hipStream_t s, int32_t** host_slot, int32_t** dev_slot, int* xccs) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kHintDevices) {
+        (void)hipGetLastError();
+        return false;
+    }
+    XcdHint& h = g_xcd_hint[dev];
+    int32_t* host = h.host.load(std::memory_order_acquire);
+    if (host == nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return false;   // no allocation while a graph is being captured
+        }
+        std::lock_guard<std::mutex> lock(h.mu);
+        if (!h.tried) {
+            h.tried = true;
+            int n = 0;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess) h.xccs = n;
+            void* p = nullptr;
+            if (hipHostMalloc(&p, kHintSlots * sizeof(int32_t), hipHostMallocCoherent) == hipSuccess &&
+                p != nullptr) {
+                void* d = nullptr;
+                if (hipHostGetDevicePointer(&d, p, 0) == hipSuccess && d != nullptr) {
+                    int32_t* q = static_cast<int32_t*>(p);
+                    for (int i = 0; i < kHintSlots; ++i) q[i] = -1;
+                    h.dev = static_cast<int32_t*>(d);
+                    h.host.store(q, std::memory_order_release);
+                } else {
+                    (void)hipHostFree(p);
+                }
+            }
+            (void)hipGetLastError();   // a failure here is not the launch's error
+        }
+        host = h.host.load(std::memory_order_acquire);
+        if (host == nullptr) return false;
+    }
+    const size_t i = ((uintptr_t)s >> 4) % kHintSlots;
+    *host_slot = host + i;
+    *dev_slot = h.dev + i;
+    *xccs = h.xccs;
+    return true;
+}
+
 // Forward with or without the fused residual add: validation, then launch.
 int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, int param_dtype,
                  hipStream_t s) {
@@ -678,7 +756,22 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     g.pitch[1] = ldy;
     // the XCD-weighted deal for tiles of one vector slot (write-back stores),
     // plain forward, enough groups per workgroup
-    if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid) g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
+    if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid && DYT_XCD_EVEN_SHARE_Q != 0) {
+        g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
+        int32_t *hs = nullptr, *ds = nullptr;
+        int xccs = 0;
+        if (xcd_hint_slot(s, &hs, &ds, &xccs)) {
+            if (xccs != 0 && xccs != 8) {
+                g.even_share_q = 0;   // the deal is measured for eight XCDs
+            } else {
+                const int32_t seen = *static_cast<volatile int32_t*>(hs);
+                g.xcd_flip = seen >= 0 ? (seen & 1) : 0;
+                g.xcd_seen = ds;
+            }
+        }
+        const int ov = g_flip_override.load(std::memory_order_relaxed);
+        if (ov >= 0) g.xcd_flip = ov;
+    }
     // every vector of y on the 16-byte grid: y aligned, tiles (and, for row
     // segments, rows) a whole number of vectors
     g.buf_store = !strided && p.vec > 1 && aligned(a.y, 16) && p.T % p.vec == 0 &&
@@ -775,6 +868,24 @@ extern "C" {
 int dyt_abi_version(void) { return DYT_ABI_VERSION; }
 
 const char* dyt_build_id(void) { return kBuildId + kBuildIdSkip; }
+
+int dyt_xcd_hint(void* stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kHintDevices) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    const int32_t* host = g_xcd_hint[dev].host.load(std::memory_order_acquire);
+    if (host == nullptr) return -1;
+    const size_t i = ((uintptr_t)stream >> 4) % kHintSlots;
+    return *static_cast<const volatile int32_t*>(host + i);
+}
+
+int dyt_set_xcd_flip_override(int flip) {
+    if (flip < -1 || flip > 1) return DYT_ERR_INVALID_ARG;
+    g_flip_override.store(flip, std::memory_order_relaxed);
+    return DYT_OK;
+}
 
 #if DYT_WG_TIMELINE
 // Measurement builds only (not part of the ABI in dyt.h): the device buffer

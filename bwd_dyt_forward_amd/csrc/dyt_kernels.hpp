@@ -123,6 +123,11 @@ struct Geo {
     // Forward only: the share (x 1024) of each column block's groups that
     // the workgroups on even XCDs take (make_walk); 0: round-robin.
     int32_t even_share_q;
+    // Forward only: 1 when the workgroups of odd index are expected on the
+    // even XCDs (make_walk); xcd_seen, when not null, receives the XCD that
+    // workgroup 0 ran on (a hint for the next launch's xcd_flip).
+    int32_t xcd_flip;
+    int32_t* xcd_seen;
     // Forward only: 1 when every 16-byte vector of y lies on the 16-byte grid
     // (y aligned, rows a whole number of vectors), so its write-back stores
     // may go through store_with_policy.
@@ -436,19 +441,24 @@ __host__ __device__ __forceinline__ int64_t even_groups(int64_t ng, int share_q)
 
 //
 // XCD-weighted deal (share_q != 0, the forward's write-back-store kernels).
-// The hardware hands workgroup w to XCD w mod 8, and on MI355X workgroups
-// on the odd XCDs stream with write-back (plain) stores 12-14% slower than
-// those on the even XCDs, which end early and idle (bench.py --wg-timeline).
-// With share_q the workgroups form two classes by the parity of w, each pair
-// 2i, 2i + 1 sharing column block i mod nb; in every block the even class
-// takes the first share_q / 1024 of the groups and the odd class the rest,
-// each round-robin among its members. Needs G a multiple of 2 nb, else
-// (and with share_q = 0) every group is dealt round-robin to all of the
-// block's workgroups. The forward has no reduction: the deal changes which
-// workgroup computes an element, never its bits.
+// The hardware hands workgroup w to XCD (w + k) mod 8, k fixed per hardware
+// queue (0 in a process that uses one stream; other values once more
+// streams than hardware queues exist), and on MI355X workgroups on the odd
+// XCDs stream with write-back (plain) stores 12-14% slower than those on
+// the even XCDs, which end early and idle (bench.py --wg-timeline). With
+// share_q the workgroups form two classes by the parity of w, each pair
+// 2i, 2i + 1 sharing column block i mod nb; in every block the class
+// expected on the even XCDs (even w, or odd w when flip = 1, i.e. k odd)
+// takes the first share_q / 1024 of the groups and the other class the rest,
+// each round-robin among its members. Every group is covered once whatever
+// flip is, as long as it is the same for the whole launch (a kernel
+// argument). Needs G a multiple of 2 nb, else (and with share_q = 0) every
+// group is dealt round-robin to all of the block's workgroups. The forward
+// has no reduction: the deal changes which workgroup computes an element,
+// never its bits.
 template <int U>
 __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G,
-                                              int share_q) {
+                                              int share_q, int flip) {
     TileWalk w;
     const int64_t nb = packed ? 1 : g.nb;
     const bool weighted = share_q != 0 && G % (2 * nb) == 0;
@@ -472,9 +482,10 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t
     const int64_t ng = w.units / U;
     if (weighted) {
         const int64_t ne = even_groups(ng, share_q);
-        w.g_first = (odd ? ne : 0) + pair / nb;
+        const int64_t cls = odd ^ (int64_t)(flip & 1);   // 1: the class expected on odd XCDs
+        w.g_first = (cls ? ne : 0) + pair / nb;
         w.g_stride = w.gcount / 2;
-        w.g_end = odd ? ng : ne;
+        w.g_end = cls ? ng : ne;
     } else {
         w.g_first = w.gw;
         w.g_stride = w.gcount;
@@ -675,11 +686,16 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t wg = blockIdx.x;
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q);
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
     DYT_STAMP(g, 0);
+    if (g.xcd_seen != nullptr && wg == 0 && tid == 0) {
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        *g.xcd_seen = (int32_t)(xcc & 0xFu);
+    }
 
     float gm[K][V], bt[K][V];
 #pragma unroll
@@ -1204,7 +1220,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const float alpha = to_f32(alpha_p[0]);
     // the deal (round-robin, or XCD-weighted with g.even_share_q) depends
     // on the shape only, so do the rows summed into each partial row
-    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q);
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;

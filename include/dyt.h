@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define DYT_ABI_VERSION 6
+#define DYT_ABI_VERSION 7
 
 typedef enum dyt_dtype {
     DYT_F32 = 0,  /* IEEE binary32 */
@@ -97,6 +97,10 @@ typedef enum dyt_status {
  *   y      [M, N] x_dtype, written
  * M == 0 or N == 0: nothing is enqueued and DYT_OK is returned (pointers may
  * then be NULL).
+ * Launches that weight their workgroups by XCD (see dyt_xcd_hint) record the
+ * XCD their first workgroup ran on in pinned host memory that the library
+ * allocates once per device (256 bytes, on the first such launch outside
+ * stream capture, kept until the process ends).
  */
 int dyt_forward(const void* x, const void* alpha, const void* gamma, const void* beta,
                 void* y, int64_t M, int64_t N, int x_dtype, int param_dtype,
@@ -273,6 +277,23 @@ int dyt_abi_version(void);
  * to it.
  */
 const char* dyt_build_id(void);
+
+/*
+ * XCD parity hint of the forward (performance only; results never depend on
+ * it). The hardware places workgroup w of a launch on XCD (w + k) mod 8, k
+ * fixed per hardware queue, and on MI355X the forward's workgroups on odd
+ * XCDs stream more slowly, so the forward gives the larger share of its
+ * tiles to the workgroups it expects on even XCDs. It learns k's parity
+ * from the XCD its previous launch on the same stream started on.
+ * dyt_xcd_hint returns that recorded XCD (0-7) for `stream` on the current
+ * device, or -1 if none is recorded yet. dyt_set_xcd_flip_override forces
+ * the parity for every later forward launch in the process (0 or 1; -1
+ * returns to the recorded hint) and returns DYT_OK, or
+ * DYT_ERR_INVALID_ARG for other values; it exists so that tests can run
+ * both deals on any GPU.
+ */
+int dyt_xcd_hint(void* stream);
+int dyt_set_xcd_flip_override(int flip);
 
 /*
  * Launch geometry the library would use (for tests and reports; pure host

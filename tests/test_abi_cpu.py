@@ -32,7 +32,16 @@ def test_header_declares_expected_entry_points():
         "dyt_backward_workspace_size", "dyt_status_string", "dyt_abi_version", "dyt_get_plan",
         "dyt_forward_residual", "dyt_backward_residual", "dyt_backward_residual_partials",
         "dyt_get_forward_plan", "dyt_forward_strided", "dyt_backward_strided",
-        "dyt_get_forward_residual_plan", "dyt_build_id", "dyt_backward_noalloc"])
+        "dyt_get_forward_residual_plan", "dyt_build_id", "dyt_backward_noalloc",
+        "dyt_xcd_hint", "dyt_set_xcd_flip_override"])
+
+
+def test_xcd_flip_override_accepts_only_a_parity_or_minus_one(dyt):
+    """Host-only: the override takes -1, 0 or 1; anything else is rejected."""
+    for v in (2, -2, 7):
+        assert dyt.lib.dyt_set_xcd_flip_override(v) == 1   # DYT_ERR_INVALID_ARG
+    for v in (0, 1, -1):
+        assert dyt.lib.dyt_set_xcd_flip_override(v) == 0
 
 
 def test_library_exports_every_declared_symbol(dyt):
@@ -55,7 +64,7 @@ def test_no_cpu_fallback_in_product_path():
 
 
 def test_version_and_status_strings(dyt):
-    assert dyt.dyt_abi_version() == 6
+    assert dyt.dyt_abi_version() == 7
     names = [dyt.dyt_status_string(i) for i in range(6)]
     assert names == ["DYT_OK", "DYT_ERR_INVALID_ARG", "DYT_ERR_UNSUPPORTED_DTYPE",
                      "DYT_ERR_WORKSPACE_TOO_SMALL", "DYT_ERR_MISALIGNED", "DYT_ERR_HIP"]

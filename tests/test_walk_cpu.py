@@ -6,9 +6,10 @@ workgroup, with the XCD-weighted deal as with the round-robin one.
 Tiled walk (make_walk): G workgroups, nb column blocks, ng groups per block.
 Round-robin: workgroup w serves block w mod nb and takes groups
 w div nb, + G/nb, ... With share q (G a multiple of 2 nb): pair p = w div 2
-serves block p mod nb; the even workgroup of the pair takes groups
-i, i + G/(2 nb), ... below e = round(ng q / 1024), the odd one groups
-e + i, e + i + G/(2 nb), ... below ng (i = p div nb).
+serves block p mod nb; the workgroup of the pair whose parity equals flip
+(the launch-wide XCD parity hint) takes groups i, i + G/(2 nb), ... below
+e = round(ng q / 1024), the other one groups e + i, e + i + G/(2 nb), ...
+below ng (i = p div nb).
 
 Flat walk: ngroups whole groups and possibly a partial one (index ngroups).
 Round-robin: w takes w, w + G, ...; the partial group goes to ngroups mod G.
@@ -27,17 +28,18 @@ def even_groups(ng, q):
     return (ng * q + 512) >> 10
 
 
-def tiled_deal(G, nb, ng, q):
+def tiled_deal(G, nb, ng, q, flip=0):
     """{(block, group): workgroup} of the main loop."""
     weighted = q != 0 and G % (2 * nb) == 0
     out = {}
     for w in range(G):
         pair, odd = w >> 1, w & 1
+        cls = odd ^ flip
         b = pair % nb if weighted else w % nb
         gcount = G // nb
         if weighted:
             ne = even_groups(ng, q)
-            first, stride, end = (ne if odd else 0) + pair // nb, gcount // 2, ng if odd else ne
+            first, stride, end = (ne if cls else 0) + pair // nb, gcount // 2, ng if cls else ne
         else:
             first, stride, end = w // nb, gcount, ng
         for gi in range(first, end, stride):
@@ -71,15 +73,16 @@ def flat_deal(G, ngroups, partial, q):
 
 @settings(max_examples=400, deadline=None)
 @given(st.sampled_from([2, 4, 8, 64, 128, 256, 512, 1024, 6, 254, 510]),
-       st.sampled_from([1, 2, 3, 4]), st.integers(0, 5000), st.sampled_from([0, 512, 543, 560, 600]))
-def test_tiled_deal_covers_every_group_once(G, nb, ng, q):
+       st.sampled_from([1, 2, 3, 4]), st.integers(0, 5000), st.sampled_from([0, 512, 543, 560, 600]),
+       st.sampled_from([0, 1]))
+def test_tiled_deal_covers_every_group_once(G, nb, ng, q, flip):
     if G % nb:
         return
-    d = tiled_deal(G, nb, ng, q)
+    d = tiled_deal(G, nb, ng, q, flip)
     assert set(d) == {(b, gi) for b in range(nb) for gi in range(ng)}
     if q and G % (2 * nb) == 0 and ng >= 4 * G:
-        even = sum(1 for w in d.values() if w % 2 == 0)
-        assert abs(even - nb * even_groups(ng, q)) == 0
+        favoured = sum(1 for w in d.values() if w % 2 == flip)
+        assert abs(favoured - nb * even_groups(ng, q)) == 0
 
 
 @settings(max_examples=400, deadline=None)
