@@ -885,8 +885,10 @@ VARIANTS = {
     # the XCD-weighted deal
     "xcd_even_share_off": ["-DDYT_XCD_EVEN_SHARE_Q=0"],
     "xcd_even_share_56": ["-DDYT_XCD_EVEN_SHARE_Q=573"],
-    # the 2-byte flat walk with the tiles' 53% share
+    # the 2-byte flat walk with the tiles' 53% share, or less
     "xcd_even_share_flat_53": ["-DDYT_XCD_EVEN_SHARE_FLAT_Q=543"],
+    "xcd_even_share_flat_515": ["-DDYT_XCD_EVEN_SHARE_FLAT_Q=527"],
+    "xcd_even_share_flat_52": ["-DDYT_XCD_EVEN_SHARE_FLAT_Q=532"],
     # backward pass 1 weighted too
     "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
     "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],

@@ -283,8 +283,9 @@ double occupancy(const Plan& p, int64_t N) {
 #endif
 // The same for the 2-byte flat walk, whose odd/even gap is about half the
 // tiles' (69.8 against 74.3 us median exits at 4,194,304 x 32): 53% over-
-// corrected it (forward 81.2 -> 82.0 us, even XCDs now last), so the flat
-// walk keeps the round-robin deal.
+// corrected it (forward 81.2 -> 82.0 us, even XCDs now last); with the XCD
+// parity hint, 51.5-53% stay within 0.6 us of round-robin, so the flat walk
+// keeps the round-robin deal.
 #ifndef DYT_XCD_EVEN_SHARE_FLAT_Q
 #define DYT_XCD_EVEN_SHARE_FLAT_Q 0
 #endif
@@ -680,6 +681,28 @@ bool xcd_hint_slot(hipStream_t s, int32_t** host_slot, int32_t** dev_slot, int* 
     return true;
 }
 
+// The XCD parity of a weighted forward launch on stream s: share_q is
+// cleared on devices that report another XCD count than 8; flip and seen
+// follow the stream's hint slot and dyt_set_xcd_flip_override.
+void apply_xcd_hint(hipStream_t s, int32_t& share_q, int32_t& flip, int32_t*& seen) {
+    flip = 0;
+    seen = nullptr;
+    if (share_q == 0) return;
+    int32_t *hs = nullptr, *ds = nullptr;
+    int xccs = 0;
+    if (xcd_hint_slot(s, &hs, &ds, &xccs)) {
+        if (xccs != 0 && xccs != 8) {
+            share_q = 0;   // the deal is measured for eight XCDs
+            return;
+        }
+        const int32_t v = *static_cast<volatile int32_t*>(hs);
+        flip = v >= 0 ? (v & 1) : 0;
+        seen = ds;
+    }
+    const int ov = g_flip_override.load(std::memory_order_relaxed);
+    if (ov >= 0) flip = ov;
+}
+
 // Forward with or without the fused residual add: validation, then launch.
 int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, int param_dtype,
                  hipStream_t s) {
@@ -741,8 +764,9 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
         const bool weigh = DYT_XCD_EVEN_SHARE_FLAT_Q != 0 && sx == 2 && !res && base.flat_grid % 2 == 0 &&
                            fgroups >= 4 * base.flat_grid;
         f.even_share_q = weigh ? DYT_XCD_EVEN_SHARE_FLAT_Q : 0;
+        apply_xcd_hint(s, f.even_share_q, f.xcd_flip, f.xcd_seen);   // may clear the share
         f.buf_store = aligned(static_cast<const char*>(a.y) + head * sx, 16);
-        const int64_t fstride = weigh ? base.flat_grid / 2 : base.flat_grid;
+        const int64_t fstride = f.even_share_q != 0 ? base.flat_grid / 2 : base.flat_grid;
         f.cstep = (int32_t)((fstride * DYT_FLAT_U * kBlock * (16 / sx)) % N);
         const bool ok = with_dtype(x_dtype, [&](auto xt) {
             return dyt::host::launch_forward_flat<decltype(xt)>(param_dtype, res, base, f, a, s);
@@ -756,21 +780,9 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     g.pitch[1] = ldy;
     // the XCD-weighted deal for tiles of one vector slot (write-back stores),
     // plain forward, enough groups per workgroup
-    if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid && DYT_XCD_EVEN_SHARE_Q != 0) {
+    if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid) {
         g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
-        int32_t *hs = nullptr, *ds = nullptr;
-        int xccs = 0;
-        if (xcd_hint_slot(s, &hs, &ds, &xccs)) {
-            if (xccs != 0 && xccs != 8) {
-                g.even_share_q = 0;   // the deal is measured for eight XCDs
-            } else {
-                const int32_t seen = *static_cast<volatile int32_t*>(hs);
-                g.xcd_flip = seen >= 0 ? (seen & 1) : 0;
-                g.xcd_seen = ds;
-            }
-        }
-        const int ov = g_flip_override.load(std::memory_order_relaxed);
-        if (ov >= 0) g.xcd_flip = ov;
+        apply_xcd_hint(s, g.even_share_q, g.xcd_flip, g.xcd_seen);
     }
     // every vector of y on the 16-byte grid: y aligned, tiles (and, for row
     // segments, rows) a whole number of vectors

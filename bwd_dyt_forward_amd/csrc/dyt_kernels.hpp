@@ -836,6 +836,8 @@ struct FlatGeo {
     int32_t cstep;     // (G * U * kBlock * V) mod N
     int32_t head;      // RAG only: elements before the walk (< 128 bytes), one per thread
     int32_t even_share_q;  // share (x 1024) of the groups the even-XCD workgroups take; 0: round-robin
+    int32_t xcd_flip;      // 1: odd workgroups expected on the even XCDs (as in Geo)
+    int32_t* xcd_seen;     // not null: receives the XCD of workgroup 0 (as in Geo)
     int32_t buf_store;     // 1: y + head on the 16-byte grid (store_with_policy allowed)
     DYT_STAMPS_FIELD
 };
@@ -985,14 +987,21 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     }
     const int64_t ngroups = f.nvec / B;                 // whole groups
     // The groups of this workgroup: round-robin over all workgroups, or with
-    // even_share_q (G even) the XCD-weighted deal of make_walk: the even
-    // workgroups take the first even_groups(ngroups) groups, the odd ones the
-    // rest, each round-robin among the G / 2 of its class.
+    // even_share_q (G even) the XCD-weighted deal of make_walk: the class
+    // expected on the even XCDs (even w, or odd w with xcd_flip) takes the
+    // first even_groups(ngroups) groups, the other class the rest, each
+    // round-robin among the G / 2 of its class.
     const bool weighted = f.even_share_q != 0;
+    const int64_t cls = (w & 1) ^ (int64_t)(f.xcd_flip & 1);
     const int64_t ne = weighted ? even_groups(ngroups, f.even_share_q) : ngroups;
     const int64_t g_stride = weighted ? G / 2 : G;
-    const int64_t g_first = weighted ? ((w & 1) ? ne : 0) + (w >> 1) : w;
-    const int64_t g_end = weighted && (w & 1) ? ngroups : ne;
+    const int64_t g_first = weighted ? (cls ? ne : 0) + (w >> 1) : w;
+    const int64_t g_end = weighted && cls ? ngroups : ne;
+    if (weighted && f.xcd_seen != nullptr && w == 0 && tid == 0) {
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        *f.xcd_seen = (int32_t)(xcc & 0xFu);
+    }
     const int64_t iters = g_first < g_end ? (g_end - g_first + g_stride - 1) / g_stride : 0;
     int col[U];
 #pragma unroll
@@ -1032,7 +1041,7 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     DYT_STAMP(f, 1);
     // The partial group (index ngroups) goes to the workgroup whose sequence
     // reaches it; its columns have advanced to that group.
-    const bool owns_partial = weighted ? ((w & 1) && (w >> 1) == (ngroups - ne) % g_stride)
+    const bool owns_partial = weighted ? (cls && (w >> 1) == (ngroups - ne) % g_stride)
                                        : w == ngroups % G;
     if (ngroups * B < f.nvec && owns_partial) {
 #pragma unroll

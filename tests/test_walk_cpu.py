@@ -13,9 +13,9 @@ below ng (i = p div nb).
 
 Flat walk: ngroups whole groups and possibly a partial one (index ngroups).
 Round-robin: w takes w, w + G, ...; the partial group goes to ngroups mod G.
-Weighted (G even): even w takes w/2, w/2 + G/2, ... below e; odd w takes
-e + (w-1)/2, ... below ngroups; the partial group goes to the odd workgroup
-with (w-1)/2 = (ngroups - e) mod G/2. Its column offset advances by
+Weighted (G even): w of parity flip takes w div 2, + G/2, ... below e; the
+others take e + w div 2, ... below ngroups; the partial group goes to the
+workgroup of the other parity with w div 2 = (ngroups - e) mod G/2. Its column offset advances by
 (G' B V) mod N per group, G' = G/2 weighted, G otherwise.
 """
 import pytest
@@ -48,20 +48,21 @@ def tiled_deal(G, nb, ng, q, flip=0):
     return out
 
 
-def flat_deal(G, ngroups, partial, q):
+def flat_deal(G, ngroups, partial, q, flip=0):
     weighted = q != 0 and G % 2 == 0
     ne = even_groups(ngroups, q) if weighted else ngroups
     stride = G // 2 if weighted else G
     out = {}
     for w in range(G):
-        first = ((ne if w & 1 else 0) + (w >> 1)) if weighted else w
-        end = ngroups if (weighted and w & 1) or not weighted else ne
+        cls = (w & 1) ^ flip
+        first = ((ne if cls else 0) + (w >> 1)) if weighted else w
+        end = ngroups if (weighted and cls) or not weighted else ne
         last_next = None
         for gi in range(first, end, stride):
             assert gi not in out
             out[gi] = w
             last_next = gi + stride
-        owns = ((w & 1) and (w >> 1) == (ngroups - ne) % stride) if weighted else w == ngroups % G
+        owns = (cls and (w >> 1) == (ngroups - ne) % stride) if weighted else w == ngroups % G
         if partial and owns:
             assert ngroups not in out
             out[ngroups] = w
@@ -87,7 +88,7 @@ def test_tiled_deal_covers_every_group_once(G, nb, ng, q, flip):
 
 @settings(max_examples=400, deadline=None)
 @given(st.sampled_from([2, 4, 8, 128, 129, 256]), st.integers(0, 20000), st.booleans(),
-       st.sampled_from([0, 512, 543, 600]))
-def test_flat_deal_covers_every_group_once(G, ngroups, partial, q):
-    d = flat_deal(G, ngroups, partial, q)
+       st.sampled_from([0, 512, 527, 543, 600]), st.sampled_from([0, 1]))
+def test_flat_deal_covers_every_group_once(G, ngroups, partial, q, flip):
+    d = flat_deal(G, ngroups, partial, q, flip)
     assert set(d) == set(range(ngroups + (1 if partial else 0)))
