@@ -86,8 +86,9 @@ def algorithmic_bytes(M: int, N: int, sx: int, sp: int) -> dict:
 
 
 def graph_step_us(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt, reps: int = 50) -> float:
-    """One step (forward, pass 1, pass 2) captured in a HIP graph and replayed
-    `reps` times back to back: the per-step time without host launch cost."""
+    """One step (forward, pass 1, pass 2) captured in a HIP graph and, after
+    a settling run of replays, replayed `reps` times back to back: the
+    per-step time without host launch cost."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -102,9 +103,11 @@ def graph_step_us(dyt, torch, x, dy, a, g, b, y, dx, ws, da, dg, db, M, N, xdt, 
         dyt.dyt_forward(x, a, g, b, y=y)
         dyt.dyt_backward_partials(x, dy, a, g, dx, ws)
         dyt.dyt_backward_finish(ws, M, N, xdt, da, dg, db)
-    for _ in range(5):
-        graph.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:   # settle the clocks on replays
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -1155,9 +1158,10 @@ def report_placement(dyt, torch, path: str, name: str, variants=(), reps: int = 
 
 def graph_vs_eager(dyt, torch, name: str, steps: int = 50) -> dict:
     """The same step (forward, pass 1, pass 2) run eagerly and as a captured
-    HIP graph, each for `steps` back-to-back steps after a settling run,
-    with a 50 ms idle gap between the two phases (so that a kernel trace of
-    this run splits into them). Returns us per step for each."""
+    HIP graph: each phase a settling run of its own kind (0.3 s) followed at
+    once by `steps` timed back-to-back steps, with a 50 ms idle gap between
+    the two phases (so that a kernel trace of this run splits into them).
+    Returns us per step for each."""
     import workloads
     inp = workloads.generate(name)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -1199,12 +1203,16 @@ def graph_vs_eager(dyt, torch, name: str, steps: int = 50) -> dict:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         out = {}
         for phase in ("eager", "graph"):
+            run = step if phase == "eager" else graph.replay
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < SETTLE_S:
+                for _ in range(20):
+                    run()
+                s.synchronize()
+            run()
             e0.record(s)
             for _ in range(steps):
-                if phase == "eager":
-                    step()
-                else:
-                    graph.replay()
+                run()
             e1.record(s)
             e1.synchronize()
             out[phase] = e0.elapsed_time(e1) * 1e3 / steps
@@ -1212,11 +1220,12 @@ def graph_vs_eager(dyt, torch, name: str, steps: int = 50) -> dict:
     return out
 
 
-def graph_trace_summary(d: str) -> str:
+def graph_trace_summary(d: str, steps: int = 50) -> str:
     """From a rocprofv3 kernel trace of `bench.py --graph-vs-eager W`: the
-    dispatches of the two timed phases (the last two runs of back-to-back
-    DyT kernels separated by an idle gap), with each kernel family's mean
-    duration and the mean gap from one kernel's end to the next one's
+    dispatches of the two timed phases (the last `steps` steps of the last
+    two runs of DyT kernels separated by an idle gap; each run is a
+    settling run followed by the timed steps), with each kernel family's
+    mean duration and the mean gap from one kernel's end to the next one's
     start, per phase."""
     import csv
     import glob
@@ -1238,6 +1247,7 @@ def graph_trace_summary(d: str) -> str:
     lines = ["| phase | dispatches | " + " | ".join(f"{f} us" for f, _ in KERNEL_FAMILIES if f != "dyt_fwd_flat_kernel")
              + " | forward (flat) us | mean gap us | us per step |", "|---|---:|" + "---:|" * 6]
     for phase, run in zip(("eager", "graph"), runs[-2:]):
+        run = run[-3 * steps:]                   # the timed steps: three kernels each
         dur = {}
         for st, en, fam in run:
             dur.setdefault(fam, []).append((en - st) / 1e3)
