@@ -738,7 +738,7 @@ def _timeline_stats(st, tick_us: float) -> dict:
 
 
 def report_wg_timeline(torch, path: str, reps: int = 30,
-                       names=(HEADLINE, SECONDARY), side_streams: int = 0) -> None:
+                       names=(HEADLINE, SECONDARY), side_streams: int = 0, raw_dir: str | None = None) -> None:
     """Per-workgroup timeline of the forward and backward pass 1 in steady
     back-to-back steps (forward, pass 1, pass 2), from the timeline build of
     the library: when each workgroup starts, ends its streaming loop and
@@ -825,6 +825,9 @@ def report_wg_timeline(torch, path: str, reps: int = 30,
         e1.synchronize()
         rec_us = e0.elapsed_time(e1) * 1e3 / reps
         fa, pa = fst.cpu().numpy(), pst.cpu().numpy()
+        if raw_dir:
+            os.makedirs(raw_dir, exist_ok=True)
+            np.savez_compressed(os.path.join(raw_dir, f"{name}.npz"), forward=fa, pass1=pa)
         del x, dy, y, dx, ws, fst, pst
         torch.cuda.empty_cache()
         rows += [f"## {name} ({M} x {N})", "",
@@ -895,6 +898,11 @@ VARIANTS = {
     # backward pass 1 weighted too
     "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
     "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],
+    # the tiled forward's first half of a grid of two workgroups per CU
+    # (dispatched first) takes this share of the groups
+    "round0_52": ["-DDYT_ROUND0_SHARE_Q=532"],
+    "round0_535": ["-DDYT_ROUND0_SHARE_Q=548"],
+    "round0_55": ["-DDYT_ROUND0_SHARE_Q=563"],
     # the forward's write-back stores: ordinary stores for float32 x too
     # (default: sc1, device-scope write-through buffer stores), or sc1 for
     # 2-byte x too (default: ordinary)
@@ -1452,6 +1460,9 @@ def main() -> int:
                          "(timeline build of the library) and write a Markdown summary to FILE")
     ap.add_argument("--timeline-workloads", default=f"{HEADLINE},{SECONDARY}",
                     help="with --wg-timeline: comma-separated workload names")
+    ap.add_argument("--timeline-raw", metavar="DIR", default=None,
+                    help="with --wg-timeline: also save every recorded launch's per-workgroup words "
+                         "(entry, loop end, exit, XCC_ID << 32 | HW_ID) as DIR/<workload>.npz")
     ap.add_argument("--timeline-side-streams", type=int, default=0,
                     help="with --wg-timeline: first capture and replay this many steps in HIP graphs "
                          "on new streams")
@@ -1512,7 +1523,7 @@ def main() -> int:
         return 0
     if args.wg_timeline:
         report_wg_timeline(torch, args.wg_timeline, names=args.timeline_workloads.split(","),
-                           side_streams=args.timeline_side_streams)
+                           side_streams=args.timeline_side_streams, raw_dir=args.timeline_raw)
         log(f"[bench] workgroup timeline written to {args.wg_timeline}")
         return 0
 

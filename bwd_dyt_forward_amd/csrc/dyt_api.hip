@@ -281,6 +281,16 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_XCD_EVEN_SHARE_Q
 #define DYT_XCD_EVEN_SHARE_Q 543
 #endif
+// Share (x 1024) of those groups that the first half of a grid of two
+// workgroups per CU takes (the half dispatched first; its workgroups ended
+// their loops at 61 against 70 us for the second half at 32,768 x 4,096
+// bf16, bench.py --wg-timeline --timeline-raw); 0: both halves alike.
+// Measured at 52-55%: 0.7-0.9 us faster there, 0.3-1.7 us slower on the
+// float32 100,003-row forwards (HBM stays saturated while the second half
+// finishes), so it is off.
+#ifndef DYT_ROUND0_SHARE_Q
+#define DYT_ROUND0_SHARE_Q 0
+#endif
 // The same for the 2-byte flat walk, whose odd/even gap is about half the
 // tiles' (69.8 against 74.3 us median exits at 4,194,304 x 32): 53% over-
 // corrected it (forward 81.2 -> 82.0 us, even XCDs now last); with the XCD
@@ -463,6 +473,7 @@ Geo make_geo(const Plan& p, int64_t M, int64_t N) {
     g.even_share_q = 0;
     g.xcd_flip = 0;
     g.xcd_seen = nullptr;
+    g.round0_q = 0;
     g.buf_store = 0;
     return g;
 }
@@ -634,6 +645,28 @@ struct XcdHint {
 };
 XcdHint g_xcd_hint[kHintDevices];
 std::atomic<int> g_flip_override{-1};   // dyt_set_xcd_flip_override
+std::atomic<int> g_cus[kHintDevices];     // compute units per device: 0 unknown, -1 no answer
+
+// Compute units of the current device (0 if the runtime does not say).
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kHintDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) {
+            c = n;
+        } else {
+            (void)hipGetLastError();
+            c = -1;
+        }
+        g_cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c > 0 ? c : 0;
+}
 
 // The hint slot of stream s on the current device (host and device
 // addresses) and the device's XCD count; false when there are no slots.
@@ -783,6 +816,8 @@ int forward_impl(const FwdPtrs& a, bool res, int64_t M, int64_t N, int x_dtype, 
     if (!res && p.slots == 1 && p.vec > 1 && p.tiles >= 8 * p.grid) {
         g.even_share_q = DYT_XCD_EVEN_SHARE_Q;
         apply_xcd_hint(s, g.even_share_q, g.xcd_flip, g.xcd_seen);
+        if (g.even_share_q != 0 && DYT_ROUND0_SHARE_Q != 0 && p.grid == 2 * (int64_t)device_cus())
+            g.round0_q = DYT_ROUND0_SHARE_Q;   // two workgroups per CU
     }
     // every vector of y on the 16-byte grid: y aligned, tiles (and, for row
     // segments, rows) a whole number of vectors

@@ -128,6 +128,10 @@ struct Geo {
     // workgroup 0 ran on (a hint for the next launch's xcd_flip).
     int32_t xcd_flip;
     int32_t* xcd_seen;
+    // Forward only, with even_share_q: the share (x 1024) of each column
+    // block's groups that the first G / 2 workgroups take (make_walk); 0:
+    // no split by dispatch round.
+    int32_t round0_q;
     // Forward only: 1 when every 16-byte vector of y lies on the 16-byte grid
     // (y aligned, rows a whole number of vectors), so its write-back stores
     // may go through store_with_policy.
@@ -453,18 +457,27 @@ __host__ __device__ __forceinline__ int64_t even_groups(int64_t ng, int share_q)
 // each round-robin among its members. Every group is covered once whatever
 // flip is, as long as it is the same for the whole launch (a kernel
 // argument). Needs G a multiple of 2 nb, else (and with share_q = 0) every
-// group is dealt round-robin to all of the block's workgroups. The forward
-// has no reduction: the deal changes which workgroup computes an element,
-// never its bits.
+// group is dealt round-robin to all of the block's workgroups.
+// With round_q as well (G a multiple of 4 nb), the grid is first cut into
+// its halves, the workgroups dispatched in the first and in the second
+// round onto CUs that host two: each block's first round_q / 1024 of the
+// groups go to the first half, the rest to the second, and within each half
+// the two XCD classes split that half's range as above. The forward has no
+// reduction: the deal changes which workgroup computes an element, never
+// its bits.
 template <int U>
 __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t wg, int64_t G,
-                                              int share_q, int flip) {
+                                              int share_q, int flip, int round_q) {
     TileWalk w;
     const int64_t nb = packed ? 1 : g.nb;
     const bool weighted = share_q != 0 && G % (2 * nb) == 0;
-    const int64_t pair = wg >> 1, odd = wg & 1;
+    const bool rounds = weighted && round_q != 0 && G % (4 * nb) == 0;
+    const int64_t H = rounds ? G / 2 : G;                 // workgroups per half
+    const int64_t half = (rounds && wg >= H) ? 1 : 0;
+    const int64_t wl = wg - half * H;                     // index within the half
+    const int64_t pair = wl >> 1, odd = wl & 1;
     const int64_t b = weighted ? pair % nb : wg % nb;
-    w.gw = weighted ? 2 * (pair / nb) + odd : wg / nb;
+    w.gw = weighted ? 2 * (pair / nb) + odd + half * (H / nb) : wg / nb;
     w.gcount = G / nb;
     if (packed) {
         w.units = g.total / g.T;
@@ -481,11 +494,13 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, bool packed, int64_t
     }
     const int64_t ng = w.units / U;
     if (weighted) {
-        const int64_t ne = even_groups(ng, share_q);
+        const int64_t n0 = rounds ? even_groups(ng, round_q) : ng;   // the first half's groups
+        const int64_t lo = half ? n0 : 0, nr = half ? ng - n0 : n0;
+        const int64_t ne = even_groups(nr, share_q);
         const int64_t cls = odd ^ (int64_t)(flip & 1);   // 1: the class expected on odd XCDs
-        w.g_first = (cls ? ne : 0) + pair / nb;
-        w.g_stride = w.gcount / 2;
-        w.g_end = cls ? ng : ne;
+        w.g_first = lo + (cls ? ne : 0) + pair / nb;
+        w.g_stride = H / nb / 2;
+        w.g_end = lo + (cls ? nr : ne);
     } else {
         w.g_first = w.gw;
         w.g_stride = w.gcount;
@@ -686,7 +701,7 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     const int64_t wg = blockIdx.x;
     const int64_t G = gridDim.x;
     const float alpha = to_f32(alpha_p[0]);
-    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip);
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip, g.round0_q);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ai = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ao = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ai;
@@ -1229,7 +1244,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
     const float alpha = to_f32(alpha_p[0]);
     // the deal (round-robin, or XCD-weighted with g.even_share_q) depends
     // on the shape only, so do the rows summed into each partial row
-    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip);
+    const TileWalk w = make_walk<U>(g, PACKED, wg, G, g.even_share_q, g.xcd_flip, 0);
     const Slots<V, K> sl = make_slots<V, K, RAG>(tid, w.seg_len);
     const Addr<K, STRIDED> ax = make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[0]);
     const Addr<K, STRIDED> ad = STRIDED ? make_addr<V, K, PACKED, STRIDED>(sl, w, g, g.pitch[1]) : ax;

@@ -28,18 +28,29 @@ def even_groups(ng, q):
     return (ng * q + 512) >> 10
 
 
-def tiled_deal(G, nb, ng, q, flip=0):
-    """{(block, group): workgroup} of the main loop."""
+def tiled_deal(G, nb, ng, q, flip=0, rq=0):
+    """{(block, group): workgroup} of the main loop. With rq (G a multiple
+    of 4 nb) the first G/2 workgroups take groups [0, round(ng rq / 1024))
+    and the second half the rest, each half split by the XCD classes as
+    above with index i among the half's pairs."""
     weighted = q != 0 and G % (2 * nb) == 0
+    rounds = weighted and rq != 0 and G % (4 * nb) == 0
+    H = G // 2 if rounds else G
     out = {}
     for w in range(G):
-        pair, odd = w >> 1, w & 1
+        half = 1 if rounds and w >= H else 0
+        wl = w - half * H
+        pair, odd = wl >> 1, wl & 1
         cls = odd ^ flip
         b = pair % nb if weighted else w % nb
         gcount = G // nb
         if weighted:
-            ne = even_groups(ng, q)
-            first, stride, end = (ne if cls else 0) + pair // nb, gcount // 2, ng if cls else ne
+            n0 = even_groups(ng, rq) if rounds else ng
+            lo, nr = (n0, ng - n0) if half else (0, n0)
+            ne = even_groups(nr, q)
+            first = lo + (ne if cls else 0) + pair // nb
+            stride = H // nb // 2
+            end = lo + (nr if cls else ne)
         else:
             first, stride, end = w // nb, gcount, ng
         for gi in range(first, end, stride):
@@ -75,15 +86,18 @@ def flat_deal(G, ngroups, partial, q, flip=0):
 @settings(max_examples=400, deadline=None)
 @given(st.sampled_from([2, 4, 8, 64, 128, 256, 512, 1024, 6, 254, 510]),
        st.sampled_from([1, 2, 3, 4]), st.integers(0, 5000), st.sampled_from([0, 512, 543, 560, 600]),
-       st.sampled_from([0, 1]))
-def test_tiled_deal_covers_every_group_once(G, nb, ng, q, flip):
+       st.sampled_from([0, 1]), st.sampled_from([0, 532, 548, 600]))
+def test_tiled_deal_covers_every_group_once(G, nb, ng, q, flip, rq):
     if G % nb:
         return
-    d = tiled_deal(G, nb, ng, q, flip)
+    d = tiled_deal(G, nb, ng, q, flip, rq)
     assert set(d) == {(b, gi) for b in range(nb) for gi in range(ng)}
-    if q and G % (2 * nb) == 0 and ng >= 4 * G:
+    if q and not rq and G % (2 * nb) == 0 and ng >= 4 * G:
         favoured = sum(1 for w in d.values() if w % 2 == flip)
         assert abs(favoured - nb * even_groups(ng, q)) == 0
+    if q and rq and G % (4 * nb) == 0 and ng >= 4 * G:
+        first = sum(1 for w in d.values() if w < G // 2)
+        assert first == nb * even_groups(ng, rq)
 
 
 @settings(max_examples=400, deadline=None)
