@@ -898,6 +898,9 @@ VARIANTS = {
     # backward pass 1 weighted too
     "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
     "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],
+    # the persistent loops' earlier last load, which re-read the previous
+    # group when a workgroup has an even number of groups
+    "tail_prefetch": ["-DDYT_TAIL_PREFETCH=1"],
     # the tiled forward's first half of a grid of two workgroups per CU
     # (dispatched first) takes this share of the groups
     "round0_52": ["-DDYT_ROUND0_SHARE_Q=532"],

@@ -175,6 +175,13 @@ typedef float f32x4_m __attribute__((ext_vector_type(4), aligned(4)));
 #ifndef DYT_FWD_NT
 #define DYT_FWD_NT 1
 #endif
+// The persistent loops load group i + 1 while computing group i, two
+// register buffers in turn. With an even number of groups the last pair is
+// done without a second load; 1 restores the earlier form, whose last load
+// re-read the previous group (valid memory, never computed).
+#ifndef DYT_TAIL_PREFETCH
+#define DYT_TAIL_PREFETCH 0
+#endif
 #ifndef DYT_BWD_NT
 #define DYT_BWD_NT 1
 #endif
@@ -731,8 +738,8 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
     // alternating between two register buffers (A and B): the loads of one
     // group are in flight while the other group is computed. Each step's
     // loads are pinned above the compute that follows them by a scheduling
-    // barrier. A last A load past this workgroup's groups re-reads the
-    // previous group (valid memory, never computed).
+    // barrier. With an even number of groups the last pair is done without
+    // a further load (DYT_TAIL_PREFETCH).
     const int64_t ng = w.units / U;
     const int64_t iters = w.g_first < w.g_end ? (w.g_end - w.g_first + w.g_stride - 1) / w.g_stride : 0;
     const int64_t ustep = w.g_stride * U;        // units between this workgroup's groups
@@ -743,7 +750,8 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         int64_t boa = STRIDED ? w.col_base + w.g_first * U * ao.upitch : bia;
         fwd_load<XT, V, K, U, RES>(x, r, bia, ai, xa, ra);
         const int64_t npairs = iters / 2;
-        for (int64_t pi = 0; pi < npairs; ++pi) {
+        const int64_t nfull = (DYT_TAIL_PREFETCH || (iters & 1)) ? npairs : npairs - 1;
+        for (int64_t pi = 0; pi < nfull; ++pi) {
             const int64_t bib = bia + gsi, bob = STRIDED ? boa + gso : bib;
             fwd_load<XT, V, K, U, RES>(x, r, bib, ai, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
@@ -758,6 +766,14 @@ dyt_fwd_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             __builtin_amdgcn_sched_barrier(0);
             bia = bin;
             boa = bon;
+        }
+        if (!DYT_TAIL_PREFETCH && !(iters & 1)) {   // the last pair (iters >= 2)
+            const int64_t bib = bia + gsi, bob = STRIDED ? boa + gso : bib;
+            fwd_load<XT, V, K, U, RES>(x, r, bib, ai, xb, rb);
+            __builtin_amdgcn_sched_barrier(0);
+            fwd_tile<XT, V, K, U, ACC, RES, BUF>(xa, ra, y, h, boa, ao, gm, bt, alpha, span);
+            __builtin_amdgcn_sched_barrier(0);
+            fwd_tile<XT, V, K, U, ACC, RES, BUF>(xb, rb, y, h, bob, ao, gm, bt, alpha, span);
         }
         if (iters & 1) fwd_tile<XT, V, K, U, ACC, RES, BUF>(xa, ra, y, h, boa, ao, gm, bt, alpha, span);
     }
@@ -1022,9 +1038,9 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
 #pragma unroll
     for (int j = 0; j < U; ++j) col[j] = (int)(((g_first * B + j * kBlock + tid) * V + hd) % N);
 
-    // Same two-buffer loop as dyt_fwd_kernel; a last A load past this
-    // workgroup's groups re-reads the previous group. f.cstep advances the
-    // columns by g_stride groups.
+    // Same two-buffer loop as dyt_fwd_kernel (no load past this workgroup's
+    // groups, see DYT_TAIL_PREFETCH). f.cstep advances the columns by
+    // g_stride groups.
     const int64_t gstep = g_stride * B;
     if (iters > 0) {
         typename R::T xa[U], xb[U], ra[U], rb[U];
@@ -1032,7 +1048,8 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
         int64_t qa = qa0 + tid;
         flat_load<XT, U, RES>(x, r, qa, xa, ra);
         const int64_t npairs = iters / 2;
-        for (int64_t pi = 0; pi < npairs; ++pi) {
+        const int64_t nfull = (DYT_TAIL_PREFETCH || (iters & 1)) ? npairs : npairs - 1;
+        for (int64_t pi = 0; pi < nfull; ++pi) {
             const int64_t qb0 = qa0 + gstep, qb = qa + gstep;
             flat_load<XT, U, RES>(x, r, qb, xb, rb);
             __builtin_amdgcn_sched_barrier(0);
@@ -1048,6 +1065,16 @@ dyt_fwd_flat_kernel(const XT* __restrict__ x, const XT* __restrict__ r,
             __builtin_amdgcn_sched_barrier(0);
             qa0 = qn0;
             qa = qn;
+        }
+        if (!DYT_TAIL_PREFETCH && !(iters & 1)) {   // the last pair (iters >= 2)
+            const int64_t qb0 = qa0 + gstep, qb = qa + gstep;
+            flat_load<XT, U, RES>(x, r, qb, xb, rb);
+            __builtin_amdgcn_sched_barrier(0);
+            flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, qa0, col, sg, sb, alpha, N, f.cstep, L,
+                                             f.buf_store != 0);
+            __builtin_amdgcn_sched_barrier(0);
+            flat_group<XT, U, ACC, RES, RAG>(xb, rb, y, h, qb, qb0, col, sg, sb, alpha, N, f.cstep, L,
+                                             f.buf_store != 0);
         }
         if (iters & 1)
             flat_group<XT, U, ACC, RES, RAG>(xa, ra, y, h, qa, qa0, col, sg, sb, alpha, N, f.cstep, L,
@@ -1281,7 +1308,8 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
         int64_t bda = STRIDED ? cb + u0 * ad.upitch : bxa, boa = STRIDED ? cb + u0 * ao.upitch : bxa;
         bwd_load<XT, V, K, U, RES>(x, dy, dres, bxa, ax, bda, ad, xa, da, ra);
         const int64_t npairs = iters / 2;
-        for (int64_t pi = 0; pi < npairs; ++pi) {
+        const int64_t nfull = (DYT_TAIL_PREFETCH || (iters & 1)) ? npairs : npairs - 1;
+        for (int64_t pi = 0; pi < nfull; ++pi) {
             const int64_t bxb = bxa + gsx;
             const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
@@ -1299,6 +1327,15 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             bxa = bxn;
             bda = bdn;
             boa = bon;
+        }
+        if (!DYT_TAIL_PREFETCH && !(iters & 1)) {   // the last pair (iters >= 2)
+            const int64_t bxb = bxa + gsx;
+            const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
+            bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
+            __builtin_amdgcn_sched_barrier(0);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
+            __builtin_amdgcn_sched_barrier(0);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa);
         }
         if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
     }
