@@ -395,6 +395,57 @@ def stream_ceilings(torch, nbytes: int, reps: int = 40, rounds: int = 3) -> dict
             "tensor_bytes": nbytes}
 
 
+def residual_stream_ceilings(torch, nbytes: int, reps: int = 20, rounds: int = 3) -> dict:
+    """The streams of the residual-fused layer on tensors of nbytes each
+    (libdyt_streamref.so): two inputs and two outputs (the fused forward's
+    traffic) and three inputs and one output (the fused pass 1's), each with
+    nontemporal and with write-back stores; GB/s of the faster store kind,
+    counting every byte read and written; medians of `rounds` samples of
+    `reps` back-to-back launches after a settling run."""
+    import ctypes
+    sys.path.insert(0, os.path.join(ROOT, "bwd_dyt_forward_amd"))
+    import build as dyt_build
+    lib = ctypes.CDLL(dyt_build.STREAM_REF_PATH, mode=ctypes.RTLD_LOCAL)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.stream_ref_2in2out.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+    lib.stream_ref_3in1out.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+    nbytes -= nbytes % 16
+    t = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    o = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s = torch.cuda.current_stream().cuda_stream
+    p = [x.data_ptr() for x in t] + [x.data_ptr() for x in o]
+    ops = {}
+    for nt in (0, 1):
+        ops[("2in2out", nt)] = (lambda nt=nt: lib.stream_ref_2in2out(p[0], p[1], p[3], p[4], nbytes, nt, s), 4)
+        ops[("3in1out", nt)] = (lambda nt=nt: lib.stream_ref_3in1out(p[0], p[1], p[2], p[3], nbytes, nt, s), 4)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for f, _ in ops.values():
+            if f() != 0:
+                raise RuntimeError("a residual reference stream rejected its arguments")
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    us = {k: [] for k in ops}
+    for _ in range(rounds):
+        for k, (f, _) in ops.items():
+            f()
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            e1.synchronize()
+            us[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+    del t, o
+    torch.cuda.empty_cache()
+    out = {"tensor_bytes": nbytes}
+    for kind in ("2in2out", "3in1out"):
+        best = min((statistics.median(us[(kind, nt)]), nt) for nt in (0, 1))
+        out[f"{kind}_GBps"] = round(4 * nbytes / (best[0] * 1e-6) / 1e9, 1)
+        out[f"{kind}_stores"] = "nontemporal" if best[1] else "write-back"
+    return out
+
+
 def copy_calibration(torch, mib: int) -> None:
     """A plain elementwise kernel of known size (reads and writes mib MiB each)
     so that HBM byte counters can be scaled; used only by counter runs."""
@@ -898,6 +949,8 @@ VARIANTS = {
     # backward pass 1 weighted too
     "xcd_even_share_bwd_51": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=522"],
     "xcd_even_share_bwd_53": ["-DDYT_XCD_EVEN_SHARE_BWD_Q=543"],
+    # nontemporal instead of write-back stores of the residual-fused pass 1's dh
+    "bwd_res_nt": ["-DDYT_BWD_RES_NT=1"],
     # the persistent loops' earlier last load, which re-read the previous
     # group when a workgroup has an even number of groups
     "tail_prefetch": ["-DDYT_TAIL_PREFETCH=1"],
@@ -1034,8 +1087,98 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
         log(f"[bench] variants {name}: " + ", ".join(f"{v} {med[(v, 'step')]:.2f}" for v in libs))
         del x, dy, bufs
         torch.cuda.empty_cache()
+    rows += residual_variant_rows(torch, libs, rounds)
     with open(path, "w") as f:
         f.write("\n".join(rows) + "\n")
+
+
+def residual_variant_rows(torch, libs, rounds: int) -> list:
+    """The residual-fused layer (h = x + r, y = DyT(h); dh = dres + dx) of
+    every library on the headline shape: forward alone, backward (both
+    passes) alone and the step (forward then backward), interleaved as in
+    report_variants; outputs compared bit for bit with the default build's."""
+    import workloads
+    from bwd_dyt_forward_amd import _lib
+    inp = workloads.generate(HEADLINE)
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    xdt, pdt = tdt[inp.x_dtype], tdt[inp.p_dtype]
+    M, N = inp.M, inp.N
+    x = torch.from_numpy(inp.x).to(dev).to(xdt)
+    dy = torch.from_numpy(inp.dy).to(dev).to(xdt)
+    a = torch.from_numpy(inp.alpha).to(dev).to(pdt)
+    g = torch.from_numpy(inp.gamma).to(dev).to(pdt)
+    b = torch.from_numpy(inp.beta).to(dev).to(pdt)
+    del inp
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    r = torch.randn(M, N, generator=gen, device="cuda").to(xdt)
+    dres = torch.randn(M, N, generator=gen, device="cuda").to(xdt)
+    xc, pc = _lib._code(xdt), _lib._code(pdt)
+    sp = torch.cuda.current_stream().cuda_stream
+    bufs = {}
+    for v, L in libs.items():
+        need = L.dyt_backward_workspace_size(M, N, xc, pc)
+        bufs[v] = {"ws": torch.zeros(max(need, 16), dtype=torch.uint8, device=dev),
+                   "h": torch.empty_like(x), "y": torch.empty_like(x), "dh": torch.empty_like(x),
+                   "da": torch.empty(1, dtype=pdt, device=dev), "dg": torch.empty(N, dtype=pdt, device=dev),
+                   "db": torch.empty(N, dtype=pdt, device=dev)}
+
+    def fwd(v):
+        B = bufs[v]
+        if libs[v].dyt_forward_residual(x.data_ptr(), r.data_ptr(), a.data_ptr(), g.data_ptr(), b.data_ptr(),
+                                        B["h"].data_ptr(), B["y"].data_ptr(), M, N, xc, pc, sp) != 0:
+            raise RuntimeError(f"variant {v}: dyt_forward_residual failed")
+
+    def bwd(v):
+        B = bufs[v]
+        if libs[v].dyt_backward_residual(B["h"].data_ptr(), dy.data_ptr(), dres.data_ptr(), a.data_ptr(),
+                                         g.data_ptr(), B["dh"].data_ptr(), B["da"].data_ptr(),
+                                         B["dg"].data_ptr(), B["db"].data_ptr(), B["ws"].data_ptr(),
+                                         B["ws"].numel(), M, N, xc, pc, sp) != 0:
+            raise RuntimeError(f"variant {v}: dyt_backward_residual failed")
+
+    def step(v):
+        fwd(v)
+        bwd(v)
+
+    same = {}
+    for v in libs:
+        step(v)
+        torch.cuda.synchronize()
+        same[v] = all(torch.equal(bufs[v][k].view(torch.uint8), bufs["default"][k].view(torch.uint8))
+                      for k in ("h", "y", "dh", "da", "dg", "db"))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for v in libs:
+            step(v)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kinds = {"fwd": fwd, "bwd": bwd, "step": step}
+    us = {(v, k): [] for v in libs for k in kinds}
+    order = list(libs)
+    for rr in range(rounds):
+        for kname, fn in kinds.items():
+            for j in range(len(order)):
+                v = order[(rr + j) % len(order)]
+                fn(v)
+                e0.record()
+                for _ in range(10):
+                    fn(v)
+                e1.record()
+                e1.synchronize()
+                us[(v, kname)].append(e0.elapsed_time(e1) * 1e3 / 10)
+    med = {key: statistics.median(val) for key, val in us.items()}
+    rows = ["", f"Residual-fused layer on {HEADLINE} (r and dres ~ N(0, 1), seed 1): forward, backward "
+            "(both passes) and step (forward then backward) alone, us per call, medians as above.", "",
+            "| library | forward us | backward us | step us | step vs default | bits |",
+            "|---|---:|---:|---:|---:|---|"]
+    for v in libs:
+        rows.append(f"| {v} | {med[(v, 'fwd')]:.2f} | {med[(v, 'bwd')]:.2f} | {med[(v, 'step')]:.2f} | "
+                    f"{med[(v, 'step')] / med[('default', 'step')]:.3f} | {'equal' if same[v] else 'differ'} |")
+    del x, dy, r, dres, bufs
+    torch.cuda.empty_cache()
+    return rows
 
 
 def report_placement(dyt, torch, path: str, name: str, variants=(), reps: int = 50) -> None:
@@ -1539,6 +1682,11 @@ def main() -> int:
     resid = None
     if not args.no_residual:
         resid = measure_residual(dyt, torch, args.workload)
+        rsc = residual_stream_ceilings(torch, main_res["M"] * main_res["N"] *
+                                       (2 if main_res["x_dtype"] in ("bf16", "f16") else 4))
+        resid["stream_ceiling"] = rsc
+        resid["fwd"]["frac_of_2in2out"] = round(resid["fwd"]["fused_GBps"] / rsc["2in2out_GBps"], 4)
+        resid["bwd"]["frac_of_3in1out"] = round(resid["bwd"]["fused_GBps"] / rsc["3in1out_GBps"], 4)
         log(f"[bench] residual: {json.dumps(resid)}")
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)

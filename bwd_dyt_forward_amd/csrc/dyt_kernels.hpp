@@ -185,6 +185,16 @@ typedef float f32x4_m __attribute__((ext_vector_type(4), aligned(4)));
 #ifndef DYT_BWD_NT
 #define DYT_BWD_NT 1
 #endif
+// Store kind of the residual-fused pass 1's dh (1: nontemporal, as the plain
+// pass 1's dx; 0: write-back). Its three input streams and one output
+// stream run faster with write-back stores on MI355X: at 32,768 x 4,096
+// bf16 the residual backward took 172.9 against 184.3 us, and a residual
+// step (forward then backward) 357.1 against 368.8 us (bench.py --variants
+// bwd_res_nt reproduces the nontemporal form); a reference stream of three
+// inputs and one output measured fastest with write-back stores too.
+#ifndef DYT_BWD_RES_NT
+#define DYT_BWD_RES_NT 0
+#endif
 template <bool NT, typename T>
 __device__ __forceinline__ T stream_load(const T* p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -1246,7 +1256,8 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
 #pragma unroll
                 for (int e = 0; e < V; ++e) out[e] += rv[e];
             }
-            Raw<XT, V>::template store<DYT_BWD_NT>(dx + bo + j * ao.upitch + ao.off[k], out);
+            Raw<XT, V>::template store<(RES ? DYT_BWD_RES_NT : DYT_BWD_NT) != 0>(
+                dx + bo + j * ao.upitch + ao.off[k], out);
         }
 }
 

@@ -52,6 +52,12 @@ def test_stream_reference_library_exports_and_rejects_bad_arguments():
     assert lib.stream_ref_copy(a, a + 0x1000, 63, None) == 1          # not a multiple of 16
     assert lib.stream_ref_copy(a + 4, a + 0x1000, 64, None) == 1      # misaligned
     assert lib.stream_ref_2in1out(a, None, a + 0x1000, 64, None) == 1
+    lib.stream_ref_2in2out.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.stream_ref_3in1out.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    assert lib.stream_ref_2in2out(a, a + 0x1000, a + 0x2000, None, 64, 1, None) == 1
+    assert lib.stream_ref_2in2out(a, a + 0x1000, a + 0x2000, a + 0x3004, 64, 0, None) == 1
+    assert lib.stream_ref_3in1out(a, a + 0x1000, None, a + 0x2000, 64, 1, None) == 1
+    assert lib.stream_ref_3in1out(a, a + 0x1000, a + 0x2000, a + 0x3000, 48 + 1, 0, None) == 1
 
 
 def test_width_case_filter():
