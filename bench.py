@@ -971,7 +971,12 @@ VARIANTS = {
 
 
 def variant_library(name: str):
-    import ctypes
+    """The library of a variant name: a VARIANTS entry (built from the
+    current sources with its flags when stale), or lib:PATH, a prebuilt
+    library of the same ABI from any sources (e.g. an earlier commit's)."""
+    if name.startswith("lib:"):
+        from bwd_dyt_forward_amd import _lib
+        return _lib._load(name[4:], any_sources=True)
     flags = VARIANTS[name]
     b = _build_module()
     path = os.path.join(ROOT, "bwd_dyt_forward_amd", f"libdyt_variant_{name}.so")
@@ -979,12 +984,7 @@ def variant_library(name: str):
         log(f"[bench] building library variant {name} ({' '.join(flags)})")
         b.build(out=path, extra_flags=flags, with_stream_ref=False, cache=True)
     from bwd_dyt_forward_amd import _lib
-    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
-    for fn_name, (res, argtypes) in _lib.SIGNATURES.items():
-        fn = getattr(lib, fn_name)
-        fn.restype = res
-        fn.argtypes = argtypes
-    return lib
+    return _lib._load(path, flags)
 
 
 def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
@@ -1002,8 +1002,11 @@ def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
     rows = ["# Library variants against the default build", "",
             f"Command: `python bench.py --variants {','.join(names)} --variants-report {path}`. "
             f"Device: {torch.cuda.get_device_name(0)}.", "",
-            "Variants (compile-time options of the same sources): " +
-            "; ".join(f"`{n}`: {' '.join(VARIANTS[n])}" for n in names) + ".", "",
+            "Variants (compile-time options of the same sources, or lib:PATH, a prebuilt library "
+            "from other sources): " +
+            "; ".join(f"`{n}`: " + (f"build id {libs[n].dyt_build_id().decode()}" if n.startswith("lib:")
+                                   else ' '.join(VARIANTS[n])) for n in names) +
+            f"; default: build id {dyt.lib.dyt_build_id().decode()}.", "",
             f"us per call: forward alone, backward (pass 1 + pass 2) alone and the step (forward then "
             f"backward), each a run of back-to-back calls between two HIP events; median of {rounds} "
             "rounds in which every library's run of each kind is interleaved. 'bits' compares y, dx, "
@@ -1621,8 +1624,9 @@ def main() -> int:
     ap.add_argument("--graph-trace", metavar="DIR", default=None,
                     help="only summarise a kernel trace of --graph-vs-eager found under DIR (no GPU)")
     ap.add_argument("--variants", default=None,
-                    help="only time these library variants (comma-separated names of VARIANTS) "
-                         "against the default build on every workload")
+                    help="only time these library variants (comma-separated names of VARIANTS, "
+                         "or lib:PATH for a prebuilt library from other sources) against the "
+                         "default build on every workload")
     ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
     ap.add_argument("--placement", metavar="FILE", default=None,
                     help="only time the --workload's forward and pass 1 on tensors allocated at "

@@ -80,7 +80,11 @@ SIGNATURES = {
 }
 
 
-def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+def _load(path: str = LIB_PATH, extra_flags=(), any_sources: bool = False) -> ctypes.CDLL:
+    """Load the library at path, built from the current sources with the
+    extra compiler flags extra_flags (a variant build), or raise; with
+    any_sources, a library of this ABI built from any sources (another
+    build to measure against)."""
     if not os.path.exists(path):
         raise ImportError(
             f"DyT HIP library not found at {path}; build it first "
@@ -94,8 +98,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if found != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {found}, this binding expects {ABI_VERSION}; "
                           "rebuild the library")
-    built, want = lib.dyt_build_id().decode(), source_hash()
-    if built != want:
+    built, want = lib.dyt_build_id().decode(), source_hash(tuple(extra_flags))
+    if built != want and not any_sources:
         raise ImportError(f"{path} was built from other sources (build id {built}, sources "
                           f"{want}); rebuild it (python bwd_dyt_forward_amd/build.py)")
     return lib

@@ -233,6 +233,9 @@ double occupancy(const Plan& p, int64_t N) {
 // 181.6 / 179.7 against 180.9 / 180.6 us) and faster everywhere else (bf16
 // 1,536 / 2,560 / 3,072 / 4,104: 181-182 us against 191-227 us; f32 2,560 /
 // 4,104 / 5,120: 370-380 us against 402-512 us).
+// The fill is that of the tiles the tile table sizes for the shape: where
+// it gives float32 row segments of one slot (1,024 columns), rows such as
+// 5,120 or 3,001 wide fill them and keep the tiles.
 // The forward has no reduction, so the choice changes no result bit.
 #ifndef DYT_FLAT_OCC_2B
 #define DYT_FLAT_OCC_2B 0.85
@@ -396,6 +399,11 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         }
         if (best_occ >= occ + DYT_OCC_GAIN) p = best;
     }
+    // The forward's XCD-weighted deal pairs neighbouring workgroups of one
+    // column block (make_walk): row segments keep an even number of
+    // workgroups per block (1,020 rather than 1,023 for three blocks).
+    if (dir == Dir::Fwd && !p.packed && p.nb > 1 && (p.grid / p.nb) % 2 == 1 && p.grid / p.nb > 1)
+        p.grid -= p.nb;
     const double fill = occupancy(p, N);
     const bool k2 = sx == 2 && p.packed && p.slots >= 2;
     const bool poor_fit =

@@ -12,6 +12,10 @@ rows" autotunes BLOCK_M / BLOCK_N at run time instead).
     python bwd_dyt_forward_amd/tune.py build DIR       # CPU: one library per candidate
     python bwd_dyt_forward_amd/tune.py measure DIR OUT # GPU: time every candidate
     python bwd_dyt_forward_amd/tune.py emit OUT        # write csrc/dyt_tune_table.inc
+
+The measurement record the current table was emitted from is
+bwd_dyt_forward_amd/tune_results.json (per shape and candidate, the median
+microseconds of the forward, the backward and the residual forward).
     python bwd_dyt_forward_amd/tune.py defaults        # the table of default constants
 
 Measurement: every candidate library times the forward, the backward (both
@@ -23,11 +27,13 @@ relative; any error or disagreement aborts the run (a failing candidate is
 an error, not a loss).
 
 Each table row (dtype, row-length range, size range) has two representative
-shapes (the sizes at the range's two ends); the forward, the
-backward and the residual forward each take the candidate with the best mean
-time relative to the default over them if that mean is at least 3% better
-and neither shape gets more than 3% slower (samples of ~10 ms, five
-interleaved rounds), else the default. The residual backward shares the
+shapes (the sizes at the range's two ends), and the measured workloads that
+fall in it as further representatives. The forward, the backward and the
+residual forward each take, among the candidates whose mean time relative to
+the default over those shapes is at least 3% better and that are at most 3%
+slower at each, the one whose slowest shape (relative to the default) is the
+fastest, so that the shapes between them do well too; else the default
+(samples of ~10 ms, five interleaved rounds). The residual backward shares the
 backward's plan, so that its parameter gradients equal the plain backward's
 bit for bit.
 """
@@ -73,6 +79,9 @@ CANDIDATES = {
     "i_mt16384_k1_fg1024": (16384, 1, 1024, 256),
     "j_mt1M_k1_g512": (1 << 20, 1, 512, 512),
     "k_mt1M_k1_fg1024": (1 << 20, 1, 1024, 256),
+    # packed rows of 161-512 columns: min tiles 4,096 still gives K = 4 and
+    # 16,384 already K = 1; 8,192 reaches K = 2 (half as many rows per tile)
+    "l_mt8192_k0_g256": (8192, 0, 256, 256),
 }
 
 
@@ -96,24 +105,41 @@ def cmd_build(out_dir: str) -> None:
             print("built", name, flush=True)
 
 
+# The measured workloads (workloads/__init__.py: 1,024 x 64 float32, 65,537 x
+# 16 bfloat16, 100,003 x 17 / 100 / 255 float32; 32,768 x 4,096 and
+# 4,194,304 x 32 bfloat16 are already range ends) also represent the rows
+# they fall in: K follows M through min_tiles, so a shape inside a range can
+# get a plan that neither end measured.
+WORKLOADS = [("f32", 1024, 64), ("bf16", 65537, 16), ("f32", 100003, 17), ("f32", 100003, 100),
+             ("f32", 100003, 255)]
+
+
+def _range_of(n):
+    return next((lo, hi) for lo, hi, _ in RANGES if lo <= n <= hi)
+
+
 def _shapes():
+    """(dtype, n_lo, n_hi, size, M, N, workload) of every measured shape."""
     for d in DTYPES:
         for lo, hi, n in RANGES:
             for e in REP_SIZES:
-                yield d, lo, hi, e, max(1, e // n), n
+                yield d, lo, hi, e, max(1, e // n), n, False
+    for d, M, N in WORKLOADS:
+        lo, hi = _range_of(N)
+        yield d, lo, hi, M * N, M, N, True
 
 
 def cmd_measure(lib_dir: str, out: str, rounds: int = 5, sample_us: float = 10000.0) -> None:
     import torch
     sys.path.insert(0, os.path.dirname(PKG))
     from bwd_dyt_forward_amd import _lib
-    libs = {n: _lib._load(os.path.join(lib_dir, n + ".so")) for n in CANDIDATES}
+    libs = {n: _lib._load(os.path.join(lib_dir, n + ".so"), _flags(c)) for n, c in CANDIDATES.items()}
     td = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     s = torch.cuda.current_stream().cuda_stream
     P = lambda t: t.data_ptr()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     results = []
-    for d, lo, hi, e, M, N in _shapes():
+    for d, lo, hi, e, M, N, wl in _shapes():
         code = DTYPES[d]
         g = torch.Generator(device="cuda").manual_seed(M * 7 + N)
         x = torch.randn(M, N, device="cuda", generator=g).to(td[d])
@@ -173,7 +199,7 @@ def cmd_measure(lib_dir: str, out: str, rounds: int = 5, sample_us: float = 1000
                 e1.record()
                 e1.synchronize()
                 samples[k].append(e0.elapsed_time(e1) * 1e3 / reps)
-        res = {"dtype": d, "n_lo": lo, "n_hi": hi, "size": e, "M": M, "N": N,
+        res = {"dtype": d, "n_lo": lo, "n_hi": hi, "size": e, "M": M, "N": N, "workload": wl,
                "us": {name: {k: statistics.median(samples[(name, k)]) for k in ("fwd", "bwd", "rfwd")}
                       for name in libs}}
         results.append(res)
@@ -182,8 +208,13 @@ def cmd_measure(lib_dir: str, out: str, rounds: int = 5, sample_us: float = 1000
               f"best {best} {res['us'][best]['fwd']:.1f}/{res['us'][best]['bwd']:.1f} us", flush=True)
         del x, dy, rres, ws, outs, ops
         torch.cuda.empty_cache()
+    for r in results:    # medians to 0.001 us: the record stays small
+        r["us"] = {n: {k: round(v, 3) for k, v in t.items()} for n, t in r["us"].items()}
     with open(out, "w") as f:
-        json.dump({"candidates": CANDIDATES, "default": DEFAULT, "results": results}, f, indent=1)
+        json.dump({"device": torch.cuda.get_device_name(0), "rounds": rounds, "sample_us": sample_us,
+                   "candidates": CANDIDATES, "default": DEFAULT, "results": results}, f,
+                  separators=(",", ":"))
+        f.write("\n")
 
 
 def _dir(c, fwd: bool) -> str:
@@ -206,14 +237,15 @@ GUARD = 1.03      # ... and at most 3% slower at any representative of its range
 
 
 def _choose(reps, cands, dflt, key):
-    """The candidate with the best mean time ratio to the default over the
-    range's representatives, none of them more than 3% slower; the default
-    unless the best mean is at least 3% better."""
+    """Among the candidates at least 3% faster than the default on the mean
+    time ratio over the range's representatives and at most 3% slower at
+    each, the one whose slower representative is the fastest (the shapes
+    between a range's two ends should do well at both); else the default."""
     ratios = {n: [q["us"][n][key] / q["us"][dflt][key] for q in reps] for n in cands}
-    ok = {n: statistics.fmean(v) for n, v in ratios.items() if max(v) <= GUARD}
-    best = min(ok, key=ok.get)
-    if ok[best] > ADOPT:
-        best = dflt
+    ok = [n for n, v in ratios.items() if max(v) <= GUARD and statistics.fmean(v) <= ADOPT]
+    if not ok:
+        return dflt, ratios[dflt]
+    best = min(ok, key=lambda n: (max(ratios[n]), statistics.fmean(ratios[n])))
     return best, ratios[best]
 
 
@@ -222,8 +254,10 @@ def cmd_emit(path: str) -> None:
         data = json.load(f)
     cands = {k: tuple(v) for k, v in data["candidates"].items()}
     dflt = data["default"]
-    lines = HEADER + ["// measured with tune.py measure on one MI355X (interleaved rounds, medians); "
-                      "note = representative shapes, chosen candidate (a-k, see tune.py) and its times "
+    last = chr(ord("a") + len(cands) - 1)
+    lines = HEADER + ["// measured with tune.py measure on one MI355X (interleaved rounds, medians; "
+                      f"record: bwd_dyt_forward_amd/{os.path.basename(path)}); "
+                      f"note = representative shapes, chosen candidate (a-{last}, see tune.py) and its times "
                       "relative to the default a (forward; backward; residual forward)"]
     groups = {}
     for d in DTYPES:
@@ -231,7 +265,8 @@ def cmd_emit(path: str) -> None:
             for e_lo, e_hi, sizes in SIZES:
                 groups[(d, lo, hi, e_lo, e_hi)] = [
                     r for r in data["results"]
-                    if r["dtype"] == d and r["n_lo"] == lo and r["size"] in sizes]
+                    if r["dtype"] == d and r["n_lo"] == lo
+                    and (r["size"] in sizes if not r.get("workload") else e_lo <= r["size"] <= e_hi)]
     for (d, lo, hi, e_lo, e_hi), reps in groups.items():
         picks = [_choose(reps, cands, dflt, k) for k in ("fwd", "bwd", "rfwd")]
         note = (" ".join(f"{q['M']}x{q['N']}" for q in reps) + ": "

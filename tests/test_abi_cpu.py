@@ -110,7 +110,9 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
         assert p["bwd_grid"] % p["col_blocks"] == 0 and p["fwd_grid"] % p["col_blocks"] == 0
         # pass 1 writes whole column groups of its partial row as 16-byte stores
         assert p["tile_elems"] % 4 == 0 and p["tile_elems"] % p["vec"] == 0
-    assert 1 <= p["fwd_grid"] <= p["tiles"] and 1 <= p["bwd_grid"] <= p["tiles"]
+    # fwd_grid is the forward plan's grid, over the forward's own tiles
+    f = dyt.dyt_get_forward_plan(M, N, xdt, "f32", vec)
+    assert 1 <= p["fwd_grid"] <= f["tiles"] and 1 <= p["bwd_grid"] <= p["tiles"]
     wcols = N if p["packed"] else p["tile_elems"]
     assert p["ws_row"] >= 2 * wcols + 1 and p["ws_row"] % 4 == 0
     assert p["ws_bytes"] == p["bwd_grid"] * p["ws_row"] * 4
@@ -180,7 +182,7 @@ def _occ(p, N):
 
 # (M, N, x dtype, layout, K) of the backward and forward plans after
 # occupancy re-tiling (the GPU tests run these shapes)
-RETILED = [(301, 1500, "bf16", "packed", 3), (1100, 5120, "bf16", "segments", 3),
+RETILED = [(2800, 1500, "bf16", "packed", 3), (1100, 5120, "bf16", "segments", 3),
            (2000, 2560, "bf16", "packed", 4), (1700, 2560, "f32", "segments", 3),
            (2100, 4104, "f32", "segments", 3), (1400, 3072, "bf16", "packed", 3)]
 
@@ -199,14 +201,14 @@ def test_headline_plans_unchanged(dyt):
     b = dyt.dyt_get_plan(32768, 4096, "bf16", "f32")
     f = dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")
     assert (b["packed"], b["slots"], b["tile_elems"], b["col_blocks"], b["bwd_grid"]) == (0, 2, 4096, 1, 256)
-    assert (f["packed"], f["slots"], f["tile_elems"], f["col_blocks"], f["fwd_grid"]) == (0, 1, 2048, 2, 512)
+    assert (f["packed"], f["slots"], f["tile_elems"], f["col_blocks"], f["fwd_grid"]) == (0, 1, 2048, 2, 1024)
     b = dyt.dyt_get_plan(4194304, 32, "bf16", "f32")
     f = dyt.dyt_get_forward_plan(4194304, 32, "bf16", "f32")
     assert (b["packed"], b["slots"], b["rows_per_tile"], b["tile_elems"], b["bwd_grid"]) == (1, 2, 128, 4096, 256)
-    assert (f["packed"], f["slots"], f["rows_per_tile"], f["tile_elems"], f["fwd_grid"]) == (1, 1, 64, 2048, 512)
-    # the 4,194,304 x 32 forward walks flat (packed 2-byte tiles) from 16-byte
-    # aligned bases; its tiles stay what row-strided and unaligned launches run
-    assert f["flat"] == 1 and f["flat_grid"] == 256 and f["flat_aligned_only"] == 1
+    assert (f["packed"], f["slots"], f["rows_per_tile"], f["tile_elems"], f["fwd_grid"]) == (1, 2, 128, 4096, 256)
+    # the 4,194,304 x 32 forward walks flat (packed 2-byte tiles of two slots)
+    # from any base; its tiles are what row-strided launches run
+    assert f["flat"] == 1 and f["flat_grid"] == 256 and f["flat_aligned_only"] == 0
     assert dyt.dyt_get_forward_plan(32768, 4096, "bf16", "f32")["flat"] == 0
 
 

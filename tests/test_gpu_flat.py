@@ -40,7 +40,7 @@ SHAPES = [
     (1000, 2560, "bf16", "f32"),    # 312.5 groups; row segments 0.62 filled
     (777, 4104, "f32", "f32"),      # 778.5 groups
     (3, 1032, "bf16", "bf16"),      # less than one group; packed tiles of K = 2
-    (1, 5120, "f32", "f16"),        # 1.25 groups, one row
+    (1, 4100, "f32", "f16"),        # one row: one group and one vector
     (2, 2560, "bf16", "f32"),
     (20000, 1536, "bf16", "f32"),   # packed tiles of K = 2 at 0.75
     (1001, 4104, "bf16", "f32"),
@@ -48,8 +48,10 @@ SHAPES = [
     (4097, 1032, "f16", "f32"),
     (1234, 4100, "f32", "bf16"),
     (300, 7372, "f32", "f32"),      # 59 KB of LDS
-    (1001, 13312, "f32", "f32"),    # above 8,192 columns: 104 KB of LDS
-    (601, 17408, "f32", "bf16"),    # 136 KB of LDS
+    # float32 rows above 8,192 columns walk flat from 2^26 elements (smaller
+    # sizes fill one-slot row segments)
+    (5043, 13312, "f32", "f32"),    # above 8,192 columns: 104 KB of LDS
+    (3856, 17408, "f32", "bf16"),   # 136 KB of LDS
     (33, 8200, "bf16", "f32"),
     (5001, 32, "bf16", "f32"),      # packed tiles of one full slot (aligned bases only)
     (3001, 64, "f16", "bf16"),
@@ -64,7 +66,7 @@ SHAPES = [
     (999, 2039, "f16", "f32"),      # 4 copies of 2,048 words (64 KB of LDS)
     (301, 3575, "bf16", "f32"),     # widest: 4 copies of 3,584 words (112 KB)
     (257, 3071, "bf16", "bf16"),
-    (263, 5113, "f32", "f32"),      # widest float32: 4 copies of 5,120 words (160 KB)
+    (26251, 5113, "f32", "f32"),    # widest float32: 4 copies of 5,120 words (160 KB); 2^27 elements
     (4097, 255, "bf16", "f16"),
 ]
 
@@ -142,7 +144,7 @@ def test_flat_forward_unaligned_base(dyt, M, N, xdt, aligned_only):
     (5001, 32, "bf16", 1, 3), (5001, 32, "bf16", 3, 3),   # one-slot packed: tiles, then the shifted walk
     # rows over 8,192 columns (gamma/beta in 104-160 KB of LDS; no shifted copies fit, so
     # these walk unaligned from element 0)
-    (1001, 13312, "f32", 1, 1), (1001, 13312, "f32", 1, 2), (33, 8200, "bf16", 1, 3),
+    (5043, 13312, "f32", 1, 1), (5043, 13312, "f32", 1, 2), (33, 8200, "bf16", 1, 3),
     (33, 8200, "bf16", 5, 5), (7, 20480, "f32", 3, 0)])
 def test_flat_forward_other_misalignments(dyt, M, N, xdt, xo, yo):
     """x and y off the 16-byte grid by xo and yo elements (equal offsets

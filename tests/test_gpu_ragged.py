@@ -126,7 +126,7 @@ def test_ragged_rows(dyt, M, N, xdt, pdt):
 
 # re-tiled for slot occupancy (the CPU test test_occupancy_retiling checks
 # that these shapes get K = 3 / 4 and packed tiles beyond 4,096 elements)
-RETILED = [(301, 1500, "bf16", "f32"), (1100, 5120, "bf16", "f32"), (2000, 2560, "bf16", "bf16"),
+RETILED = [(2800, 1500, "bf16", "f32"), (1100, 5120, "bf16", "f32"), (2000, 2560, "bf16", "bf16"),
            (1700, 2560, "f32", "f32"), (2100, 4104, "f32", "f32"), (1400, 3072, "bf16", "f32")]
 
 

@@ -38,7 +38,7 @@ SHAPES = [
     (100003, 255, "f32", "f32"),      # packed rows, float32 (sc1 stores), partial tile
     (32771, 4096, "f16", "bf16"),     # rows left over after the last whole group
     (21848, 6144, "bf16", "f32"),     # three segments per row, 510 workgroups
-    (100003, 64, "f32", "f32"),       # packed rows of 16
+    (300007, 64, "f32", "f32"),       # packed rows of 16
 ]
 
 

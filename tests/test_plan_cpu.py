@@ -166,7 +166,7 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
     (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
     (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0),
-    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 0), (10000, "f32", 1),
+    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 0), (4096, "f32", 0), (10000, "f32", 1),
     (9216, "f32", 1), (13312, "f32", 1), (17408, "f32", 1), (18432, "f32", 0), (20480, "f32", 0),
     (8200, "bf16", 1), (11264, "bf16", 0), (24576, "f32", 0),
     (2560, "f16", 1),
@@ -175,13 +175,16 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2039, "bf16", 1), (2047, "bf16", 1), (3071, "bf16", 1), (3575, "bf16", 1), (3577, "bf16", 0),
     (4095, "bf16", 0), (5111, "bf16", 0),
     (8183, "bf16", 0), (1500, "f16", 1),
-    (1501, "f32", 1), (3001, "f32", 1), (5113, "f32", 1), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
+    (1501, "f32", 1), (3001, "f32", 0), (5113, "f32", 0), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
     (2043, "f32", 0)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
-    """At 2^27 elements the measured choice: the flat walk for widths the
-    tiles fill poorly and for rows that are not a whole number of vectors
-    (float32: only when the tiles fill poorly), the tiles where they fill
-    or gamma/beta would not fit the LDS copy."""
+    """Just under 2^27 elements (M = 2^27 // N) the measured choice: the flat
+    walk for widths the tiles fill poorly and for rows that are not a whole
+    number of vectors (float32: only when the tiles fill poorly), the tiles
+    where they fill or gamma/beta would not fit the LDS copy. The tiles are
+    those of the tile table: float32 rows of 2,049-6,144 columns get
+    one-slot segments there (5,120 and 3,001 wide fill them), wider rows
+    segments of up to 8 slots."""
     M = (1 << 27) // N
     f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
     assert f["flat"] == flat
