@@ -249,7 +249,8 @@ def _choose(reps, cands, dflt, key):
     return best, ratios[best]
 
 
-def cmd_emit(path: str) -> None:
+def emit_text(path: str) -> str:
+    """The table (dyt_tune_table.inc) that the measurement record at path gives."""
     with open(path) as f:
         data = json.load(f)
     cands = {k: tuple(v) for k, v in data["candidates"].items()}
@@ -273,9 +274,14 @@ def cmd_emit(path: str) -> None:
                 + "; ".join(f"{b[0]} " + "/".join(f"{v:.3f}" for v in rt) for b, rt in picks))
         lines.append(_entry(DTYPES[d], lo, hi, e_lo, e_hi, cands[picks[0][0]], cands[picks[1][0]],
                             cands[picks[2][0]], note))
+    return "\n".join(lines) + "\n"
+
+
+def cmd_emit(path: str) -> None:
+    text = emit_text(path)
     with open(TABLE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+        f.write(text)
+    print(text, end="")
 
 
 def cmd_defaults() -> None:
