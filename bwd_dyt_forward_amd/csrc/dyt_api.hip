@@ -426,7 +426,11 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
                               fill >= DYT_FLAT_OCC_2B;
         p.flat_shift = rag_fits && DYT_FLAT_SHIFT;
     }
-    p.ld = round_up(2 * p.wcols + 1, 4);
+    // Partial rows are a whole number of 128-byte lines apart: pass 2 reads
+    // 64 consecutive floats of each row per workgroup, two lines instead of
+    // three when rows start on the line grid (a 16-byte multiple fetched
+    // 1.44x the workspace at 4,096 columns).
+    p.ld = round_up(2 * p.wcols + 1, 32);
     p.fin_grid = ceil_div(2 * N + 1, 64);
     p.ws_bytes = p.grid * p.ld * (int64_t)sizeof(float);
 #if DYT_FUSED_FIN

@@ -114,7 +114,7 @@ def test_plan_invariants(dyt, M, N, xdt, vec):
     f = dyt.dyt_get_forward_plan(M, N, xdt, "f32", vec)
     assert 1 <= p["fwd_grid"] <= f["tiles"] and 1 <= p["bwd_grid"] <= p["tiles"]
     wcols = N if p["packed"] else p["tile_elems"]
-    assert p["ws_row"] >= 2 * wcols + 1 and p["ws_row"] % 4 == 0
+    assert p["ws_row"] >= 2 * wcols + 1 and p["ws_row"] % 32 == 0   # whole 128-byte lines
     assert p["ws_bytes"] == p["bwd_grid"] * p["ws_row"] * 4
     assert p["fin_grid"] == -(-(2 * N + 1) // 64)
     ws = dyt.dyt_backward_workspace_size(M, N, xdt, "f32")
