@@ -930,9 +930,12 @@ VARIANTS = {
     "fused_finish": ["-DDYT_FUSED_FIN=1"],
     # plain loads and stores instead of nontemporal ones in both directions
     "no_nt_hints": ["-DDYT_FWD_NT=0", "-DDYT_BWD_NT=0"],
-    # two tiles per pipeline buffer in pass 1 / one in the forward
+    # two tiles per pipeline buffer in pass 1 / one or four in the forward
     "bwd_two_units": ["-DDYT_BWD_U=2"],
     "fwd_one_unit": ["-DDYT_FWD_U=1"],
+    "fwd_four_units": ["-DDYT_FWD_U=4"],
+    # two tiles per buffer for the plain forward of 2-byte x as well
+    "fwd_two_units_2b": ["-DDYT_FWD_U_2B=2"],
     # the default constants (one 256-thread workgroup per CU, largest tiles)
     # instead of the measured tile table
     "default_constants": ["-DDYT_TUNE_TABLE=0"],

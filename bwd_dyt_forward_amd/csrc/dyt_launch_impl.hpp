@@ -18,14 +18,28 @@
 // The residual forward (two inputs, two outputs) uses the forward's U as
 // well: on 32768 x 4096 and 4194304 x 32 bf16 U = 2 measured 0.2-0.8%
 // faster than U = 1.
+// The plain forward of 2-byte x with 16-byte vectors takes DYT_FWD_U_2B
+// tiles per buffer: four measured 2.0% faster than two on 32,768 x 4,096
+// bf16 (81.2 -> 79.6 us), while four lost 0.9-4.5% on the float32
+// 100,003-row forwards and 4% on the residual forward (bench.py --variants
+// fwd_four_units), and the element-wise kernels (V = 1, K = 32) spill
+// registers with four.
+#ifndef DYT_FWD_U_2B
+#define DYT_FWD_U_2B 4
+#endif
 
 namespace dyt {
 namespace host {
 
+template <typename XT, int V, bool RES>
+constexpr int fwd_units() {
+    return (!RES && sizeof(XT) == 2 && V > 1) ? DYT_FWD_U_2B : DYT_FWD_U;
+}
+
 // The element-wise variant (V = 1) exists only for row-strided packed tiles.
 template <typename XT, typename PT, int V, int K, bool RES, bool STRIDED>
 bool launch_fwd_vk(const Plan& p, const Geo& g, const FwdPtrs& a, hipStream_t s) {
-    constexpr int U = DYT_FWD_U;
+    constexpr int U = fwd_units<XT, V, RES>();
     const dim3 grid((unsigned)p.grid), block(kBlock);
     if constexpr (V == 1) {
         if constexpr (!STRIDED || RES) return false;
