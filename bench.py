@@ -936,6 +936,11 @@ VARIANTS = {
     "fwd_four_units": ["-DDYT_FWD_U=4"],
     # two tiles per buffer for the plain forward of 2-byte x as well
     "fwd_two_units_2b": ["-DDYT_FWD_U_2B=2"],
+    # the flat forward on two or four workgroups per CU, or with eight
+    # vectors per thread and step
+    "flat_grid_512": ["-DDYT_FLAT_GRID=512"],
+    "flat_grid_1024": ["-DDYT_FLAT_GRID=1024"],
+    "flat_u8": ["-DDYT_FLAT_U=8"],
     # the default constants (one 256-thread workgroup per CU, largest tiles)
     # instead of the measured tile table
     "default_constants": ["-DDYT_TUNE_TABLE=0"],
