@@ -941,6 +941,11 @@ VARIANTS = {
     "flat_grid_512": ["-DDYT_FLAT_GRID=512"],
     "flat_grid_1024": ["-DDYT_FLAT_GRID=1024"],
     "flat_u8": ["-DDYT_FLAT_U=8"],
+    # pass 1's dx stores through a buffer descriptor with cache-policy bits:
+    # sc0, sc1, sc1 + nontemporal
+    "bwd_store_sc0": ["-DDYT_BWD_STORE_POL=1"],
+    "bwd_store_sc1": ["-DDYT_BWD_STORE_POL=16"],
+    "bwd_store_sc1_nt": ["-DDYT_BWD_STORE_POL=18"],
     # the default constants (one 256-thread workgroup per CU, largest tiles)
     # instead of the measured tile table
     "default_constants": ["-DDYT_TUNE_TABLE=0"],

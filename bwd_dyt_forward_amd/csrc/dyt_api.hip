@@ -609,6 +609,9 @@ int enqueue_pass1(const Plan& base, const BwdPtrs& a, int64_t M, int64_t N, int 
     g.pitch[1] = lddy;
     g.pitch[2] = lddx;
     if (p.vec > 1 && p.tiles >= 8 * p.grid) g.even_share_q = DYT_XCD_EVEN_SHARE_BWD_Q;
+    // every vector of dx on the 16-byte grid (as for the forward's y)
+    g.buf_store = !strided && !res && p.vec > 1 && aligned(a.dx, 16) && p.T % p.vec == 0 &&
+                  (p.packed || N % p.vec == 0);
 #if DYT_FUSED_FIN
     g.fin_out[0] = g.fin_out[1] = g.fin_out[2] = nullptr;
     g.ctr = nullptr;

@@ -195,6 +195,15 @@ typedef float f32x4_m __attribute__((ext_vector_type(4), aligned(4)));
 #ifndef DYT_BWD_RES_NT
 #define DYT_BWD_RES_NT 0
 #endif
+// Measurement builds only: pass 1 writes dx through a buffer descriptor with
+// these cache-policy bits (contiguous, 16-byte aligned, no residual) instead
+// of the stores above; 0 keeps them. Measured on MI355X (bench.py --variants
+// bwd_store_sc0,bwd_store_sc1,bwd_store_sc1_nt): sc0, sc1 and sc1 +
+// nontemporal made the 32,768 x 4,096 bf16 backward 23-26% slower (162-166
+// against 131.6 us) and the float32 100,003-row ones 4-16% slower.
+#ifndef DYT_BWD_STORE_POL
+#define DYT_BWD_STORE_POL 0
+#endif
 template <bool NT, typename T>
 __device__ __forceinline__ T stream_load(const T* p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -1241,7 +1250,8 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
                                          const typename Raw<XT, V>::T (&rr)[U][K],
                                          XT* __restrict__ dx, int64_t bo, const AD& ao,
                                          const float (&gm)[K][V], float alpha, const int (&lo)[K],
-                                         float (&ag)[K][V], float (&ab)[K][V], float (&aa)[K]) {
+                                         float (&ag)[K][V], float (&ab)[K][V], float (&aa)[K],
+                                         uint32_t span_bytes = 0) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -1255,6 +1265,14 @@ __device__ __forceinline__ void bwd_tile(const typename Raw<XT, V>::T (&rx)[U][K
                 Raw<XT, V>::unpack(rr[j][k], rv);
 #pragma unroll
                 for (int e = 0; e < V; ++e) out[e] += rv[e];
+            }
+            if constexpr (DYT_BWD_STORE_POL != 0 && !RES && !RAG && V > 1) {
+                if (span_bytes != 0) {
+                    store_with_policy<DYT_BWD_STORE_POL>(dx + bo + j * ao.upitch, span_bytes,
+                                                         (uint32_t)(ao.off[k] * (int)sizeof(XT)),
+                                                         Raw<XT, V>::pack(out));
+                    continue;
+                }
             }
             Raw<XT, V>::template store<(RES ? DYT_BWD_RES_NT : DYT_BWD_NT) != 0>(
                 dx + bo + j * ao.upitch + ao.off[k], out);
@@ -1306,6 +1324,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
 
     // Same two-buffer persistent loop over groups of U adjacent units as the
     // forward.
+    const uint32_t span = (DYT_BWD_STORE_POL != 0 && g.buf_store) ? (uint32_t)w.seg_len * (uint32_t)sizeof(XT) : 0u;
     const int64_t ng = w.units / U;
     const int64_t iters = w.g_first < w.g_end ? (w.g_end - w.g_first + w.g_stride - 1) / w.g_stride : 0;
     const int64_t ustep = w.g_stride * U;
@@ -1325,7 +1344,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa, span);
             __builtin_amdgcn_sched_barrier(0);
             const bool more = 2 * pi + 2 < iters;
             const int64_t bxn = more ? bxb + gsx : bxb;
@@ -1333,7 +1352,7 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int64_t bon = STRIDED ? (more ? bob + gso : bob) : bxn;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxn, ax, bdn, ad, xa, da, ra);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa, span);
             __builtin_amdgcn_sched_barrier(0);
             bxa = bxn;
             bda = bdn;
@@ -1344,17 +1363,17 @@ dyt_bwd_partial_kernel(const XT* __restrict__ x, const XT* __restrict__ dy,
             const int64_t bdb = STRIDED ? bda + gsd : bxb, bob = STRIDED ? boa + gso : bxb;
             bwd_load<XT, V, K, U, RES>(x, dy, dres, bxb, ax, bdb, ad, xb, db, rb);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa, span);
             __builtin_amdgcn_sched_barrier(0);
-            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa);
+            bwd_tile<XT, V, K, U, ACC, RES, RAG>(xb, db, rb, dx, bob, ao, gm, alpha, sl.lo, ag, ab, aa, span);
         }
-        if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa);
+        if (iters & 1) bwd_tile<XT, V, K, U, ACC, RES, RAG>(xa, da, ra, dx, boa, ao, gm, alpha, sl.lo, ag, ab, aa, span);
     }
     for (int64_t u = ng * U + w.gw; u < w.units; u += w.gcount) {
         typename R::T x1[1][K], d1[1][K], r1[1][K];
         bwd_load<XT, V, K, 1, RES>(x, dy, dres, cb + u * ax.upitch, ax, cb + u * ad.upitch, ad, x1, d1, r1);
         bwd_tile<XT, V, K, 1, ACC, RES, RAG>(x1, d1, r1, dx, cb + u * ao.upitch, ao, gm, alpha, sl.lo, ag,
-                                             ab, aa);
+                                             ab, aa, span);
     }
 
     if (PACKED && w.tail) {
