@@ -941,6 +941,10 @@ VARIANTS = {
     "flat_grid_512": ["-DDYT_FLAT_GRID=512"],
     "flat_grid_1024": ["-DDYT_FLAT_GRID=1024"],
     "flat_u8": ["-DDYT_FLAT_U=8"],
+    # the flat forward for float32 rows however full their tiles are
+    "flat_f32_all": ["-DDYT_FLAT_OCC_4B=1.01"],
+    # float32 row segments keep their tiles at any size
+    "flat_f32_big_off": ["-DDYT_FLAT_BIG_4B=4611686018427387904LL"],
     # pass 1's dx stores through a buffer descriptor with cache-policy bits:
     # sc0, sc1, sc1 + nontemporal
     "bwd_store_sc0": ["-DDYT_BWD_STORE_POL=1"],
@@ -998,6 +1002,77 @@ def variant_library(name: str):
         b.build(out=path, extra_flags=flags, with_stream_ref=False, cache=True)
     from bwd_dyt_forward_amd import _lib
     return _lib._load(path, flags)
+
+
+def report_flat_crossover(dyt, torch, path: str, rounds: int = 7) -> None:
+    """Contiguous float32 forwards of row widths that fill their tiles
+    (3,072 / 4,096 / 5,120), at sizes from 2^22 to 2^27 elements: their
+    tiles (the flat_f32_big_off variant) against the flat walk (the
+    flat_f32_all variant, which walks every such row flat), every output
+    compared bit for bit, and which of the two the default plan takes; runs
+    of back-to-back calls between two HIP events, the two libraries
+    interleaved over rounds, medians. Writes Markdown."""
+    import ctypes
+    import statistics
+    from bwd_dyt_forward_amd import _lib
+    libs = {"tiles": variant_library("flat_f32_big_off"), "flat": variant_library("flat_f32_all")}
+    s = torch.cuda.current_stream().cuda_stream
+    sizes = (1 << 22, 1 << 24, 1 << 26, 80_000_000, 104_000_000, 1 << 27)
+    rows = ["# Float32 forward: tiles against the flat walk by size", "",
+            f"Command: `python bench.py --flat-crossover {path}`. Device: {torch.cuda.get_device_name(0)}. "
+            f"Build id {dyt.lib.dyt_build_id().decode()}.", "",
+            "us per call: a run of back-to-back forwards between two HIP events, the tiles (variant "
+            f"flat_f32_big_off: {' '.join(VARIANTS['flat_f32_big_off'])}) and the flat walk (variant "
+            f"flat_f32_all: {' '.join(VARIANTS['flat_f32_all'])}) interleaved over {rounds} rounds; "
+            "medians. x ~ N(0, 1), fp32 parameters; y compared bit for bit. The default plan takes the "
+            "flat walk for float32 row segments beyond 2^26 elements.", "",
+            "| N | M | elements | tiles | tiles us | flat us | flat / tiles | default plan |",
+            "|---:|---:|---:|---|---:|---:|---:|---|"]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for N in (3072, 4096, 5120):
+        for e in sizes:
+            M = e // N
+            x = torch.randn(M, N, device="cuda")
+            a = torch.full((1,), 0.5, device="cuda")
+            g = 1 + 0.1 * torch.randn(N, device="cuda")
+            b = 0.1 * torch.randn(N, device="cuda")
+            ys = {k: torch.empty_like(x) for k in libs}
+
+            def call(k):
+                return libs[k].dyt_forward(x.data_ptr(), a.data_ptr(), g.data_ptr(), b.data_ptr(),
+                                           ys[k].data_ptr(), M, N, 0, 0, s)
+            for k in libs:
+                if call(k) != 0:
+                    raise RuntimeError(f"forward failed on {M} x {N}")
+            torch.cuda.synchronize()
+            if not torch.equal(ys["tiles"], ys["flat"]):
+                raise RuntimeError(f"the flat walk differs from the tiles on {M} x {N}")
+            reps = max(5, int(20000 / (e / 2 ** 27 * 180 + 5)))
+            t = {k: [] for k in libs}
+            for rnd in range(rounds):
+                for k in (list(libs) if rnd % 2 == 0 else list(libs)[::-1]):
+                    for _ in range(3):
+                        call(k)
+                    e0.record()
+                    for _ in range(reps):
+                        call(k)
+                    e1.record()
+                    e1.synchronize()
+                    t[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+            d, f = statistics.median(t["tiles"]), statistics.median(t["flat"])
+            pt, pd = _lib.DytPlan(), _lib.DytPlan()
+            libs["tiles"].dyt_get_forward_plan(M, N, 0, 0, 1, ctypes.byref(pt))
+            dyt.lib.dyt_get_forward_plan(M, N, 0, 0, 1, ctypes.byref(pd))
+            desc = f"{'packed' if pt.packed else 'rows'} nb={pt.col_blocks}, K={pt.slots}, grid {pt.fwd_grid}"
+            if pt.flat:
+                desc = "flat walk (tiles fill poorly)"
+            rows.append(f"| {N:,} | {M:,} | {M * N:,} | {desc} | {d:.1f} | {f:.1f} | {f / d:.3f} | "
+                        f"{'flat walk' if pd.flat else 'tiles'} |")
+            log(f"[bench] flat crossover {M} x {N}: tiles {d:.1f} us, flat {f:.1f} us")
+            del x, ys
+            torch.cuda.empty_cache()
+    with open(path, "w") as fh:
+        fh.write("\n".join(rows) + "\n")
 
 
 def report_variants(dyt, torch, path: str, names, rounds: int = 8) -> None:
@@ -1641,6 +1716,9 @@ def main() -> int:
                          "or lib:PATH for a prebuilt library from other sources) against the "
                          "default build on every workload")
     ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
+    ap.add_argument("--flat-crossover", metavar="FILE", default=None,
+                    help="only time float32 forwards of full-tile widths by size, the default plan "
+                         "against the flat walk (variant flat_f32_all), and write Markdown")
     ap.add_argument("--placement", metavar="FILE", default=None,
                     help="only time the --workload's forward and pass 1 on tensors allocated at "
                          "process start, after sustained steps and after reallocation (Markdown to FILE)")
@@ -1674,6 +1752,10 @@ def main() -> int:
     if args.graph_vs_eager:
         r = graph_vs_eager(dyt, torch, args.graph_vs_eager)
         log(f"[bench] {args.graph_vs_eager}: eager {r['eager']:.2f} us per step, graph {r['graph']:.2f} us per step")
+        return 0
+    if args.flat_crossover:
+        report_flat_crossover(dyt, torch, args.flat_crossover)
+        log(f"[bench] flat crossover written to {args.flat_crossover}")
         return 0
     if args.variants:
         report_variants(dyt, torch, args.variants_report, args.variants.split(","))

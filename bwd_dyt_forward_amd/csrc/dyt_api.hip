@@ -248,6 +248,17 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_RAG
 #define DYT_FLAT_RAG 1
 #endif
+// Float32 rows in row segments walk flat above DYT_FLAT_BIG_4B elements
+// however full their tiles are: x then exceeds the 256 MB last-level cache,
+// which the tiles' write-back stores profit from in back-to-back calls.
+// Measured on MI355X (contiguous forwards, interleaved medians, outputs
+// bit-identical): rows of 3,072 / 4,096 / 5,120 at 8.0e7-1.3e8 elements
+// took 0.90-0.96 of the tiles' time flat, at 2^26 elements 1.08-1.17 of it
+// (the tiles there: one-slot segments from the tile table), at 2^24 and 2^22
+// 1.12-1.83 of it.
+#ifndef DYT_FLAT_BIG_4B
+#define DYT_FLAT_BIG_4B (int64_t(1) << 26)
+#endif
 // The residual-fused forward as well, with the same rule: bf16 rows of 17 /
 // 255 / 1,001 / 1,500 / 3,071 181-186 us against 214-234 us tiled, float32
 // 1,501 / 3,001 (0.73 filled) 384 / 387 against 516 / 502, float32 255
@@ -408,8 +419,9 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         p.grid -= p.nb;
     const double fill = occupancy(p, N);
     const bool k2 = sx == 2 && p.packed && p.slots >= 2;
+    const bool big_4b = dir == Dir::Fwd && sx == 4 && !p.packed && M * N > DYT_FLAT_BIG_4B;
     const bool poor_fit =
-        dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B)
+        dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B || big_4b)
                         : fill < 1.0 - 1e-9 || k2;
     const bool rag = N % vmax != 0;
     const bool rag_fits = kFlatMaxN > 0 && N <= kFlatMaxN &&
@@ -418,7 +430,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
     const bool rag_dir = dir == Dir::Fwd || (dir == Dir::ResFwd && DYT_FLAT_RAG_RES);
     const int64_t max_n = dir == Dir::ResFwd ? std::min<int64_t>(kFlatMaxN, DYT_FLAT_MAX_N_RES) : kFlatMaxN;
     const bool flat_ok = rag ? rag_dir && DYT_FLAT_RAG && rag_fits && N <= max_n &&
-                                   (sx == 2 || fill < DYT_FLAT_OCC_4B)
+                                   (sx == 2 || fill < DYT_FLAT_OCC_4B || big_4b)
                              : dir != Dir::Bwd && N <= max_n && poor_fit;
     if (flat_ok) {
         const int64_t groups = ceil_div(M * N / vmax, (int64_t)DYT_FLAT_U * kBlock);

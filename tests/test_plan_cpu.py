@@ -89,17 +89,20 @@ def _check_flat(f, M, N, xdt, residual=False):
     aligned bases alone. Rows that are not a whole number of vectors walk
     flat (plain and residual forward) when N + V rounded up to 4 is at most 3,584
     (2-byte x, always) or 5,120 (float32 x, below 0.9): four copies of both
-    parameters in at most 160 KB of LDS."""
+    parameters in at most 160 KB of LDS. Float32 row segments (not packed
+    rows) of the plain forward count as filled poorly at any fill beyond 2^26
+    elements."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
+    big = not residual and xdt == "f32" and not f["packed"] and M * N > (1 << 26)
     if residual:
         poor = occ < 1 - 1e-9 or k2
     else:
-        poor = occ < 0.9 if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
+        poor = (occ < 0.9 or big) if xdt == "f32" else (occ < 0.85 or bool(f["packed"]))
     if N % v:
         fits = -(-(N + v) // 4) * 4 <= (5120 if xdt == "f32" else 3584)
-        want = fits and (xdt != "f32" or occ < 0.9)
+        want = fits and (xdt != "f32" or occ < 0.9 or big)
     else:
         want = N <= (8192 if residual else 20480) and poor
     assert f["flat"] == int(want)
@@ -166,8 +169,8 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2560, "bf16", 1), (4104, "bf16", 1), (1536, "bf16", 1), (768, "bf16", 1), (2048, "bf16", 1),
     (3072, "bf16", 1), (5120, "bf16", 1), (32, "bf16", 1), (64, "bf16", 1), (4096, "bf16", 0),
     (7168, "bf16", 0), (6144, "bf16", 0), (8192, "bf16", 0),
-    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 0), (4096, "f32", 0), (10000, "f32", 1),
-    (9216, "f32", 1), (13312, "f32", 1), (17408, "f32", 1), (18432, "f32", 0), (20480, "f32", 0),
+    (2560, "f32", 1), (4104, "f32", 1), (5120, "f32", 1), (4096, "f32", 1), (10000, "f32", 1),
+    (9216, "f32", 1), (13312, "f32", 1), (17408, "f32", 1), (18432, "f32", 1), (20480, "f32", 1),
     (8200, "bf16", 1), (11264, "bf16", 0), (24576, "f32", 0),
     (2560, "f16", 1),
     # rows that are not a whole number of vectors
@@ -175,16 +178,16 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2039, "bf16", 1), (2047, "bf16", 1), (3071, "bf16", 1), (3575, "bf16", 1), (3577, "bf16", 0),
     (4095, "bf16", 0), (5111, "bf16", 0),
     (8183, "bf16", 0), (1500, "f16", 1),
-    (1501, "f32", 1), (3001, "f32", 0), (5113, "f32", 0), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
-    (2043, "f32", 0)])
+    (1501, "f32", 1), (3001, "f32", 1), (5113, "f32", 1), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
+    (2043, "f32", 1)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
-    """Just under 2^27 elements (M = 2^27 // N) the measured choice: the flat
-    walk for widths the tiles fill poorly and for rows that are not a whole
-    number of vectors (float32: only when the tiles fill poorly), the tiles
-    where they fill or gamma/beta would not fit the LDS copy. The tiles are
-    those of the tile table: float32 rows of 2,049-6,144 columns get
-    one-slot segments there (5,120 and 3,001 wide fill them), wider rows
-    segments of up to 8 slots."""
+    """Just under 2^27 elements (M = 2^27 // N) the measured choice: for
+    2-byte x the flat walk for widths the tiles fill poorly and for rows that
+    are not a whole number of vectors, the tiles where they fill; float32 row
+    segments walk flat at any fill beyond 2^26 elements (x larger than the
+    last-level cache), while float32 packed rows (255, 17 wide) keep their
+    tiles. Rows whose gamma/beta would not fit the LDS copy (24,576 wide,
+    5,117 wide with its shifted copies) keep the tiles."""
     M = (1 << 27) // N
     f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
     assert f["flat"] == flat
