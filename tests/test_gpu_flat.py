@@ -308,3 +308,34 @@ def test_flat_forward_ieee_special_values(dyt, M, N, xdt):
     yn = to_np(y)
     assert np.isnan(yn.reshape(-1)[zi]).all() and np.isnan(yn).sum() == np.unique(zi).size
     assert np.array_equal(_bits(ys), _bits(y))
+
+
+def test_large_float32_rows_walk_flat(dyt):
+    """Float32 row segments beyond 2^26 elements walk flat however full
+    their tiles (4,096 wide: four full one-slot segments per row), while the
+    same rows at 2^26 elements keep their tiles; y equals the tiled
+    (row-strided) launch bit for bit and the oracle on sampled elements."""
+    M, N = 20000, 4096
+    plan = dyt.dyt_get_forward_plan(M, N, "f32", "f32")
+    log(f"[flat large f32] M={M} N={N} plan={plan}")
+    assert plan["flat"] == 1 and plan["packed"] == 0
+    assert dyt.dyt_get_forward_plan(16384, N, "f32", "f32")["flat"] == 0
+    inp, x, a, g, b = _inputs(dyt, M, N, "f32", "f32", seed=11)
+    y = dyt.dyt_forward(x, a, g, b)
+    xs_buf = torch.empty((M, N + 8), device="cuda")
+    xs = xs_buf[:, :N]
+    xs.copy_(x)
+    ys_buf = torch.full((M, N + 8), CANARY, device="cuda")
+    ys = ys_buf[:, :N]
+    dyt.dyt_forward(xs, a, g, b, y=ys)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ys), _bits(y))
+    assert bool((ys_buf[:, N:] == CANARY).all())
+    rng = np.random.default_rng(3)
+    total = M * N
+    idx = np.unique(np.concatenate([rng.integers(0, total, size=1 << 18), np.arange(4096),
+                                    np.arange(total - 4096, total)]))
+    rows, cols = np.divmod(idx, N)
+    ref, scale = dyt_oracle.forward_at(inp.x[rows, cols], cols, inp.alpha, inp.gamma, inp.beta)
+    y_s = to_np(y.reshape(-1)[torch.from_numpy(idx).cuda()])
+    assert_reports(f"flat large f32 M={M} N={N}", [compare.check_y(y_s, ref, scale, "f32", "y[sampled]")])
