@@ -1004,7 +1004,7 @@ def variant_library(name: str):
     return _lib._load(path, flags)
 
 
-def report_flat_crossover(dyt, torch, path: str, rounds: int = 7) -> None:
+def report_flat_crossover(dyt, torch, path: str, widths=(3072, 4096, 5120), rounds: int = 7) -> None:
     """Contiguous float32 forwards of row widths that fill their tiles
     (3,072 / 4,096 / 5,120), at sizes from 2^22 to 2^27 elements: their
     tiles (the flat_f32_big_off variant) against the flat walk (the
@@ -1019,7 +1019,9 @@ def report_flat_crossover(dyt, torch, path: str, rounds: int = 7) -> None:
     s = torch.cuda.current_stream().cuda_stream
     sizes = (1 << 22, 1 << 24, 1 << 26, 80_000_000, 104_000_000, 1 << 27)
     rows = ["# Float32 forward: tiles against the flat walk by size", "",
-            f"Command: `python bench.py --flat-crossover {path}`. Device: {torch.cuda.get_device_name(0)}. "
+            f"Command: `python bench.py --flat-crossover {path}"
+            + ("" if tuple(widths) == (3072, 4096, 5120) else f" --flat-crossover-widths {','.join(map(str, widths))}")
+            + f"`. Device: {torch.cuda.get_device_name(0)}. "
             f"Build id {dyt.lib.dyt_build_id().decode()}.", "",
             "us per call: a run of back-to-back forwards between two HIP events, the tiles (variant "
             f"flat_f32_big_off: {' '.join(VARIANTS['flat_f32_big_off'])}) and the flat walk (variant "
@@ -1029,7 +1031,7 @@ def report_flat_crossover(dyt, torch, path: str, rounds: int = 7) -> None:
             "| N | M | elements | tiles | tiles us | flat us | flat / tiles | default plan |",
             "|---:|---:|---:|---|---:|---:|---:|---|"]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for N in (3072, 4096, 5120):
+    for N in widths:
         for e in sizes:
             M = e // N
             x = torch.randn(M, N, device="cuda")
@@ -1717,8 +1719,11 @@ def main() -> int:
                          "default build on every workload")
     ap.add_argument("--variants-report", metavar="FILE", default="variants.md")
     ap.add_argument("--flat-crossover", metavar="FILE", default=None,
-                    help="only time float32 forwards of full-tile widths by size, the default plan "
-                         "against the flat walk (variant flat_f32_all), and write Markdown")
+                    help="only time float32 forwards of full-tile widths by size, their tiles "
+                         "(variant flat_f32_big_off) against the flat walk (variant flat_f32_all), "
+                         "and write Markdown")
+    ap.add_argument("--flat-crossover-widths", default="3072,4096,5120",
+                    help="row widths of --flat-crossover (comma-separated)")
     ap.add_argument("--placement", metavar="FILE", default=None,
                     help="only time the --workload's forward and pass 1 on tensors allocated at "
                          "process start, after sustained steps and after reallocation (Markdown to FILE)")
@@ -1754,7 +1759,8 @@ def main() -> int:
         log(f"[bench] {args.graph_vs_eager}: eager {r['eager']:.2f} us per step, graph {r['graph']:.2f} us per step")
         return 0
     if args.flat_crossover:
-        report_flat_crossover(dyt, torch, args.flat_crossover)
+        report_flat_crossover(dyt, torch, args.flat_crossover,
+                              tuple(int(v) for v in args.flat_crossover_widths.split(",")))
         log(f"[bench] flat crossover written to {args.flat_crossover}")
         return 0
     if args.variants:

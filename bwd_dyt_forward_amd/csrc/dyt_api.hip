@@ -248,14 +248,15 @@ double occupancy(const Plan& p, int64_t N) {
 #ifndef DYT_FLAT_RAG
 #define DYT_FLAT_RAG 1
 #endif
-// Float32 rows in row segments walk flat above DYT_FLAT_BIG_4B elements
-// however full their tiles are: x then exceeds the 256 MB last-level cache,
-// which the tiles' write-back stores profit from in back-to-back calls.
-// Measured on MI355X (contiguous forwards, interleaved medians, outputs
-// bit-identical): rows of 3,072 / 4,096 / 5,120 at 8.0e7-1.3e8 elements
-// took 0.90-0.96 of the tiles' time flat, at 2^26 elements 1.08-1.17 of it
-// (the tiles there: one-slot segments from the tile table), at 2^24 and 2^22
-// 1.12-1.83 of it.
+// Float32 rows walk flat above DYT_FLAT_BIG_4B elements however full their
+// tiles are: x then exceeds the 256 MB last-level cache, which the tiles'
+// write-back stores profit from in back-to-back calls. Measured on MI355X
+// (bench.py --flat-crossover, contiguous forwards, interleaved medians,
+// outputs bit-identical): row segments 3,072 / 4,096 / 5,120 wide at
+// 8.0e7-1.3e8 elements took 0.90-0.97 of the tiles' time flat, packed rows
+// 64 / 100 / 255 / 1,000 wide 0.66-0.96 of it; at 2^26 elements the flat
+// walk took 1.07-1.14 of the tiles' time (255 wide: 0.90), at 2^24 and
+// 2^22 1.04-1.57 of it.
 #ifndef DYT_FLAT_BIG_4B
 #define DYT_FLAT_BIG_4B (int64_t(1) << 26)
 #endif
@@ -419,7 +420,7 @@ int make_plan(int64_t M, int64_t N, int xdt, int pdt, Dir dir, Plan& p) {
         p.grid -= p.nb;
     const double fill = occupancy(p, N);
     const bool k2 = sx == 2 && p.packed && p.slots >= 2;
-    const bool big_4b = dir == Dir::Fwd && sx == 4 && !p.packed && M * N > DYT_FLAT_BIG_4B;
+    const bool big_4b = dir == Dir::Fwd && sx == 4 && M * N > DYT_FLAT_BIG_4B;
     const bool poor_fit =
         dir == Dir::Fwd ? (sx == 2 ? fill < DYT_FLAT_OCC_2B || p.packed : fill < DYT_FLAT_OCC_4B || big_4b)
                         : fill < 1.0 - 1e-9 || k2;

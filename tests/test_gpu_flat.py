@@ -310,17 +310,22 @@ def test_flat_forward_ieee_special_values(dyt, M, N, xdt):
     assert np.array_equal(_bits(ys), _bits(y))
 
 
-def test_large_float32_rows_walk_flat(dyt):
-    """Float32 row segments beyond 2^26 elements walk flat however full
-    their tiles (4,096 wide: four full one-slot segments per row), while the
-    same rows at 2^26 elements keep their tiles; y equals the tiled
-    (row-strided) launch bit for bit and the oracle on sampled elements."""
-    M, N = 20000, 4096
+@pytest.mark.parametrize("M,N,packed", [
+    (20000, 4096, 0),    # four full one-slot row segments per row
+    (700000, 100, 1),    # packed rows
+    (270000, 255, 1),    # packed rows that are not a whole number of vectors
+])
+def test_large_float32_rows_walk_flat(dyt, M, N, packed):
+    """Float32 rows beyond 2^26 elements walk flat however full their tiles,
+    while the same rows at 2^26 elements keep their tiles; y equals the
+    tiled (row-strided) launch bit for bit and the oracle on sampled
+    elements."""
     plan = dyt.dyt_get_forward_plan(M, N, "f32", "f32")
     log(f"[flat large f32] M={M} N={N} plan={plan}")
-    assert plan["flat"] == 1 and plan["packed"] == 0
-    assert dyt.dyt_get_forward_plan(16384, N, "f32", "f32")["flat"] == 0
-    inp, x, a, g, b = _inputs(dyt, M, N, "f32", "f32", seed=11)
+    assert M * N > 1 << 26
+    assert plan["flat"] == 1 and plan["packed"] == packed
+    assert dyt.dyt_get_forward_plan((1 << 26) // N, N, "f32", "f32")["flat"] == 0
+    inp, x, a, g, b = _inputs(dyt, M, N, "f32", "f32", seed=N)
     y = dyt.dyt_forward(x, a, g, b)
     xs_buf = torch.empty((M, N + 8), device="cuda")
     xs = xs_buf[:, :N]

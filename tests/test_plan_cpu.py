@@ -89,13 +89,12 @@ def _check_flat(f, M, N, xdt, residual=False):
     aligned bases alone. Rows that are not a whole number of vectors walk
     flat (plain and residual forward) when N + V rounded up to 4 is at most 3,584
     (2-byte x, always) or 5,120 (float32 x, below 0.9): four copies of both
-    parameters in at most 160 KB of LDS. Float32 row segments (not packed
-    rows) of the plain forward count as filled poorly at any fill beyond 2^26
-    elements."""
+    parameters in at most 160 KB of LDS. Float32 rows of the plain forward
+    count as filled poorly at any fill beyond 2^26 elements."""
     v = VEC[xdt]
     occ = _occupancy(f, N)
     k2 = xdt != "f32" and f["packed"] and f["slots"] >= 2
-    big = not residual and xdt == "f32" and not f["packed"] and M * N > (1 << 26)
+    big = not residual and xdt == "f32" and M * N > (1 << 26)
     if residual:
         poor = occ < 1 - 1e-9 or k2
     else:
@@ -178,16 +177,15 @@ def test_slot_rule_rejects_the_old_short_segment_offsets():
     (2039, "bf16", 1), (2047, "bf16", 1), (3071, "bf16", 1), (3575, "bf16", 1), (3577, "bf16", 0),
     (4095, "bf16", 0), (5111, "bf16", 0),
     (8183, "bf16", 0), (1500, "f16", 1),
-    (1501, "f32", 1), (3001, "f32", 1), (5113, "f32", 1), (5117, "f32", 0), (255, "f32", 0), (17, "f32", 0),
+    (1501, "f32", 1), (3001, "f32", 1), (5113, "f32", 1), (5117, "f32", 0), (255, "f32", 1), (17, "f32", 1),
     (2043, "f32", 1)])
 def test_flat_forward_choice(dyt, N, xdt, flat):
     """Just under 2^27 elements (M = 2^27 // N) the measured choice: for
     2-byte x the flat walk for widths the tiles fill poorly and for rows that
-    are not a whole number of vectors, the tiles where they fill; float32 row
-    segments walk flat at any fill beyond 2^26 elements (x larger than the
-    last-level cache), while float32 packed rows (255, 17 wide) keep their
-    tiles. Rows whose gamma/beta would not fit the LDS copy (24,576 wide,
-    5,117 wide with its shifted copies) keep the tiles."""
+    are not a whole number of vectors, the tiles where they fill; float32
+    rows walk flat at any fill beyond 2^26 elements (x larger than the
+    last-level cache). Rows whose gamma/beta would not fit the LDS copy
+    (24,576 wide, 5,117 wide with its shifted copies) keep the tiles."""
     M = (1 << 27) // N
     f = dyt.dyt_get_forward_plan(M, N, xdt, "f32")
     assert f["flat"] == flat
