@@ -253,10 +253,10 @@ double occupancy(const Plan& p, int64_t N) {
 // write-back stores profit from in back-to-back calls. Measured on MI355X
 // (bench.py --flat-crossover, contiguous forwards, interleaved medians,
 // outputs bit-identical): row segments 3,072 / 4,096 / 5,120 wide at
-// 8.0e7-1.3e8 elements took 0.90-0.97 of the tiles' time flat, packed rows
-// 64 / 100 / 255 / 1,000 wide 0.66-0.96 of it; at 2^26 elements the flat
-// walk took 1.07-1.14 of the tiles' time (255 wide: 0.90), at 2^24 and
-// 2^22 1.04-1.57 of it.
+// 8.0e7-1.3e8 elements took 0.92-0.97 of the tiles' time flat, packed rows
+// 64 / 100 / 255 / 1,000 wide 0.67-0.97 of it; at 2^26 elements and below
+// the flat walk took 1.05-1.60 of the tiles' time (255 wide at 2^26: 0.89,
+// 1,000 wide at 2^24: 0.97).
 #ifndef DYT_FLAT_BIG_4B
 #define DYT_FLAT_BIG_4B (int64_t(1) << 26)
 #endif
