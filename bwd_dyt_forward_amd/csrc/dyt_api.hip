@@ -225,8 +225,8 @@ double occupancy(const Plan& p, int64_t N) {
 // 255 / 511 / 1,001 / 1,500 / 2,039: 81.9-88.4 us against 89.2-113.2 us for
 // the shifted-slot tiles (1,500 at a base one element off: 99.3 against
 // 118.2); float32 1,501 (0.73 filled): 192.9 against 236.0 us, while full
-// float32 tiles tie at 2^27 elements and win at 100,003 x 255 (37.3 against
-// 41.2 us).
+// float32 tiles win at 100,003 x 255 (37.3 against 41.2 us); beyond 2^26
+// elements float32 rows walk flat at any fill (DYT_FLAT_BIG_4B).
 // The residual-fused forward (two inputs, two outputs) walks flat whenever
 // its tiles leave any slot empty or are 2-byte packed tiles of K >= 2: there
 // the flat walk measured as fast as full tiles (4,096 and 32 wide bf16:
