@@ -955,6 +955,10 @@ VARIANTS = {
     "default_constants": ["-DDYT_TUNE_TABLE=0"],
     # the tiled forward everywhere (no flat walk)
     "no_flat_forward": ["-DDYT_FLAT_MAX_N=0"],
+    # one-slot tiles (packed rows of one slot, row segments of one slot) on
+    # 1,024 workgroups everywhere, and no flat walk
+    "tiles_k1_g1024": ["-DDYT_TUNE_TABLE=0", "-DDYT_MIN_TILES=1048576", "-DDYT_WIDE_KCAP=1",
+                       "-DDYT_FWD_GRID=1024", "-DDYT_FLAT_MAX_N=0"],
     # the forward's groups dealt round-robin to every workgroup instead of
     # the XCD-weighted deal
     "xcd_even_share_off": ["-DDYT_XCD_EVEN_SHARE_Q=0"],
