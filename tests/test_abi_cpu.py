@@ -437,6 +437,19 @@ def test_library_build_id_matches_current_sources(dyt):
     assert not build.is_stale()
 
 
+def test_loader_checks_the_build_id_unless_told_otherwise(dyt):
+    """_load refuses the in-tree library when told to expect a variant build
+    (other flags, so another id), and loads it with any_sources (how
+    bench.py --variants lib:PATH compares prebuilt libraries from other
+    sources); the ABI version is checked either way."""
+    from bwd_dyt_forward_amd import _lib, build
+    with pytest.raises(ImportError, match="build id"):
+        _lib._load(build.LIB_PATH, ["-DDYT_FWD_U=1"])
+    lib = _lib._load(build.LIB_PATH, ["-DDYT_FWD_U=1"], any_sources=True)
+    assert lib.dyt_abi_version() == _lib.ABI_VERSION
+    assert lib.dyt_build_id().decode() == build.source_hash()
+
+
 def test_source_hash_follows_code_and_flags_not_comments(tmp_path, monkeypatch):
     from bwd_dyt_forward_amd import build
     src = tmp_path / "k.hpp"
