@@ -66,6 +66,7 @@ SHAPES = [
     (33, 20000, "f32", "f32", 0.5),
     (1, 5000, "f32", "bf16", 0.5),
     (7, 3, "bf16", "f32", 0.5),
+    (100003, 255, "f32", "f32", 0.5),   # packed tiles of two slots (the plain backward's plan)
 ]
 
 
