@@ -319,7 +319,7 @@ typedef struct dyt_plan {
     int64_t tiles;         /* number of tiles */
     int64_t fwd_grid;      /* forward workgroups */
     int64_t bwd_grid;      /* backward pass-1 workgroups = partial rows */
-    int64_t ws_row;        /* floats per partial row */
+    int64_t ws_row;        /* floats between partial rows (a multiple of 32: 128-byte lines) */
     int64_t fin_grid;      /* backward pass-2 workgroups */
     int64_t ws_bytes;      /* workspace bytes this plan uses */
     int64_t flat;          /* forward: 1 if a contiguous launch walks the problem as one
