@@ -15,7 +15,9 @@ rows" autotunes BLOCK_M / BLOCK_N at run time instead).
 
 The measurement record the current table was emitted from is
 bwd_dyt_forward_amd/tune_results.json (per shape and candidate, the median
-microseconds of the forward, the backward and the residual forward).
+microseconds of the forward, the backward and the residual forward);
+tune_results_repeat.json is a second, later run of the same measurement,
+kept to show how much the choice moves between runs.
     python bwd_dyt_forward_amd/tune.py defaults        # the table of default constants
 
 Measurement: every candidate library times the forward, the backward (both
