@@ -70,6 +70,8 @@ SWEEP = [
     # float16 activations and/or parameters
     (65537, 16, "f16", "f32", 0.8), (37, 4096, "f16", "f32", 0.5), (1031, 300, "f16", "f16", 1.5),
     (513, 17, "f32", "f16", 0.9), (257, 64, "bf16", "f16", 0.7), (9, 4100, "f16", "bf16", 0.5),
+    # negative alpha (a learnable scale may change sign)
+    (1003, 255, "f32", "f32", -0.7), (300, 4096, "bf16", "f32", -1.3),
 ]
 
 

@@ -2,8 +2,9 @@
 oracle's tolerances: run-to-run determinism, exact power-of-two scaling,
 poisoned tails and guard canaries (no NaN leakage from padding, no writes
 outside the outputs), closed forms (alpha = 0, alpha = +inf with integer
-data), odd symmetry, subnormal inputs, and tensors at bases aligned only to
-the element size giving the same bits as 16-byte aligned ones."""
+data), odd symmetry in x and in alpha, subnormal inputs, and tensors at
+bases aligned only to the element size giving the same bits as 16-byte
+aligned ones."""
 import os
 
 import numpy as np
@@ -186,6 +187,35 @@ def test_odd_symmetry_bitwise(dyt, xdt):
     y2 = dyt.dyt_forward(-d["x"], d["alpha"], d["gamma"], d["beta"])
     torch.cuda.synchronize()
     assert np.array_equal(_bits(-y1), _bits(y2))
+
+
+@pytest.mark.parametrize("M,N,xdt,pdt", [
+    (100003, 255, "f32", "f32"),    # packed tiles of two slots
+    (300, 4096, "bf16", "f32"),     # row segments
+    (1000, 2560, "bf16", "f32"),    # the flat forward
+    (1031, 300, "f16", "f16"),
+    (41, 4100, "f32", "bf16"),      # rows that are not a whole number of vectors
+])
+def test_negated_alpha_bitwise(dyt, M, N, xdt, pdt):
+    """alpha -> -alpha: tanh is odd and sech^2 even, and rounding to nearest
+    is symmetric, so y(x, -alpha) equals y(-x, alpha), dx and dgamma change
+    sign, and dbeta and dalpha stay the same, all bit for bit."""
+    log(f"[negated alpha] M={M} N={N} x={xdt} p={pdt}")
+    inp = workloads.custom(M, N, xdt, pdt, alpha=0.7, x_sigma=2.0, seed=N)
+    d = upload(inp)
+    na = -d["alpha"]
+    y1 = dyt.dyt_forward(d["x"], na, d["gamma"], d["beta"])
+    y2 = dyt.dyt_forward(-d["x"], d["alpha"], d["gamma"], d["beta"])
+    g1 = dyt.dyt_backward(d["x"], d["dy"], d["alpha"], d["gamma"])
+    g2 = dyt.dyt_backward(d["x"], d["dy"], na, d["gamma"])
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y1), _bits(y2))
+    dx1, da1, dg1, db1 = g1
+    dx2, da2, dg2, db2 = g2
+    assert np.array_equal(_bits(dx2), _bits(-dx1))
+    assert np.array_equal(_bits(dg2), _bits(-dg1))
+    assert np.array_equal(_bits(db2), _bits(db1))
+    assert np.array_equal(_bits(da2), _bits(da1))
 
 
 @pytest.mark.parametrize("name,M", [("c2_65537x16_bf16", 4097), ("c1_1024x64_f32", 1024),
