@@ -2,11 +2,14 @@
 widths near multiples of 256 and 4,096), all three x dtypes and parameter
 dtypes, sizes across the tile table's first three size ranges, and three
 layouts (contiguous; every activation one element off 16-byte alignment;
-row-strided with random pitches). Each is compared with the fp64 oracle:
-element by element up to 2^21 elements, on sampled y/dx (plus full-sum
-gradients) above. The case list is fixed by the seed, so a failure names
-a reproducible case."""
+row-strided with random pitches), alpha of either sign (negative in about
+a quarter of the cases). Each is compared with the fp64 oracle: element by
+element up to 2^21 elements, on sampled y/dx (plus full-sum gradients)
+above. The case list is fixed by the seed, so a failure names a
+reproducible case; DYT_FUZZ_CASES and DYT_FUZZ_SEED select a longer or
+another list (default 36 cases, seed 20251202)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -20,8 +23,10 @@ pytestmark = pytest.mark.gpu
 _DT = ["f32", "bf16", "f16"]
 
 
-def _cases(seed=20251202, n=36):
+def _cases(seed=int(os.environ.get("DYT_FUZZ_SEED", "20251202")),
+           n=int(os.environ.get("DYT_FUZZ_CASES", "36"))):
     rng = np.random.default_rng(seed)
+    sign = np.random.default_rng(seed + 1)   # its own stream: the other draws stay as they were
     out = []
     for i in range(n):
         if rng.random() < 0.7:
@@ -38,7 +43,7 @@ def _cases(seed=20251202, n=36):
         pdt = _DT[int(rng.integers(0, 3))]
         layout = ["contiguous", "unaligned", "strided"][int(rng.integers(0, 3))]
         pad = int(rng.integers(1, 41))
-        alpha = float(rng.choice([0.3, 0.8, 1.7]))
+        alpha = float(rng.choice([0.3, 0.8, 1.7])) * (-1.0 if sign.random() < 0.25 else 1.0)
         out.append((i, M, N, xdt, pdt, layout, pad, alpha))
     return out
 
