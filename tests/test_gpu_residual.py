@@ -2,10 +2,14 @@
 and its backward dh = dres + dx with the layer's parameter gradients.
 
 Parity: h bit for bit against the oracle's rounded sum; y, dh and the
-gradients within the oracle tolerances (oracle/compare.py). Properties
-(bitwise): a zero branch reproduces the plain forward, a zero residual
+gradients within the oracle tolerances (oracle/compare.py), on fixed
+shapes and on a seeded random list (widths, dtypes, alpha of either sign,
+aligned or unaligned bases). Properties (bitwise): a zero branch reproduces the plain forward, a zero residual
 gradient the plain backward, the split backward the single call, and
 unaligned bases the aligned call."""
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -78,6 +82,51 @@ def test_residual_parity(dyt, M, N, xdt, pdt, alpha):
     dh, da, dg, db = dyt.dyt_backward_residual(h, d["dy"], d["dres"], d["alpha"], d["gamma"])
     torch.cuda.synchronize()
     assert_reports(f"residual {M}x{N} {xdt}/{pdt}", _reports(inp, r, dres, h, y, dh, da, dg, db))
+
+
+def _fuzz_cases(seed=int(os.environ.get("DYT_FUZZ_SEED", "20251203")),
+                n=int(os.environ.get("DYT_RES_FUZZ_CASES", "24"))):
+    """Random residual problems of at most 2^21 elements (every element is
+    compared): N log-uniform in 1 .. 24,000, all dtype pairs, alpha in
+    +-{0.3, 0.8, 1.7}, every activation and output at an aligned base or one
+    element off it."""
+    rng = np.random.default_rng(seed)
+    out = []
+    dts = ["f32", "bf16", "f16"]
+    for i in range(n):
+        N = int(round(math.exp(rng.uniform(0.0, math.log(24000.0)))))
+        M = max(1, int(rng.integers(1 << 10, 1 << 21)) // N)
+        xdt, pdt = dts[int(rng.integers(0, 3))], dts[int(rng.integers(0, 3))]
+        alpha = float(rng.choice([0.3, 0.8, 1.7])) * float(rng.choice([-1.0, 1.0]))
+        out.append((i, M, N, xdt, pdt, alpha, bool(rng.integers(0, 2))))
+    return out
+
+
+FUZZ = _fuzz_cases()
+
+
+def _off_by_one(t: torch.Tensor) -> torch.Tensor:
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=[f"{c[0]}-{c[1]}x{c[2]}-{c[3]}-{c[4]}" for c in FUZZ])
+def test_residual_fuzz(dyt, case):
+    i, M, N, xdt, pdt, alpha, unaligned = case
+    log(f"[residual fuzz {i}] M={M} N={N} x={xdt} p={pdt} alpha={alpha} unaligned={unaligned}")
+    inp, r, dres, d = _setup(M, N, xdt, pdt, alpha, seed=2000 + i, sigma=1.5)
+    place = _off_by_one if unaligned else (lambda t: t)
+    x, rr, dy, dr = (place(d[k]) for k in ("x", "r", "dy", "dres"))
+    h = place(torch.zeros_like(d["x"]))
+    y = place(torch.zeros_like(d["x"]))
+    dh = place(torch.zeros_like(d["x"]))
+    dyt.dyt_forward_residual(x, rr, d["alpha"], d["gamma"], d["beta"], h=h, y=y)
+    _, da, dg, db = dyt.dyt_backward_residual(h, dy, dr, d["alpha"], d["gamma"], dh=dh)
+    torch.cuda.synchronize()
+    assert (h.data_ptr() % 16 != 0) == unaligned
+    assert_reports(f"residual fuzz {i}", _reports(inp, r, dres, h, y, dh, da, dg, db))
 
 
 @pytest.mark.parametrize("M,N,xdt", [(2049, 32, "bf16"), (40, 4096, "f16"), (501, 100, "f32")])
