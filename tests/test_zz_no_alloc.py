@@ -92,3 +92,28 @@ def test_noalloc_rejects_problems_beyond_the_scratch(dyt):
     with pytest.raises(dyt.DytError) as e:
         dyt.dyt_backward_noalloc(x, x, p[:1], p, torch.empty_like(x), p[:1].clone(), p.clone(), p.clone())
     assert e.value.status == 3   # DYT_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_noalloc_over_a_sequence_of_problems(dyt):
+    """Sixteen seeded problems in a row (widths log-uniform in 1 .. 20,000,
+    up to 2^22 elements, every dtype pair), sizes going up and down, so the
+    shared scratch holds an earlier, larger or smaller problem's partial rows
+    when each call starts: each equals dyt_backward bit for bit."""
+    import math
+    import numpy as np
+    rng = np.random.default_rng(20251203)
+    dts = [torch.float32, torch.bfloat16, torch.float16]
+    for k in range(16):
+        N = int(round(math.exp(rng.uniform(0.0, math.log(20000.0)))))
+        M = max(1, int(rng.integers(1 << 8, 1 << 22)) // N)
+        xdt, pdt = dts[int(rng.integers(0, 3))], dts[int(rng.integers(0, 3))]
+        log(f"[noalloc sequence] call {k + 1}: M={M} N={N} x={xdt} p={pdt}")
+        x, dy, a, gm = _inputs(M, N, xdt, pdt, seed=500 + k)
+        ref = dyt.dyt_backward(x, dy, a, gm)
+        outs = (torch.full_like(x, float("nan")), torch.full((1,), float("nan"), dtype=pdt, device="cuda"),
+                torch.full((N,), float("nan"), dtype=pdt, device="cuda"),
+                torch.full((N,), float("nan"), dtype=pdt, device="cuda"))
+        assert _noalloc_raw(dyt, x, dy, a, gm, *outs) == 0
+        torch.cuda.synchronize()
+        for name, r, o in zip(("dx", "dalpha", "dgamma", "dbeta"), ref, outs):
+            assert torch.equal(_bits(r), _bits(o)), f"{name} differs (call {k + 1}, M={M}, N={N})"
