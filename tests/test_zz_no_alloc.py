@@ -117,3 +117,33 @@ def test_noalloc_over_a_sequence_of_problems(dyt):
         torch.cuda.synchronize()
         for name, r, o in zip(("dx", "dalpha", "dgamma", "dbeta"), ref, outs):
             assert torch.equal(_bits(r), _bits(o)), f"{name} differs (call {k + 1}, M={M}, N={N})"
+
+
+@pytest.mark.parametrize("M,N,xdt", [(100003, 255, torch.float32), (1000, 4096, torch.bfloat16)])
+def test_noalloc_graph_replay_matches_eager(dyt, M, N, xdt):
+    """Callers that cannot allocate include code under HIP graph capture: the
+    allocation-free backward captured in a graph replays bit-identical to
+    dyt_backward, replay after replay, with eager work in between."""
+    log(f"[noalloc graph] M={M} N={N} x={xdt}")
+    x, dy, a, gm = _inputs(M, N, xdt, torch.float32, seed=77)
+    ref = dyt.dyt_backward(x, dy, a, gm)
+    torch.cuda.synchronize()
+    outs = (torch.empty_like(x), torch.empty(1, device="cuda"), torch.empty(N, device="cuda"),
+            torch.empty(N, device="cuda"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        assert _noalloc_raw(dyt, x, dy, a, gm, *outs) == 0
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert _noalloc_raw(dyt, x, dy, a, gm, *outs) == 0
+    for rep in range(4):
+        for t in outs:
+            t.fill_(-7.0)                     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, r, o in zip(("dx", "dalpha", "dgamma", "dbeta"), ref, outs):
+            assert torch.equal(_bits(r), _bits(o)), f"{name} differs (replay {rep})"
