@@ -19,14 +19,15 @@ def dyt():
 
 @pytest.mark.parametrize("xdt,pdt", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")])
 @pytest.mark.parametrize("shape", [(4, 129, 64), (3, 5, 4096), (1000, 17)])
-def test_module_forward_backward_matches_oracle(dyt, xdt, pdt, shape):
-    log(f"[module] shape={shape} x={xdt} p={pdt}")
+@pytest.mark.parametrize("alpha0", [0.7, -0.9])
+def test_module_forward_backward_matches_oracle(dyt, xdt, pdt, shape, alpha0):
+    log(f"[module] shape={shape} x={xdt} p={pdt} alpha={alpha0}")
     g = torch.Generator().manual_seed(sum(shape))
     N = shape[-1]
     x32 = torch.randn(shape, generator=g) * 1.5
     dy32 = torch.randn(shape, generator=g)
     xd, pd = TORCH_DT[xdt], TORCH_DT[pdt]
-    layer = dyt.DyT(N, alpha_init=0.7, dtype=pd, device="cuda")
+    layer = dyt.DyT(N, alpha_init=alpha0, dtype=pd, device="cuda")
     with torch.no_grad():
         layer.weight.copy_((1 + 0.1 * torch.randn(N, generator=g)).to(pd))
         layer.bias.copy_((0.1 * torch.randn(N, generator=g)).to(pd))
@@ -44,7 +45,7 @@ def test_module_forward_backward_matches_oracle(dyt, xdt, pdt, shape):
     f = dyt_oracle.forward(xs, a, gm, bt)
     r = dyt_oracle.backward(xs, dys, a, gm)
     t = lambda v: v.detach().float().cpu().numpy().astype(np.float64)
-    assert_reports(f"module {shape} {xdt}/{pdt}", [
+    assert_reports(f"module {shape} {xdt}/{pdt} alpha {alpha0}", [
         compare.check_y(t(y).reshape(-1, N), f.y, f.scale, xdt),
         compare.check_dx(t(x.grad).reshape(-1, N), r.dx, xdt),
         compare.check_grad(t(layer.weight.grad), r.dgamma, r.rss_dgamma, pdt, "dgamma"),
